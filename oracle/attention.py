@@ -1,0 +1,136 @@
+"""The plain definition of exact softmax attention, in float64, on the CPU.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): only the tests, the
+smoke check and the benchmark's CPU baseline may use this module.
+
+Per head, with Q, K in R^{N x d}, V in R^{N x dv} and softmax scale tau:
+
+    S = tau * Q K^T                          (N x N, materialized)
+    S_ij = -inf for j > i  under the causal mask
+    P = row-wise softmax(S), computed stably by subtracting the row max
+    O = P V,   LSE_i = m_i + ln(sum_j exp(S_ij - m_i))
+
+Sources, by page and section:
+  * definition S = tau Q K^T, P = softmax(S), O = P V and the causal mask
+    s_ij = -inf for j > i: "FlashAttention 원 논문 해부" (sj-techlog),
+    sections "원 논문의 정의" and "Q·K·V와 한 행의 의미";
+  * stable softmax (subtract the row max m; the value is unchanged): same page,
+    section "stable softmax는 overflow를 막는 필수 변형이다";
+  * LSE L = m + log(l), with P = exp(S - L) recovered from it in the backward:
+    "FlashAttention-2: Faster Attention with Better Parallelism and Work
+    Partitioning" (wonbeomjang.kr), section "개선 2: m과 l 대신 L만 저장".
+    "log" is read as the natural log, since P = exp(S - L) must hold.
+  * backward dV = P^T dO, dP = dO V^T, dS_ij = P_ij (dP_ij - D_i) with
+    D_i = sum_j P_ij dP_ij, dQ = dS K, dK = dS^T Q: the FlashAttention-2 page,
+    section "Standard Attention Implementation / Backward Pass".  That page
+    writes S = Q K^T without tau; with S = tau Q K^T the chain rule puts one
+    factor tau on dQ and dK (dV is unaffected), and the oracle includes it.
+    Finite-difference tests pin this reading.
+
+Fully masked rows (impossible under the square causal mask, but defined here
+so the functions are total): P row = 0, O row = 0, LSE = -inf, no gradient.
+
+Every array is converted to float64 on entry.  No blocking, fusion or
+reordering: each step is one numpy expression of the definition above.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def causal_visible(n_q: int, n_k: int) -> np.ndarray:
+    """Boolean [n_q, n_k]: key j is visible to query i iff j <= i."""
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    return j <= i
+
+
+def scores(q, k, scale: float, causal: bool) -> np.ndarray:
+    """S = scale * Q K^T for one head, with -inf where the causal mask hides a key."""
+    q, k = _f64(q), _f64(k)
+    s = float(scale) * (q @ k.T)
+    if causal:
+        s = np.where(causal_visible(q.shape[0], k.shape[0]), s, -np.inf)
+    return s
+
+
+def row_softmax(s) -> tuple[np.ndarray, np.ndarray]:
+    """Stable row softmax of S.  Returns (P, LSE) with LSE in natural-log units."""
+    s = _f64(s)
+    m = s.max(axis=1)                      # row maximum
+    has_key = np.isfinite(m)
+    m_ref = np.where(has_key, m, 0.0)      # reference point (0 for empty rows)
+    e = np.exp(s - m_ref[:, None])         # exp(-inf) = 0 for hidden keys
+    l = e.sum(axis=1)                      # normalizer
+    p = np.zeros_like(e)
+    np.divide(e, l[:, None], out=p, where=l[:, None] > 0)
+    lse = np.full(l.shape, -np.inf)
+    pos = l > 0
+    lse[pos] = m_ref[pos] + np.log(l[pos])
+    return p, lse
+
+
+def probabilities(q, k, scale: float, causal: bool) -> np.ndarray:
+    """P = softmax(scale * Q K^T + mask) for one head."""
+    p, _ = row_softmax(scores(q, k, scale, causal))
+    return p
+
+
+def forward_head(q, k, v, scale: float, causal: bool) -> tuple[np.ndarray, np.ndarray]:
+    """O = P V and LSE for one head (q: [N,d], k: [N,d], v: [N,dv])."""
+    p, lse = row_softmax(scores(q, k, scale, causal))
+    o = p @ _f64(v)
+    return o, lse
+
+
+def backward_head(q, k, v, do, scale: float, causal: bool) -> dict:
+    """Analytic gradients of sum(O * dO) for one head.
+
+    Returns dict(dq, dk, dv, D, p, dp, ds); D is computed as rowsum(P * dP).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    p, _ = row_softmax(scores(q, k, scale, causal))
+    dv = p.T @ do                          # dV = P^T dO
+    dp = do @ v.T                          # dP = dO V^T
+    D = (p * dp).sum(axis=1)               # D_i = sum_j P_ij dP_ij
+    ds = p * (dp - D[:, None])             # dS_ij = P_ij (dP_ij - D_i)
+    dq = float(scale) * (ds @ k)           # dQ = tau dS K
+    dk = float(scale) * (ds.T @ q)         # dK = tau dS^T Q
+    return {"dq": dq, "dk": dk, "dv": dv, "D": D, "p": p, "dp": dp, "ds": ds}
+
+
+def _heads(shape):
+    return np.ndindex(*shape[:-2])
+
+
+def forward(q, k, v, scale: float, causal: bool, heads=None):
+    """Batched forward over leading axes ([..., N, d]); returns (O, LSE).
+
+    ``heads`` optionally restricts the work to a list of leading-index tuples;
+    the other heads of the returned arrays are left as NaN.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead = q.shape[:-2]
+    o = np.full(lead + (q.shape[-2], v.shape[-1]), np.nan)
+    lse = np.full(lead + (q.shape[-2],), np.nan)
+    for idx in (heads if heads is not None else _heads(q.shape)):
+        o[idx], lse[idx] = forward_head(q[idx], k[idx], v[idx], scale, causal)
+    return o, lse
+
+
+def backward(q, k, v, do, scale: float, causal: bool, heads=None):
+    """Batched backward over leading axes; returns (dQ, dK, dV, D)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    lead = q.shape[:-2]
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    D = np.full(lead + (q.shape[-2],), np.nan)
+    for idx in (heads if heads is not None else _heads(q.shape)):
+        g = backward_head(q[idx], k[idx], v[idx], do[idx], scale, causal)
+        dq[idx], dk[idx], dv[idx], D[idx] = g["dq"], g["dk"], g["dv"], g["D"]
+    return dq, dk, dv, D

@@ -1,0 +1,227 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import pins
+
+
+def fwd(q, k, v, scale, causal):
+    return oracle.forward_head(q, k, v, scale, causal)
+
+
+def bwd(q, k, v, do, scale, causal):
+    g = oracle.backward_head(q, k, v, do, scale, causal)
+    return g["dq"], g["dk"], g["dv"]
+
+
+# ----------------------------------------------------------------- page values
+
+
+def test_page_causal_first_row():
+    pins.check_page_cpu_vectors(fwd)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block", [1, 2, 3])
+def test_page_tiled_recurrence_equals_standard(causal, block):
+    """The page checks tile widths 1, 2, 3, causal on and off, to 1e-12."""
+    g = pins.load_golden("cpu_check_vectors.json")
+    q, k, v = (np.array(g[n], dtype=np.float64) for n in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(3.0)
+    o_ref, lse_ref = oracle.forward_head(q, k, v, scale, causal)
+    o, lse, _ = oracle.online_forward_head(q, k, v, scale, causal, block)
+    assert np.max(np.abs(o - o_ref)) <= g["tiled_vs_standard_tolerance"]
+    assert np.max(np.abs(lse - lse_ref)) <= g["tiled_vs_standard_tolerance"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_page_printed_row_states(causal):
+    """Row 4 (0-based) with tile width 2 passes through the printed (m, l) states."""
+    g = pins.load_golden("cpu_check_vectors.json")
+    q, k, v = (np.array(g[n], dtype=np.float64) for n in ("q", "k", "v"))
+    _, _, states = oracle.online_forward_head(q, k, v, 1.0 / math.sqrt(3.0), causal, 2,
+                                              record_row=4)
+    printed = g["printed"]["row4_block2_states"]
+    half_ulp = 0.5 * 10.0 ** -g["printed"]["printed_decimals"]
+    assert len(states) == len(printed)
+    for (start, end, m, l), p in zip(states, printed):
+        assert (start, end) == (p["start"], p["end"])
+        assert abs(m - p["m"]) <= half_ulp + 1e-12
+        assert abs(l - p["l"]) <= half_ulp + 1e-12
+
+
+def test_page_merge_example():
+    g = pins.load_golden("merge_example.json")
+    st = g["state"]
+    r = oracle.merge_tile(st["m"], st["l"], [st["u"]], g["tile_scores"],
+                          np.array(g["tile_values"])[:, None])
+    p = g["printed"]
+    assert r["m_t"] == p["m_tile"] and r["m"] == p["m_new"] and r["b"] == p["b"]
+    for key, name in (("l_t", "l_tile"), ("a", "a"), ("l", "l_new")):
+        assert abs(float(np.ravel(r[key])[0]) - p[name]) <= 1e-4, key
+    assert abs(float(r["u_t"][0]) - p["u_tile"]) <= 1e-4
+    assert abs(float(r["u"][0]) - p["u_new"]) <= 1e-4
+    assert abs(float(r["o"][0]) - p["o_new"]) <= 5e-4
+
+
+def test_page_rescale_example():
+    g = pins.load_golden("rescale_example.json")
+    # A block whose maximum is 5 (its other score is far below, so it barely matters).
+    r = oracle.merge_tile(g["m_old"], g["l_old"], [0.0], [g["m_block"], -50.0], np.zeros((2, 1)))
+    p = g["printed"]
+    assert r["m"] == g["m_block"]
+    assert abs(r["a"] - p["factor"]) <= 5e-3 * p["factor"]
+    assert abs(r["a"] * g["l_old"] - p["l_old_rescaled"]) <= 5e-3 * p["l_old_rescaled"]
+
+
+def test_merge_equals_softmax_of_concatenation():
+    """Merging tile by tile from (m, l, u) = (-inf, 0, 0) is the softmax of the whole row."""
+    r = np.random.default_rng(11)
+    s = 4.0 * r.standard_normal(13)
+    v = r.standard_normal((13, 3))
+    state = {"m": -np.inf, "l": 0.0, "u": np.zeros(3)}
+    for a, b in ((0, 4), (4, 5), (5, 13)):
+        state = oracle.merge_tile(state["m"], state["l"], state["u"], s[a:b], v[a:b])
+    w = np.exp(s - s.max())
+    np.testing.assert_allclose(state["o"], (w / w.sum()) @ v, atol=1e-14)
+    np.testing.assert_allclose(state["m"] + math.log(state["l"]),
+                               s.max() + math.log(w.sum()), atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block", [1, 2, 3, 7, 16, 40])
+def test_recurrence_equals_definition(causal, block):
+    r = np.random.default_rng(12)
+    q, k, v = (3.0 * r.standard_normal((40, 8)) for _ in range(3))
+    o_ref, lse_ref = oracle.forward_head(q, k, v, 0.35, causal)
+    o, lse, _ = oracle.online_forward_head(q, k, v, 0.35, causal, block)
+    assert np.max(np.abs(o - o_ref)) <= 1e-12
+    assert np.max(np.abs(lse - lse_ref)) <= 1e-12
+
+
+# ----------------------------------------------------------------- closed forms
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_mean_of_values(causal):
+    pins.check_zero_query(fwd, causal=causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("jstar", [0, 3, 7])
+def test_dominant_score(causal, jstar):
+    pins.check_dominant_score(fwd, causal=causal, jstar=jstar)
+
+
+def test_dominant_score_selects_one_row():
+    """As the dominant score grows, O_i tends to v_{j*}."""
+    r = np.random.default_rng(13)
+    n, d = 6, 4
+    q = np.zeros((n, d))
+    q[:, 0] = 200.0
+    k = r.standard_normal((n, d))
+    k[:, 0] = 0.0
+    k[2] = np.eye(d)[0]
+    v = r.standard_normal((n, 2))
+    o, _ = oracle.forward_head(q, k, v, 1.0, False)
+    np.testing.assert_allclose(o, np.repeat(v[2:3], n, axis=0), atol=1e-12)
+
+
+def test_single_key():
+    pins.check_single_key(fwd, bwd)
+
+
+# ----------------------------------------------------------------- invariants
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows(causal):
+    """P >= 0, rows sum to 1, hidden keys get exactly 0."""
+    r = np.random.default_rng(14)
+    q, k = 2.0 * r.standard_normal((12, 5)), 2.0 * r.standard_normal((12, 5))
+    p = oracle.probabilities(q, k, 0.5, causal)
+    assert np.all(p >= 0)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    if causal:
+        assert np.all(p[~oracle.causal_visible(12, 12)] == 0.0)
+        assert np.all(p[oracle.causal_visible(12, 12)] > 0.0)
+
+
+def test_large_scores_do_not_overflow():
+    """Scores around 1e3 would overflow exp without the max subtraction."""
+    r = np.random.default_rng(15)
+    q, k, v = 40.0 * r.standard_normal((8, 4)), 40.0 * r.standard_normal((8, 4)), r.standard_normal((8, 3))
+    o, lse = oracle.forward_head(q, k, v, 1.0, False)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    o2, lse2 = oracle.forward_head(q, k + 7.0, v, 1.0, False)   # shift by a row constant
+    np.testing.assert_allclose(o2, o, atol=1e-10)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_invariance(causal):
+    pins.check_key_shift(fwd, bwd, causal=causal)
+
+
+def test_value_linearity():
+    pins.check_value_linearity(fwd)
+
+
+def test_fully_hidden_rows_are_zero():
+    """A row with no visible key (possible only with a non-causal mask pattern) is defined as
+    O = 0, LSE = -inf."""
+    s = np.array([[0.0, 1.0], [-np.inf, -np.inf]])
+    p, lse = oracle.row_softmax(s)
+    assert np.all(p[1] == 0.0) and lse[1] == -np.inf
+    np.testing.assert_allclose(p[0].sum(), 1.0)
+
+
+# ----------------------------------------------------------------- backward
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [2, 5, 16])
+def test_finite_differences(causal, n):
+    pins.check_finite_differences(fwd, bwd, n=n, causal=causal)
+
+
+def test_finite_differences_unit_scale_wide_values():
+    pins.check_finite_differences(fwd, bwd, n=7, d=3, dv=5, scale=1.0, causal=True, seed=21)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gradients(causal):
+    pins.check_zero_query_gradients(bwd, causal=causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_delta_identity(causal):
+    """D_i = rowsum(P * dP) equals rowsum(dO * O)."""
+    r = np.random.default_rng(16)
+    q, k, v, do = (r.standard_normal((11, 6)) for _ in range(4))
+    g = oracle.backward_head(q, k, v, do, 0.4, causal)
+    o, _ = oracle.forward_head(q, k, v, 0.4, causal)
+    np.testing.assert_allclose(g["D"], (do * o).sum(axis=1), atol=1e-13)
+    np.testing.assert_allclose(g["ds"].sum(axis=1), 0.0, atol=1e-13)
+
+
+def test_batched_wrappers_match_heads():
+    r = np.random.default_rng(17)
+    q, k, v, do = (r.standard_normal((2, 3, 9, 4)) for _ in range(4))
+    o, lse = oracle.forward(q, k, v, 0.5, True)
+    dq, dk, dv, D = oracle.backward(q, k, v, do, 0.5, True)
+    for b in range(2):
+        for h in range(3):
+            o1, l1 = oracle.forward_head(q[b, h], k[b, h], v[b, h], 0.5, True)
+            g = oracle.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], 0.5, True)
+            np.testing.assert_array_equal(o[b, h], o1)
+            np.testing.assert_array_equal(lse[b, h], l1)
+            np.testing.assert_array_equal(dq[b, h], g["dq"])
+            np.testing.assert_array_equal(dk[b, h], g["dk"])
+            np.testing.assert_array_equal(dv[b, h], g["dv"])
+            np.testing.assert_array_equal(D[b, h], g["D"])
+    o_s, _ = oracle.forward(q, k, v, 0.5, True, heads=[(1, 2)])
+    np.testing.assert_array_equal(o_s[1, 2], o[1, 2])
+    assert np.isnan(o_s[0, 0]).all()

@@ -1,0 +1,99 @@
+"""Seeded synthetic attention workloads, shared by the tests and the benchmark.
+
+This module only draws random numbers and rounds them to the storage dtype.
+It holds none of the attention arithmetic: the HIP library computes attention,
+and the fp64 oracle under ``oracle/`` recomputes it for checking.  Both sides
+receive the very same rounded tensors from here.
+
+Every workload is Q, K, V and an upstream gradient dO, each [B, H, N, d] and
+contiguous with d fastest, plus the softmax scale (1/sqrt(d)).  Draw order for
+one workload, from a CPU ``torch.Generator`` seeded with the workload's seed:
+[the per-head offset, only when ``offset`` is set], Q, K, V, dO, all as fp32
+standard normals.  Q and K are then multiplied by ``qk_std``; with ``offset``
+the per-head vector c[h] (one N(0,1)^d draw per head index, shared by every Q
+and K row of that head in every batch entry) is added to Q and K.  Finally all
+four tensors are rounded to the workload dtype (round to nearest even).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+_TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "f32" | "f16" | "bf16"
+    causal: bool
+    seed: int
+    qk_std: float = 1.0
+    offset: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPES[self.dtype]
+
+    def fwd_flops(self) -> float:
+        """Forward FLOPs counted as 4*B*H*N^2*d, halved under the causal mask."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        """Backward FLOPs counted as 2.5x the forward count."""
+        return 2.5 * self.fwd_flops()
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the method's measurement plan, named by what they are.
+SINGLE_HEAD_F32 = Workload("b1h1n128d64-f32", 1, 1, 128, 64, "f32", False, 1001)
+SHORT_F16 = Workload("b8h16n1024d64-f16", 8, 16, 1024, 64, "f16", False, 1002)
+CAUSAL_BF16 = Workload("b4h32n4096d128-bf16-causal", 4, 32, 4096, 128, "bf16", True, 1003)
+LONG_CAUSAL_F16 = Workload("b1h16n16384d64-f16-causal-qkstd2", 1, 16, 16384, 64, "f16",
+                           True, 1004, qk_std=2.0)
+PEAKED_BF16 = Workload("b2h32n8192d128-bf16-offset", 2, 32, 8192, 128, "bf16", False, 1005,
+                       offset=True)
+
+ALL = (SINGLE_HEAD_F32, SHORT_F16, CAUSAL_BF16, LONG_CAUSAL_F16, PEAKED_BF16)
+BY_NAME = {w.name: w for w in ALL}
+
+
+def make_inputs(w: Workload) -> dict:
+    """Return {"q","k","v","do"} as contiguous CPU tensors in the workload dtype."""
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    shape = (w.B, w.H, w.N, w.d)
+    c = torch.randn((w.H, w.d), generator=g, dtype=torch.float32) if w.offset else None
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    do = torch.randn(shape, generator=g, dtype=torch.float32)
+    if w.qk_std != 1.0:
+        q.mul_(w.qk_std)
+        k.mul_(w.qk_std)
+    if c is not None:
+        q.add_(c[None, :, None, :])
+        k.add_(c[None, :, None, :])
+    dt = w.torch_dtype
+    return {name: t.to(dt).contiguous() for name, t in (("q", q), ("k", k), ("v", v), ("do", do))}
+
+
+def make_random(shape, dtype: str, seed: int, std: float = 1.0) -> torch.Tensor:
+    """One seeded N(0, std^2) tensor rounded to ``dtype`` (for edge-case tests)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    t = torch.randn(shape, generator=g, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(_TORCH_DTYPES[dtype]).contiguous()
