@@ -1,0 +1,123 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
+ *
+ * What the library computes, per (batch b, head h), with Q, K, V, O in
+ * R^{N x d} and the softmax scale tau:
+ *
+ *     S = tau * Q K^T,   S_ij = -inf for j > i when causal,
+ *     P = row-wise softmax(S),   O = P V,   LSE_i = ln sum_j exp(S_ij).
+ *
+ * Definition and causal mask: "FlashAttention 원 논문 해부" (sj-techlog),
+ * sections "원 논문의 정의" and "Q·K·V와 한 행의 의미".  The forward is computed
+ * tile by tile with per-row online-softmax state (running max, normalizer,
+ * unnormalized accumulator) so that S and P never reach device memory:
+ * same page, section "두 tile을 한 row로 합치는 식", and "FlashAttention-2:
+ * Faster Attention with Better Parallelism and Work Partitioning"
+ * (wonbeomjang.kr), section "결과: FlashAttention-2 Forward 알고리즘".  The
+ * backward recomputes P from Q, K and the stored LSE (same FlashAttention-2
+ * page, sections "개선 2: m과 l 대신 L만 저장" and "Backward Pass").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors q, k, v, o, dout, dq, dk, dv: device pointers to contiguous
+ *    [B, H, N, d] arrays of `dtype` (d fastest), 16-byte aligned.
+ *  - lse: device pointer to a contiguous [B, H, N] float32 array, natural-log
+ *    units (LSE_i = m_i + ln l_i).
+ *  - causal != 0: key j is visible to query i iff j <= i (square, top-left
+ *    aligned).  Any N >= 1 is accepted; tiles past N are masked.
+ *  - scale: the softmax scale tau, used as given (callers usually pass
+ *    1/sqrt(d)).  Must be finite.
+ *  - Supported: dtype in {FA_F32, FA_F16, FA_BF16}, d in {64, 128}.
+ *  - stream: a hipStream_t passed as void* (NULL = the default stream).  All
+ *    work is enqueued asynchronously on it; no call synchronizes.
+ *  - Ownership: the caller allocates and owns every buffer, the backward
+ *    workspace included.  The library allocates no device or host memory and
+ *    keeps no state between calls beyond its loaded code objects and a
+ *    per-device "is this a gfx950" cache; calls are reentrant.  Inputs must
+ *    not alias outputs.
+ *  - Errors: a status code, never an exception.  Every argument check runs
+ *    before any HIP call; on an argument error nothing is launched and no
+ *    output is touched.  Checks: null pointers, B/H/N <= 0, element counts
+ *    that overflow 64 bits, non-finite scale (FA_ERR_INVALID_ARGUMENT);
+ *    unknown dtype or d outside {64, 128} (FA_ERR_UNSUPPORTED); workspace
+ *    too small or not 256-byte aligned (FA_ERR_WORKSPACE); the current HIP
+ *    device is not gfx950 or cannot be queried (FA_ERR_DEVICE); a launch
+ *    reported an error (FA_ERR_LAUNCH, outputs then undefined).
+ */
+#ifndef IO_AWARE_EXACT_FA_AMD_FA_H
+#define IO_AWARE_EXACT_FA_AMD_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_WORKSPACE = 3,
+  FA_ERR_DEVICE = 4,
+  FA_ERR_LAUNCH = 5
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_F32 = 0,  /* IEEE binary32 */
+  FA_F16 = 1,  /* IEEE binary16 */
+  FA_BF16 = 2  /* bfloat16 */
+} fa_dtype;
+
+/* Returns FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+/* Returns a static, NUL-terminated description of a status code. */
+const char* fa_status_string(fa_status status);
+
+/*
+ * Forward pass: o = softmax(scale * q k^T + mask) v and lse, for all B*H heads.
+ *
+ * Writes every element of o [B,H,N,d] (dtype, rounded to nearest even from
+ * the fp32 accumulator after the single division by the row normalizer) and
+ * lse [B,H,N] (float32, natural log).  Reads q, k, v.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float scale,
+                 fa_dtype dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this shape (0 if the shape is
+ * invalid).  Layout, from the workspace base (offsets rounded up to 256 B):
+ *   D      float32 [B,H,N]    D_i = rowsum(dO_i * O_i)
+ *   dQacc  float32 [B,H,N,d]  unscaled dQ accumulator (sum over key tiles)
+ * Both regions are fully rewritten by every fa_bwd call.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward pass: gradients of sum(O * dout) with respect to q, k, v.
+ *
+ * o and lse must be what fa_fwd wrote for the same q, k, v, causal and scale.
+ * Computes D = rowsum(dout * o), then per key tile recomputes P from q, k and
+ * lse and forms dS = P * (dP - D) with dP = dout v^T; dV = P^T dout,
+ * dK = scale * dS^T q, dQ = scale * dS k ("FlashAttention-2: Faster Attention
+ * with Better Parallelism and Work Partitioning", sections "Backward Pass";
+ * the factor scale follows from S = scale * q k^T by the chain rule).
+ * Writes every element of dq, dk, dv (dtype) and of the workspace.
+ * workspace must hold at least fa_bwd_workspace_size(B,H,N,d) bytes and be
+ * 256-byte aligned.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv,
+                 int B, int H, int N, int d, int causal, float scale,
+                 fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IO_AWARE_EXACT_FA_AMD_FA_H */

@@ -1,0 +1,181 @@
+"""Python binding of libfa.so, the gfx950 exact-attention library.
+
+Argument marshalling only: every step of the forward and backward runs in
+the library's HIP kernels.  PyTorch supplies device memory and the current
+stream.  If libfa.so is missing, importing the binding raises instead of
+falling back to anything else.
+
+Two layers:
+  * ``fa_fwd`` / ``fa_bwd`` / ``fa_bwd_workspace_size`` / ``fa_status_string``
+    / ``fa_abi_version``: the C entry points with the same names and the same
+    arguments (device pointers as Python ints, sizes, dtype code, stream
+    handle); they return the status code.
+  * ``forward`` / ``backward``: torch tensors in, torch tensors out; they
+    check shapes, allocate outputs (and the backward workspace) with torch
+    and raise ``FaError`` on a non-zero status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARGUMENT = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_WORKSPACE = 3
+FA_ERR_DEVICE = 4
+FA_ERR_LAUNCH = 5
+
+FA_F32 = 0
+FA_F16 = 1
+FA_BF16 = 2
+
+EXPORTED = ("fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m io_aware_exact_fa_amd._build` "
+            "(or __graft_entry__.build()) first")
+    # torch ships its own HIP runtime (same soname as the system one).  Load torch
+    # first so libfa.so binds to that runtime: device memory and streams come from
+    # torch, and two HIP runtimes in one process would not share them.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    _check_single_runtime()
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_abi_version.restype = i
+    lib.fa_abi_version.argtypes = []
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    return lib
+
+
+def _check_single_runtime() -> None:
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return
+    if len(paths) > 1:
+        raise ImportError(f"two HIP runtimes are loaded in this process: {sorted(paths)}")
+
+
+_lib = _load()
+
+
+# ------------------------------------------------------------------ C entry points
+
+
+def fa_abi_version() -> int:
+    return _lib.fa_abi_version()
+
+
+def fa_status_string(status: int) -> str:
+    return _lib.fa_status_string(int(status)).decode()
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> int:
+    return _lib.fa_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), int(dtype), stream)
+
+
+def fa_bwd_workspace_size(B, H, N, d) -> int:
+    return _lib.fa_bwd_workspace_size(B, H, N, d)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype,
+           workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
+                       int(dtype), workspace, workspace_bytes, stream)
+
+
+# ------------------------------------------------------------------ torch helpers
+
+
+def dtype_code(torch_dtype) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if torch_dtype not in codes:
+        raise TypeError(f"unsupported dtype {torch_dtype}")
+    return codes[torch_dtype]
+
+
+def _check(name, t, shape, dtype):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} cuda tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} "
+                         f"device={t.device}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
+    """O, LSE for [B, H, N, d] tensors q, k, v (all one dtype, on the GPU)."""
+    import torch
+    B, H, N, d = q.shape
+    _check("q", q, (B, H, N, d), q.dtype)
+    _check("k", k, (B, H, N, d), q.dtype)
+    _check("v", v, (B, H, N, d), q.dtype)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check("o", o, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                B, H, N, d, causal, scale, dtype_code(q.dtype), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+    return o, lse
+
+
+def workspace(B, H, N, d, device):
+    """A torch uint8 buffer big enough (and aligned) for fa_bwd at this shape."""
+    import torch
+    n = fa_bwd_workspace_size(B, H, N, d)
+    if n == 0:
+        raise FaError(FA_ERR_INVALID_ARGUMENT, "fa_bwd_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)   # caching allocator: 512 B aligned
+
+
+def backward(q, k, v, o, dout, lse, causal: bool, scale: float, dq=None, dk=None, dv=None,
+             ws=None, stream=None):
+    """dQ, dK, dV for the forward that produced o and lse."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    ws = workspace(B, H, N, d, q.device) if ws is None else ws
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal,
+                scale, dtype_code(q.dtype), ws.data_ptr(), ws.numel(), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,122 @@
+// C ABI of libfa.so: argument validation, device check, dispatch to the
+// kernel instances, no allocation, no synchronization.  The contract of every
+// entry point is documented in include/fa.h.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "fa.h"
+#include "fa_kernels.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxGridYZ = 65535;   // grid y (heads) and z (batch) limit
+constexpr int kMaxDevices = 64;
+constexpr int kMaxN = (1 << 30);                 // keeps tile index arithmetic in int
+constexpr uint64_t kMaxRows = (uint64_t)1 << 34;  // keeps 1-D row grids below 2^31 blocks
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// B*H*N*d without overflow; 0 if it does not fit comfortably in 63 bits.
+uint64_t elements(int B, int H, int N, int d) {
+  const unsigned __int128 n = (unsigned __int128)(uint64_t)B * (uint64_t)H * (uint64_t)N * (uint64_t)d;
+  if (n > ((unsigned __int128)1 << 62)) return 0;
+  return (uint64_t)n;
+}
+
+fa_status check_shape(int B, int H, int N, int d, float scale, fa_dtype dtype) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (elements(B, H, N, d) == 0) return FA_ERR_INVALID_ARGUMENT;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_UNSUPPORTED;
+  if (N > kMaxN) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)B * H * N > kMaxRows) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// 1 = gfx950, 2 = something else; 0 = not yet known.
+std::atomic<int> g_device_ok[kMaxDevices];
+
+fa_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int known = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (known == 1) return FA_OK;
+    if (known == 2) return FA_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_DEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FA_OK : FA_ERR_DEVICE;
+}
+
+fa::Dt to_dt(fa_dtype d) {
+  return d == FA_F32 ? fa::Dt::f32 : (d == FA_F16 ? fa::Dt::f16 : fa::Dt::bf16);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(fa_status status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported dtype, head dimension or size";
+    case FA_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case FA_ERR_DEVICE: return "current HIP device is not a gfx950 GPU";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, int causal, float scale, fa_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
+  fa_status st = check_shape(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, scale};
+  const hipError_t e = fa::launch_fwd(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  const uint64_t n = elements(B, H, N, d);
+  if (n == 0) return 0;
+  const uint64_t rows = (uint64_t)B * H * N;
+  return align_up(rows * sizeof(float)) + align_up(n * sizeof(float));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                 int causal, float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
+  fa_status st = check_shape(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+    return FA_ERR_WORKSPACE;
+  st = check_device();
+  if (st != FA_OK) return st;
+  const uint64_t rows = (uint64_t)B * H * N;
+  float* delta = static_cast<float*>(workspace);
+  float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * sizeof(float)));
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, dq_acc, B, H, N, scale};
+  const hipError_t e = fa::launch_bwd(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

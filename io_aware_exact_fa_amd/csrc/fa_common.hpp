@@ -1,0 +1,183 @@
+// Device helpers shared by the gfx950 attention kernels: MFMA fragments,
+// LDS operand loads (plain and transposing), wave64 half exchanges, exp2.
+//
+// Register layouts used throughout (CDNA4 MFMA, 64-lane wavefront; lane l,
+// col = l % 32, half h = l / 32):
+//   v_mfma_f32_32x32x16_{bf16,f16}: A operand A[col][8h + e], B operand
+//     B[8h + e][col] (e = 0..7); result element i (0..15) is
+//     C[8*(i/4) + 4h + i%4][col].
+//   v_mfma_f32_32x32x2_f32: the same with one k value per lane (k = h).
+// So a 32x32 result keeps one column per lane and spreads the rows over the
+// 16 result registers and the two lane halves.  A result tile can therefore
+// feed a later MFMA straight from registers whenever that MFMA contracts
+// over the tile's rows: the contraction index is free to be permuted, and
+// the "slot" order below is the one the result registers already have.
+//
+// Slot order of a transposed operand: for MFMA step u over a block of 32 rows
+// (16-bit types: u = 0..1, 16 rows per step; f32: u = 0..15, 2 rows per step),
+// lane (col, h) supplies, in slot t, row
+//     16-bit: 16u + 8(t/4) + 4h + t%4   (t = 0..7)
+//     f32:    8(u/4) + 4h + u%4
+// of the block, which is exactly result element i = 8u + t (16-bit) or
+// i = u (f32) of the same lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T> struct Mfma;
+
+template <> struct Mfma<__bf16> {
+  static constexpr int KPL = 8;      // k values per lane per MFMA
+  typedef bf16x8 frag;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<_Float16> {
+  static constexpr int KPL = 8;
+  typedef f16x8 frag;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KPL = 1;
+  typedef float frag;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Steps (MFMAs) needed to contract over a block of 32 rows.
+template <typename T> constexpr int steps32() { return 32 / (2 * Mfma<T>::KPL); }
+
+// ---------------------------------------------------------------- fragments
+
+// Plain operand: KPL consecutive elements starting at p (16-byte aligned for 16-bit types).
+template <typename T>
+__device__ inline typename Mfma<T>::frag load_frag(const T* p) {
+  return *reinterpret_cast<const typename Mfma<T>::frag*>(p);
+}
+
+// Transposed operand from a row-major LDS matrix M (row pitch `pitch`
+// elements): slot t of lane (col, h) gets M[rb + row(u, t, h)][cb + col], with
+// the slot order described at the top of this file.
+template <typename T>
+__device__ inline typename Mfma<T>::frag load_frag_tr(const T* M, int pitch, int rb, int u, int cb,
+                                                      int lane);
+
+template <>
+__device__ inline float load_frag_tr<float>(const float* M, int pitch, int rb, int u, int cb,
+                                            int lane) {
+  const int row = rb + 8 * (u >> 2) + 4 * (lane >> 5) + (u & 3);
+  return M[row * pitch + cb + (lane & 31)];
+}
+
+// 16-bit: two ds_read_b64_tr_b16.  Within each group of 16 lanes, lane 4a+e
+// receives element e of the 8-byte rows addressed by lanes a, a+4, a+8, a+12.
+// Each lane therefore addresses row rb + 16u + 8q + 4h + (lane%16)/4 at
+// column cb + 16((lane/16)%2) + 4(lane%4); read q yields slots 4q..4q+3.
+__device__ inline s16x8 load_tr16_pair(const void* M, int pitch, int rb, int u, int cb, int lane) {
+  const int row = rb + 16 * u + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int colx = cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const short* base = reinterpret_cast<const short*>(M) + row * pitch + colx;
+  s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+  s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * pitch));
+  return __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <>
+__device__ inline bf16x8 load_frag_tr<__bf16>(const __bf16* M, int pitch, int rb, int u, int cb,
+                                              int lane) {
+  return __builtin_bit_cast(bf16x8, load_tr16_pair(M, pitch, rb, u, cb, lane));
+}
+
+template <>
+__device__ inline f16x8 load_frag_tr<_Float16>(const _Float16* M, int pitch, int rb, int u, int cb,
+                                               int lane) {
+  return __builtin_bit_cast(f16x8, load_tr16_pair(M, pitch, rb, u, cb, lane));
+}
+
+// Pack result elements 8u..8u+7 (16-bit) or element u (f32) of a 32x32 result
+// tile into an operand fragment, rounding to T (nearest even).
+template <typename T>
+__device__ inline typename Mfma<T>::frag pack_frag(const f32x16& c, int u);
+
+template <>
+__device__ inline float pack_frag<float>(const f32x16& c, int u) { return c[u]; }
+
+template <>
+__device__ inline bf16x8 pack_frag<__bf16>(const f32x16& c, int u) {
+  bf16x8 r;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r[t] = (__bf16)c[8 * u + t];
+  return r;
+}
+
+template <>
+__device__ inline f16x8 pack_frag<_Float16>(const f32x16& c, int u) {
+  f16x8 r;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r[t] = (_Float16)c[8 * u + t];
+  return r;
+}
+
+// Negate every element of a fragment (exact).
+template <typename T>
+__device__ inline typename Mfma<T>::frag neg_frag(typename Mfma<T>::frag a) { return -a; }
+
+// ---------------------------------------------------------------- lane halves
+
+// Combine a value with the same lane of the other 32-lane half.
+__device__ inline float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- stores
+
+// Store 4 consecutive values (rounded to T) at p.
+template <typename T> __device__ inline void store4(T* p, float a, float b, float c, float d);
+
+template <> __device__ inline void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+template <> __device__ inline void store4<__bf16>(__bf16* p, float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+}
+
+template <>
+__device__ inline void store4<_Float16>(_Float16* p, float a, float b, float c, float d) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<f16x4*>(p) = f16x4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+}
+
+template <typename T> __device__ inline float to_f32(T x) { return (float)x; }
+
+}  // namespace fa

@@ -1,0 +1,42 @@
+// Host-side declarations of the kernel launchers (one per dtype x head dim x
+// causal instance).  Every launcher only enqueues work on `stream` and
+// returns hipGetLastError(); argument checks live in fa_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N;
+  float scale;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;   // [B,H,N]   workspace
+  float* dq_acc;  // [B,H,N,d] workspace
+  int B, H, N;
+  float scale;
+};
+
+enum class Dt { f32 = 0, f16 = 1, bf16 = 2 };
+
+hipError_t launch_fwd(Dt dt, int d, bool causal, const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s);
+
+}  // namespace fa

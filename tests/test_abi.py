@@ -1,0 +1,133 @@
+"""The C ABI: the library loads, exports what include/fa.h declares, and rejects bad
+arguments with the documented status before touching the GPU (CPU only)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import io_aware_exact_fa_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
+
+# Valid-looking (non-null) pointers: argument checks must fail before any of them is used.
+P = 0x1000
+
+
+def declared_functions():
+    names = []
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b(fa_[a-z0-9_]+)\s*\(",
+                            text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(fa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert fa.fa_abi_version() == 1
+    for st in range(6):
+        assert fa.fa_status_string(st) and fa.fa_status_string(st) != "unknown status"
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+def _fwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, causal=0, scale=0.125,
+                dtype=fa.FA_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd(**args)
+
+
+def _bwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, H=1, N=128, d=64,
+                causal=0, scale=0.125, dtype=fa.FA_BF16, workspace=0x10000,
+                workspace_bytes=fa.fa_bwd_workspace_size(1, 1, 128, 64), stream=None)
+    args.update(kw)
+    return fa.fa_bwd(**args)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse"])
+def test_fwd_null_pointer(name):
+    assert _fwd(**{name: None}) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(N=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(d=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=math.nan), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=math.inf), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(B=2**20, H=2**20, N=2**20, d=64), fa.FA_ERR_INVALID_ARGUMENT),   # > 2^62 elements
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=-1), fa.FA_ERR_UNSUPPORTED),
+    (dict(H=70000), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=2**30 + 1), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects(kw, status):
+    assert _fwd(**kw) == status
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"])
+def test_bwd_null_pointer(name):
+    assert _bwd(**{name: None}) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-5), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=math.nan), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=9), fa.FA_ERR_UNSUPPORTED),
+    (dict(workspace=None), fa.FA_ERR_WORKSPACE),
+    (dict(workspace_bytes=100), fa.FA_ERR_WORKSPACE),
+    (dict(workspace=0x10000 + 64), fa.FA_ERR_WORKSPACE),   # not 256-byte aligned
+])
+def test_bwd_rejects(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_workspace_size():
+    B, H, N, d = 2, 3, 100, 64
+    rows = B * H * N
+    up = lambda x: (x + 255) // 256 * 256
+    assert fa.fa_bwd_workspace_size(B, H, N, d) == up(4 * rows) + up(4 * rows * d)
+    assert fa.fa_bwd_workspace_size(0, 1, 1, 64) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, -3, 64) == 0
+
+
+def _has_gpu():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_has_gpu(), reason="would launch kernels on the bogus pointers")
+def test_valid_arguments_without_gpu_report_device_error():
+    assert _fwd() == fa.FA_ERR_DEVICE
+    assert _bwd() == fa.FA_ERR_DEVICE
+
+
+def test_binding_refuses_missing_library(tmp_path, monkeypatch):
+    """The binding raises on import when libfa.so is absent; it never falls back."""
+    import importlib.util
+    import shutil
+    pkg = tmp_path / "io_aware_exact_fa_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "io_aware_exact_fa_amd", "__init__.py"), pkg / "__init__.py")
+    spec = importlib.util.spec_from_file_location("fa_copy", pkg / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError):
+        spec.loader.exec_module(mod)

@@ -1,0 +1,262 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
+
+Tolerances: O max-abs 2e-3 (fp16) / 1e-2 (bf16); dQ, dK, dV max-abs error
+relative to the reference's max-abs 5e-3 (fp16) / 2e-2 (bf16).  fp32 has no
+stated tolerance; 1e-5 on O and 1e-4 on gradients is derived from fp32
+accumulation over at most a few thousand terms.  LSE: 1e-3 (16-bit), 1e-4 (fp32).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import pins
+
+pytestmark = pytest.mark.gpu
+
+TOL = {
+    "f32": dict(o=1e-5, lse=1e-4, grad=1e-4),
+    "f16": dict(o=2e-3, lse=1e-3, grad=5e-3),
+    "bf16": dict(o=1e-2, lse=1e-3, grad=2e-2),
+}
+TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import io_aware_exact_fa_amd
+    return io_aware_exact_fa_amd
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_run(fa, inp, causal, scale, backward=True):
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, causal, scale)
+    out = {"o": o, "lse": lse}
+    if backward:
+        ws = fa.workspace(*q.shape, dev)
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal, scale, ws=ws)
+        out.update(dq=dq, dk=dk, dv=dv, ws=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def rel_err(got, ref):
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def compare(out, inp, causal, scale, dtype, heads=None, backward=True, tag=""):
+    """Compare GPU outputs with the oracle on the given (b, h) heads (all if None)."""
+    tol = TOL[dtype]
+    q, k, v, do = (f64(inp[n]) for n in ("q", "k", "v", "do"))
+    B, H = q.shape[:2]
+    heads = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    o_ref, lse_ref = oracle.forward(q, k, v, scale, causal, heads=heads)
+    sel = tuple(np.array(x) for x in zip(*heads))
+    o_gpu, lse_gpu = f64(out["o"])[sel], f64(out["lse"])[sel]
+    err_o = float(np.max(np.abs(o_gpu - o_ref[sel])))
+    err_l = float(np.max(np.abs(lse_gpu - lse_ref[sel])))
+    say(f"  {tag} O max-abs {err_o:.3e} (tol {tol['o']}), LSE max-abs {err_l:.3e}")
+    assert err_o <= tol["o"], f"O error {err_o}"
+    assert err_l <= tol["lse"], f"LSE error {err_l}"
+    if not backward:
+        return
+    dq_ref, dk_ref, dv_ref, D_ref = oracle.backward(q, k, v, do, scale, causal, heads=heads)
+    for name, ref in (("dq", dq_ref), ("dk", dk_ref), ("dv", dv_ref)):
+        e = rel_err(f64(out[name])[sel], ref[sel])
+        say(f"  {tag} {name} rel-to-max {e:.3e} (tol {tol['grad']})")
+        assert e <= tol["grad"], f"{name} error {e}"
+
+
+# ------------------------------------------------------------------ small seeded grid
+
+
+def grid_cases():
+    for dtype in ("bf16", "f16", "f32"):
+        for d in (64, 128):
+            for causal in (False, True):
+                for n in (1, 17, 128, 129, 300):
+                    yield dtype, d, causal, n
+
+
+@pytest.mark.parametrize("dtype,d,causal,n", list(grid_cases()))
+def test_small_shapes(fa, dtype, d, causal, n):
+    w = workloads.Workload(f"grid-{dtype}-d{d}-n{n}", 2, 2, n, d, dtype, causal, seed=7 + n + d)
+    inp = workloads.make_inputs(w)
+    say(f"case {w.name} causal={causal}")
+    out = gpu_run(fa, inp, causal, w.scale)
+    compare(out, inp, causal, w.scale, dtype, tag=w.name)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_several_tiles_with_ragged_tail(fa, dtype, causal):
+    """N = 520: eight 64-key tiles plus a tail of 8 keys; five query tiles forward,
+    five key tiles backward, with a ragged last tile."""
+    w = workloads.Workload("ragged-520", 1, 3, 520, 128, dtype, causal, seed=31, qk_std=1.5)
+    inp = workloads.make_inputs(w)
+    say(f"case {w.name} {dtype} causal={causal}")
+    compare(gpu_run(fa, inp, causal, w.scale), inp, causal, w.scale, dtype, tag=w.name)
+
+
+# ------------------------------------------------------------------ page vectors
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_page_vectors_zero_padded(fa, dtype, causal):
+    """The page's 5x3 / 5x2 integer vectors, zero-padded to d = 64 (zeros leave the dot
+    products unchanged), scale 1/sqrt(3); all values are exact in every dtype."""
+    g = pins.load_golden("cpu_check_vectors.json")
+    qkv = {}
+    for n in ("q", "k", "v"):
+        a = np.array(g[n], dtype=np.float32)
+        pad = np.zeros((5, 64), dtype=np.float32)
+        pad[:, : a.shape[1]] = a
+        qkv[n] = torch.from_numpy(pad)[None, None].to(TORCH[dtype]).contiguous()
+    qkv["do"] = workloads.make_random((1, 1, 5, 64), dtype, seed=5)
+    scale = 1.0 / math.sqrt(3.0)
+    say(f"case page-vectors {dtype} causal={causal}")
+    out = gpu_run(fa, qkv, causal, scale)
+    compare(out, qkv, causal, scale, dtype, tag="page")
+    if causal:
+        o = f64(out["o"])[0, 0]
+        np.testing.assert_allclose(o[0, :2], g["printed"]["causal_row0_output"], atol=TOL[dtype]["o"])
+
+
+# ------------------------------------------------------------------ closed forms / invariants
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gives_prefix_mean(fa, dtype, causal):
+    w = workloads.Workload("zeroq", 1, 2, 200, 64, dtype, causal, seed=41)
+    inp = workloads.make_inputs(w)
+    inp["q"] = torch.zeros_like(inp["q"])
+    out = gpu_run(fa, inp, causal, w.scale, backward=False)
+    v = f64(inp["v"])
+    n = np.arange(1, 201)[:, None] if causal else 200
+    expect = (np.cumsum(v, axis=2) / n) if causal else np.repeat(v.mean(axis=2, keepdims=True), 200, 2)
+    assert np.max(np.abs(f64(out["o"]) - expect)) <= TOL[dtype]["o"]
+    lse_expect = np.log(np.arange(1, 201)) if causal else np.full(200, math.log(200))
+    assert np.max(np.abs(f64(out["lse"]) - lse_expect)) <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_key_shift_invariance(fa, dtype):
+    """K + 1 c^T shifts row i of the scores by scale q_i.c: O and the gradients stay put
+    (to tolerance), LSE moves by exactly that amount."""
+    w = workloads.Workload("shift", 1, 2, 150, 64, dtype, False, seed=43)
+    inp = workloads.make_inputs(w)
+    c = torch.zeros(64)
+    c[:8] = 1.0                               # exact in every dtype
+    inp2 = dict(inp)
+    inp2["k"] = (inp["k"].float() + c).to(TORCH[dtype])
+    a, b = gpu_run(fa, inp, False, w.scale), gpu_run(fa, inp2, False, w.scale)
+    # Compare each against the oracle of its own inputs, and LSE shift directly.
+    compare(a, inp, False, w.scale, dtype, tag="shift-a")
+    compare(b, inp2, False, w.scale, dtype, tag="shift-b")
+    # the shifted keys are exact in dtype only where k + c rounds exactly; use the oracle's shift
+    q = f64(inp["q"])
+    shift = w.scale * (q @ c.double().numpy())
+    dl = f64(b["lse"]) - f64(a["lse"])
+    k_exact = torch.equal(inp2["k"].float(), inp["k"].float() + c)
+    if k_exact:
+        assert np.max(np.abs(dl - shift)) <= 2e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scale_sign_and_zero(fa, dtype):
+    for scale in (-0.2, 0.0, 0.9):
+        w = workloads.Workload("scale", 1, 2, 100, 64, dtype, True, seed=47)
+        inp = workloads.make_inputs(w)
+        say(f"case scale={scale} {dtype}")
+        compare(gpu_run(fa, inp, True, scale), inp, True, scale, dtype, tag=f"scale{scale}")
+
+
+def test_peaked_rows_stress_rescaling(fa):
+    """Scores with std ~8 make the running max jump between tiles."""
+    w = workloads.Workload("peaked", 1, 2, 400, 64, "f16", True, seed=53, qk_std=2.8)
+    inp = workloads.make_inputs(w)
+    compare(gpu_run(fa, inp, True, w.scale), inp, True, w.scale, "f16", tag="peaked")
+
+
+# ------------------------------------------------------------------ repeatability, workspace
+
+
+def test_repeatable_and_delta(fa):
+    w = workloads.Workload("repeat", 2, 2, 333, 128, "bf16", True, seed=59)
+    inp = workloads.make_inputs(w)
+    a = gpu_run(fa, inp, True, w.scale)
+    b = gpu_run(fa, inp, True, w.scale)
+    for name in ("o", "lse", "dk", "dv"):
+        assert torch.equal(a[name], b[name]), f"{name} differs between runs"
+    # D = rowsum(dO * O) sits at the start of the workspace.
+    rows = 2 * 2 * 333
+    D = a["ws"][: 4 * rows].view(torch.float32).reshape(2, 2, 333)
+    expect = (f64(inp["do"]) * f64(a["o"])).sum(-1)
+    assert np.max(np.abs(f64(D) - expect)) <= 1e-4
+
+
+def test_non_default_stream(fa):
+    w = workloads.Workload("stream", 1, 2, 256, 64, "f16", False, seed=61)
+    inp = workloads.make_inputs(w)
+    s = torch.cuda.Stream()
+    dev = torch.device("cuda:0")
+    with torch.cuda.stream(s):
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+        o, lse = fa.forward(q, k, v, False, w.scale, stream=s)
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, False, w.scale, stream=s)
+    s.synchronize()
+    compare(dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv), inp, False, w.scale, "f16", tag="stream")
+
+
+# ------------------------------------------------------------------ the five workloads
+
+
+@pytest.mark.parametrize("w", [workloads.SINGLE_HEAD_F32, workloads.SHORT_F16], ids=lambda w: w.name)
+def test_small_workloads_full(fa, w):
+    inp = workloads.make_inputs(w)
+    say(f"case {w.name} (every head)")
+    compare(gpu_run(fa, inp, w.causal, w.scale), inp, w.causal, w.scale, w.dtype, tag=w.name)
+
+
+LARGE = [workloads.CAUSAL_BF16, workloads.LONG_CAUSAL_F16, workloads.PEAKED_BF16]
+
+
+@pytest.mark.parametrize("w", LARGE, ids=lambda w: w.name)
+def test_large_workloads_sampled_heads(fa, w):
+    """Full-size launch (the configuration the benchmark times); the oracle checks the
+    last head exactly, and properties that hold for every head are checked on all."""
+    inp = workloads.make_inputs(w)
+    say(f"case {w.name} full size")
+    out = gpu_run(fa, inp, w.causal, w.scale)
+    heads = [(w.B - 1, w.H - 1)]
+    compare(out, inp, w.causal, w.scale, w.dtype, heads=heads, tag=w.name)
+    # Every head: sum_j dV_j = sum_i dO_i (rows of P sum to 1) and sum_j dK_j = 0
+    # (rows of dS sum to 0), both in fp64 over the GPU's outputs.
+    dv = out["dv"].double().sum(dim=2)
+    do = inp["do"].to("cuda").double().sum(dim=2)
+    dk = out["dk"].double().sum(dim=2)
+    scale_dv = out["dv"].double().abs().sum(dim=2).max().item()
+    scale_dk = out["dk"].double().abs().sum(dim=2).max().item()
+    tol = 4 * TOL[w.dtype]["grad"]
+    assert (dv - do).abs().max().item() <= tol * scale_dv
+    assert dk.abs().max().item() <= tol * scale_dk
+    assert torch.isfinite(out["lse"]).all() and torch.isfinite(out["o"]).all()
