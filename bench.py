@@ -1,0 +1,257 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = the whole path over one batch of seeded synthetic inputs already
+resident in HBM: fa_fwd, then fa_bwd_preprocess, fa_bwd_main and
+fa_bwd_finalize (the three steps of fa_bwd), all through the C ABI on one
+stream.  Throughput is counted with the method's FLOP formula: forward
+4*B*H*N^2*d (halved under the causal mask), backward 2.5x the forward.
+
+Prints ONE JSON line.  Besides the step throughput it reports:
+  * per-kernel times from HIP events recorded on the launch stream around
+    every launch inside the timed region;
+  * "roofline" for the dominant kernel (the backward main kernel) against the
+    dense MFMA peak of the workload's dtype, with HBM traffic from committed
+    rocprofv3 counter runs when they were taken on the current kernel source;
+  * "cpu_baseline": the fp64 CPU oracle timed on a bounded sample (one head)
+    of the same workload, plus the GPU-vs-oracle error on that head.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--mode step|copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+DEFAULT_WORKLOAD = workloads.PEAKED_BF16.name
+METRIC = "attention fwd/bwd TFLOPS on 1 MI355X and % of bf16 MFMA peak"
+# Published dense MFMA peaks of MI355X (TFLOP/s): bf16/fp16 2.5 PFLOP/s
+# (2516.6 = 256 CUs x 4096 flop/clk x 2.4 GHz), fp32 157.3.
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+DOMINANT = "bwd_kernel"
+KERNEL_SOURCES = ("io_aware_exact_fa_amd/csrc/fa_bwd.hip", "io_aware_exact_fa_amd/csrc/fa_common.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="step", choices=["step", "copy"])
+    return ap.parse_args()
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name: str):
+    """HBM bytes per launch of the dominant kernel from committed counter runs, if they
+    were taken on the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(DOMINANT, {}).get(workload_name)
+    if not e or e.get("source_sha") != source_sha():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(steps: int):
+    """A plain 1 GiB device-to-device copy, for scaling the HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(max(steps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": max(steps, 1)}))
+
+
+def cpu_baseline(w, inp, gpu_out, budget_s: float = 10.0):
+    """Time the fp64 oracle, forward then backward, on whole heads taken from the last
+    one backwards until about ``budget_s`` seconds of CPU work (at least one head)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:   # threadpoolctl missing: report the process's CPU affinity
+        cores = len(os.sched_getaffinity(0))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][::-1]
+    f64 = lambda t, b, h: t[b, h].to(dtype=torch.float64).numpy()
+    rel = lambda a, r: float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-30))
+    secs, done, check = 0.0, 0, None
+    for b, h in heads:
+        q, k, v, do = (f64(inp[n], b, h) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        o, lse = oracle.forward_head(q, k, v, w.scale, w.causal)
+        g = oracle.backward_head(q, k, v, do, w.scale, w.causal)
+        secs += time.perf_counter() - t0
+        done += 1
+        if check is None:   # GPU-vs-oracle error on the first sampled head
+            g64 = {n: gpu_out[n][b, h].double().numpy() for n in ("o", "lse", "dq", "dk", "dv")}
+            check = {
+                "head": [b, h],
+                "o_maxabs": float(np.max(np.abs(g64["o"] - o))),
+                "lse_maxabs": float(np.max(np.abs(g64["lse"] - lse))),
+                "dq_rel": rel(g64["dq"], g["dq"]),
+                "dk_rel": rel(g64["dk"], g["dk"]),
+                "dv_rel": rel(g64["dv"], g["dv"]),
+            }
+        if secs >= budget_s:
+            break
+    head_flops = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H)
+    return {
+        "value": head_flops * done / secs / 1e12,
+        "unit": "TFLOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.H} heads (the last ones), forward + backward each, fp64 "
+                  f"numpy oracle with S and P materialized; {secs:.2f} s wall",
+        "seconds": round(secs, 3),
+        "parity_on_sample": check,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "every workload here is one GPU's share, see the sharding paragraph of the design "
+              "notes", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import io_aware_exact_fa_amd as fa
+
+    if args.mode == "copy":
+        copy_calibration(args.steps)
+        return
+
+    w = workloads.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    inp = workloads.make_inputs(w)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = fa.workspace(B, H, N, d, dev)
+    code = fa.dtype_code(q.dtype)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    P = lambda t: t.data_ptr()
+
+    def check(st, where):
+        if st != fa.FA_OK:
+            raise fa.FaError(st, where)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        check(fa.fa_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, N, d, w.causal, w.scale, code, sh), "fwd")
+        if ev is not None:
+            ev[1].record(stream)
+        check(fa.fa_bwd_preprocess(P(o), P(do), B, H, N, d, code, P(ws), ws.numel(), sh), "pre")
+        if ev is not None:
+            ev[2].record(stream)
+        check(fa.fa_bwd_main(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, N, d, w.causal,
+                             w.scale, code, P(ws), ws.numel(), sh), "main")
+        if ev is not None:
+            ev[3].record(stream)
+        check(fa.fa_bwd_finalize(P(dq), B, H, N, d, w.scale, code, P(ws), ws.numel(), sh), "fin")
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = lambda a, b_: sum(e[a].elapsed_time(e[b_]) for e in events) / args.steps
+    fwd_ms, pre_ms, main_ms, fin_ms = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4)
+    bwd_ms = pre_ms + main_ms + fin_ms
+    ms_per_step = wall * 1e3 / args.steps
+    fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
+    peak = PEAK_TFLOPS[w.dtype]
+    value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = fwd_f / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
+    main_tf = bwd_f / (main_ms * 1e-3) / 1e12
+
+    traffic = load_traffic(w.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal Q/K/V/dO of the workload's shape and distribution)",
+        "config": {
+            "workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+            "step": "fa_fwd + fa_bwd (preprocess, main, finalize)",
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "bwd_pre_ms": round(pre_ms, 4), "bwd_main_ms": round(main_ms, 4),
+            "bwd_finalize_ms": round(fin_ms, 4),
+            "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
+            "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),
+            "bwd_pct_of_peak": round(100 * bwd_tf / peak, 2),
+            "step_pct_of_peak": round(100 * value / peak, 2),
+            "peak_tflops": peak,
+        },
+        "roofline": {
+            "kernel": DOMINANT,
+            "bound": "mfma",
+            "achieved": round(main_tf, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(main_tf / peak, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        gpu_out = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+        out["cpu_baseline"] = cpu_baseline(w, inp, gpu_out)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

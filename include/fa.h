@@ -39,7 +39,8 @@
  *    before any HIP call; on an argument error nothing is launched and no
  *    output is touched.  Checks: null pointers, B/H/N <= 0, element counts
  *    that overflow 64 bits, non-finite scale (FA_ERR_INVALID_ARGUMENT);
- *    unknown dtype or d outside {64, 128} (FA_ERR_UNSUPPORTED); workspace
+ *    unknown dtype, d outside {64, 128}, B or H above 65535, N above 2^30 or
+ *    B*H*N above 2^34 (FA_ERR_UNSUPPORTED); workspace
  *    too small or not 256-byte aligned (FA_ERR_WORKSPACE); the current HIP
  *    device is not gfx950 or cannot be queried (FA_ERR_DEVICE); a launch
  *    reported an error (FA_ERR_LAUNCH, outputs then undefined).
@@ -100,14 +101,9 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * Backward pass: gradients of sum(O * dout) with respect to q, k, v.
  *
  * o and lse must be what fa_fwd wrote for the same q, k, v, causal and scale.
- * Computes D = rowsum(dout * o), then per key tile recomputes P from q, k and
- * lse and forms dS = P * (dP - D) with dP = dout v^T; dV = P^T dout,
- * dK = scale * dS^T q, dQ = scale * dS k ("FlashAttention-2: Faster Attention
- * with Better Parallelism and Work Partitioning", sections "Backward Pass";
- * the factor scale follows from S = scale * q k^T by the chain rule).
- * Writes every element of dq, dk, dv (dtype) and of the workspace.
- * workspace must hold at least fa_bwd_workspace_size(B,H,N,d) bytes and be
- * 256-byte aligned.
+ * Equivalent to fa_bwd_preprocess, fa_bwd_main and fa_bwd_finalize enqueued
+ * in that order on `stream` with the same arguments.  Writes every element
+ * of dq, dk, dv (dtype) and of the workspace.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse,
@@ -115,6 +111,41 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  int B, int H, int N, int d, int causal, float scale,
                  fa_dtype dtype, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/*
+ * Backward step 1: D_i = rowsum(dout_i * o_i) in float32 into the workspace's
+ * D region, and zero its dQacc region.  D is the row term of the softmax
+ * gradient, precomputed from O instead of from P and dP ("FlashAttention-2:
+ * Faster Attention with Better Parallelism and Work Partitioning", sections
+ * "Standard Attention Implementation / Backward Pass" and "Backward Pass").
+ */
+fa_status fa_bwd_preprocess(const void* o, const void* dout,
+                            int B, int H, int N, int d, fa_dtype dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward step 2 (the main kernel): for every key tile, recompute
+ * P = exp(scale q k^T - lse) per query tile, form dP = dout v^T and
+ * dS = P * (dP - D), write dk = scale * dS^T q and dv = P^T dout, and add
+ * dS k (unscaled) into the workspace's dQacc with float32 atomics (same
+ * FlashAttention-2 page, sections "Backward Pass" and "Parallelism: 시퀀스 길이
+ * 차원 병렬화"; the factor scale follows from S = scale q k^T by the chain
+ * rule).  Needs the workspace as left by fa_bwd_preprocess.  The order of
+ * the atomic additions is not fixed, so dQacc (and dq) may differ in the
+ * last bits between runs; dk and dv are bitwise repeatable.
+ */
+fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dk, void* dv,
+                      int B, int H, int N, int d, int causal, float scale,
+                      fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * Backward step 3: dq = scale * dQacc, rounded to dtype (nearest even).
+ */
+fa_status fa_bwd_finalize(void* dq, int B, int H, int N, int d, float scale,
+                          fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 #ifdef __cplusplus
 }

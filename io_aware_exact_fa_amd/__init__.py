@@ -33,7 +33,8 @@ FA_F32 = 0
 FA_F16 = 1
 FA_BF16 = 2
 
-EXPORTED = ("fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd")
+EXPORTED = ("fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
+            "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_finalize")
 
 
 class FaError(RuntimeError):
@@ -64,6 +65,12 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_preprocess.restype = i
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_main.restype = i
+    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_finalize.restype = i
+    lib.fa_bwd_finalize.argtypes = [vp, i, i, i, i, f, i, vp, sz, vp]
     return lib
 
 
@@ -103,6 +110,21 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype,
            workspace, workspace_bytes, stream) -> int:
     return _lib.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
                        int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_bwd_preprocess(o, dout, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_preprocess(o, dout, B, H, N, d, int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_bwd_main(q, k, v, dout, lse, dk, dv, B, H, N, d, causal, scale, dtype,
+                workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_main(q, k, v, dout, lse, dk, dv, B, H, N, d, int(causal), float(scale),
+                            int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_bwd_finalize(dq, B, H, N, d, scale, dtype, workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_finalize(dq, B, H, N, d, float(scale), int(dtype), workspace,
+                                workspace_bytes, stream)
 
 
 # ------------------------------------------------------------------ torch helpers

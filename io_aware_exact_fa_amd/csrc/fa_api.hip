@@ -61,6 +61,12 @@ fa::Dt to_dt(fa_dtype d) {
   return d == FA_F32 ? fa::Dt::f32 : (d == FA_F16 ? fa::Dt::f16 : fa::Dt::bf16);
 }
 
+fa_status launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+// Shared checks of the backward entry points, then the workspace split.
+fa_status bwd_setup(int B, int H, int N, int d, float scale, fa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, fa::BwdArgs* a);
+
 }  // namespace
 
 extern "C" {
@@ -87,8 +93,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   st = check_device();
   if (st != FA_OK) return st;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, scale};
-  const hipError_t e = fa::launch_fwd(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return launched(fa::launch_fwd(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream));
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
@@ -99,11 +104,77 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   return align_up(rows * sizeof(float)) + align_up(n * sizeof(float));
 }
 
+fa_status fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
+                            fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!o || !dout) return FA_ERR_INVALID_ARGUMENT;
+  fa::BwdArgs a{};
+  fa_status st = bwd_setup(B, H, N, d, 1.0f, dtype, workspace, workspace_bytes, &a);
+  if (st != FA_OK) return st;
+  a.o = o;
+  a.dout = dout;
+  return launched(fa::launch_bwd_pre(to_dt(dtype), d, a, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                      float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!q || !k || !v || !dout || !lse || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
+  fa::BwdArgs a{};
+  fa_status st = bwd_setup(B, H, N, d, scale, dtype, workspace, workspace_bytes, &a);
+  if (st != FA_OK) return st;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dk = dk;
+  a.dv = dv;
+  return launched(fa::launch_bwd_main(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_finalize(void* dq, int B, int H, int N, int d, float scale, fa_dtype dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dq) return FA_ERR_INVALID_ARGUMENT;
+  fa::BwdArgs a{};
+  fa_status st = bwd_setup(B, H, N, d, scale, dtype, workspace, workspace_bytes, &a);
+  if (st != FA_OK) return st;
+  a.dq = dq;
+  return launched(fa::launch_bwd_fin(to_dt(dtype), d, a, (hipStream_t)stream));
+}
+
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                  int causal, float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                  void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
+  fa::BwdArgs a{};
+  fa_status st = bwd_setup(B, H, N, d, scale, dtype, workspace, workspace_bytes, &a);
+  if (st != FA_OK) return st;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const fa::Dt dt = to_dt(dtype);
+  hipStream_t s = (hipStream_t)stream;
+  st = launched(fa::launch_bwd_pre(dt, d, a, s));
+  if (st != FA_OK) return st;
+  st = launched(fa::launch_bwd_main(dt, d, causal != 0, a, s));
+  if (st != FA_OK) return st;
+  return launched(fa::launch_bwd_fin(dt, d, a, s));
+}
+
+}  // extern "C"
+
+namespace {
+
+fa_status bwd_setup(int B, int H, int N, int d, float scale, fa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, fa::BwdArgs* a) {
   fa_status st = check_shape(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
   const size_t need = fa_bwd_workspace_size(B, H, N, d);
@@ -112,11 +183,13 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   st = check_device();
   if (st != FA_OK) return st;
   const uint64_t rows = (uint64_t)B * H * N;
-  float* delta = static_cast<float*>(workspace);
-  float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * sizeof(float)));
-  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, dq_acc, B, H, N, scale};
-  const hipError_t e = fa::launch_bwd(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  a->delta = static_cast<float*>(workspace);
+  a->dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * sizeof(float)));
+  a->B = B;
+  a->H = H;
+  a->N = N;
+  a->scale = scale;
+  return FA_OK;
 }
 
-}  // extern "C"
+}  // namespace

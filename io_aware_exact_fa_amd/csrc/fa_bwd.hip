@@ -273,42 +273,56 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, long n4) {
 
 // ------------------------------------------------------------------ launchers
 
+enum class Step { pre, main, fin };
+
 template <typename T, int D, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+static hipError_t launch_bwd_t(Step step, const BwdArgs& a, hipStream_t s) {
   using C = BwdTile<T, D>;
-  constexpr int LPR = D / (16 / sizeof(T));
   const long rows = (long)a.B * a.H * a.N;
-  const long pre_blocks = (rows + (256 / LPR) - 1) / (256 / LPR);
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)pre_blocks), dim3(256), 0, s, a, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 grid((a.N + C::BKC - 1) / C::BKC, a.H, a.B);
-  hipLaunchKernelGGL((bwd_kernel<T, D, CAUSAL>), grid, dim3(C::NT), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long n4 = rows * D / 4;
-  const long dq_blocks = n4 / 256 < 8192 ? (n4 + 255) / 256 : 8192;
-  hipLaunchKernelGGL((bwd_dq_kernel<T>), dim3((unsigned)dq_blocks), dim3(256), 0, s, a, n4);
+  if (step == Step::pre) {
+    constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
+    const long blocks = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a, rows);
+  } else if (step == Step::main) {
+    dim3 grid((a.N + C::BKC - 1) / C::BKC, a.H, a.B);
+    hipLaunchKernelGGL((bwd_kernel<T, D, CAUSAL>), grid, dim3(C::NT), 0, s, a);
+  } else {
+    const long n4 = rows * D / 4;
+    const long blocks = n4 / 256 < 8192 ? (n4 + 255) / 256 : 8192;
+    hipLaunchKernelGGL((bwd_dq_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, s, a, n4);
+  }
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_bwd_c(bool causal, const BwdArgs& a, hipStream_t s) {
-  return causal ? launch_bwd_t<T, D, true>(a, s) : launch_bwd_t<T, D, false>(a, s);
+static hipError_t launch_bwd_c(Step st, bool causal, const BwdArgs& a, hipStream_t s) {
+  return causal ? launch_bwd_t<T, D, true>(st, a, s) : launch_bwd_t<T, D, false>(st, a, s);
 }
 
 template <typename T>
-static hipError_t launch_bwd_d(int d, bool causal, const BwdArgs& a, hipStream_t s) {
-  return d == 64 ? launch_bwd_c<T, 64>(causal, a, s) : launch_bwd_c<T, 128>(causal, a, s);
+static hipError_t launch_bwd_d(Step st, int d, bool causal, const BwdArgs& a, hipStream_t s) {
+  return d == 64 ? launch_bwd_c<T, 64>(st, causal, a, s) : launch_bwd_c<T, 128>(st, causal, a, s);
 }
 
-hipError_t launch_bwd(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s) {
+static hipError_t launch_step(Step st, Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s) {
   switch (dt) {
-    case Dt::f32: return launch_bwd_d<float>(d, causal, a, s);
-    case Dt::f16: return launch_bwd_d<_Float16>(d, causal, a, s);
-    case Dt::bf16: return launch_bwd_d<__bf16>(d, causal, a, s);
+    case Dt::f32: return launch_bwd_d<float>(st, d, causal, a, s);
+    case Dt::f16: return launch_bwd_d<_Float16>(st, d, causal, a, s);
+    case Dt::bf16: return launch_bwd_d<__bf16>(st, d, causal, a, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_pre(Dt dt, int d, const BwdArgs& a, hipStream_t s) {
+  return launch_step(Step::pre, dt, d, false, a, s);
+}
+
+hipError_t launch_bwd_main(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s) {
+  return launch_step(Step::main, dt, d, causal, a, s);
+}
+
+hipError_t launch_bwd_fin(Dt dt, int d, const BwdArgs& a, hipStream_t s) {
+  return launch_step(Step::fin, dt, d, false, a, s);
 }
 
 }  // namespace fa

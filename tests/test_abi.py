@@ -100,6 +100,21 @@ def test_bwd_rejects(kw, status):
     assert _bwd(**kw) == status
 
 
+def test_split_backward_rejects():
+    ws, nb = 0x10000, fa.fa_bwd_workspace_size(1, 1, 128, 64)
+    assert fa.fa_bwd_preprocess(None, P, 1, 1, 128, 64, fa.FA_F16, ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_bwd_preprocess(P, P, 1, 1, 128, 96, fa.FA_F16, ws, nb, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_preprocess(P, P, 1, 1, 128, 64, fa.FA_F16, ws, nb - 1, None) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_main(P, P, P, P, P, P, None, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws, nb,
+                          None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_bwd_main(P, P, P, P, P, P, P, 1, 1, 128, 64, 0, math.nan, fa.FA_F16, ws, nb,
+                          None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_bwd_main(P, P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws + 8, nb,
+                          None) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_finalize(None, 1, 1, 128, 64, 0.1, fa.FA_F16, ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_bwd_finalize(P, 1, 1, 128, 64, 0.1, 5, ws, nb, None) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_workspace_size():
     B, H, N, d = 2, 3, 100, 64
     rows = B * H * N
@@ -118,6 +133,9 @@ def _has_gpu():
 def test_valid_arguments_without_gpu_report_device_error():
     assert _fwd() == fa.FA_ERR_DEVICE
     assert _bwd() == fa.FA_ERR_DEVICE
+    nb = fa.fa_bwd_workspace_size(1, 1, 128, 64)
+    assert fa.fa_bwd_preprocess(P, P, 1, 1, 128, 64, fa.FA_F16, 0x10000, nb, None) == fa.FA_ERR_DEVICE
+    assert fa.fa_bwd_finalize(P, 1, 1, 128, 64, 0.1, fa.FA_F16, 0x10000, nb, None) == fa.FA_ERR_DEVICE
 
 
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):
