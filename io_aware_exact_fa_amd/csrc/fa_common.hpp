@@ -158,6 +158,62 @@ __device__ inline float half_sum(float x) {
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- register transposes
+
+// Four rows of 16 bytes (rows = consecutive keys or queries, 16 bytes = 16/sizeof(T)
+// consecutive columns) -> for each column e, the four row values packed in 8
+// (16-bit) or 16 (f32) bytes, ready for one LDS store into a transposed tile.
+__device__ inline void transpose4_16bit(const uint4 (&x)[4], uint2 (&out)[8]) {
+  const uint32_t* a = reinterpret_cast<const uint32_t*>(&x[0]);
+  const uint32_t* b = reinterpret_cast<const uint32_t*>(&x[1]);
+  const uint32_t* c = reinterpret_cast<const uint32_t*>(&x[2]);
+  const uint32_t* d = reinterpret_cast<const uint32_t*>(&x[3]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    // v_perm_b32 selectors: low halves (0x05040100) or high halves (0x07060302) of (S1, S0).
+    out[2 * w] = uint2{__builtin_amdgcn_perm(b[w], a[w], 0x05040100u),
+                       __builtin_amdgcn_perm(d[w], c[w], 0x05040100u)};
+    out[2 * w + 1] = uint2{__builtin_amdgcn_perm(b[w], a[w], 0x07060302u),
+                           __builtin_amdgcn_perm(d[w], c[w], 0x07060302u)};
+  }
+}
+
+__device__ inline void transpose4_32bit(const uint4 (&x)[4], uint4 (&out)[4]) {
+  out[0] = uint4{x[0].x, x[1].x, x[2].x, x[3].x};
+  out[1] = uint4{x[0].y, x[1].y, x[2].y, x[3].y};
+  out[2] = uint4{x[0].z, x[1].z, x[2].z, x[3].z};
+  out[3] = uint4{x[0].w, x[1].w, x[2].w, x[3].w};
+}
+
+// Store the transpose of a 4-row x (16/sizeof(T))-column block: row r (0..3),
+// column e goes to dst[e * pitch + r].  dst must be 8-byte (16-bit T) or
+// 16-byte (f32) aligned, pitch in elements.
+template <typename T>
+__device__ inline void store_transposed4(T* dst, int pitch, const uint4 (&x)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    uint2 t[8];
+    transpose4_16bit(x, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2*>(dst + e * pitch) = t[e];
+  } else {
+    uint4 t[4];
+    transpose4_32bit(x, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(dst + e * pitch) = t[e];
+  }
+}
+
+// Row permutation inside each group of 16 result rows that swaps bit 2 (the
+// lane half) and bit 3 of the row index.  If the A operand of an MFMA that
+// produces a 32x32 tile supplies row perm16(r) in place of row r, then the
+// eight result elements 8u..8u+7 of lane half h hold rows 16u + 8h + t
+// (t = 0..7): a later MFMA that contracts over these rows can read its
+// other operand as 8 consecutive rows of a transposed tile (one 16-byte
+// load).  Only used for 16-bit types (8 k values per lane).
+__device__ inline int perm16(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
 // ---------------------------------------------------------------- stores
 
 // Store 4 consecutive values (rounded to T) at p.

@@ -45,26 +45,53 @@ struct FwdTile {
   static constexpr int NKS = D / KM;             // MFMAs per 32x32 block of S
   static constexpr int NU = steps32<T>();        // MFMAs per 32 keys of P V
   static constexpr int E16 = 16 / sizeof(T);     // elements per 16-byte chunk
-  static constexpr int PITCH = D + E16;          // LDS row pitch (16 B pad)
-  static constexpr int CPR = D / E16;            // 16-byte chunks per row
-  static constexpr int CPT = BC * CPR / NT;      // chunks per thread per tile
-  static_assert(BC * CPR % NT == 0, "tile must split evenly over the threads");
+  static constexpr int KP = D + E16;             // K row pitch (elements)
+  static constexpr int VP = BC + 8;              // V^T row pitch (elements)
+  static constexpr int CPR = D / E16;            // 16-byte chunks per K row
+  static constexpr int KCPT = BC * CPR / NT;     // K chunks per thread per tile
+  static constexpr int VGRP = (BC / 4) * CPR;    // 4-key x 16-byte V groups per tile
+  static constexpr int VGPT = (VGRP + NT - 1) / NT;
+  static constexpr int KS_EL = BC * KP;          // one K buffer, elements
+  static constexpr int VS_EL = D * VP;           // one V^T buffer, elements
+  static_assert(BC * CPR % NT == 0, "K tile must split evenly over the threads");
 };
+
+// V^T tile layout: row d (head dimension) holds the tile's keys, in 16-byte
+// chunks whose order is XOR-swizzled by the row, so that both the transposed
+// stores (each lane writes 4 keys of one row) and the 16-byte operand reads
+// (32 consecutive rows, one chunk each) hit distinct LDS banks.
+template <typename T>
+__device__ inline int vt_index(int d, int key) {
+  constexpr int KPC = 16 / sizeof(T);                      // keys per 16-byte chunk
+  constexpr int SW = sizeof(T) == 2 ? 7 : 15;
+  const int swz = sizeof(T) == 2 ? (d >> 4) & SW : (d >> 2) & SW;
+  return ((key / KPC) ^ swz) * KPC + (key % KPC);
+}
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using C = FwdTile<T, D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
-  __shared__ __attribute__((aligned(16))) T Ks[C::BC * C::PITCH];
-  __shared__ __attribute__((aligned(16))) T Vs[C::BC * C::PITCH];
+  constexpr bool kPerm = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) T Ks[2][C::KS_EL];
+  __shared__ __attribute__((aligned(16))) T Vt[2][C::VS_EL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, col = lane & 31, h = lane >> 5;
   const int N = a.N;
-  const int qt = CAUSAL ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+
+  // Workgroup -> (head, query tile).  Workgroups are dealt to the 8 XCDs
+  // round-robin by linear id; give each XCD a contiguous range of (head, tile)
+  // pairs so the tiles of one head share their K/V through one L2.  Under the
+  // causal mask the tiles of a head run heaviest (most key tiles) first.
+  const int ntq = gridDim.x;
+  const int nwork = ntq * gridDim.y * gridDim.z;
+  int lin = blockIdx.x + ntq * (blockIdx.y + gridDim.y * blockIdx.z);
+  if ((nwork & 7) == 0) lin = (lin & 7) * (nwork >> 3) + (lin >> 3);
+  const int qt = CAUSAL ? ntq - 1 - (lin % ntq) : (lin % ntq);
   const int q0 = qt * C::BR;
-  const size_t head = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const size_t head = (size_t)(lin / ntq);
   const T* Q = static_cast<const T*>(a.q) + head * N * D;
   const T* K = static_cast<const T*>(a.k) + head * N * D;
   const T* V = static_cast<const T*>(a.v) + head * N * D;
@@ -74,15 +101,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int qw = q0 + 32 * w;   // first query row of this wave
   const int myq = qw + col;     // the query row of this lane
 
-  // Q^T operand, held for the whole kernel.  A negative scale is folded into Q
-  // (exact sign flip) so that c > 0 and max(c S) = c max(S).
+  // Q^T operand, held for the whole kernel.  Rows past N read row N-1 (their
+  // results are never stored).  A negative scale is folded into Q (exact sign
+  // flip) so that c > 0 and max(c S) = c max(S).
   const float c = fabsf(a.scale) * kLog2e;
   frag qf[C::NKS];
+  {
+    const T* qrow = Q + (size_t)min(myq, N - 1) * D + C::KPL * h;
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
-    frag f = {};
-    if (myq < N) f = load_frag<T>(Q + (size_t)myq * D + ks * C::KM + C::KPL * h);
-    qf[ks] = (a.scale < 0.f) ? neg_frag<T>(f) : f;
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const frag f = load_frag<T>(qrow + ks * C::KM);
+      qf[ks] = (a.scale < 0.f) ? neg_frag<T>(f) : f;
+    }
   }
 
   const int ntiles_all = (N + C::BC - 1) / C::BC;
@@ -91,28 +121,54 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // Last tile this wave needs; -1 if the wave holds no row below N.
   const int wlast = (qw >= N) ? -1 : (CAUSAL ? min(qw + 31, N - 1) / C::BC : ntiles - 1);
 
-  uint4 kst[C::CPT], vst[C::CPT];
+  // This lane's K row inside each 32-key block (permuted for 16-bit types, so
+  // that lane half h ends up holding keys 16u + 8h + t of the P~ operand).
+  const int krow = kPerm ? perm16(col) : col;
+  // Key (inside a 32-key block) of result element i of this lane: key0_of(i) + hoff,
+  // with key0_of(i) the key of lane half 0 (a compile-time constant per i).
+  const int hoff = kPerm ? 8 * h : 4 * h;
+  auto key0_of = [](int i) {
+    const int r = 8 * (i >> 2) + (i & 3);
+    return kPerm ? perm16(r) : r;
+  };
+
+  // Staging registers: the next tile's K chunks and V groups.  Rows past N are
+  // clamped to row N-1: their scores are masked to -inf and their P~ set to 0.
+  uint4 kst[C::KCPT];
+  uint4 vst[C::VGPT][4];
   auto gload = [&](int j) {
     const int key0 = j * C::BC;
 #pragma unroll
-    for (int r = 0; r < C::CPT; ++r) {
+    for (int r = 0; r < C::KCPT; ++r) {
       const int ch = tid + r * C::NT, row = ch / C::CPR, cc = ch % C::CPR;
-      if (key0 + row < N) {
-        const size_t off = (size_t)(key0 + row) * D + cc * C::E16;
-        kst[r] = *reinterpret_cast<const uint4*>(K + off);
-        vst[r] = *reinterpret_cast<const uint4*>(V + off);
-      } else {
-        kst[r] = uint4{0, 0, 0, 0};   // keys past N: masked scores, zero values
-        vst[r] = uint4{0, 0, 0, 0};
+      kst[r] = *reinterpret_cast<const uint4*>(K + (size_t)min(key0 + row, N - 1) * D + cc * C::E16);
+    }
+#pragma unroll
+    for (int r = 0; r < C::VGPT; ++r) {
+      const int g = tid + r * C::NT;
+      const int dg = g % C::CPR, kg = g / C::CPR;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = min(key0 + 4 * kg + i, N - 1);
+        if (g < C::VGRP) vst[r][i] = *reinterpret_cast<const uint4*>(V + (size_t)key * D + dg * C::E16);
       }
     }
   };
-  auto sstore = [&]() {
+  auto sstore = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < C::CPT; ++r) {
+    for (int r = 0; r < C::KCPT; ++r) {
       const int ch = tid + r * C::NT, row = ch / C::CPR, cc = ch % C::CPR;
-      *reinterpret_cast<uint4*>(&Ks[row * C::PITCH + cc * C::E16]) = kst[r];
-      *reinterpret_cast<uint4*>(&Vs[row * C::PITCH + cc * C::E16]) = vst[r];
+      *reinterpret_cast<uint4*>(&Ks[buf][row * C::KP + cc * C::E16]) = kst[r];
+    }
+#pragma unroll
+    for (int r = 0; r < C::VGPT; ++r) {
+      const int g = tid + r * C::NT;
+      if (g < C::VGRP) {
+        const int dg = g % C::CPR, kg = g / C::CPR;
+        const int d0 = dg * C::E16;
+        // The E16 rows d0..d0+E16-1 share one swizzle (it changes every 4 or 16 rows).
+        store_transposed4<T>(&Vt[buf][d0 * C::VP + vt_index<T>(d0, 4 * kg)], C::VP, vst[r]);
+      }
     }
   };
 
@@ -123,30 +179,35 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   float l_run = 0.f;         // this lane's share of the running normalizer
 
   gload(0);
-  sstore();
+  sstore(0);
   __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
     if (j + 1 < ntiles) gload(j + 1);
     if (j <= wlast) {
       const int key0 = j * C::BC;
+      const T* Kb = Ks[buf];
+      const T* Vb = Vt[buf];
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        frag kf[C::NKS];
+        const T* krowp = &Kb[(kb * 32 + krow) * C::KP + C::KPL * h];
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) kf[ks] = load_frag<T>(krowp + ks * C::KM);
         s[kb] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks)
-          s[kb] = M::mma(load_frag<T>(&Ks[(kb * 32 + col) * C::PITCH + ks * C::KM + C::KPL * h]),
-                         qf[ks], s[kb]);
+        for (int ks = 0; ks < C::NKS; ++ks) s[kb] = M::mma(kf[ks], qf[ks], s[kb]);
       }
       const bool masked = (CAUSAL && key0 + C::BC - 1 > qw) || (key0 + C::BC > N);
       if (masked) {
+        // Visible keys of this lane's row: key <= myq (causal) and key < N.
+        const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - key0 - hoff;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (key >= N || (CAUSAL && key > myq)) s[kb][i] = -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + key0_of(i) > lim) s[kb][i] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -154,52 +215,56 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
       mx = half_max(mx);
-      const float m_new = (mx == -INFINITY) ? m_run : fmaxf(m_run, mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      float lsum = 0.f;
+      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+      // Rescale only when the max of some row of the wave grew.  The max is tracked
+      // exactly so that the largest P~ of a row is exactly 1 and its rounding to
+      // the 16-bit operand type costs nothing (it dominates peaked rows).
+      if (__any(mt > m_run)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
       if (masked) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float x = s[kb][i];
-            const float p = (x == -INFINITY) ? 0.f : exp2_fast(fmaf(x, c, -m_use));
+            const float p = (x == -INFINITY) ? 0.f : exp2_fast(fmaf(x, c, nm));   // exact for c == 0
             s[kb][i] = p;
-            lsum += p;
+            ps[i & 3] += p;
           }
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float p = exp2_fast(fmaf(s[kb][i], c, -m_use));
+            const float p = exp2_fast(fmaf(s[kb][i], c, nm));
             s[kb][i] = p;
-            lsum += p;
+            ps[i & 3] += p;
           }
       }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      if (alpha != 1.f) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-      }
-      frag pf[2][C::NU];
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      // O^T += V_j^T P~^T: A operand = 8 consecutive keys of one head-dim row of V^T.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int u = 0; u < C::NU; ++u) pf[kb][u] = pack_frag<T>(s[kb], u);
+        for (int u = 0; u < C::NU; ++u) {
+          const frag pf = pack_frag<T>(s[kb], u);
+          const int kofs = kb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int u = 0; u < C::NU; ++u)
-            acc[db] = M::mma(load_frag_tr<T>(Vs, C::PITCH, kb * 32, u, db * 32, lane), pf[kb][u],
-                             acc[db]);
+          for (int db = 0; db < D / 32; ++db) {
+            const int d = db * 32 + col;
+            acc[db] = M::mma(load_frag<T>(&Vb[d * C::VP + vt_index<T>(d, kofs)]), pf, acc[db]);
+          }
+        }
     }
-    __syncthreads();
-    if (j + 1 < ntiles) sstore();
+    if (j + 1 < ntiles) sstore(buf ^ 1);
     __syncthreads();
   }
 
