@@ -1,15 +1,14 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
 One step = the whole path over one batch of seeded synthetic inputs already
-resident in HBM: fa_fwd, then fa_bwd_preprocess, fa_bwd_main and
-fa_bwd_finalize (the three steps of fa_bwd), all through the C ABI on one
-stream.  Throughput is counted with the method's FLOP formula: forward
+resident in HBM: fa_fwd, then fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq
+(the three steps of fa_bwd), all through the C ABI on one stream.  Throughput is counted with the method's FLOP formula: forward
 4*B*H*N^2*d (halved under the causal mask), backward 2.5x the forward.
 
 Prints ONE JSON line.  Besides the step throughput it reports:
   * per-kernel times from HIP events recorded on the launch stream around
     every launch inside the timed region;
-  * "roofline" for the dominant kernel (the backward main kernel) against the
+  * "roofline" for the dominant kernel (the backward dK/dV kernel) against the
     dense MFMA peak of the workload's dtype, with HBM traffic from committed
     rocprofv3 counter runs when they were taken on the current kernel source;
   * "cpu_baseline": the fp64 CPU oracle timed on a bounded sample (one head)
@@ -38,7 +37,7 @@ METRIC = "attention fwd/bwd TFLOPS on 1 MI355X and % of bf16 MFMA peak"
 # (2516.6 = 256 CUs x 4096 flop/clk x 2.4 GHz), fp32 157.3.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
-DOMINANT = "bwd_kernel"
+DOMINANT = "bwd_dkdv_kernel"
 KERNEL_SOURCES = ("io_aware_exact_fa_amd/csrc/fa_bwd.hip", "io_aware_exact_fa_amd/csrc/fa_common.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -180,11 +179,12 @@ def main():
         check(fa.fa_bwd_preprocess(P(o), P(do), B, H, N, d, code, P(ws), ws.numel(), sh), "pre")
         if ev is not None:
             ev[2].record(stream)
-        check(fa.fa_bwd_main(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, N, d, w.causal,
-                             w.scale, code, P(ws), ws.numel(), sh), "main")
+        check(fa.fa_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, N, d, w.causal,
+                             w.scale, code, P(ws), ws.numel(), sh), "dkdv")
         if ev is not None:
             ev[3].record(stream)
-        check(fa.fa_bwd_finalize(P(dq), B, H, N, d, w.scale, code, P(ws), ws.numel(), sh), "fin")
+        check(fa.fa_bwd_dq(P(q), P(k), P(v), P(do), P(lse), P(dq), B, H, N, d, w.causal, w.scale,
+                           code, P(ws), ws.numel(), sh), "dq")
         if ev is not None:
             ev[4].record(stream)
 
@@ -201,15 +201,18 @@ def main():
     wall = time.perf_counter() - t0
 
     ms = lambda a, b_: sum(e[a].elapsed_time(e[b_]) for e in events) / args.steps
-    fwd_ms, pre_ms, main_ms, fin_ms = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4)
-    bwd_ms = pre_ms + main_ms + fin_ms
+    fwd_ms, pre_ms, dkdv_ms, dq_ms = ms(0, 1), ms(1, 2), ms(2, 3), ms(3, 4)
+    bwd_ms = pre_ms + dkdv_ms + dq_ms
     ms_per_step = wall * 1e3 / args.steps
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
     peak = PEAK_TFLOPS[w.dtype]
     value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
     fwd_tf = fwd_f / (fwd_ms * 1e-3) / 1e12
     bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
-    main_tf = bwd_f / (main_ms * 1e-3) / 1e12
+    # Algorithmic FLOPs of the dK/dV kernel: four of the backward's five N^2 d
+    # products (S, dP, dV, dK), i.e. 4/5 of the backward count.
+    dkdv_f = 0.8 * bwd_f
+    dkdv_tf = dkdv_f / (dkdv_ms * 1e-3) / 1e12
 
     traffic = load_traffic(w.name)
     out = {
@@ -227,10 +230,10 @@ def main():
         "data": "synthetic (seeded normal Q/K/V/dO of the workload's shape and distribution)",
         "config": {
             "workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
-            "step": "fa_fwd + fa_bwd (preprocess, main, finalize)",
+            "step": "fa_fwd + fa_bwd (preprocess, dkdv, dq)",
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
-            "bwd_pre_ms": round(pre_ms, 4), "bwd_main_ms": round(main_ms, 4),
-            "bwd_finalize_ms": round(fin_ms, 4),
+            "bwd_pre_ms": round(pre_ms, 4), "bwd_dkdv_ms": round(dkdv_ms, 4),
+            "bwd_dq_ms": round(dq_ms, 4),
             "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
             "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),
             "bwd_pct_of_peak": round(100 * bwd_tf / peak, 2),
@@ -240,10 +243,10 @@ def main():
         "roofline": {
             "kernel": DOMINANT,
             "bound": "mfma",
-            "achieved": round(main_tf, 2),
+            "achieved": round(dkdv_tf, 2),
             "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(main_tf / peak, 4),
+            "frac": round(dkdv_tf / peak, 4),
             "traffic": traffic,
         },
     }

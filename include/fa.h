@@ -90,10 +90,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 /*
  * Bytes of device workspace fa_bwd needs for this shape (0 if the shape is
- * invalid).  Layout, from the workspace base (offsets rounded up to 256 B):
- *   D      float32 [B,H,N]    D_i = rowsum(dO_i * O_i)
- *   dQacc  float32 [B,H,N,d]  unscaled dQ accumulator (sum over key tiles)
- * Both regions are fully rewritten by every fa_bwd call.
+ * invalid): D float32 [B,H,N], D_i = rowsum(dO_i * O_i), rounded up to 256 B.
+ * fa_bwd (and fa_bwd_preprocess) rewrite it completely on every call.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -101,9 +99,10 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * Backward pass: gradients of sum(O * dout) with respect to q, k, v.
  *
  * o and lse must be what fa_fwd wrote for the same q, k, v, causal and scale.
- * Equivalent to fa_bwd_preprocess, fa_bwd_main and fa_bwd_finalize enqueued
- * in that order on `stream` with the same arguments.  Writes every element
- * of dq, dk, dv (dtype) and of the workspace.
+ * Equivalent to fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq enqueued in that
+ * order on `stream` with the same arguments.  Writes every element of dq, dk,
+ * dv (dtype, rounded to nearest even from fp32 accumulators) and of the
+ * workspace.  No atomics: results are bitwise repeatable.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* lse,
@@ -113,39 +112,43 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  void* stream);
 
 /*
- * Backward step 1: D_i = rowsum(dout_i * o_i) in float32 into the workspace's
- * D region, and zero its dQacc region.  D is the row term of the softmax
- * gradient, precomputed from O instead of from P and dP ("FlashAttention-2:
- * Faster Attention with Better Parallelism and Work Partitioning", sections
- * "Standard Attention Implementation / Backward Pass" and "Backward Pass").
+ * Backward step 1: D_i = rowsum(dout_i * o_i) in float32 into the workspace.
+ * D is the row term of the softmax gradient, precomputed from O instead of
+ * from P and dP ("FlashAttention-2: Faster Attention with Better Parallelism
+ * and Work Partitioning", sections "Standard Attention Implementation /
+ * Backward Pass" and "Backward Pass").
  */
 fa_status fa_bwd_preprocess(const void* o, const void* dout,
                             int B, int H, int N, int d, fa_dtype dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Backward step 2 (the main kernel): for every key tile, recompute
- * P = exp(scale q k^T - lse) per query tile, form dP = dout v^T and
- * dS = P * (dP - D), write dk = scale * dS^T q and dv = P^T dout, and add
- * dS k (unscaled) into the workspace's dQacc with float32 atomics (same
- * FlashAttention-2 page, sections "Backward Pass" and "Parallelism: 시퀀스 길이
- * 차원 병렬화"; the factor scale follows from S = scale q k^T by the chain
- * rule).  Needs the workspace as left by fa_bwd_preprocess.  The order of
- * the atomic additions is not fixed, so dQacc (and dq) may differ in the
- * last bits between runs; dk and dv are bitwise repeatable.
+ * Backward step 2: for every tile of keys, recompute P = exp(scale q k^T - lse)
+ * query tile by query tile, form dP = dout v^T and dS = P * (dP - D), and write
+ * dv = P^T dout and dk = scale * dS^T q (same FlashAttention-2 page, sections
+ * "Standard Attention Implementation / Backward Pass" and "Backward Pass": the
+ * key/value tile is the outer loop so that one workgroup owns dK_j and dV_j; the
+ * factor scale follows from S = scale q k^T by the chain rule).  Needs the
+ * workspace as left by fa_bwd_preprocess.
  */
-fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                       const float* lse, void* dk, void* dv,
                       int B, int H, int N, int d, int causal, float scale,
                       fa_dtype dtype, void* workspace, size_t workspace_bytes,
                       void* stream);
 
 /*
- * Backward step 3: dq = scale * dQacc, rounded to dtype (nearest even).
+ * Backward step 3: for every tile of queries, recompute P and dS key tile by
+ * key tile and write dq = scale * dS k.  This is the separate pass that sums
+ * dQ over all key tiles (same FlashAttention-2 page, section "Parallelism:
+ * 시퀀스 길이 차원 병렬화", which allows dQ by atomic adds or by a separate
+ * reduction).  Needs the workspace as left by fa_bwd_preprocess.
  */
-fa_status fa_bwd_finalize(void* dq, int B, int H, int N, int d, float scale,
-                          fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                          void* stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse, void* dq,
+                    int B, int H, int N, int d, int causal, float scale,
+                    fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ FA_F16 = 1
 FA_BF16 = 2
 
 EXPORTED = ("fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
-            "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_finalize")
+            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq")
 
 
 class FaError(RuntimeError):
@@ -46,7 +46,7 @@ class FaError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m io_aware_exact_fa_amd._build` "
+            f"{LIB_PATH} is not built; run `python io_aware_exact_fa_amd/_build.py` "
             "(or __graft_entry__.build()) first")
     # torch ships its own HIP runtime (same soname as the system one).  Load torch
     # first so libfa.so binds to that runtime: device memory and streams come from
@@ -67,10 +67,10 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
-    lib.fa_bwd_main.restype = i
-    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
-    lib.fa_bwd_finalize.restype = i
-    lib.fa_bwd_finalize.argtypes = [vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dkdv.restype = i
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dq.restype = i
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     return lib
 
 
@@ -116,15 +116,16 @@ def fa_bwd_preprocess(o, dout, B, H, N, d, dtype, workspace, workspace_bytes, st
     return _lib.fa_bwd_preprocess(o, dout, B, H, N, d, int(dtype), workspace, workspace_bytes, stream)
 
 
-def fa_bwd_main(q, k, v, dout, lse, dk, dv, B, H, N, d, causal, scale, dtype,
+def fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, H, N, d, causal, scale, dtype,
                 workspace, workspace_bytes, stream) -> int:
-    return _lib.fa_bwd_main(q, k, v, dout, lse, dk, dv, B, H, N, d, int(causal), float(scale),
+    return _lib.fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, H, N, d, int(causal), float(scale),
                             int(dtype), workspace, workspace_bytes, stream)
 
 
-def fa_bwd_finalize(dq, B, H, N, d, scale, dtype, workspace, workspace_bytes, stream) -> int:
-    return _lib.fa_bwd_finalize(dq, B, H, N, d, float(scale), int(dtype), workspace,
-                                workspace_bytes, stream)
+def fa_bwd_dq(q, k, v, dout, lse, dq, B, H, N, d, causal, scale, dtype,
+              workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_dq(q, k, v, dout, lse, dq, B, H, N, d, int(causal), float(scale),
+                          int(dtype), workspace, workspace_bytes, stream)
 
 
 # ------------------------------------------------------------------ torch helpers

@@ -1,6 +1,8 @@
 """Build libfa.so (the gfx950 attention library) in-tree with hipcc.
 
-Usage: ``python -m io_aware_exact_fa_amd._build`` (or ``build()`` from Python).
+Usage: ``python io_aware_exact_fa_amd/_build.py`` (or ``__graft_entry__.build()``);
+run it by path, not as ``-m io_aware_exact_fa_amd._build``, which would import
+the package and load the library that is about to be replaced.
 Every call compiles from scratch: each ``csrc/*.hip`` file to an object in
 ``_build/`` (in parallel), then links ``libfa.so`` next to this file.
 """

@@ -98,10 +98,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
-  const uint64_t n = elements(B, H, N, d);
-  if (n == 0) return 0;
+  if (elements(B, H, N, d) == 0) return 0;
   const uint64_t rows = (uint64_t)B * H * N;
-  return align_up(rows * sizeof(float)) + align_up(n * sizeof(float));
+  return align_up(rows * sizeof(float));
 }
 
 fa_status fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
@@ -115,7 +114,7 @@ fa_status fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N
   return launched(fa::launch_bwd_pre(to_dt(dtype), d, a, (hipStream_t)stream));
 }
 
-fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                       const float* lse, void* dk, void* dv, int B, int H, int N, int d, int causal,
                       float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                       void* stream) {
@@ -130,17 +129,24 @@ fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* d
   a.lse = lse;
   a.dk = dk;
   a.dv = dv;
-  return launched(fa::launch_bwd_main(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream));
+  return launched(fa::launch_bwd_dkdv(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream));
 }
 
-fa_status fa_bwd_finalize(void* dq, int B, int H, int N, int d, float scale, fa_dtype dtype,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-  if (!dq) return FA_ERR_INVALID_ARGUMENT;
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse, void* dq, int B, int H, int N, int d, int causal,
+                    float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!q || !k || !v || !dout || !lse || !dq) return FA_ERR_INVALID_ARGUMENT;
   fa::BwdArgs a{};
   fa_status st = bwd_setup(B, H, N, d, scale, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
   a.dq = dq;
-  return launched(fa::launch_bwd_fin(to_dt(dtype), d, a, (hipStream_t)stream));
+  return launched(fa::launch_bwd_dq(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream));
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -164,9 +170,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   hipStream_t s = (hipStream_t)stream;
   st = launched(fa::launch_bwd_pre(dt, d, a, s));
   if (st != FA_OK) return st;
-  st = launched(fa::launch_bwd_main(dt, d, causal != 0, a, s));
+  st = launched(fa::launch_bwd_dkdv(dt, d, causal != 0, a, s));
   if (st != FA_OK) return st;
-  return launched(fa::launch_bwd_fin(dt, d, a, s));
+  return launched(fa::launch_bwd_dq(dt, d, causal != 0, a, s));
 }
 
 }  // extern "C"
@@ -182,9 +188,7 @@ fa_status bwd_setup(int B, int H, int N, int d, float scale, fa_dtype dtype, voi
     return FA_ERR_WORKSPACE;
   st = check_device();
   if (st != FA_OK) return st;
-  const uint64_t rows = (uint64_t)B * H * N;
   a->delta = static_cast<float*>(workspace);
-  a->dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * sizeof(float)));
   a->B = B;
   a->H = H;
   a->N = N;

@@ -1,19 +1,19 @@
 // Backward attention kernels for gfx950.
 //
-// Three launches on the caller's stream:
-//   1. bwd_pre_kernel: D_i = rowsum(dO_i * O_i) in fp32, and zero the fp32 dQ
-//      accumulator row (a fill kernel, not a memset, so the sequence can be
-//      captured in a graph).  HBM-bound.
-//   2. bwd_kernel: one workgroup of 4 wavefronts per (batch, head, tile of 128
-//      keys); each wave owns 32 keys and keeps K, V of those keys and its dK,
-//      dV accumulators in registers.  The workgroup loops over query tiles of
-//      BQ rows (Q, dO, LSE, D staged in LDS) and per tile computes
-//        S  = Q K^T,  P = 2^(c S - LSE log2 e)           (recomputed from LSE)
-//        dP = dO V^T, dS = P * (dP - D)
-//        dV += P^T dO,  dK += dS^T Q                    (registers)
-//        dQacc += dS K                                  (fp32 atomics, via dS in LDS)
-//      and stores dK * scale and dV once at the end.
-//   3. bwd_dq_kernel: dq = scale * dQacc rounded to the input type.
+// Three launches on the caller's stream, no atomics and no fp32 accumulator
+// in device memory:
+//   1. bwd_pre_kernel:  D_i = rowsum(dO_i * O_i) in fp32 (HBM-bound).
+//   2. bwd_dkdv_kernel: one workgroup per (batch, head, 128-key tile); each wave
+//      owns 32 keys.  For every query tile, recompute
+//        S = Q K^T, P = 2^(c S - LSE log2 e), dP = dO V^T, dS = P (dP - D)
+//      and accumulate dV += P^T dO, dK += dS^T Q in registers; dk = scale dK.
+//   3. bwd_dq_kernel:   one workgroup per (batch, head, 128-query tile), the
+//      forward's loop order: for every key tile, recompute S^T, P, dP^T, dS and
+//      accumulate dQ^T += K^T dS^T in registers; dq = scale dQ at the end.
+// dQ is computed by its own pass instead of being summed across key-tile
+// workgroups: the two GEMMs it recomputes cost less than the fp32 atomic
+// traffic they replace, and every output is written exactly once (bitwise
+// repeatable).
 //
 // Sources: the gradients dV = P^T dO, dP = dO V^T, dS = P (dP - D),
 // D_i = sum_j P_ij dP_ij, dQ = dS K, dK = dS^T Q ("FlashAttention-2: Faster
@@ -21,18 +21,15 @@
 // "Standard Attention Implementation / Backward Pass"; the factor scale on dQ
 // and dK comes from S = scale Q K^T by the chain rule); D precomputed as
 // rowsum(dO * O), P recomputed from the stored L, the key/value-tile-outer
-// order and dQ accumulated across workgroups (same page, sections
+// order for dK/dV and a separate reduction for dQ (same page, sections
 // "Backward Pass" and "Parallelism: 시퀀스 길이 차원 병렬화"); S and P are never
 // stored, only regenerated per tile ("FlashAttention 원 논문 해부", section
 // "forward가 끝난 뒤 backward는 무엇을 저장하고 무엇을 다시 계산하는가").
 //
-// Register orientation: S and dP are computed as Q K^T and dO V^T, so each
-// lane holds one key (column) and the query rows sit in the result registers.
-// dV = P^T dO and dK = dS^T Q contract over queries, i.e. over the result rows,
-// so P and dS feed those MFMAs from registers; dO and Q enter as transposed
-// operands read from row-major LDS tiles with ds_read_b64_tr_b16.  dQ = dS K
-// contracts over keys, so dS goes through LDS once (stored as dS^T, read back
-// transposed).
+// Operands: every MFMA reads one operand from registers (a result tile of an
+// earlier MFMA, or rows held for the whole kernel) and the other with 16-byte
+// LDS reads, from a row-major tile or from a transposed, swizzled tile written
+// at load time (no transposing LDS reads).
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -54,81 +51,206 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long rows) {
     const T* g = static_cast<const T*>(a.dout) + off;
 #pragma unroll
     for (int e = 0; e < E16; ++e) part = fmaf(to_f32(o[e]), to_f32(g[e]), part);
-    float* acc = a.dq_acc + off;
-#pragma unroll
-    for (int e = 0; e < E16; e += 4) *reinterpret_cast<f32x4*>(acc + e) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int m = LPR / 2; m > 0; m >>= 1) part += __shfl_xor(part, m, LPR);
   if (row < rows && sub == 0) a.delta[row] = part;
 }
 
-// ------------------------------------------------------------------ main
+// Work index of this workgroup: workgroups are dealt to the 8 XCDs round-robin
+// by linear id; give each XCD a contiguous range so that the tiles of one head
+// share their K/V (or Q/dO) through one L2.
+__device__ inline int xcd_work_index() {
+  const int nwork = gridDim.x * gridDim.y * gridDim.z;
+  int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  if ((nwork & 7) == 0) lin = (lin & 7) * (nwork >> 3) + (lin >> 3);
+  return lin;
+}
+
+// ------------------------------------------------------------------ dQ
 
 template <typename T, int D>
-struct BwdTile {
-  static constexpr int BKC = 128;                          // keys per workgroup
-  static constexpr int BQ = sizeof(T) == 4 ? 32 : 64;      // queries per tile
-  static constexpr int NT = 256;
+struct DqTile {
+  static constexpr int BR = 128;                 // queries per workgroup
+  static constexpr int BC = kTrCols;             // keys per tile (64)
   static constexpr int KPL = Mfma<T>::KPL;
   static constexpr int KM = 2 * KPL;
   static constexpr int NKS = D / KM;
   static constexpr int NU = steps32<T>();
   static constexpr int E16 = 16 / sizeof(T);
-  static constexpr int PITCH = D + E16;                    // Q, dO, K rows
-  static constexpr int SPITCH = BQ + E16;                  // dS^T rows (keys)
-  static constexpr int CPR = D / E16;
-  static constexpr int NQB = BQ / 32;                      // 32-query blocks per tile
-  static constexpr int NDQ = NQB * (D / 32);               // 32x32 dQ blocks per tile
+  static constexpr int KP = D + E16;             // row pitch of the K and V tiles
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs a) {
-  using C = BwdTile<T, D>;
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  using C = DqTile<T, D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
-  __shared__ __attribute__((aligned(16))) T Ks[C::BKC * C::PITCH];
-  __shared__ __attribute__((aligned(16))) T Qs[C::BQ * C::PITCH];
-  __shared__ __attribute__((aligned(16))) T dOs[C::BQ * C::PITCH];
-  __shared__ __attribute__((aligned(16))) T dSt[C::BKC * C::SPITCH];
+  constexpr bool kPerm = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) T Ks[C::BC * C::KP];
+  __shared__ __attribute__((aligned(16))) T Vs[C::BC * C::KP];
+  __shared__ __attribute__((aligned(16))) T Kt[D * kTrPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, col = lane & 31, h = lane >> 5;
+  const int N = a.N;
+  const int ntq = gridDim.x;
+  const int lin = xcd_work_index();
+  const int qt = CAUSAL ? ntq - 1 - (lin % ntq) : (lin % ntq);
+  const int q0 = qt * C::BR;
+  const size_t head = (size_t)(lin / ntq);
+  const T* Q = static_cast<const T*>(a.q) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head * N * D;
+  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  const T* dO = static_cast<const T*>(a.dout) + head * N * D;
+  T* dQ = static_cast<T*>(a.dq) + head * N * D;
+  const float c = a.scale * kLog2e;
+
+  const int qw = q0 + 32 * w;
+  const int myq = qw + col;
+  const int qrow = min(myq, N - 1);
+  // Q^T and dO^T operands of this lane's query, held for the whole kernel.
+  frag qf[C::NKS], gf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    qf[ks] = load_frag<T>(Q + (size_t)qrow * D + ks * C::KM + C::KPL * h);
+    gf[ks] = load_frag<T>(dO + (size_t)qrow * D + ks * C::KM + C::KPL * h);
+  }
+  // Row statistics of this lane's query.  A row with no visible key (LSE = -inf)
+  // has P = 0: use +inf as its log2-domain LSE.
+  const float lse = a.lse[head * N + qrow];
+  const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+  const float dl = a.delta[head * N + qrow];
+
+  const int ntiles_all = (N + C::BC - 1) / C::BC;
+  const int qlast = min(q0 + C::BR, N) - 1;
+  const int ntiles = CAUSAL ? min(ntiles_all, qlast / C::BC + 1) : ntiles_all;
+  const int wlast = (qw >= N) ? -1 : (CAUSAL ? min(qw + 31, N - 1) / C::BC : ntiles - 1);
+  const int krow = kPerm ? perm16(col) : col;
+  const int hoff = kPerm ? 8 * h : 4 * h;
+  auto key0_of = [](int i) {
+    const int r = 8 * (i >> 2) + (i & 3);
+    return kPerm ? perm16(r) : r;
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+  TileStage<T, D> ks_stage, vs_stage;
+  ks_stage.load(K, 0, N, tid);
+  vs_stage.load(V, 0, N, tid);
+  for (int j = 0; j < ntiles; ++j) {
+    ks_stage.store_rows(Ks, C::KP, tid);
+    ks_stage.store_transposed(Kt, tid);
+    vs_stage.store_rows(Vs, C::KP, tid);
+    __syncthreads();
+    if (j + 1 < ntiles) {
+      ks_stage.load(K, (j + 1) * C::BC, N, tid);
+      vs_stage.load(V, (j + 1) * C::BC, N, tid);
+    }
+    if (j <= wlast) {
+      const int key0 = j * C::BC;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // S^T and dP^T for 32 keys x 32 queries.
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const T* kr = &Ks[(kb * 32 + krow) * C::KP + C::KPL * h];
+        const T* vr = &Vs[(kb * 32 + krow) * C::KP + C::KPL * h];
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          s = M::mma(load_frag<T>(kr + ks * C::KM), qf[ks], s);
+          dp = M::mma(load_frag<T>(vr + ks * C::KM), gf[ks], dp);
+        }
+        const int kb0 = key0 + kb * 32;
+        const bool masked = (CAUSAL && kb0 + 31 > qw) || (kb0 + 32 > N);
+        const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kb0 - hoff;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = exp2_fast(fmaf(s[i], c, -l2));
+          if (masked && key0_of(i) > lim) p = 0.f;
+          s[i] = p * (dp[i] - dl);                     // dS
+        }
+        // dQ^T += K^T dS^T: A operand = 8 consecutive keys of one head-dim row of K^T.
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u) {
+          const frag sf = pack_frag<T>(s, u);
+          const int kofs = kb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            acc[db] = M::mma(load_frag<T>(&Kt[tr_index<T>(db * 32 + col, kofs)]), sf, acc[db]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (myq < N) {
+    T* orow = dQ + (size_t)myq * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        store4<T>(orow + db * 32 + 8 * r + 4 * h, acc[db][4 * r] * sc, acc[db][4 * r + 1] * sc,
+                  acc[db][4 * r + 2] * sc, acc[db][4 * r + 3] * sc);
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV
+
+template <typename T, int D>
+struct DkvTile {
+  static constexpr int BKC = 128;                // keys per workgroup (32 per wave)
+  static constexpr int BQ = kTrCols;             // queries per tile (64)
+  static constexpr int KPL = Mfma<T>::KPL;
+  static constexpr int KM = 2 * KPL;
+  static constexpr int NKS = D / KM;
+  static constexpr int NU = steps32<T>();
+  static constexpr int E16 = 16 / sizeof(T);
+  static constexpr int QP = D + E16;             // row pitch of the Q and dO tiles
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = DkvTile<T, D>;
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr bool kPerm = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) T Qs[C::BQ * C::QP];
+  __shared__ __attribute__((aligned(16))) T Gs[C::BQ * C::QP];      // dO
+  __shared__ __attribute__((aligned(16))) T Qt[D * kTrPitch];
+  __shared__ __attribute__((aligned(16))) T Gt[D * kTrPitch];
   __shared__ __attribute__((aligned(16))) float lse2s[C::BQ];
   __shared__ __attribute__((aligned(16))) float dls[C::BQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, col = lane & 31, h = lane >> 5;
   const int N = a.N;
-  const int k0 = blockIdx.x * C::BKC;
-  const size_t head = (size_t)blockIdx.z * a.H + blockIdx.y;
-  const size_t hoff = head * N * D;
-  const T* Q = static_cast<const T*>(a.q) + hoff;
-  const T* K = static_cast<const T*>(a.k) + hoff;
-  const T* V = static_cast<const T*>(a.v) + hoff;
-  const T* dO = static_cast<const T*>(a.dout) + hoff;
+  const int ntk = gridDim.x;
+  const int lin = xcd_work_index();
+  // Under the causal mask the key tiles near the start see the most queries and
+  // come first in each head's range.
+  const int kt = lin % ntk;
+  const int k0 = kt * C::BKC;
+  const size_t head = (size_t)(lin / ntk);
+  const T* Q = static_cast<const T*>(a.q) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head * N * D;
+  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  const T* dO = static_cast<const T*>(a.dout) + head * N * D;
   const float* LSE = a.lse + head * N;
   const float* Dl = a.delta + head * N;
-  float* dQacc = a.dq_acc + hoff;
   const float c = a.scale * kLog2e;
 
-  const int kw = k0 + 32 * w;   // first key of this wave
-  const int myk = kw + col;     // the key of this lane (column of S)
-
-  // K tile of the workgroup in LDS (read transposed by the dQ product).
-  for (int ch = tid; ch < C::BKC * C::CPR; ch += C::NT) {
-    const int row = ch / C::CPR, cc = ch % C::CPR;
-    uint4 x = uint4{0, 0, 0, 0};
-    if (k0 + row < N) x = *reinterpret_cast<const uint4*>(K + (size_t)(k0 + row) * D + cc * C::E16);
-    *reinterpret_cast<uint4*>(&Ks[row * C::PITCH + cc * C::E16]) = x;
-  }
-  // K and V operands of this lane's key, held for the whole kernel.
+  const int kw = k0 + 32 * w;    // first key of this wave
+  const int myk = kw + col;      // this lane's key (column of S)
+  const int kg = min(myk, N - 1);
+  // K and V operands (B of S = Q K^T and of dP = dO V^T) of this lane's key.
   frag kf[C::NKS], vf[C::NKS];
 #pragma unroll
   for (int ks = 0; ks < C::NKS; ++ks) {
-    kf[ks] = frag{};
-    vf[ks] = frag{};
-    if (myk < N) {
-      kf[ks] = load_frag<T>(K + (size_t)myk * D + ks * C::KM + C::KPL * h);
-      vf[ks] = load_frag<T>(V + (size_t)myk * D + ks * C::KM + C::KPL * h);
-    }
+    kf[ks] = load_frag<T>(K + (size_t)kg * D + ks * C::KM + C::KPL * h);
+    vf[ks] = load_frag<T>(V + (size_t)kg * D + ks * C::KM + C::KPL * h);
   }
   f32x16 dv[D / 32], dk[D / 32];
 #pragma unroll
@@ -136,116 +258,90 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs a) {
     dv[db] = f32x16{};
     dk[db] = f32x16{};
   }
+  // Query (inside a 32-query block) of result element i of this lane:
+  // qoff_of(i) + hoff (rows of the Q and dO operands are permuted for 16-bit types).
+  const int qrow = kPerm ? perm16(col) : col;
+  const int hoff = kPerm ? 8 * h : 4 * h;
+  auto qoff_of = [](int i) {
+    const int r = 8 * (i >> 2) + (i & 3);
+    return kPerm ? perm16(r) : r;
+  };
 
   const int nqt = (N + C::BQ - 1) / C::BQ;
   const int qt0 = CAUSAL ? k0 / C::BQ : 0;   // earlier query tiles see none of these keys
+  TileStage<T, D> qs_stage, gs_stage;
+  if (qt0 < nqt) {
+    qs_stage.load(Q, qt0 * C::BQ, N, tid);
+    gs_stage.load(dO, qt0 * C::BQ, N, tid);
+  }
   for (int qt = qt0; qt < nqt; ++qt) {
     const int qi0 = qt * C::BQ;
-    __syncthreads();   // previous tile's LDS reads are done
-    for (int ch = tid; ch < C::BQ * C::CPR; ch += C::NT) {
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      uint4 xq = uint4{0, 0, 0, 0}, xo = uint4{0, 0, 0, 0};
-      if (qi0 + row < N) {
-        const size_t off = (size_t)(qi0 + row) * D + cc * C::E16;
-        xq = *reinterpret_cast<const uint4*>(Q + off);
-        xo = *reinterpret_cast<const uint4*>(dO + off);
-      }
-      *reinterpret_cast<uint4*>(&Qs[row * C::PITCH + cc * C::E16]) = xq;
-      *reinterpret_cast<uint4*>(&dOs[row * C::PITCH + cc * C::E16]) = xo;
-    }
-    for (int r = tid; r < C::BQ; r += C::NT) {
-      const int qq = qi0 + r;
+    qs_stage.store_rows(Qs, C::QP, tid);
+    qs_stage.store_transposed(Qt, tid);
+    gs_stage.store_rows(Gs, C::QP, tid);
+    gs_stage.store_transposed(Gt, tid);
+    if (tid < C::BQ) {
+      const int qq = qi0 + tid;
       float l2 = INFINITY, dd = 0.f;   // rows past N (or with no visible key) get P = 0
       if (qq < N) {
         const float lse = LSE[qq];
         if (lse != -INFINITY) l2 = lse * kLog2e;
         dd = Dl[qq];
       }
-      lse2s[r] = l2;
-      dls[r] = dd;
+      lse2s[tid] = l2;
+      dls[tid] = dd;
     }
     __syncthreads();
-
-    const bool idle = CAUSAL && (qi0 + C::BQ - 1 < kw);   // every query of the tile precedes every key
-    if (idle) {
+    if (qt + 1 < nqt) {
+      qs_stage.load(Q, qi0 + C::BQ, N, tid);
+      gs_stage.load(dO, qi0 + C::BQ, N, tid);
+    }
+    // Every query of the tile precedes every key of this wave: nothing to do.
+    const bool idle = CAUSAL && (qi0 + C::BQ - 1 < kw);
+    if (!idle) {
 #pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          store4<T>(&dSt[(32 * w + col) * C::SPITCH + qb * 32 + 8 * r + 4 * h], 0.f, 0.f, 0.f, 0.f);
-    } else {
-      f32x16 p[C::NQB], ds[C::NQB];
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) {
+      for (int qb = 0; qb < 2; ++qb) {
         f32x16 s = f32x16{}, dp = f32x16{};
+        const T* qr = &Qs[(qb * 32 + qrow) * C::QP + C::KPL * h];
+        const T* gr = &Gs[(qb * 32 + qrow) * C::QP + C::KPL * h];
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-          const int off = (qb * 32 + col) * C::PITCH + ks * C::KM + C::KPL * h;
-          s = M::mma(load_frag<T>(&Qs[off]), kf[ks], s);
-          dp = M::mma(load_frag<T>(&dOs[off]), vf[ks], dp);
+          s = M::mma(load_frag<T>(qr + ks * C::KM), kf[ks], s);
+          dp = M::mma(load_frag<T>(gr + ks * C::KM), vf[ks], dp);
         }
-        const bool mask = (myk >= N) || (CAUSAL && qi0 + qb * 32 < kw + 31);
+        const int qb0 = qi0 + qb * 32;
+        const bool masked = (myk >= N) || (CAUSAL && qb0 < kw + 31);
+        f32x16 ds;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[qb * 32 + 8 * r + 4 * h]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dls[qb * 32 + 8 * r + 4 * h]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * r + e;
-            float pv = exp2_fast(fmaf(s[i], c, -l4[e]));
-            if (mask) {
-              const int qq = qi0 + qb * 32 + 8 * r + 4 * h + e;
-              if (myk >= N || (CAUSAL && qq < myk)) pv = 0.f;
-            }
-            p[qb][i] = pv;
-            ds[qb][i] = pv * (dp[i] - d4[e]);
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int qo = qb * 32 + qoff_of(i) + hoff;
+          float p = exp2_fast(fmaf(s[i], c, -lse2s[qo]));
+          if (masked && (myk >= N || (CAUSAL && qi0 + qo < myk))) p = 0.f;
+          s[i] = p;
+          ds[i] = p * (dp[i] - dls[qo]);
         }
-      }
-      // dV += P^T dO and dK += dS^T Q  (contraction over the tile's queries)
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb)
+        // dV += P^T dO and dK += dS^T Q (contraction over the block's queries):
+        // B operand = 8 consecutive queries of one head-dim row of dO^T / Q^T.
 #pragma unroll
         for (int u = 0; u < C::NU; ++u) {
-          const frag pa = pack_frag<T>(p[qb], u);
-          const frag sa = pack_frag<T>(ds[qb], u);
+          const frag pa = pack_frag<T>(s, u);
+          const frag sa = pack_frag<T>(ds, u);
+          const int qofs = qb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            dv[db] = M::mma(pa, load_frag_tr<T>(dOs, C::PITCH, qb * 32, u, db * 32, lane), dv[db]);
-            dk[db] = M::mma(sa, load_frag_tr<T>(Qs, C::PITCH, qb * 32, u, db * 32, lane), dk[db]);
+            const int idx = tr_index<T>(db * 32 + col, qofs);
+            dv[db] = M::mma(pa, load_frag<T>(&Gt[idx]), dv[db]);
+            dk[db] = M::mma(sa, load_frag<T>(&Qt[idx]), dk[db]);
           }
         }
-      // dS^T (keys x queries) to LDS for the dQ product.
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          store4<T>(&dSt[(32 * w + col) * C::SPITCH + qb * 32 + 8 * r + 4 * h], ds[qb][4 * r],
-                    ds[qb][4 * r + 1], ds[qb][4 * r + 2], ds[qb][4 * r + 3]);
-    }
-    __syncthreads();
-
-    // dQacc[tile] += dS K over the workgroup's 128 keys; 32x32 blocks split over waves.
-    for (int bi = w; bi < C::NDQ; bi += 4) {
-      const int qb = bi / (D / 32), db = bi % (D / 32);
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < C::BKC / 32; ++kb)
-#pragma unroll
-        for (int u = 0; u < C::NU; ++u)
-          acc = M::mma(load_frag_tr<T>(dSt, C::SPITCH, kb * 32, u, qb * 32, lane),
-                       load_frag_tr<T>(Ks, C::PITCH, kb * 32, u, db * 32, lane), acc);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qq = qi0 + qb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (qq < N) unsafeAtomicAdd(&dQacc[(size_t)qq * D + db * 32 + col], acc[i]);
       }
     }
+    __syncthreads();
   }
 
-  // Epilogue: dK = scale * dS^T Q, dV; lane (col = d, h) holds keys 8(i/4) + 4h + i%4.
-  T* dK = static_cast<T*>(a.dk) + hoff;
-  T* dV = static_cast<T*>(a.dv) + hoff;
+  // Epilogue: lane (col = d, h) holds keys kw + 8(i/4) + 4h + i%4.
+  T* dK = static_cast<T*>(a.dk) + head * N * D;
+  T* dV = static_cast<T*>(a.dv) + head * N * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -259,37 +355,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(BwdArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ dQ finalize
-
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, long n4) {
-  const float* acc = a.dq_acc;
-  T* dq = static_cast<T*>(a.dq);
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(acc + 4 * i);
-    store4<T>(dq + 4 * i, x[0] * a.scale, x[1] * a.scale, x[2] * a.scale, x[3] * a.scale);
-  }
-}
-
 // ------------------------------------------------------------------ launchers
 
-enum class Step { pre, main, fin };
+enum class Step { pre, dkdv, dq };
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(Step step, const BwdArgs& a, hipStream_t s) {
-  using C = BwdTile<T, D>;
   const long rows = (long)a.B * a.H * a.N;
   if (step == Step::pre) {
     constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
     const long blocks = (rows + RPB - 1) / RPB;
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a, rows);
-  } else if (step == Step::main) {
-    dim3 grid((a.N + C::BKC - 1) / C::BKC, a.H, a.B);
-    hipLaunchKernelGGL((bwd_kernel<T, D, CAUSAL>), grid, dim3(C::NT), 0, s, a);
+  } else if (step == Step::dkdv) {
+    dim3 grid((a.N + DkvTile<T, D>::BKC - 1) / DkvTile<T, D>::BKC, a.H, a.B);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
   } else {
-    const long n4 = rows * D / 4;
-    const long blocks = n4 / 256 < 8192 ? (n4 + 255) / 256 : 8192;
-    hipLaunchKernelGGL((bwd_dq_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, s, a, n4);
+    dim3 grid((a.N + DqTile<T, D>::BR - 1) / DqTile<T, D>::BR, a.H, a.B);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -317,12 +399,12 @@ hipError_t launch_bwd_pre(Dt dt, int d, const BwdArgs& a, hipStream_t s) {
   return launch_step(Step::pre, dt, d, false, a, s);
 }
 
-hipError_t launch_bwd_main(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s) {
-  return launch_step(Step::main, dt, d, causal, a, s);
+hipError_t launch_bwd_dkdv(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s) {
+  return launch_step(Step::dkdv, dt, d, causal, a, s);
 }
 
-hipError_t launch_bwd_fin(Dt dt, int d, const BwdArgs& a, hipStream_t s) {
-  return launch_step(Step::fin, dt, d, false, a, s);
+hipError_t launch_bwd_dq(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s) {
+  return launch_step(Step::dq, dt, d, causal, a, s);
 }
 
 }  // namespace fa

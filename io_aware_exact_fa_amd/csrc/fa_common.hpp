@@ -214,6 +214,65 @@ __device__ inline int perm16(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// ---------------------------------------------------------------- transposed LDS tiles
+
+// Index of element (row, col) in a transposed LDS tile whose rows (one per head
+// dimension) hold 64 consecutive keys or queries.  The 16-byte chunks of each
+// row are XOR-swizzled by the row so that (a) the transposed stores of the
+// 4-row x 16-byte register groups and (b) the 16-byte operand reads of 32
+// consecutive rows both hit distinct LDS banks (64 banks x 4 bytes).  Pitch:
+// kTrPitch elements.
+constexpr int kTrCols = 64;
+constexpr int kTrPitch = kTrCols + 8;
+
+template <typename T>
+__device__ inline int tr_index(int row, int col) {
+  constexpr int KPC = 16 / sizeof(T);                      // elements per 16-byte chunk
+  const int swz = sizeof(T) == 2 ? (row >> 4) & 7 : (row >> 2) & 15;
+  return row * kTrPitch + ((col / KPC) ^ swz) * KPC + (col % KPC);
+}
+
+// A [64 x D] tile (rows = keys or queries) staged global -> registers in groups of
+// 4 rows x 16 bytes (group g: column chunk g % CPR, rows 4 (g / CPR) .. +3), then
+// stored row-major and/or transposed into LDS.  Rows past `nvalid` are clamped to
+// the last valid row (callers mask their contribution).
+template <typename T, int D>
+struct TileStage {
+  static constexpr int E16 = 16 / sizeof(T);
+  static constexpr int CPR = D / E16;
+  static constexpr int NG = (kTrCols / 4) * CPR;
+  static constexpr int GPT = (NG + 255) / 256;
+  uint4 x[GPT][4];
+
+  __device__ inline void load(const T* src, int row0, int nvalid, int tid) {
+#pragma unroll
+    for (int r = 0; r < GPT; ++r) {
+      const int g = tid + 256 * r;
+      const int dg = g % CPR, rg = g / CPR;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(row0 + 4 * rg + i, nvalid - 1);
+        if (g < NG) x[r][i] = *reinterpret_cast<const uint4*>(src + (size_t)row * D + dg * E16);
+      }
+    }
+  }
+  // Row-major copy: element (row, c) at dst[row * pitch + c].
+  __device__ inline void store_rows(T* dst, int pitch, int tid) const {
+#pragma unroll
+    for (int r = 0; r < GPT; ++r) {
+      const int g = tid + 256 * r;
+      const int dg = g % CPR, rg = g / CPR;
+      if (g < NG) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<uint4*>(dst + (4 * rg + i) * pitch + dg * E16) = x[r][i];
+      }
+    }
+  }
+  // Transposed copy: element (row, c) at dst[tr_index(c, row)].
+  __device__ inline void store_transposed(T* dst, int tid) const;
+};
+
 // ---------------------------------------------------------------- stores
 
 // Store 4 consecutive values (rounded to T) at p.
@@ -235,5 +294,21 @@ __device__ inline void store4<_Float16>(_Float16* p, float a, float b, float c, 
 }
 
 template <typename T> __device__ inline float to_f32(T x) { return (float)x; }
+
+template <typename T, int D>
+__device__ inline void TileStage<T, D>::store_transposed(T* dst, int tid) const {
+#pragma unroll
+  for (int r = 0; r < GPT; ++r) {
+    const int g = tid + 256 * r;
+    const int dg = g % CPR, rg = g / CPR;
+    if (g < NG) {
+      const int c0 = dg * E16;
+      // The E16 transposed rows c0..c0+E16-1 share one swizzle (it changes every
+      // 16 rows for 16-bit types and every 4 rows for f32), so one base index
+      // serves all of them.
+      store_transposed4<T>(dst + tr_index<T>(c0, 4 * rg), kTrPitch, x[r]);
+    }
+  }
+}
 
 }  // namespace fa

@@ -178,94 +178,103 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY;   // running max of c*S (log2 units)
   float l_run = 0.f;         // this lane's share of the running normalizer
 
+  // S^T for one 32-key block of the tile in buffer `buf`.
+  auto s_block = [&](int buf, int kb) {
+    const T* krowp = &Ks[buf][(kb * 32 + krow) * C::KP + C::KPL * h];
+    frag kf[C::NKS];
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) kf[ks] = load_frag<T>(krowp + ks * C::KM);
+    f32x16 sb = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) sb = M::mma(kf[ks], qf[ks], sb);
+    return sb;
+  };
+  // Online softmax of one 32-key block (keys key0..key0+31): masks, updates the
+  // running max / normalizer, rescales the accumulator when the max grew, and
+  // leaves P~ in sb.
+  auto softmax_block = [&](f32x16& sb, int key0) {
+    const bool masked = (CAUSAL && key0 + 31 > qw) || (key0 + 32 > N);
+    if (masked) {
+      // Visible keys of this lane's row: key <= myq (causal) and key < N.
+      const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - key0 - hoff;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0_of(i) > lim) sb[i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sb[i]);
+    mx = half_max(mx);
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+    // Rescale only when the max of some row of the wave grew.  The max is tracked
+    // exactly so that the largest P~ of a row is exactly 1 and its rounding to
+    // the 16-bit operand type costs nothing (it dominates peaked rows).
+    if (__any(mt > m_run)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    if (masked) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = sb[i];
+        const float p = (x == -INFINITY) ? 0.f : exp2_fast(fmaf(x, c, nm));   // exact for c == 0
+        sb[i] = p;
+        ps[i & 3] += p;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2_fast(fmaf(sb[i], c, nm));
+        sb[i] = p;
+        ps[i & 3] += p;
+      }
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+  // O^T += V^T P~^T for one 32-key block: A operand = 8 consecutive keys of one
+  // head-dim row of V^T.
+  auto pv_block = [&](int buf, int kb, const f32x16& pb) {
+    const T* Vb = Vt[buf];
+#pragma unroll
+    for (int u = 0; u < C::NU; ++u) {
+      const frag pf = pack_frag<T>(pb, u);
+      const int kofs = kb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int d = db * 32 + col;
+        acc[db] = M::mma(load_frag<T>(&Vb[d * C::VP + vt_index<T>(d, kofs)]), pf, acc[db]);
+      }
+    }
+  };
+
+  // Software pipeline over 32-key blocks: the S MFMAs of the next block are issued
+  // before the softmax of the current one, so the matrix core works while the
+  // vector unit computes exponentials.  One barrier per tile; K/V double-buffered.
   gload(0);
   sstore(0);
+  if (ntiles > 1) gload(1);
   __syncthreads();
+  f32x16 s0 = f32x16{};
+  if (wlast >= 0) s0 = s_block(0, 0);
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
     if (j <= wlast) {
-      const int key0 = j * C::BC;
-      const T* Kb = Ks[buf];
-      const T* Vb = Vt[buf];
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        frag kf[C::NKS];
-        const T* krowp = &Kb[(kb * 32 + krow) * C::KP + C::KPL * h];
-#pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) kf[ks] = load_frag<T>(krowp + ks * C::KM);
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) s[kb] = M::mma(kf[ks], qf[ks], s[kb]);
-      }
-      const bool masked = (CAUSAL && key0 + C::BC - 1 > qw) || (key0 + C::BC > N);
-      if (masked) {
-        // Visible keys of this lane's row: key <= myq (causal) and key < N.
-        const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - key0 - hoff;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (kb * 32 + key0_of(i) > lim) s[kb][i] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = half_max(mx);
-      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-      // Rescale only when the max of some row of the wave grew.  The max is tracked
-      // exactly so that the largest P~ of a row is exactly 1 and its rounding to
-      // the 16-bit operand type costs nothing (it dominates peaked rows).
-      if (__any(mt > m_run)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-        m_run = m_new;
-      }
-      const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
-      if (masked) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float x = s[kb][i];
-            const float p = (x == -INFINITY) ? 0.f : exp2_fast(fmaf(x, c, nm));   // exact for c == 0
-            s[kb][i] = p;
-            ps[i & 3] += p;
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = exp2_fast(fmaf(s[kb][i], c, nm));
-            s[kb][i] = p;
-            ps[i & 3] += p;
-          }
-      }
-      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-      // O^T += V_j^T P~^T: A operand = 8 consecutive keys of one head-dim row of V^T.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int u = 0; u < C::NU; ++u) {
-          const frag pf = pack_frag<T>(s[kb], u);
-          const int kofs = kb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const int d = db * 32 + col;
-            acc[db] = M::mma(load_frag<T>(&Vb[d * C::VP + vt_index<T>(d, kofs)]), pf, acc[db]);
-          }
-        }
+      f32x16 s1 = s_block(buf, 1);
+      softmax_block(s0, j * C::BC);
+      pv_block(buf, 0, s0);
+      softmax_block(s1, j * C::BC + 32);
+      pv_block(buf, 1, s1);
     }
     if (j + 1 < ntiles) sstore(buf ^ 1);
     __syncthreads();
+    if (j + 2 < ntiles) gload(j + 2);
+    if (j + 1 <= wlast) s0 = s_block(buf ^ 1, 0);
   }
 
   const float l = half_sum(l_run);

@@ -28,8 +28,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;   // [B,H,N]   workspace
-  float* dq_acc;  // [B,H,N,d] workspace
+  float* delta;   // [B,H,N] workspace: D_i = rowsum(dO_i * O_i)
   int B, H, N;
   float scale;
 };
@@ -37,11 +36,10 @@ struct BwdArgs {
 enum class Dt { f32 = 0, f16 = 1, bf16 = 2 };
 
 hipError_t launch_fwd(Dt dt, int d, bool causal, const FwdArgs& a, hipStream_t s);
-// The backward in three launches: D and the zeroed dQ accumulator; dK, dV and
-// the dQ accumulation; dq = scale * accumulator.  Only the fields each step
+// The backward in three launches: D; dK and dV; dQ.  Only the fields each step
 // reads or writes need to be set.
 hipError_t launch_bwd_pre(Dt dt, int d, const BwdArgs& a, hipStream_t s);
-hipError_t launch_bwd_main(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s);
-hipError_t launch_bwd_fin(Dt dt, int d, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dkdv(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s);
 
 }  // namespace fa

@@ -105,21 +105,24 @@ def test_split_backward_rejects():
     assert fa.fa_bwd_preprocess(None, P, 1, 1, 128, 64, fa.FA_F16, ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
     assert fa.fa_bwd_preprocess(P, P, 1, 1, 128, 96, fa.FA_F16, ws, nb, None) == fa.FA_ERR_UNSUPPORTED
     assert fa.fa_bwd_preprocess(P, P, 1, 1, 128, 64, fa.FA_F16, ws, nb - 1, None) == fa.FA_ERR_WORKSPACE
-    assert fa.fa_bwd_main(P, P, P, P, P, P, None, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws, nb,
+    assert fa.fa_bwd_dkdv(P, P, P, P, P, P, None, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws, nb,
                           None) == fa.FA_ERR_INVALID_ARGUMENT
-    assert fa.fa_bwd_main(P, P, P, P, P, P, P, 1, 1, 128, 64, 0, math.nan, fa.FA_F16, ws, nb,
+    assert fa.fa_bwd_dkdv(P, P, P, P, P, P, P, 1, 1, 128, 64, 0, math.nan, fa.FA_F16, ws, nb,
                           None) == fa.FA_ERR_INVALID_ARGUMENT
-    assert fa.fa_bwd_main(P, P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws + 8, nb,
+    assert fa.fa_bwd_dkdv(P, P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws + 8, nb,
                           None) == fa.FA_ERR_WORKSPACE
-    assert fa.fa_bwd_finalize(None, 1, 1, 128, 64, 0.1, fa.FA_F16, ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
-    assert fa.fa_bwd_finalize(P, 1, 1, 128, 64, 0.1, 5, ws, nb, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_dq(P, P, P, P, P, None, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws, nb,
+                        None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_bwd_dq(P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, 5, ws, nb, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_dq(P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws, nb - 1,
+                        None) == fa.FA_ERR_WORKSPACE
 
 
 def test_workspace_size():
     B, H, N, d = 2, 3, 100, 64
     rows = B * H * N
     up = lambda x: (x + 255) // 256 * 256
-    assert fa.fa_bwd_workspace_size(B, H, N, d) == up(4 * rows) + up(4 * rows * d)
+    assert fa.fa_bwd_workspace_size(B, H, N, d) == up(4 * rows)
     assert fa.fa_bwd_workspace_size(0, 1, 1, 64) == 0
     assert fa.fa_bwd_workspace_size(1, 1, -3, 64) == 0
 
@@ -135,7 +138,8 @@ def test_valid_arguments_without_gpu_report_device_error():
     assert _bwd() == fa.FA_ERR_DEVICE
     nb = fa.fa_bwd_workspace_size(1, 1, 128, 64)
     assert fa.fa_bwd_preprocess(P, P, 1, 1, 128, 64, fa.FA_F16, 0x10000, nb, None) == fa.FA_ERR_DEVICE
-    assert fa.fa_bwd_finalize(P, 1, 1, 128, 64, 0.1, fa.FA_F16, 0x10000, nb, None) == fa.FA_ERR_DEVICE
+    assert fa.fa_bwd_dq(P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, 0x10000, nb,
+                        None) == fa.FA_ERR_DEVICE
 
 
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):

@@ -205,7 +205,7 @@ def test_repeatable_and_delta(fa):
     inp = workloads.make_inputs(w)
     a = gpu_run(fa, inp, True, w.scale)
     b = gpu_run(fa, inp, True, w.scale)
-    for name in ("o", "lse", "dk", "dv"):
+    for name in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(a[name], b[name]), f"{name} differs between runs"
     # D = rowsum(dO * O) sits at the start of the workspace.
     rows = 2 * 2 * 333
