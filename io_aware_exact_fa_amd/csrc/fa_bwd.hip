@@ -71,7 +71,12 @@ __device__ inline int xcd_work_index() {
 
 template <typename T, int D>
 struct DqTile {
-  static constexpr int BR = 128;                 // queries per workgroup
+  // 16-bit types: 8 waves x 32 queries, so each K/V tile streamed from L2 serves
+  // 256 query rows; f32 keeps 4 waves (1 wave per SIMD for registers).
+  static constexpr int NW = sizeof(T) == 2 ? 8 : 4;
+  static constexpr int NT = 64 * NW;
+  static constexpr int WAVES_PER_SIMD = sizeof(T) == 2 ? 2 : 1;
+  static constexpr int BR = 32 * NW;             // queries per workgroup
   static constexpr int BC = kTrCols;             // keys per tile (64)
   static constexpr int KPL = Mfma<T>::KPL;
   static constexpr int KM = 2 * KPL;
@@ -82,7 +87,8 @@ struct DqTile {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__((DqTile<T, D>::NT), (DqTile<T, D>::WAVES_PER_SIMD))
+void bwd_dq_kernel(BwdArgs a) {
   using C = DqTile<T, D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
-  TileStage<T, D> ks_stage, vs_stage;
+  TileStage<T, D, C::NT> ks_stage, vs_stage;
   ks_stage.load(K, 0, N, tid);
   vs_stage.load(V, 0, N, tid);
   for (int j = 0; j < ntiles; ++j) {
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int nqt = (N + C::BQ - 1) / C::BQ;
   const int qt0 = CAUSAL ? k0 / C::BQ : 0;   // earlier query tiles see none of these keys
-  TileStage<T, D> qs_stage, gs_stage;
+  TileStage<T, D, 256> qs_stage, gs_stage;
   if (qt0 < nqt) {
     qs_stage.load(Q, qt0 * C::BQ, N, tid);
     gs_stage.load(dO, qt0 * C::BQ, N, tid);
@@ -371,7 +377,7 @@ static hipError_t launch_bwd_t(Step step, const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
   } else {
     dim3 grid((a.N + DqTile<T, D>::BR - 1) / DqTile<T, D>::BR, a.H, a.B);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(DqTile<T, D>::NT), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -232,22 +232,22 @@ __device__ inline int tr_index(int row, int col) {
   return row * kTrPitch + ((col / KPC) ^ swz) * KPC + (col % KPC);
 }
 
-// A [64 x D] tile (rows = keys or queries) staged global -> registers in groups of
-// 4 rows x 16 bytes (group g: column chunk g % CPR, rows 4 (g / CPR) .. +3), then
+// A [64 x D] tile (rows = keys or queries) staged global -> registers by NT threads
+// in groups of 4 rows x 16 bytes (group g: column chunk g % CPR, rows 4 (g / CPR) .. +3), then
 // stored row-major and/or transposed into LDS.  Rows past `nvalid` are clamped to
 // the last valid row (callers mask their contribution).
-template <typename T, int D>
+template <typename T, int D, int NT>
 struct TileStage {
   static constexpr int E16 = 16 / sizeof(T);
   static constexpr int CPR = D / E16;
   static constexpr int NG = (kTrCols / 4) * CPR;
-  static constexpr int GPT = (NG + 255) / 256;
+  static constexpr int GPT = (NG + NT - 1) / NT;
   uint4 x[GPT][4];
 
   __device__ inline void load(const T* src, int row0, int nvalid, int tid) {
 #pragma unroll
     for (int r = 0; r < GPT; ++r) {
-      const int g = tid + 256 * r;
+      const int g = tid + NT * r;
       const int dg = g % CPR, rg = g / CPR;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -260,7 +260,7 @@ struct TileStage {
   __device__ inline void store_rows(T* dst, int pitch, int tid) const {
 #pragma unroll
     for (int r = 0; r < GPT; ++r) {
-      const int g = tid + 256 * r;
+      const int g = tid + NT * r;
       const int dg = g % CPR, rg = g / CPR;
       if (g < NG) {
 #pragma unroll
@@ -295,11 +295,11 @@ __device__ inline void store4<_Float16>(_Float16* p, float a, float b, float c, 
 
 template <typename T> __device__ inline float to_f32(T x) { return (float)x; }
 
-template <typename T, int D>
-__device__ inline void TileStage<T, D>::store_transposed(T* dst, int tid) const {
+template <typename T, int D, int NT>
+__device__ inline void TileStage<T, D, NT>::store_transposed(T* dst, int tid) const {
 #pragma unroll
   for (int r = 0; r < GPT; ++r) {
-    const int g = tid + 256 * r;
+    const int g = tid + NT * r;
     const int dg = g % CPR, rg = g / CPR;
     if (g < NG) {
       const int c0 = dg * E16;

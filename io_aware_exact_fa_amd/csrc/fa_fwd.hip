@@ -37,9 +37,13 @@ namespace fa {
 
 template <typename T, int D>
 struct FwdTile {
-  static constexpr int BR = 128;                 // query rows per workgroup
+  // 16-bit types: 8 waves x 32 query rows, so each K/V tile streamed from L2
+  // serves 256 rows (the tile traffic, not the MFMA work, bounded 4-wave tiles);
+  // f32 (1 wave per SIMD for registers) keeps 4 waves.
+  static constexpr int NW = sizeof(T) == 2 ? 8 : 4;
+  static constexpr int BR = 32 * NW;             // query rows per workgroup
   static constexpr int BC = 64;                  // keys per tile
-  static constexpr int NT = 256;                 // threads per workgroup
+  static constexpr int NT = 64 * NW;             // threads per workgroup
   static constexpr int KPL = Mfma<T>::KPL;
   static constexpr int KM = 2 * KPL;             // MFMA k depth
   static constexpr int NKS = D / KM;             // MFMAs per 32x32 block of S
@@ -51,6 +55,7 @@ struct FwdTile {
   static constexpr int KCPT = BC * CPR / NT;     // K chunks per thread per tile
   static constexpr int VGRP = (BC / 4) * CPR;    // 4-key x 16-byte V groups per tile
   static constexpr int VGPT = (VGRP + NT - 1) / NT;
+  static constexpr int WAVES_PER_SIMD = sizeof(T) == 2 ? 2 : 1;
   static constexpr int KS_EL = BC * KP;          // one K buffer, elements
   static constexpr int VS_EL = D * VP;           // one V^T buffer, elements
   static_assert(BC * CPR % NT == 0, "K tile must split evenly over the threads");
@@ -69,7 +74,8 @@ __device__ inline int vt_index(int d, int key) {
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__((FwdTile<T, D>::NT), (FwdTile<T, D>::WAVES_PER_SIMD))
+void fwd_kernel(FwdArgs a) {
   using C = FwdTile<T, D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
@@ -132,17 +138,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     return kPerm ? perm16(r) : r;
   };
 
-  // Staging registers: the next tile's K chunks and V groups.  Rows past N are
-  // clamped to row N-1: their scores are masked to -inf and their P~ set to 0.
+  // Staging registers: K of tile j+2 and V of tile j+1 while tile j is computed.
+  // Rows past N are clamped to row N-1: their scores are masked to -inf and their
+  // P~ set to 0.
   uint4 kst[C::KCPT];
   uint4 vst[C::VGPT][4];
-  auto gload = [&](int j) {
+  auto gload_k = [&](int j) {
     const int key0 = j * C::BC;
 #pragma unroll
     for (int r = 0; r < C::KCPT; ++r) {
       const int ch = tid + r * C::NT, row = ch / C::CPR, cc = ch % C::CPR;
       kst[r] = *reinterpret_cast<const uint4*>(K + (size_t)min(key0 + row, N - 1) * D + cc * C::E16);
     }
+  };
+  auto gload_v = [&](int j) {
+    const int key0 = j * C::BC;
 #pragma unroll
     for (int r = 0; r < C::VGPT; ++r) {
       const int g = tid + r * C::NT;
@@ -154,12 +164,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore_k = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < C::KCPT; ++r) {
       const int ch = tid + r * C::NT, row = ch / C::CPR, cc = ch % C::CPR;
       *reinterpret_cast<uint4*>(&Ks[buf][row * C::KP + cc * C::E16]) = kst[r];
     }
+  };
+  auto sstore_v = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < C::VGPT; ++r) {
       const int g = tid + r * C::NT;
@@ -178,103 +190,131 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY;   // running max of c*S (log2 units)
   float l_run = 0.f;         // this lane's share of the running normalizer
 
-  // S^T for one 32-key block of the tile in buffer `buf`.
-  auto s_block = [&](int buf, int kb) {
-    const T* krowp = &Ks[buf][(kb * 32 + krow) * C::KP + C::KPL * h];
-    frag kf[C::NKS];
+  // S^T of one 64-key tile (two 32-key blocks) from K buffer `kbuf`.
+  auto s_tile = [&](int kbuf, f32x16 (&sn)[2]) {
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) kf[ks] = load_frag<T>(krowp + ks * C::KM);
-    f32x16 sb = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) {
+      const T* krowp = &Ks[kbuf][(kb * 32 + krow) * C::KP + C::KPL * h];
+      frag kf[C::NKS];
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) sb = M::mma(kf[ks], qf[ks], sb);
-    return sb;
-  };
-  // Online softmax of one 32-key block (keys key0..key0+31): masks, updates the
-  // running max / normalizer, rescales the accumulator when the max grew, and
-  // leaves P~ in sb.
-  auto softmax_block = [&](f32x16& sb, int key0) {
-    const bool masked = (CAUSAL && key0 + 31 > qw) || (key0 + 32 > N);
-    if (masked) {
-      // Visible keys of this lane's row: key <= myq (causal) and key < N.
-      const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - key0 - hoff;
+      for (int ks = 0; ks < C::NKS; ++ks) kf[ks] = load_frag<T>(krowp + ks * C::KM);
+      sn[kb] = f32x16{};
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (key0_of(i) > lim) sb[i] = -INFINITY;
+      for (int ks = 0; ks < C::NKS; ++ks) sn[kb] = M::mma(kf[ks], qf[ks], sn[kb]);
     }
+  };
+  // P~ = 2^(c S - m) for the tile with reference max m_use, row-sum partials.
+  auto exp_tile = [&](f32x16 (&sc)[2], float m_use, bool masked) {
+    const float nm = -m_use;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = sc[kb][i];
+        float p = exp2_fast(fmaf(x, c, nm));
+        if (masked) p = (x == -INFINITY) ? 0.f : p;   // exact also for c == 0
+        sc[kb][i] = p;
+        ps[i & 3] += p;
+      }
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+  auto tile_max = [&](const f32x16 (&sc)[2]) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sb[i]);
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
     mx = half_max(mx);
-    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-    // Rescale only when the max of some row of the wave grew.  The max is tracked
-    // exactly so that the largest P~ of a row is exactly 1 and its rounding to
-    // the 16-bit operand type costs nothing (it dominates peaked rows).
-    if (__any(mt > m_run)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-      m_run = m_new;
-    }
-    const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-    if (masked) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = sb[i];
-        const float p = (x == -INFINITY) ? 0.f : exp2_fast(fmaf(x, c, nm));   // exact for c == 0
-        sb[i] = p;
-        ps[i & 3] += p;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2_fast(fmaf(sb[i], c, nm));
-        sb[i] = p;
-        ps[i & 3] += p;
-      }
-    }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-  };
-  // O^T += V^T P~^T for one 32-key block: A operand = 8 consecutive keys of one
-  // head-dim row of V^T.
-  auto pv_block = [&](int buf, int kb, const f32x16& pb) {
-    const T* Vb = Vt[buf];
-#pragma unroll
-    for (int u = 0; u < C::NU; ++u) {
-      const frag pf = pack_frag<T>(pb, u);
-      const int kofs = kb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int d = db * 32 + col;
-        acc[db] = M::mma(load_frag<T>(&Vb[d * C::VP + vt_index<T>(d, kofs)]), pf, acc[db]);
-      }
-    }
+    return (mx == -INFINITY) ? -INFINITY : mx * c;
   };
 
-  // Software pipeline over 32-key blocks: the S MFMAs of the next block are issued
-  // before the softmax of the current one, so the matrix core works while the
-  // vector unit computes exponentials.  One barrier per tile; K/V double-buffered.
-  gload(0);
-  sstore(0);
-  if (ntiles > 1) gload(1);
+  // Software pipeline: during iteration j the matrix core computes S of tile j+1
+  // while the vector unit computes the softmax of tile j, then P~_j V_j is
+  // issued.  K therefore runs one tile ahead of V in LDS (two buffers each, one
+  // barrier per iteration): iteration j reads K_{j+1} and V_j and writes
+  // K_{j+2} and V_{j+1}.
+  gload_k(0);
+  gload_v(0);
+  sstore_k(0);
+  sstore_v(0);
+  if (ntiles > 1) {
+    gload_k(1);
+    sstore_k(1);
+  }
   __syncthreads();
-  f32x16 s0 = f32x16{};
-  if (wlast >= 0) s0 = s_block(0, 0);
+  f32x16 sc[2];
+  if (wlast >= 0) s_tile(0, sc);
+  // Iteration 0 overwrites K buffer 0 (read just above) with K_2.
+  __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
+    if (j + 2 < ntiles) gload_k(j + 2);
+    if (j + 1 < ntiles) gload_v(j + 1);
     if (j <= wlast) {
-      f32x16 s1 = s_block(buf, 1);
-      softmax_block(s0, j * C::BC);
-      pv_block(buf, 0, s0);
-      softmax_block(s1, j * C::BC + 32);
-      pv_block(buf, 1, s1);
+      const int key0 = j * C::BC;
+      const bool masked = (CAUSAL && key0 + C::BC - 1 > qw) || (key0 + C::BC > N);
+      f32x16 sn[2];
+      float m_new, lsum;
+      if (!masked) {
+        // One scheduling region: the 16 MFMAs of S_{j+1} interleaved with the
+        // softmax of tile j.  (When j is the last tile the S_{j+1} result is unused;
+        // the reads stay inside the LDS buffers.)
+        s_tile((j + 1) & 1, sn);
+        m_new = fmaxf(m_run, tile_max(sc));
+        lsum = exp_tile(sc, m_new, false);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // 8 LDS reads (K operands)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
+          }
+        }
+      } else {
+        // Visible keys of this lane's row: key <= myq (causal) and key < N.
+        const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - key0 - hoff;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + key0_of(i) > lim) sc[kb][i] = -INFINITY;
+        const float mt = tile_max(sc);
+        m_new = (mt == -INFINITY) ? m_run : fmaxf(m_run, mt);
+        lsum = exp_tile(sc, (m_new == -INFINITY) ? 0.f : m_new, true);
+        s_tile((j + 1) & 1, sn);
+      }
+      // Rescale the accumulator only when the max of some row of the wave grew.  The
+      // max is tracked exactly so that the largest P~ of a row is exactly 1 and its
+      // rounding to the 16-bit operand type costs nothing (it dominates peaked rows).
+      if (__any(m_new > m_run)) {
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      }
+      m_run = m_new;
+      l_run += lsum;
+      // O^T += V_j^T P~^T: A operand = 8 consecutive keys of one head-dim row of V^T.
+      const T* Vb = Vt[j & 1];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u) {
+          const frag pf = pack_frag<T>(sc[kb], u);
+          const int kofs = kb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const int d = db * 32 + col;
+            acc[db] = M::mma(load_frag<T>(&Vb[d * C::VP + vt_index<T>(d, kofs)]), pf, acc[db]);
+          }
+        }
+      sc[0] = sn[0];
+      sc[1] = sn[1];
     }
-    if (j + 1 < ntiles) sstore(buf ^ 1);
+    if (j + 2 < ntiles) sstore_k(j & 1);
+    if (j + 1 < ntiles) sstore_v((j + 1) & 1);
     __syncthreads();
-    if (j + 2 < ntiles) gload(j + 2);
-    if (j + 1 <= wlast) s0 = s_block(buf ^ 1, 0);
   }
 
   const float l = half_sum(l_run);
