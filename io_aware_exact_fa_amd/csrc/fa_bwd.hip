@@ -215,6 +215,9 @@ struct DkvTile {
   static constexpr int NU = steps32<T>();
   static constexpr int E16 = 16 / sizeof(T);
   static constexpr int QP = D + E16;             // row pitch of the Q and dO tiles
+  // Two LDS buffers (one barrier per query tile) when they fit beside each other.
+  static constexpr int BUF_BYTES = (2 * BQ * QP + 2 * D * kTrPitch) * (int)sizeof(T) + 2 * BQ * 4;
+  static constexpr int NBUF = 2 * BUF_BYTES <= 160 * 1024 ? 2 : 1;
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -223,12 +226,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   constexpr bool kPerm = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) T Qs[C::BQ * C::QP];
-  __shared__ __attribute__((aligned(16))) T Gs[C::BQ * C::QP];      // dO
-  __shared__ __attribute__((aligned(16))) T Qt[D * kTrPitch];
-  __shared__ __attribute__((aligned(16))) T Gt[D * kTrPitch];
-  __shared__ __attribute__((aligned(16))) float lse2s[C::BQ];
-  __shared__ __attribute__((aligned(16))) float dls[C::BQ];
+  // Double-buffered query tiles: row-major Q and dO (A operands of S and dP),
+  // transposed Q^T and dO^T (B operands of dK and dV), LSE and D.
+  __shared__ __attribute__((aligned(16))) T Qs[C::NBUF][C::BQ * C::QP];
+  __shared__ __attribute__((aligned(16))) T Gs[C::NBUF][C::BQ * C::QP];      // dO
+  __shared__ __attribute__((aligned(16))) T Qt[C::NBUF][D * kTrPitch];
+  __shared__ __attribute__((aligned(16))) T Gt[C::NBUF][D * kTrPitch];
+  __shared__ __attribute__((aligned(16))) float lse2s[C::NBUF][C::BQ];
+  __shared__ __attribute__((aligned(16))) float dls[C::NBUF][C::BQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, col = lane & 31, h = lane >> 5;
@@ -276,40 +281,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nqt = (N + C::BQ - 1) / C::BQ;
   const int qt0 = CAUSAL ? k0 / C::BQ : 0;   // earlier query tiles see none of these keys
   TileStage<T, D, 256> qs_stage, gs_stage;
-  if (qt0 < nqt) {
-    qs_stage.load(Q, qt0 * C::BQ, N, tid);
-    gs_stage.load(dO, qt0 * C::BQ, N, tid);
-  }
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int qi0 = qt * C::BQ;
-    qs_stage.store_rows(Qs, C::QP, tid);
-    qs_stage.store_transposed(Qt, tid);
-    gs_stage.store_rows(Gs, C::QP, tid);
-    gs_stage.store_transposed(Gt, tid);
+  auto stage_load = [&](int qt) {
+    qs_stage.load(Q, qt * C::BQ, N, tid);
+    gs_stage.load(dO, qt * C::BQ, N, tid);
+  };
+  auto stage_store = [&](int buf, int qt) {
+    qs_stage.store_rows(Qs[buf], C::QP, tid);
+    qs_stage.store_transposed(Qt[buf], tid);
+    gs_stage.store_rows(Gs[buf], C::QP, tid);
+    gs_stage.store_transposed(Gt[buf], tid);
     if (tid < C::BQ) {
-      const int qq = qi0 + tid;
+      const int qq = qt * C::BQ + tid;
       float l2 = INFINITY, dd = 0.f;   // rows past N (or with no visible key) get P = 0
       if (qq < N) {
         const float lse = LSE[qq];
         if (lse != -INFINITY) l2 = lse * kLog2e;
         dd = Dl[qq];
       }
-      lse2s[tid] = l2;
-      dls[tid] = dd;
+      lse2s[buf][tid] = l2;
+      dls[buf][tid] = dd;
     }
-    __syncthreads();
-    if (qt + 1 < nqt) {
-      qs_stage.load(Q, qi0 + C::BQ, N, tid);
-      gs_stage.load(dO, qi0 + C::BQ, N, tid);
-    }
+  };
+  if (qt0 < nqt) {
+    stage_load(qt0);
+    stage_store(0, qt0);
+    if (qt0 + 1 < nqt) stage_load(qt0 + 1);
+  }
+  __syncthreads();
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int qi0 = qt * C::BQ;
+    const int buf = C::NBUF == 2 ? (qt - qt0) & 1 : 0;
     // Every query of the tile precedes every key of this wave: nothing to do.
     const bool idle = CAUSAL && (qi0 + C::BQ - 1 < kw);
     if (!idle) {
+      const T* Qb = Qs[buf];
+      const T* Gb = Gs[buf];
+      const T* Qtb = Qt[buf];
+      const T* Gtb = Gt[buf];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         f32x16 s = f32x16{}, dp = f32x16{};
-        const T* qr = &Qs[(qb * 32 + qrow) * C::QP + C::KPL * h];
-        const T* gr = &Gs[(qb * 32 + qrow) * C::QP + C::KPL * h];
+        const T* qr = &Qb[(qb * 32 + qrow) * C::QP + C::KPL * h];
+        const T* gr = &Gb[(qb * 32 + qrow) * C::QP + C::KPL * h];
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
           s = M::mma(load_frag<T>(qr + ks * C::KM), kf[ks], s);
@@ -321,10 +334,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qo = qb * 32 + qoff_of(i) + hoff;
-          float p = exp2_fast(fmaf(s[i], c, -lse2s[qo]));
+          float p = exp2_fast(fmaf(s[i], c, -lse2s[buf][qo]));
           if (masked && (myk >= N || (CAUSAL && qi0 + qo < myk))) p = 0.f;
           s[i] = p;
-          ds[i] = p * (dp[i] - dls[qo]);
+          ds[i] = p * (dp[i] - dls[buf][qo]);
         }
         // dV += P^T dO and dK += dS^T Q (contraction over the block's queries):
         // B operand = 8 consecutive queries of one head-dim row of dO^T / Q^T.
@@ -336,13 +349,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
             const int idx = tr_index<T>(db * 32 + col, qofs);
-            dv[db] = M::mma(pa, load_frag<T>(&Gt[idx]), dv[db]);
-            dk[db] = M::mma(sa, load_frag<T>(&Qt[idx]), dk[db]);
+            dv[db] = M::mma(pa, load_frag<T>(&Gtb[idx]), dv[db]);
+            dk[db] = M::mma(sa, load_frag<T>(&Qtb[idx]), dk[db]);
           }
         }
       }
     }
-    __syncthreads();
+    if (C::NBUF == 2) {
+      // The other buffer was last read in the previous iteration (before the barrier).
+      if (qt + 1 < nqt) stage_store(buf ^ 1, qt + 1);
+      __syncthreads();
+      if (qt + 2 < nqt) stage_load(qt + 2);
+    } else {
+      __syncthreads();
+      if (qt + 1 < nqt) {
+        stage_store(0, qt + 1);
+        if (qt + 2 < nqt) stage_load(qt + 2);
+      }
+      __syncthreads();
+    }
   }
 
   // Epilogue: lane (col = d, h) holds keys kw + 8(i/4) + 4h + i%4.
