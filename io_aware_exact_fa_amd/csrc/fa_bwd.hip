@@ -279,87 +279,129 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   const int nqt = (N + C::BQ - 1) / C::BQ;
-  const int qt0 = CAUSAL ? k0 / C::BQ : 0;   // earlier query tiles see none of these keys
+  // Earlier query tiles see none of these keys (qt0 < nqt because k0 < N).
+  const int qt0 = CAUSAL ? k0 / C::BQ : 0;
   TileStage<T, D, 256> qs_stage, gs_stage;
+  float lse_st, d_st;   // LSE and D of query row (tile start + lane) of the staged tile
   auto stage_load = [&](int qt) {
     qs_stage.load(Q, qt * C::BQ, N, tid);
     gs_stage.load(dO, qt * C::BQ, N, tid);
+    const int qq = min(qt * C::BQ + lane, N - 1);
+    lse_st = LSE[qq];
+    d_st = Dl[qq];
   };
+  // Every wave writes the same LSE and D values (64 rows, one per lane).
   auto stage_store = [&](int buf, int qt) {
     qs_stage.store_rows(Qs[buf], C::QP, tid);
     qs_stage.store_transposed(Qt[buf], tid);
     gs_stage.store_rows(Gs[buf], C::QP, tid);
     gs_stage.store_transposed(Gt[buf], tid);
-    if (tid < C::BQ) {
-      const int qq = qt * C::BQ + tid;
-      float l2 = INFINITY, dd = 0.f;   // rows past N (or with no visible key) get P = 0
-      if (qq < N) {
-        const float lse = LSE[qq];
-        if (lse != -INFINITY) l2 = lse * kLog2e;
-        dd = Dl[qq];
-      }
-      lse2s[buf][tid] = l2;
-      dls[buf][tid] = dd;
-    }
+    // Rows past N, and rows that see no key at all, get P = exp2(-inf) = 0.
+    const bool live = qt * C::BQ + lane < N && lse_st != -INFINITY;
+    lse2s[buf][lane] = live ? lse_st * kLog2e : INFINITY;
+    dls[buf][lane] = live ? d_st : 0.f;
   };
-  if (qt0 < nqt) {
-    stage_load(qt0);
-    stage_store(0, qt0);
-    if (qt0 + 1 < nqt) stage_load(qt0 + 1);
-  }
+  // The K/V fragments must have landed before the loop, whose waits then cover
+  // only the loads issued inside it.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  stage_load(qt0);
+  stage_store(0, qt0);
+  if (qt0 + 1 < nqt) stage_load(qt0 + 1);
   __syncthreads();
+
+  // One query tile is a fixed stream of NM MFMAs, in issue order:
+  //   [0, NS)            S = Q K^T and dP = dO V^T of block 0 (32 queries)
+  //   [NS, 2NS)          the same for block 1
+  //   [2NS, 2NS+NV)      dV += P^T dO and dK += dS^T Q of block 0
+  //   [2NS+NV, NM)       the same for block 1
+  // The LDS operand of MFMA m (a Q / dO row fragment, or 8 consecutive queries
+  // of one head-dim row of dO^T / Q^T) is read PD slots ahead, and the P / dS
+  // arithmetic of a block, one element at a time, fills the slots between its
+  // S/dP MFMAs and its dV/dK MFMAs, so one wave keeps the matrix unit busy.
+  constexpr int NS = 2 * C::NKS;
+  constexpr int NVB = 2 * (D / 32);
+  constexpr int NV = C::NU * NVB;
+  constexpr int NM = 2 * NS + 2 * NV;
+  constexpr int PD = 4;
+  constexpr int EPU = 16 / C::NU;   // elements of P (and dS) per packed fragment
+  // Slot that computes element i of P/dS of block b (blocks overlap S/dP of
+  // block 1 and dV/dK of block 0 respectively).
+  constexpr auto elem_slot = [](int b, int i) {
+    return b == 0 ? NS + 2 + (i * (NS - 2)) / 16 : 2 * NS + 2 + (i * (NV - 2)) / 16;
+  };
+  auto lds_opnd = [&](int buf, int m) -> frag {
+    if (m < 2 * NS) {
+      const int qb = m / NS, ks = (m % NS) / 2;
+      const T* base = (m & 1) ? Gs[buf] : Qs[buf];
+      return load_frag<T>(&base[(qb * 32 + qrow) * C::QP + C::KPL * h + ks * C::KM]);
+    }
+    const int r = m - 2 * NS, qb = r / NV, u = (r % NV) / NVB, db = (r % NVB) / 2;
+    const int qofs = qb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
+    const T* base = (r & 1) ? Qt[buf] : Gt[buf];
+    return load_frag<T>(&base[tr_index<T>(db * 32 + col, qofs)]);
+  };
+
   for (int qt = qt0; qt < nqt; ++qt) {
     const int qi0 = qt * C::BQ;
     const int buf = C::NBUF == 2 ? (qt - qt0) & 1 : 0;
-    // Every query of the tile precedes every key of this wave: nothing to do.
-    const bool idle = CAUSAL && (qi0 + C::BQ - 1 < kw);
-    if (!idle) {
-      const T* Qb = Qs[buf];
-      const T* Gb = Gs[buf];
-      const T* Qtb = Qt[buf];
-      const T* Gtb = Gt[buf];
+    f32x16 s[2], dp[2], p[2], ds[2];
+    frag pa[2][C::NU], sa[2][C::NU];
+    f32x4 l4[2][4], d4[2][4];   // lse2 and D of 4 consecutive queries, per element group
+    frag opq[PD];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const T* qr = &Qb[(qb * 32 + qrow) * C::QP + C::KPL * h];
-        const T* gr = &Gb[(qb * 32 + qrow) * C::QP + C::KPL * h];
-#pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-          s = M::mma(load_frag<T>(qr + ks * C::KM), kf[ks], s);
-          dp = M::mma(load_frag<T>(gr + ks * C::KM), vf[ks], dp);
-        }
-        const int qb0 = qi0 + qb * 32;
-        const bool masked = (myk >= N) || (CAUSAL && qb0 < kw + 31);
-        f32x16 ds;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qo = qb * 32 + qoff_of(i) + hoff;
-          float p = exp2_fast(fmaf(s[i], c, -lse2s[buf][qo]));
-          if (masked && (myk >= N || (CAUSAL && qi0 + qo < myk))) p = 0.f;
-          s[i] = p;
-          ds[i] = p * (dp[i] - dls[buf][qo]);
-        }
-        // dV += P^T dO and dK += dS^T Q (contraction over the block's queries):
-        // B operand = 8 consecutive queries of one head-dim row of dO^T / Q^T.
-#pragma unroll
-        for (int u = 0; u < C::NU; ++u) {
-          const frag pa = pack_frag<T>(s, u);
-          const frag sa = pack_frag<T>(ds, u);
-          const int qofs = qb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const int idx = tr_index<T>(db * 32 + col, qofs);
-            dv[db] = M::mma(pa, load_frag<T>(&Gtb[idx]), dv[db]);
-            dk[db] = M::mma(sa, load_frag<T>(&Qtb[idx]), dk[db]);
-          }
-        }
-      }
+    for (int b = 0; b < 2; ++b) {
+      s[b] = f32x16{};
+      dp[b] = f32x16{};
     }
+#pragma unroll
+    for (int m = 0; m < PD; ++m) opq[m] = lds_opnd(buf, m);
+    static_for<0, NM>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      // LSE / D reads, PD slots before the first element of their group.
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if (m == elem_slot(b, 4 * g) - PD) {
+            const int row = b * 32 + qoff_of(4 * g) + hoff;
+            l4[b][g] = *reinterpret_cast<const f32x4*>(&lse2s[buf][row]);
+            d4[b][g] = *reinterpret_cast<const f32x4*>(&dls[buf][row]);
+          }
+      const frag x = opq[m % PD];
+      if constexpr (m + PD < NM) opq[m % PD] = lds_opnd(buf, m + PD);
+      if constexpr (m < 2 * NS) {
+        constexpr int qb = m / NS, ks = (m % NS) / 2;
+        if constexpr (m & 1) dp[qb] = M::mma(x, vf[ks], dp[qb]);
+        else s[qb] = M::mma(x, kf[ks], s[qb]);
+      } else {
+        constexpr int r = m - 2 * NS, qb = r / NV, u = (r % NV) / NVB, db = (r % NVB) / 2;
+        if constexpr (r & 1) dk[db] = M::mma(sa[qb][u], x, dk[db]);
+        else dv[db] = M::mma(pa[qb][u], x, dv[db]);
+      }
+      // P = exp2(S c - lse2), dS = P (dP - D); keys past N need no mask (their
+      // results are never stored), rows past N have lse2 = +inf.
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (m == elem_slot(b, i)) {
+            const int qo = b * 32 + qoff_of(i) + hoff;
+            float e = exp2_fast(fmaf(s[b][i], c, -l4[b][i / 4][i % 4]));
+            if (CAUSAL && qi0 + qo < myk) e = 0.f;
+            p[b][i] = e;
+            ds[b][i] = e * (dp[b][i] - d4[b][i / 4][i % 4]);
+            if ((i + 1) % EPU == 0) {
+              pa[b][i / EPU] = pack_frag<T>(p[b], i / EPU);
+              sa[b][i / EPU] = pack_frag<T>(ds[b], i / EPU);
+            }
+          }
+      __builtin_amdgcn_sched_barrier(0);
+    });
     if (C::NBUF == 2) {
-      // The other buffer was last read in the previous iteration (before the barrier).
+      // The other buffer was last read before the previous barrier.
       if (qt + 1 < nqt) stage_store(buf ^ 1, qt + 1);
-      __syncthreads();
       if (qt + 2 < nqt) stage_load(qt + 2);
+      __syncthreads();
     } else {
       __syncthreads();
       if (qt + 1 < nqt) {

@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -37,6 +39,19 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Calls f(std::integral_constant<int, I>{}) for I = B, ..., E - 1 in order, so
+// that each call sees its index as a compile-time constant.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// s_waitcnt operand that waits for every outstanding vector-memory load and
+// leaves the other counters alone (vmcnt = 0, expcnt = 7, lgkmcnt = 15).
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <typename T> struct Mfma;
