@@ -281,32 +281,106 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nqt = (N + C::BQ - 1) / C::BQ;
   // Earlier query tiles see none of these keys (qt0 < nqt because k0 < N).
   const int qt0 = CAUSAL ? k0 / C::BQ : 0;
-  TileStage<T, D, 256> qs_stage, gs_stage;
+  // Staging of a query tile (Q and dO, 64 rows each) through registers, as
+  // 2 NGM units of 4 rows x 16 bytes: thread tid owns units tid + 256 u, which
+  // belong to Q (mat 0) or dO (mat 1).  The work is split into single
+  // operations (st_op / ld_op) with no branches, so that the tile loop can
+  // place them between its MFMAs; addresses are clamped to row N - 1, so a
+  // tile past the end is loaded (and stored) harmlessly.
+  constexpr int E16 = 16 / (int)sizeof(T), CPR = D / E16, NGM = (C::BQ / 4) * CPR;
+  constexpr int UPT = 2 * NGM / 256;
+  static_assert(2 * NGM % 256 == 0, "units must divide among the threads");
+  uint4 stx[UPT][4];
   float lse_st, d_st;   // LSE and D of query row (tile start + lane) of the staged tile
-  auto stage_load = [&](int qt) {
-    qs_stage.load(Q, qt * C::BQ, N, tid);
-    gs_stage.load(dO, qt * C::BQ, N, tid);
-    const int qq = min(qt * C::BQ + lane, N - 1);
-    lse_st = LSE[qq];
-    d_st = Dl[qq];
+  auto unit = [&](int u, int& mat, int& dg, int& rg) {
+    const int gu = tid + 256 * u;
+    mat = gu / NGM;
+    dg = (gu % NGM) % CPR;
+    rg = (gu % NGM) / CPR;
   };
-  // Every wave writes the same LSE and D values (64 rows, one per lane).
-  auto stage_store = [&](int buf, int qt) {
-    qs_stage.store_rows(Qs[buf], C::QP, tid);
-    qs_stage.store_transposed(Qt[buf], tid);
-    gs_stage.store_rows(Gs[buf], C::QP, tid);
-    gs_stage.store_transposed(Gt[buf], tid);
-    // Rows past N, and rows that see no key at all, get P = exp2(-inf) = 0.
-    const bool live = qt * C::BQ + lane < N && lse_st != -INFINITY;
-    lse2s[buf][lane] = live ? lse_st * kLog2e : INFINITY;
-    dls[buf][lane] = live ? d_st : 0.f;
+  // Loads: 4 per unit (one row each), then LSE and D.
+  constexpr int NLD = 4 * UPT + 1;
+  auto ld_op = [&](int qt, int j) {
+    if (j < 4 * UPT) {
+      const int u = j / 4, i = j % 4;
+      int mat, dg, rg;
+      unit(u, mat, dg, rg);
+      const int row = min(qt * C::BQ + 4 * rg + i, N - 1);
+      const T* src = mat ? dO : Q;
+      stx[u][i] = *reinterpret_cast<const uint4*>(src + (size_t)row * D + dg * E16);
+    } else {
+      const int qq = min(qt * C::BQ + lane, N - 1);
+      lse_st = LSE[qq];
+      d_st = Dl[qq];
+    }
+  };
+  // Stores: per unit 4 row-major rows, then the transposed block in 4 parts;
+  // last LSE and D (every wave writes the same 64 values).
+  constexpr int NST = 8 * UPT + 1;
+  auto st_op = [&](int buf, int qt, int j) {
+    if (j < 8 * UPT) {
+      const int u = j / 8, o = j % 8;
+      int mat, dg, rg;
+      unit(u, mat, dg, rg);
+      if (o < 4) {
+        T* dst = mat ? Gs[buf] : Qs[buf];
+        *reinterpret_cast<uint4*>(dst + (4 * rg + o) * C::QP + dg * E16) = stx[u][o];
+      } else {
+        // Rows dg E16 .. dg E16 + E16 - 1 of the transposed tile share one swizzle.
+        T* dst = (mat ? Gt[buf] : Qt[buf]) + tr_index<T>(dg * E16, 4 * rg);
+        const int wd = o - 4;   // dword of the 16-byte rows
+        const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&stx[u][0]);
+        const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&stx[u][1]);
+        const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&stx[u][2]);
+        const uint32_t* x3 = reinterpret_cast<const uint32_t*>(&stx[u][3]);
+        if constexpr (sizeof(T) == 2) {
+          // Dword wd holds columns 2 wd and 2 wd + 1 of the 4 rows.
+          *reinterpret_cast<uint2*>(dst + (2 * wd) * kTrPitch) =
+              uint2{__builtin_amdgcn_perm(x1[wd], x0[wd], 0x05040100u),
+                    __builtin_amdgcn_perm(x3[wd], x2[wd], 0x05040100u)};
+          *reinterpret_cast<uint2*>(dst + (2 * wd + 1) * kTrPitch) =
+              uint2{__builtin_amdgcn_perm(x1[wd], x0[wd], 0x07060302u),
+                    __builtin_amdgcn_perm(x3[wd], x2[wd], 0x07060302u)};
+        } else {
+          *reinterpret_cast<uint4*>(dst + wd * kTrPitch) = uint4{x0[wd], x1[wd], x2[wd], x3[wd]};
+        }
+      }
+    } else {
+      // Rows past N, and rows that see no key at all, get P = exp2(-inf) = 0.
+      const bool live = qt * C::BQ + lane < N && lse_st != -INFINITY;
+      lse2s[buf][lane] = live ? lse_st * kLog2e : INFINITY;
+      dls[buf][lane] = live ? d_st : 0.f;
+    }
+  };
+  // Staging operation k of a tile's sequence: unit 0's stores, unit 0's loads,
+  // unit 1's stores, ...; then the LSE/D store and load.  Returns the operation
+  // kind (0 none, 1 store j, 2 load j).
+  constexpr int NSTAGE = NST + NLD;
+  constexpr auto stage_seq = [](int k, int& j) {
+    if (k < 12 * UPT) {
+      const int u = k / 12, o = k % 12;
+      j = o < 8 ? 8 * u + o : 4 * u + (o - 8);
+      return o < 8 ? 1 : 2;
+    }
+    if (k == 12 * UPT) { j = 8 * UPT; return 1; }
+    if (k == 12 * UPT + 1) { j = 4 * UPT; return 2; }
+    return 0;
+  };
+  auto stage_all = [&](int buf, int qt_st, int qt_ld) {
+#pragma unroll
+    for (int k = 0; k < NSTAGE; ++k) {
+      int j = 0;
+      const int kind = stage_seq(k, j);
+      if (kind == 1) st_op(buf, qt_st, j);
+      if (kind == 2) ld_op(qt_ld, j);
+    }
   };
   // The K/V fragments must have landed before the loop, whose waits then cover
   // only the loads issued inside it.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  stage_load(qt0);
-  stage_store(0, qt0);
-  if (qt0 + 1 < nqt) stage_load(qt0 + 1);
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) ld_op(qt0, j);
+  stage_all(0, qt0, qt0 + 1);
   __syncthreads();
 
   // One query tile is a fixed stream of NM MFMAs, in issue order:
@@ -322,6 +396,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NVB = 2 * (D / 32);
   constexpr int NV = C::NU * NVB;
   constexpr int NM = 2 * NS + 2 * NV;
+  static_assert(C::NBUF == 1 || NSTAGE + 1 <= NM, "every staging operation needs a slot");
   constexpr int PD = 4;
   constexpr int EPU = 16 / C::NU;   // elements of P (and dS) per packed fragment
   // Slot that computes element i of P/dS of block b (blocks overlap S/dP of
@@ -378,6 +453,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
         if constexpr (r & 1) dk[db] = M::mma(sa[qb][u], x, dk[db]);
         else dv[db] = M::mma(pa[qb][u], x, dv[db]);
       }
+      // Staging of tile qt + 1 into the other buffer (free since the previous
+      // barrier) and loads of tile qt + 2, one operation per slot from slot 1.
+      if constexpr (C::NBUF == 2 && m >= 1 && m - 1 < NSTAGE) {
+        int j = 0;
+        constexpr int k = m - 1;
+        const int kind = stage_seq(k, j);
+        if (kind == 1) st_op(buf ^ 1, qt + 1, j);
+        if (kind == 2) ld_op(qt + 2, j);
+      }
       // P = exp2(S c - lse2), dS = P (dP - D); keys past N need no mask (their
       // results are never stored), rows past N have lse2 = +inf.
 #pragma unroll
@@ -397,17 +481,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           }
       __builtin_amdgcn_sched_barrier(0);
     });
-    if (C::NBUF == 2) {
-      // The other buffer was last read before the previous barrier.
-      if (qt + 1 < nqt) stage_store(buf ^ 1, qt + 1);
-      if (qt + 2 < nqt) stage_load(qt + 2);
+    if constexpr (C::NBUF == 2) {
       __syncthreads();
     } else {
       __syncthreads();
-      if (qt + 1 < nqt) {
-        stage_store(0, qt + 1);
-        if (qt + 2 < nqt) stage_load(qt + 2);
-      }
+      stage_all(0, qt + 1, qt + 2);
       __syncthreads();
     }
   }
