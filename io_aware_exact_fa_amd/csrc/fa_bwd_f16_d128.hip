@@ -1,0 +1,7 @@
+// Backward kernels instantiated for _Float16, head dimension 128 (one translation
+// unit per instance so that they compile in parallel).
+#include "fa_bwd_kernels.hpp"
+
+namespace fa {
+template hipError_t launch_bwd_inst<_Float16, 128>(BwdStep, bool, const BwdArgs&, hipStream_t);
+}  // namespace fa

@@ -1,0 +1,535 @@
+// Backward attention kernels for gfx950.
+//
+// Three launches on the caller's stream, no atomics and no fp32 accumulator
+// in device memory:
+//   1. bwd_pre_kernel:  D_i = rowsum(dO_i * O_i) in fp32 (HBM-bound).
+//   2. bwd_dkdv_kernel: one workgroup per (batch, head, 128-key tile); each wave
+//      owns 32 keys.  For every query tile, recompute
+//        S = Q K^T, P = 2^(c S - LSE log2 e), dP = dO V^T, dS = P (dP - D)
+//      and accumulate dV += P^T dO, dK += dS^T Q in registers; dk = scale dK.
+//   3. bwd_dq_kernel:   one workgroup per (batch, head, 128-query tile), the
+//      forward's loop order: for every key tile, recompute S^T, P, dP^T, dS and
+//      accumulate dQ^T += K^T dS^T in registers; dq = scale dQ at the end.
+// dQ is computed by its own pass instead of being summed across key-tile
+// workgroups: the two GEMMs it recomputes cost less than the fp32 atomic
+// traffic they replace, and every output is written exactly once (bitwise
+// repeatable).
+//
+// Sources: the gradients dV = P^T dO, dP = dO V^T, dS = P (dP - D),
+// D_i = sum_j P_ij dP_ij, dQ = dS K, dK = dS^T Q ("FlashAttention-2: Faster
+// Attention with Better Parallelism and Work Partitioning", section
+// "Standard Attention Implementation / Backward Pass"; the factor scale on dQ
+// and dK comes from S = scale Q K^T by the chain rule); D precomputed as
+// rowsum(dO * O), P recomputed from the stored L, the key/value-tile-outer
+// order for dK/dV and a separate reduction for dQ (same page, sections
+// "Backward Pass" and "Parallelism: 시퀀스 길이 차원 병렬화"); S and P are never
+// stored, only regenerated per tile ("FlashAttention 원 논문 해부", section
+// "forward가 끝난 뒤 backward는 무엇을 저장하고 무엇을 다시 계산하는가").
+//
+// Operands: every MFMA reads one operand from registers (a result tile of an
+// earlier MFMA, or rows held for the whole kernel) and the other with 16-byte
+// LDS reads, from a row-major tile or from a transposed, swizzled tile written
+// at load time (no transposing LDS reads).
+#pragma once
+
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+// ------------------------------------------------------------------ preprocess
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long rows) {
+  constexpr int E16 = 16 / sizeof(T);
+  constexpr int LPR = D / E16;          // lanes per row
+  constexpr int RPB = 256 / LPR;        // rows per block
+  const int sub = threadIdx.x % LPR;
+  const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+  float part = 0.f;
+  if (row < rows) {
+    const size_t off = (size_t)row * D + sub * E16;
+    const T* o = static_cast<const T*>(a.o) + off;
+    const T* g = static_cast<const T*>(a.dout) + off;
+#pragma unroll
+    for (int e = 0; e < E16; ++e) part = fmaf(to_f32(o[e]), to_f32(g[e]), part);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m > 0; m >>= 1) part += __shfl_xor(part, m, LPR);
+  if (row < rows && sub == 0) a.delta[row] = part;
+}
+
+// Work index of this workgroup: workgroups are dealt to the 8 XCDs round-robin
+// by linear id; give each XCD a contiguous range so that the tiles of one head
+// share their K/V (or Q/dO) through one L2.
+__device__ inline int xcd_work_index() {
+  const int nwork = gridDim.x * gridDim.y * gridDim.z;
+  int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  if ((nwork & 7) == 0) lin = (lin & 7) * (nwork >> 3) + (lin >> 3);
+  return lin;
+}
+
+// ------------------------------------------------------------------ dQ
+
+template <typename T, int D>
+struct DqTile {
+  // 16-bit types: 8 waves x 32 queries, so each K/V tile streamed from L2 serves
+  // 256 query rows; f32 keeps 4 waves (1 wave per SIMD for registers).
+  static constexpr int NW = sizeof(T) == 2 ? 8 : 4;
+  static constexpr int NT = 64 * NW;
+  static constexpr int WAVES_PER_SIMD = sizeof(T) == 2 ? 2 : 1;
+  static constexpr int BR = 32 * NW;             // queries per workgroup
+  static constexpr int BC = kTrCols;             // keys per tile (64)
+  static constexpr int KPL = Mfma<T>::KPL;
+  static constexpr int KM = 2 * KPL;
+  static constexpr int NKS = D / KM;
+  static constexpr int NU = steps32<T>();
+  static constexpr int E16 = 16 / sizeof(T);
+  static constexpr int KP = D + E16;             // row pitch of the K and V tiles
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__((DqTile<T, D>::NT), (DqTile<T, D>::WAVES_PER_SIMD))
+void bwd_dq_kernel(BwdArgs a) {
+  using C = DqTile<T, D>;
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr bool kPerm = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) T Ks[C::BC * C::KP];
+  __shared__ __attribute__((aligned(16))) T Vs[C::BC * C::KP];
+  __shared__ __attribute__((aligned(16))) T Kt[D * kTrPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, col = lane & 31, h = lane >> 5;
+  const int N = a.N;
+  const int ntq = gridDim.x;
+  const int lin = xcd_work_index();
+  const int qt = CAUSAL ? ntq - 1 - (lin % ntq) : (lin % ntq);
+  const int q0 = qt * C::BR;
+  const size_t head = (size_t)(lin / ntq);
+  const T* Q = static_cast<const T*>(a.q) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head * N * D;
+  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  const T* dO = static_cast<const T*>(a.dout) + head * N * D;
+  T* dQ = static_cast<T*>(a.dq) + head * N * D;
+  const float c = a.scale * kLog2e;
+
+  const int qw = q0 + 32 * w;
+  const int myq = qw + col;
+  const int qrow = min(myq, N - 1);
+  // Q^T and dO^T operands of this lane's query, held for the whole kernel.
+  frag qf[C::NKS], gf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    qf[ks] = load_frag<T>(Q + (size_t)qrow * D + ks * C::KM + C::KPL * h);
+    gf[ks] = load_frag<T>(dO + (size_t)qrow * D + ks * C::KM + C::KPL * h);
+  }
+  // Row statistics of this lane's query.  A row with no visible key (LSE = -inf)
+  // has P = 0: use +inf as its log2-domain LSE.
+  const float lse = a.lse[head * N + qrow];
+  const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+  const float dl = a.delta[head * N + qrow];
+
+  const int ntiles_all = (N + C::BC - 1) / C::BC;
+  const int qlast = min(q0 + C::BR, N) - 1;
+  const int ntiles = CAUSAL ? min(ntiles_all, qlast / C::BC + 1) : ntiles_all;
+  const int wlast = (qw >= N) ? -1 : (CAUSAL ? min(qw + 31, N - 1) / C::BC : ntiles - 1);
+  const int krow = kPerm ? perm16(col) : col;
+  const int hoff = kPerm ? 8 * h : 4 * h;
+  auto key0_of = [](int i) {
+    const int r = 8 * (i >> 2) + (i & 3);
+    return kPerm ? perm16(r) : r;
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+  TileStage<T, D, C::NT> ks_stage, vs_stage;
+  ks_stage.load(K, 0, N, tid);
+  vs_stage.load(V, 0, N, tid);
+  for (int j = 0; j < ntiles; ++j) {
+    ks_stage.store_rows(Ks, C::KP, tid);
+    ks_stage.store_transposed(Kt, tid);
+    vs_stage.store_rows(Vs, C::KP, tid);
+    __syncthreads();
+    if (j + 1 < ntiles) {
+      ks_stage.load(K, (j + 1) * C::BC, N, tid);
+      vs_stage.load(V, (j + 1) * C::BC, N, tid);
+    }
+    if (j <= wlast) {
+      const int key0 = j * C::BC;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // S^T and dP^T for 32 keys x 32 queries.
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const T* kr = &Ks[(kb * 32 + krow) * C::KP + C::KPL * h];
+        const T* vr = &Vs[(kb * 32 + krow) * C::KP + C::KPL * h];
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          s = M::mma(load_frag<T>(kr + ks * C::KM), qf[ks], s);
+          dp = M::mma(load_frag<T>(vr + ks * C::KM), gf[ks], dp);
+        }
+        const int kb0 = key0 + kb * 32;
+        const bool masked = (CAUSAL && kb0 + 31 > qw) || (kb0 + 32 > N);
+        const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kb0 - hoff;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = exp2_fast(fmaf(s[i], c, -l2));
+          if (masked && key0_of(i) > lim) p = 0.f;
+          s[i] = p * (dp[i] - dl);                     // dS
+        }
+        // dQ^T += K^T dS^T: A operand = 8 consecutive keys of one head-dim row of K^T.
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u) {
+          const frag sf = pack_frag<T>(s, u);
+          const int kofs = kb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            acc[db] = M::mma(load_frag<T>(&Kt[tr_index<T>(db * 32 + col, kofs)]), sf, acc[db]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (myq < N) {
+    T* orow = dQ + (size_t)myq * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        store4<T>(orow + db * 32 + 8 * r + 4 * h, acc[db][4 * r] * sc, acc[db][4 * r + 1] * sc,
+                  acc[db][4 * r + 2] * sc, acc[db][4 * r + 3] * sc);
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV
+
+template <typename T, int D>
+struct DkvTile {
+  static constexpr int BKC = 128;                // keys per workgroup (32 per wave)
+  static constexpr int BQ = kTrCols;             // queries per tile (64)
+  static constexpr int KPL = Mfma<T>::KPL;
+  static constexpr int KM = 2 * KPL;
+  static constexpr int NKS = D / KM;
+  static constexpr int NU = steps32<T>();
+  static constexpr int E16 = 16 / sizeof(T);
+  static constexpr int QP = D + E16;             // row pitch of the Q and dO tiles
+  // Two LDS buffers (one barrier per query tile) when they fit beside each other.
+  static constexpr int BUF_BYTES = (2 * BQ * QP + 2 * D * kTrPitch) * (int)sizeof(T) + 2 * BQ * 4;
+  static constexpr int NBUF = 2 * BUF_BYTES <= 160 * 1024 ? 2 : 1;
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = DkvTile<T, D>;
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr bool kPerm = sizeof(T) == 2;
+  // Double-buffered query tiles: row-major Q and dO (A operands of S and dP),
+  // transposed Q^T and dO^T (B operands of dK and dV), LSE and D.
+  __shared__ __attribute__((aligned(16))) T Qs[C::NBUF][C::BQ * C::QP];
+  __shared__ __attribute__((aligned(16))) T Gs[C::NBUF][C::BQ * C::QP];      // dO
+  __shared__ __attribute__((aligned(16))) T Qt[C::NBUF][D * kTrPitch];
+  __shared__ __attribute__((aligned(16))) T Gt[C::NBUF][D * kTrPitch];
+  __shared__ __attribute__((aligned(16))) float lse2s[C::NBUF][C::BQ];
+  __shared__ __attribute__((aligned(16))) float dls[C::NBUF][C::BQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, col = lane & 31, h = lane >> 5;
+  const int N = a.N;
+  const int ntk = gridDim.x;
+  const int lin = xcd_work_index();
+  // Under the causal mask the key tiles near the start see the most queries and
+  // come first in each head's range.
+  const int kt = lin % ntk;
+  const int k0 = kt * C::BKC;
+  const size_t head = (size_t)(lin / ntk);
+  const T* Q = static_cast<const T*>(a.q) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head * N * D;
+  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  const T* dO = static_cast<const T*>(a.dout) + head * N * D;
+  const float* LSE = a.lse + head * N;
+  const float* Dl = a.delta + head * N;
+  const float c = a.scale * kLog2e;
+
+  const int kw = k0 + 32 * w;    // first key of this wave
+  const int myk = kw + col;      // this lane's key (column of S)
+  const int kg = min(myk, N - 1);
+  // K and V operands (B of S = Q K^T and of dP = dO V^T) of this lane's key.
+  frag kf[C::NKS], vf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    kf[ks] = load_frag<T>(K + (size_t)kg * D + ks * C::KM + C::KPL * h);
+    vf[ks] = load_frag<T>(V + (size_t)kg * D + ks * C::KM + C::KPL * h);
+  }
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dv[db] = f32x16{};
+    dk[db] = f32x16{};
+  }
+  // Query (inside a 32-query block) of result element i of this lane:
+  // qoff_of(i) + hoff (rows of the Q and dO operands are permuted for 16-bit types).
+  const int qrow = kPerm ? perm16(col) : col;
+  const int hoff = kPerm ? 8 * h : 4 * h;
+  auto qoff_of = [](int i) {
+    const int r = 8 * (i >> 2) + (i & 3);
+    return kPerm ? perm16(r) : r;
+  };
+
+  const int nqt = (N + C::BQ - 1) / C::BQ;
+  // Earlier query tiles see none of these keys (qt0 < nqt because k0 < N).
+  const int qt0 = CAUSAL ? k0 / C::BQ : 0;
+  // Staging of a query tile (Q and dO, 64 rows each) through registers, as
+  // 2 NGM units of 4 rows x 16 bytes: thread tid owns units tid + 256 u, which
+  // belong to Q (mat 0) or dO (mat 1).  The work is split into single
+  // operations (st_op / ld_op) with no branches, so that the tile loop can
+  // place them between its MFMAs; addresses are clamped to row N - 1, so a
+  // tile past the end is loaded (and stored) harmlessly.
+  constexpr int E16 = 16 / (int)sizeof(T), CPR = D / E16, NGM = (C::BQ / 4) * CPR;
+  constexpr int UPT = 2 * NGM / 256;
+  static_assert(2 * NGM % 256 == 0, "units must divide among the threads");
+  uint4 stx[UPT][4];
+  float lse_st, d_st;   // LSE and D of query row (tile start + lane) of the staged tile
+  auto unit = [&](int u, int& mat, int& dg, int& rg) {
+    const int gu = tid + 256 * u;
+    mat = gu / NGM;
+    dg = (gu % NGM) % CPR;
+    rg = (gu % NGM) / CPR;
+  };
+  // Loads: 4 per unit (one row each), then LSE and D.
+  constexpr int NLD = 4 * UPT + 1;
+  auto ld_op = [&](int qt, int j) {
+    if (j < 4 * UPT) {
+      const int u = j / 4, i = j % 4;
+      int mat, dg, rg;
+      unit(u, mat, dg, rg);
+      const int row = min(qt * C::BQ + 4 * rg + i, N - 1);
+      const T* src = mat ? dO : Q;
+      stx[u][i] = *reinterpret_cast<const uint4*>(src + (size_t)row * D + dg * E16);
+    } else {
+      const int qq = min(qt * C::BQ + lane, N - 1);
+      lse_st = LSE[qq];
+      d_st = Dl[qq];
+    }
+  };
+  // Stores: per unit 4 row-major rows, then the transposed block in 4 parts;
+  // last LSE and D (every wave writes the same 64 values).
+  constexpr int NST = 8 * UPT + 1;
+  auto st_op = [&](int buf, int qt, int j) {
+    if (j < 8 * UPT) {
+      const int u = j / 8, o = j % 8;
+      int mat, dg, rg;
+      unit(u, mat, dg, rg);
+      if (o < 4) {
+        T* dst = mat ? Gs[buf] : Qs[buf];
+        *reinterpret_cast<uint4*>(dst + (4 * rg + o) * C::QP + dg * E16) = stx[u][o];
+      } else {
+        // Rows dg E16 .. dg E16 + E16 - 1 of the transposed tile share one swizzle.
+        T* dst = (mat ? Gt[buf] : Qt[buf]) + tr_index<T>(dg * E16, 4 * rg);
+        const int wd = o - 4;   // dword of the 16-byte rows
+        const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&stx[u][0]);
+        const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&stx[u][1]);
+        const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&stx[u][2]);
+        const uint32_t* x3 = reinterpret_cast<const uint32_t*>(&stx[u][3]);
+        if constexpr (sizeof(T) == 2) {
+          // Dword wd holds columns 2 wd and 2 wd + 1 of the 4 rows.
+          *reinterpret_cast<uint2*>(dst + (2 * wd) * kTrPitch) =
+              uint2{__builtin_amdgcn_perm(x1[wd], x0[wd], 0x05040100u),
+                    __builtin_amdgcn_perm(x3[wd], x2[wd], 0x05040100u)};
+          *reinterpret_cast<uint2*>(dst + (2 * wd + 1) * kTrPitch) =
+              uint2{__builtin_amdgcn_perm(x1[wd], x0[wd], 0x07060302u),
+                    __builtin_amdgcn_perm(x3[wd], x2[wd], 0x07060302u)};
+        } else {
+          *reinterpret_cast<uint4*>(dst + wd * kTrPitch) = uint4{x0[wd], x1[wd], x2[wd], x3[wd]};
+        }
+      }
+    } else {
+      // Rows past N, and rows that see no key at all, get P = exp2(-inf) = 0.
+      const bool live = qt * C::BQ + lane < N && lse_st != -INFINITY;
+      lse2s[buf][lane] = live ? lse_st * kLog2e : INFINITY;
+      dls[buf][lane] = live ? d_st : 0.f;
+    }
+  };
+  // Staging operation k of a tile's sequence: unit 0's stores, unit 0's loads,
+  // unit 1's stores, ...; then the LSE/D store and load.  Returns the operation
+  // kind (0 none, 1 store j, 2 load j).
+  constexpr int NSTAGE = NST + NLD;
+  constexpr auto stage_seq = [](int k, int& j) {
+    if (k < 12 * UPT) {
+      const int u = k / 12, o = k % 12;
+      j = o < 8 ? 8 * u + o : 4 * u + (o - 8);
+      return o < 8 ? 1 : 2;
+    }
+    if (k == 12 * UPT) { j = 8 * UPT; return 1; }
+    if (k == 12 * UPT + 1) { j = 4 * UPT; return 2; }
+    return 0;
+  };
+  auto stage_all = [&](int buf, int qt_st, int qt_ld) {
+#pragma unroll
+    for (int k = 0; k < NSTAGE; ++k) {
+      int j = 0;
+      const int kind = stage_seq(k, j);
+      if (kind == 1) st_op(buf, qt_st, j);
+      if (kind == 2) ld_op(qt_ld, j);
+    }
+  };
+  // The K/V fragments must have landed before the loop, whose waits then cover
+  // only the loads issued inside it.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) ld_op(qt0, j);
+  stage_all(0, qt0, qt0 + 1);
+  __syncthreads();
+
+  // One query tile is a fixed stream of NM MFMAs, in issue order:
+  //   [0, NS)            S = Q K^T and dP = dO V^T of block 0 (32 queries)
+  //   [NS, 2NS)          the same for block 1
+  //   [2NS, 2NS+NV)      dV += P^T dO and dK += dS^T Q of block 0
+  //   [2NS+NV, NM)       the same for block 1
+  // The LDS operand of MFMA m (a Q / dO row fragment, or 8 consecutive queries
+  // of one head-dim row of dO^T / Q^T) is read PD slots ahead, and the P / dS
+  // arithmetic of a block, one element at a time, fills the slots between its
+  // S/dP MFMAs and its dV/dK MFMAs, so one wave keeps the matrix unit busy.
+  constexpr int NS = 2 * C::NKS;
+  constexpr int NVB = 2 * (D / 32);
+  constexpr int NV = C::NU * NVB;
+  constexpr int NM = 2 * NS + 2 * NV;
+  static_assert(C::NBUF == 1 || NSTAGE + 1 <= NM, "every staging operation needs a slot");
+  constexpr int PD = 4;
+  constexpr int EPU = 16 / C::NU;   // elements of P (and dS) per packed fragment
+  // Slot that computes element i of P/dS of block b (blocks overlap S/dP of
+  // block 1 and dV/dK of block 0 respectively).
+  constexpr auto elem_slot = [](int b, int i) {
+    return b == 0 ? NS + 2 + (i * (NS - 2)) / 16 : 2 * NS + 2 + (i * (NV - 2)) / 16;
+  };
+  auto lds_opnd = [&](int buf, int m) -> frag {
+    if (m < 2 * NS) {
+      const int qb = m / NS, ks = (m % NS) / 2;
+      const T* base = (m & 1) ? Gs[buf] : Qs[buf];
+      return load_frag<T>(&base[(qb * 32 + qrow) * C::QP + C::KPL * h + ks * C::KM]);
+    }
+    const int r = m - 2 * NS, qb = r / NV, u = (r % NV) / NVB, db = (r % NVB) / 2;
+    const int qofs = qb * 32 + (kPerm ? 16 * u + 8 * h : 8 * (u >> 2) + 4 * h + (u & 3));
+    const T* base = (r & 1) ? Qt[buf] : Gt[buf];
+    return load_frag<T>(&base[tr_index<T>(db * 32 + col, qofs)]);
+  };
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int qi0 = qt * C::BQ;
+    const int buf = C::NBUF == 2 ? (qt - qt0) & 1 : 0;
+    f32x16 s[2], dp[2], p[2], ds[2];
+    frag pa[2][C::NU], sa[2][C::NU];
+    f32x4 l4[2][4], d4[2][4];   // lse2 and D of 4 consecutive queries, per element group
+    frag opq[PD];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = f32x16{};
+      dp[b] = f32x16{};
+    }
+#pragma unroll
+    for (int m = 0; m < PD; ++m) opq[m] = lds_opnd(buf, m);
+    static_for<0, NM>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      // LSE / D reads, PD slots before the first element of their group.
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if (m == elem_slot(b, 4 * g) - PD) {
+            const int row = b * 32 + qoff_of(4 * g) + hoff;
+            l4[b][g] = *reinterpret_cast<const f32x4*>(&lse2s[buf][row]);
+            d4[b][g] = *reinterpret_cast<const f32x4*>(&dls[buf][row]);
+          }
+      const frag x = opq[m % PD];
+      if constexpr (m + PD < NM) opq[m % PD] = lds_opnd(buf, m + PD);
+      if constexpr (m < 2 * NS) {
+        constexpr int qb = m / NS, ks = (m % NS) / 2;
+        if constexpr (m & 1) dp[qb] = M::mma(x, vf[ks], dp[qb]);
+        else s[qb] = M::mma(x, kf[ks], s[qb]);
+      } else {
+        constexpr int r = m - 2 * NS, qb = r / NV, u = (r % NV) / NVB, db = (r % NVB) / 2;
+        if constexpr (r & 1) dk[db] = M::mma(sa[qb][u], x, dk[db]);
+        else dv[db] = M::mma(pa[qb][u], x, dv[db]);
+      }
+      // Staging of tile qt + 1 into the other buffer (free since the previous
+      // barrier) and loads of tile qt + 2, one operation per slot from slot 1.
+      if constexpr (C::NBUF == 2 && m >= 1 && m - 1 < NSTAGE) {
+        int j = 0;
+        constexpr int k = m - 1;
+        const int kind = stage_seq(k, j);
+        if (kind == 1) st_op(buf ^ 1, qt + 1, j);
+        if (kind == 2) ld_op(qt + 2, j);
+      }
+      // P = exp2(S c - lse2), dS = P (dP - D); keys past N need no mask (their
+      // results are never stored), rows past N have lse2 = +inf.
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (m == elem_slot(b, i)) {
+            const int qo = b * 32 + qoff_of(i) + hoff;
+            float e = exp2_fast(fmaf(s[b][i], c, -l4[b][i / 4][i % 4]));
+            if (CAUSAL && qi0 + qo < myk) e = 0.f;
+            p[b][i] = e;
+            ds[b][i] = e * (dp[b][i] - d4[b][i / 4][i % 4]);
+            if ((i + 1) % EPU == 0) {
+              pa[b][i / EPU] = pack_frag<T>(p[b], i / EPU);
+              sa[b][i / EPU] = pack_frag<T>(ds[b], i / EPU);
+            }
+          }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (C::NBUF == 2) {
+      __syncthreads();
+    } else {
+      __syncthreads();
+      stage_all(0, qt + 1, qt + 2);
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: lane (col = d, h) holds keys kw + 8(i/4) + 4h + i%4.
+  T* dK = static_cast<T*>(a.dk) + head * N * D;
+  T* dV = static_cast<T*>(a.dv) + head * N * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kw + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (key < N) {
+        const size_t off = (size_t)key * D + db * 32 + col;
+        dK[off] = (T)(dk[db][i] * a.scale);
+        dV[off] = (T)dv[db][i];
+      }
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
+  const long rows = (long)a.B * a.H * a.N;
+  if (step == BwdStep::pre) {
+    constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
+    const long blocks = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a, rows);
+  } else if (step == BwdStep::dkdv) {
+    dim3 grid((a.N + DkvTile<T, D>::BKC - 1) / DkvTile<T, D>::BKC, a.H, a.B);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
+  } else {
+    dim3 grid((a.N + DqTile<T, D>::BR - 1) / DqTile<T, D>::BR, a.H, a.B);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(DqTile<T, D>::NT), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_inst(BwdStep st, bool causal, const BwdArgs& a, hipStream_t s) {
+  return causal ? launch_bwd_t<T, D, true>(st, a, s) : launch_bwd_t<T, D, false>(st, a, s);
+}
+
+}  // namespace fa

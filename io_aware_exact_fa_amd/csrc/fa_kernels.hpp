@@ -42,4 +42,19 @@ hipError_t launch_bwd_pre(Dt dt, int d, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s);
 
+// Backward instances per dtype (T = float, _Float16, __bf16) and head dimension
+// (D = 64, 128), defined in one translation unit each (fa_bwd_<dtype>_d<D>.hip).
+enum class BwdStep { pre, dkdv, dq };
+template <typename T, int D>
+hipError_t launch_bwd_inst(BwdStep st, bool causal, const BwdArgs& a, hipStream_t s);
+#define FA_BWD_EXTERN(T, D) \
+  extern template hipError_t launch_bwd_inst<T, D>(BwdStep, bool, const BwdArgs&, hipStream_t);
+FA_BWD_EXTERN(float, 64)
+FA_BWD_EXTERN(float, 128)
+FA_BWD_EXTERN(_Float16, 64)
+FA_BWD_EXTERN(_Float16, 128)
+FA_BWD_EXTERN(__bf16, 64)
+FA_BWD_EXTERN(__bf16, 128)
+#undef FA_BWD_EXTERN
+
 }  // namespace fa
