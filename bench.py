@@ -176,7 +176,7 @@ def main():
         check(fa.fa_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, N, d, w.causal, w.scale, code, sh), "fwd")
         if ev is not None:
             ev[1].record(stream)
-        check(fa.fa_bwd_preprocess(P(o), P(do), B, H, N, d, code, P(ws), ws.numel(), sh), "pre")
+        check(fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, code, P(ws), ws.numel(), sh), "pre")
         if ev is not None:
             ev[2].record(stream)
         check(fa.fa_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, N, d, w.causal,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -90,7 +90,13 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 /*
  * Bytes of device workspace fa_bwd needs for this shape (0 if the shape is
- * invalid): D float32 [B,H,N], D_i = rowsum(dO_i * O_i), rounded up to 256 B.
+ * invalid).  With Np = N rounded up to a multiple of 64, the workspace holds
+ * two float32 arrays [B,H,Np], 256-byte aligned and in this order:
+ *   D   D_i = rowsum(dout_i * o_i)            (rows i >= N: 0)
+ *   L2  L2_i = LSE_i * log2(e), the log-sum-exp in base-2 units
+ *                                             (rows i >= N: +inf)
+ * so that a tile of 64 rows can be copied whole, and P = exp2(S log2(e) - L2)
+ * is exactly 0 on padding rows.  Size 2 * 4 * B * H * Np rounded up to 256 B.
  * fa_bwd (and fa_bwd_preprocess) rewrite it completely on every call.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
@@ -112,13 +118,15 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  void* stream);
 
 /*
- * Backward step 1: D_i = rowsum(dout_i * o_i) in float32 into the workspace.
- * D is the row term of the softmax gradient, precomputed from O instead of
- * from P and dP ("FlashAttention-2: Faster Attention with Better Parallelism
- * and Work Partitioning", sections "Standard Attention Implementation /
- * Backward Pass" and "Backward Pass").
+ * Backward step 1: D_i = rowsum(dout_i * o_i) and L2_i = LSE_i * log2(e) in
+ * float32 into the workspace (layout at fa_bwd_workspace_size).  D is the row
+ * term of the softmax gradient, precomputed from O instead of from P and dP
+ * ("FlashAttention-2: Faster Attention with Better Parallelism and Work
+ * Partitioning", sections "Standard Attention Implementation / Backward Pass"
+ * and "Backward Pass"); L2 is the stored LSE in the base-2 units the kernels
+ * exponentiate in (same page, section "개선 2: m과 l 대신 L만 저장").
  */
-fa_status fa_bwd_preprocess(const void* o, const void* dout,
+fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
                             int B, int H, int N, int d, fa_dtype dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 

@@ -66,7 +66,7 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_preprocess.restype = i
-    lib.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_dkdv.restype = i
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_dq.restype = i
@@ -112,8 +112,9 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype,
                        int(dtype), workspace, workspace_bytes, stream)
 
 
-def fa_bwd_preprocess(o, dout, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
-    return _lib.fa_bwd_preprocess(o, dout, B, H, N, d, int(dtype), workspace, workspace_bytes, stream)
+def fa_bwd_preprocess(o, dout, lse, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_preprocess(o, dout, lse, B, H, N, d, int(dtype), workspace, workspace_bytes,
+                                  stream)
 
 
 def fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, B, H, N, d, causal, scale, dtype,

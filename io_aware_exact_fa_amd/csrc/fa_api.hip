@@ -19,6 +19,8 @@ constexpr int kMaxN = (1 << 30);                 // keeps tile index arithmetic 
 constexpr uint64_t kMaxRows = (uint64_t)1 << 34;  // keeps 1-D row grids below 2^31 blocks
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+// Rows per head of the workspace arrays: N rounded up to whole 64-row tiles.
+int padded_rows(int N) { return (N + 63) / 64 * 64; }
 
 // B*H*N*d without overflow; 0 if it does not fit comfortably in 63 bits.
 uint64_t elements(int B, int H, int N, int d) {
@@ -99,18 +101,20 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
   if (elements(B, H, N, d) == 0) return 0;
-  const uint64_t rows = (uint64_t)B * H * N;
-  return align_up(rows * sizeof(float));
+  const uint64_t rows = (uint64_t)B * H * padded_rows(N);
+  return align_up(2 * rows * sizeof(float));
 }
 
-fa_status fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
-                            fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!o || !dout) return FA_ERR_INVALID_ARGUMENT;
+fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H,
+                            int N, int d, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!o || !dout || !lse) return FA_ERR_INVALID_ARGUMENT;
   fa::BwdArgs a{};
   fa_status st = bwd_setup(B, H, N, d, 1.0f, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
   a.o = o;
   a.dout = dout;
+  a.lse = lse;
   return launched(fa::launch_bwd_pre(to_dt(dtype), d, a, (hipStream_t)stream));
 }
 
@@ -188,7 +192,9 @@ fa_status bwd_setup(int B, int H, int N, int d, float scale, fa_dtype dtype, voi
     return FA_ERR_WORKSPACE;
   st = check_device();
   if (st != FA_OK) return st;
+  a->Np = padded_rows(N);
   a->delta = static_cast<float*>(workspace);
+  a->l2 = a->delta + (size_t)B * H * a->Np;
   a->B = B;
   a->H = H;
   a->N = N;

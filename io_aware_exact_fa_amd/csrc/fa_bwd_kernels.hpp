@@ -45,10 +45,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long rows) {
   constexpr int LPR = D / E16;          // lanes per row
   constexpr int RPB = 256 / LPR;        // rows per block
   const int sub = threadIdx.x % LPR;
+  // Workspace row (head, q) with q < Np; rows q >= N are padding.
   const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const long head = row / a.Np;
+  const int q = (int)(row - head * a.Np);
+  const bool live = row < rows && q < a.N;
+  const size_t src = (size_t)head * a.N + q;
   float part = 0.f;
-  if (row < rows) {
-    const size_t off = (size_t)row * D + sub * E16;
+  if (live) {
+    const size_t off = src * D + sub * E16;
     const T* o = static_cast<const T*>(a.o) + off;
     const T* g = static_cast<const T*>(a.dout) + off;
 #pragma unroll
@@ -56,7 +61,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long rows) {
   }
 #pragma unroll
   for (int m = LPR / 2; m > 0; m >>= 1) part += __shfl_xor(part, m, LPR);
-  if (row < rows && sub == 0) a.delta[row] = part;
+  if (row < rows && sub == 0) {
+    float l2 = INFINITY;   // P = exp2(-inf) = 0 on padding rows and rows that see no key
+    if (live) {
+      const float lse = a.lse[src];
+      if (lse != -INFINITY) l2 = lse * kLog2e;
+    }
+    a.delta[row] = part;
+    a.l2[row] = l2;
+  }
 }
 
 // Work index of this workgroup: workgroups are dealt to the 8 XCDs round-robin
@@ -128,7 +141,7 @@ void bwd_dq_kernel(BwdArgs a) {
   // has P = 0: use +inf as its log2-domain LSE.
   const float lse = a.lse[head * N + qrow];
   const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
-  const float dl = a.delta[head * N + qrow];
+  const float dl = a.delta[head * a.Np + qrow];
 
   const int ntiles_all = (N + C::BC - 1) / C::BC;
   const int qlast = min(q0 + C::BR, N) - 1;
@@ -252,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const T* V = static_cast<const T*>(a.v) + head * N * D;
   const T* dO = static_cast<const T*>(a.dout) + head * N * D;
   const float* LSE = a.lse + head * N;
-  const float* Dl = a.delta + head * N;
+  const float* Dl = a.delta + head * a.Np;
   const float c = a.scale * kLog2e;
 
   const int kw = k0 + 32 * w;    // first key of this wave
@@ -508,18 +521,266 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ dK, dV (16-bit types)
+
+// Layout of the 16-bit dK/dV kernel.  Query tiles (Q and dO, 64 rows) live in
+// LDS only row-major, with rows padded to D + 16 elements and the 8-byte slots
+// of row r permuted by XOR-ing the low two slot bits with (r >> 3) & 3.  With
+// the A-operand rows of S taken in the order pi (below), both kinds of operand
+// read touch 32 distinct 8-byte bank pairs per half wave (no bank conflicts):
+//   S = Q K^T, dP = dO V^T: A operand = two 8-byte reads from one Q / dO row;
+//   dV += P^T dO, dK += dS^T Q: B operand = two transposing reads
+//     (ds_read_b64_tr_b16), each gathering 4 queries of one head-dim column.
+// Tiles are copied from global memory straight into LDS (global_load_lds),
+// three buffers deep, so the copy of tile t + 2 runs during tile t.
+template <int D>
+struct Dkv16 {
+  static constexpr int BKC = 128;                // keys per workgroup (32 per wave)
+  static constexpr int BQ = 64;                  // queries per tile
+  static constexpr int PB = 2 * (D + 16);        // row pitch in bytes
+  static constexpr int TILE = BQ * PB;           // bytes of one Q or dO tile
+  static constexpr int BUF = 2 * TILE + 2 * BQ * 4;   // Q, dO, L2, D
+  static constexpr int NB = 3;
+  static constexpr bool HALF = D == 64;          // a row (128 bytes) is copied by lanes 0..31
+  static constexpr int NKS = D / 16;             // k steps of S and dP
+  static constexpr int NS = 2 * NKS;             // S/dP MFMAs per 32-query block
+  static constexpr int NVB = 2 * (D / 32);       // dV/dK MFMAs per 16 queries
+  static constexpr int NV = 2 * NVB;             // dV/dK MFMAs per block
+  static constexpr int NM = 2 * NS + 2 * NV;     // MFMAs per tile
+  static constexpr int NLD = 2 * BQ / 4 + 2;     // copies per wave per tile: Q, dO rows; L2, D
+};
+
+// Row of a 32-query block that supplies S row m (m = 8a + 4h + s -> 8a + 2s + h):
+// the 4 rows of one transposing read are then 2 apart.
+__device__ constexpr int dkv16_pi(int m) { return (m & ~7) | ((m & 3) << 1) | ((m >> 2) & 1); }
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
+  using C = Dkv16<D>;
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, col = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = a.N;
+  const int ntk = gridDim.x;
+  const int lin = xcd_work_index();
+  // Under the causal mask the key tiles near the start see the most queries and
+  // come first in each head's range.
+  const int kt = lin % ntk;
+  const int k0 = kt * C::BKC;
+  const size_t head = (size_t)(lin / ntk);
+  const T* Q = static_cast<const T*>(a.q) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head * N * D;
+  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  const T* dO = static_cast<const T*>(a.dout) + head * N * D;
+  const float* L2 = a.l2 + head * a.Np;
+  const float* Dl = a.delta + head * a.Np;
+  const float c = a.scale * kLog2e;
+
+  const int kw = k0 + 32 * w;    // first key of this wave
+  const int myk = kw + col;      // this lane's key (column of S)
+  const int kg = min(myk, N - 1);
+  // K and V operands (B of S = Q K^T and of dP = dO V^T) of this lane's key.
+  frag kf[C::NKS], vf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    kf[ks] = load_frag<T>(K + (size_t)kg * D + ks * 16 + 8 * h);
+    vf[ks] = load_frag<T>(V + (size_t)kg * D + ks * 16 + 8 * h);
+  }
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dv[db] = f32x16{};
+    dk[db] = f32x16{};
+  }
+  const int nqt = (N + C::BQ - 1) / C::BQ;
+  const int qt0 = CAUSAL ? k0 / C::BQ : 0;   // earlier tiles see none of these keys
+
+  // Lane parts of the LDS addresses (bytes from the start of a buffer).
+  const int arow = dkv16_pi(col);
+  const int aA0 = arow * C::PB + 8 * ((2 * h) ^ (col >> 3));
+  const int aA1 = arow * C::PB + 8 * ((2 * h + 1) ^ (col >> 3));
+  // Transposing reads: source lane (group g, a4, s) points at row 2s + h, columns
+  // 16 g + 4 a4 .. + 3 of its 32-column block; x is the slot XOR of the row.
+  const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
+  int aT[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) aT[x] = (2 * ts + h) * C::PB + 32 * tg + 8 * (ta ^ x);
+  // Row copies (one dword per lane): byte offset inside a global row of the
+  // data that lands on this lane's LDS dword, for slot XOR f.
+  int gofs[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) gofs[f] = 8 * ((lane >> 1) ^ f) + 4 * (lane & 1);
+  // Copy op j of tile qt into buffer b: j < 32: wave w copies rows 4 jj + w
+  // (jj = 0..15) of Q (j < 16) or dO; j = 32, 33: the tile's L2 and D, lane p
+  // holding query dkv16_pi(p) of the tile (the order of a lane half's P
+  // elements).  Every wave copies the same L2 and D.  Rows past N are clamped
+  // (their P is 0 through L2 = +inf), tiles past the end copy the last tile.
+  auto copy_op = [&](int b, int qt, int j) {
+    const uint32_t base = lds_address(smem) + b * C::BUF;
+    if (j < 32) {
+      const int mat = j / 16, jj = j % 16;
+      const int rr = 4 * jj + w;
+      const int f = (jj >> 1) & 3;             // slot XOR of row rr: (rr >> 3) & 3
+      const int rowg = min(qt * C::BQ + rr, N - 1);
+      const char* src = reinterpret_cast<const char*>(mat ? dO : Q) + (size_t)rowg * (2 * D) + gofs[f];
+      copy_to_lds<C::HALF>(src, base + mat * C::TILE + rr * C::PB);
+    } else {
+      const int q = min(qt, nqt - 1) * C::BQ + dkv16_pi(lane);
+      copy_to_lds<false>((j == 32 ? L2 : Dl) + q, base + 2 * C::TILE + (j - 32) * C::BQ * 4);
+    }
+  };
+
+  // Prologue: tiles qt0 and qt0 + 1 into buffers 0 and 1.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+  for (int j = 0; j < C::NLD; ++j) copy_op(0, qt0, j);
+#pragma unroll
+  for (int j = 0; j < C::NLD; ++j) copy_op(1, qt0 + 1, j);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+
+  // The MFMA stream of one tile: S/dP of blocks 0 and 1 (32 queries each), then
+  // dV/dK of blocks 0 and 1; each LDS operand is read PD slots ahead, and the
+  // P/dS arithmetic of a block fills the slots between its S/dP and dV/dK MFMAs.
+  constexpr int NS = C::NS, NV = C::NV, NVB = C::NVB, NM = C::NM;
+  constexpr int PD = 4;
+  constexpr auto elem_slot = [](int b, int i) {
+    return b == 0 ? NS + 2 + (i * (NS - 2)) / 16 : 2 * NS + 2 + (i * (NV - 2)) / 16;
+  };
+  // Slot of copy k of the next-but-one tile.
+  constexpr auto copy_slot = [](int k) { return 1 + (k * (NM - 6)) / C::NLD; };
+  int bcur = 0;
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int qi0 = qt * C::BQ;
+    const int b1 = bcur == 2 ? 0 : bcur + 1;
+    const int b2 = b1 == 2 ? 0 : b1 + 1;
+    const int boff = bcur * C::BUF;
+    const int pA0 = aA0 + boff, pA1 = aA1 + boff;
+    int pT[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) pT[x] = aT[x] + boff;
+    auto operand = [&](int m) -> frag {
+      if (m < 2 * NS) {
+        const int qb = m / NS, ks = (m % NS) / 2, mat = m & 1;
+        const int off = mat * C::TILE + qb * 32 * C::PB + 32 * ks;
+        const uint2 lo = *reinterpret_cast<const uint2*>(smem + pA0 + off);
+        const uint2 hi = *reinterpret_cast<const uint2*>(smem + pA1 + off);
+        return __builtin_bit_cast(frag, uint4{lo.x, lo.y, hi.x, hi.y});
+      }
+      const int r = m - 2 * NS, qb = r / NV, u = (r % NV) / NVB, db = (r % NVB) / 2;
+      const int mat = (r & 1) ? 0 : 1;         // dK reads Q, dV reads dO
+      s16x4 v[2];
+#pragma unroll
+      for (int rp = 0; rp < 2; ++rp) {
+        const int off = mat * C::TILE + (qb * 32 + 16 * u + 8 * rp) * C::PB + 64 * db;
+        v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(smem + pT[(2 * u + rp) & 3] + off));
+      }
+      return __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
+                                            v[1][0], v[1][1], v[1][2], v[1][3]});
+    };
+    f32x16 s[2], dp[2], p[2], ds[2];
+    frag pa[2][2], sa[2][2];
+    f32x4 l4[2][4], d4[2][4];
+    frag opq[PD];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = f32x16{};
+      dp[b] = f32x16{};
+    }
+#pragma unroll
+    for (int m = 0; m < PD; ++m) opq[m] = operand(m);
+    static_for<0, NM>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+#pragma unroll
+      for (int k = 0; k < C::NLD; ++k)
+        if (m == copy_slot(k)) copy_op(b2, qt + 2, k);
+      // L2 and D of 4 queries (one element group), PD slots before first use.
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if (m == elem_slot(b, 4 * g) - PD) {
+            const float* l2 = reinterpret_cast<const float*>(smem + boff + 2 * C::TILE);
+            l4[b][g] = *reinterpret_cast<const f32x4*>(&l2[b * 32 + 8 * g + 4 * h]);
+            d4[b][g] = *reinterpret_cast<const f32x4*>(&l2[C::BQ + b * 32 + 8 * g + 4 * h]);
+          }
+      const frag x = opq[m % PD];
+      if constexpr (m + PD < NM) opq[m % PD] = operand(m + PD);
+      if constexpr (m < 2 * NS) {
+        constexpr int qb = m / NS, ks = (m % NS) / 2;
+        if constexpr (m & 1) dp[qb] = M::mma(x, vf[ks], dp[qb]);
+        else s[qb] = M::mma(x, kf[ks], s[qb]);
+      } else {
+        constexpr int r = m - 2 * NS, qb = r / NV, u = (r % NV) / NVB, db = (r % NVB) / 2;
+        if constexpr (r & 1) dk[db] = M::mma(sa[qb][u], x, dk[db]);
+        else dv[db] = M::mma(pa[qb][u], x, dv[db]);
+      }
+      // P = exp2(S c - L2), dS = P (dP - D).  Element i of lane half h is
+      // query 8 (i / 4) + 2 (i % 4) + h of its block; keys past N need no mask
+      // (their results are never stored).
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (m == elem_slot(b, i)) {
+            float e = exp2_fast(fmaf(s[b][i], c, -l4[b][i / 4][i % 4]));
+            if (CAUSAL && qi0 + b * 32 + 8 * (i / 4) + 2 * (i % 4) + h < myk) e = 0.f;
+            p[b][i] = e;
+            ds[b][i] = e * (dp[b][i] - d4[b][i / 4][i % 4]);
+            if ((i + 1) % 8 == 0) {
+              pa[b][i / 8] = pack_frag<T>(p[b], i / 8);
+              sa[b][i / 8] = pack_frag<T>(ds[b], i / 8);
+            }
+          }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // Tile qt + 1 (copied during the previous tile) must have landed; the
+    // copies of tile qt + 2 may still be in flight.
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
+    __syncthreads();
+    bcur = b1;
+  }
+  // No copy may still be writing LDS when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  // Epilogue: lane (col = d, h) holds keys kw + 8(i/4) + 4h + i%4.
+  T* dK = static_cast<T*>(a.dk) + head * N * D;
+  T* dV = static_cast<T*>(a.dv) + head * N * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kw + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (key < N) {
+        const size_t off = (size_t)key * D + db * 32 + col;
+        dK[off] = (T)(dk[db][i] * a.scale);
+        dV[off] = (T)dv[db][i];
+      }
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
-  const long rows = (long)a.B * a.H * a.N;
+  const long rows = (long)a.B * a.H * a.Np;
   if (step == BwdStep::pre) {
     constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
     const long blocks = (rows + RPB - 1) / RPB;
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a, rows);
   } else if (step == BwdStep::dkdv) {
-    dim3 grid((a.N + DkvTile<T, D>::BKC - 1) / DkvTile<T, D>::BKC, a.H, a.B);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
+    if constexpr (sizeof(T) == 2) {
+      dim3 grid((a.N + Dkv16<D>::BKC - 1) / Dkv16<D>::BKC, a.H, a.B);
+      hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
+    } else {
+      dim3 grid((a.N + DkvTile<T, D>::BKC - 1) / DkvTile<T, D>::BKC, a.H, a.B);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
+    }
   } else {
     dim3 grid((a.N + DqTile<T, D>::BR - 1) / DqTile<T, D>::BR, a.H, a.B);
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(DqTile<T, D>::NT), 0, s, a);

@@ -288,6 +288,43 @@ struct TileStage {
   __device__ inline void store_transposed(T* dst, int tid) const;
 };
 
+// ---------------------------------------------------------------- copies into LDS
+
+// Byte address in LDS of a pointer into a __shared__ array.
+__device__ inline uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Copy 4 bytes per lane from global memory straight into LDS: lane i's dword
+// lands at LDS byte address lds + 4 i (lds must be wave-uniform); with
+// HALF, only lanes 0..31 copy (128 bytes).  Issued as inline assembly so that
+// the compiler adds no waits of its own for it: the caller waits with
+// s_waitcnt vmcnt before the data is read, and before the barrier that hands
+// it to the other waves.  Expects every lane of the wave active.
+template <bool HALF>
+__device__ inline void copy_to_lds(const void* src, uint32_t lds) {
+  if constexpr (HALF) {
+    uint64_t saved;
+    asm volatile(
+        "s_mov_b64 %0, exec\n\t"
+        "s_mov_b32 exec_hi, 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b64 exec, %0"
+        : "=&s"(saved)
+        : "v"(src), "{m0}"(lds)
+        : "memory");
+  } else {
+    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+  }
+}
+
+// s_waitcnt operand that waits until at most n vector-memory loads are
+// outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima).
+__host__ __device__ constexpr int wait_vmcnt(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 // ---------------------------------------------------------------- stores
 
 // Store 4 consecutive values (rounded to T) at p.

@@ -28,8 +28,10 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;   // [B,H,N] workspace: D_i = rowsum(dO_i * O_i)
+  float* delta;   // workspace [B,H,Np]: D_i = rowsum(dO_i * O_i), 0 past N
+  float* l2;      // workspace [B,H,Np]: LSE_i * log2(e), +inf past N
   int B, H, N;
+  int Np;         // N rounded up to a multiple of 64
   float scale;
 };
 

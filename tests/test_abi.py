@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
     for st in range(6):
         assert fa.fa_status_string(st) and fa.fa_status_string(st) != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -102,9 +102,10 @@ def test_bwd_rejects(kw, status):
 
 def test_split_backward_rejects():
     ws, nb = 0x10000, fa.fa_bwd_workspace_size(1, 1, 128, 64)
-    assert fa.fa_bwd_preprocess(None, P, 1, 1, 128, 64, fa.FA_F16, ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
-    assert fa.fa_bwd_preprocess(P, P, 1, 1, 128, 96, fa.FA_F16, ws, nb, None) == fa.FA_ERR_UNSUPPORTED
-    assert fa.fa_bwd_preprocess(P, P, 1, 1, 128, 64, fa.FA_F16, ws, nb - 1, None) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_preprocess(None, P, P, 1, 1, 128, 64, fa.FA_F16, ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_bwd_preprocess(P, P, None, 1, 1, 128, 64, fa.FA_F16, ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_bwd_preprocess(P, P, P, 1, 1, 128, 96, fa.FA_F16, ws, nb, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_preprocess(P, P, P, 1, 1, 128, 64, fa.FA_F16, ws, nb - 1, None) == fa.FA_ERR_WORKSPACE
     assert fa.fa_bwd_dkdv(P, P, P, P, P, P, None, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws, nb,
                           None) == fa.FA_ERR_INVALID_ARGUMENT
     assert fa.fa_bwd_dkdv(P, P, P, P, P, P, P, 1, 1, 128, 64, 0, math.nan, fa.FA_F16, ws, nb,
@@ -119,10 +120,11 @@ def test_split_backward_rejects():
 
 
 def test_workspace_size():
-    B, H, N, d = 2, 3, 100, 64
-    rows = B * H * N
+    # Two float32 arrays [B, H, Np], Np = N rounded up to a multiple of 64.
     up = lambda x: (x + 255) // 256 * 256
-    assert fa.fa_bwd_workspace_size(B, H, N, d) == up(4 * rows)
+    for B, H, N, d in ((2, 3, 100, 64), (1, 1, 64, 128), (1, 1, 65, 128), (4, 32, 4096, 128)):
+        Np = (N + 63) // 64 * 64
+        assert fa.fa_bwd_workspace_size(B, H, N, d) == up(2 * 4 * B * H * Np)
     assert fa.fa_bwd_workspace_size(0, 1, 1, 64) == 0
     assert fa.fa_bwd_workspace_size(1, 1, -3, 64) == 0
 
@@ -137,7 +139,7 @@ def test_valid_arguments_without_gpu_report_device_error():
     assert _fwd() == fa.FA_ERR_DEVICE
     assert _bwd() == fa.FA_ERR_DEVICE
     nb = fa.fa_bwd_workspace_size(1, 1, 128, 64)
-    assert fa.fa_bwd_preprocess(P, P, 1, 1, 128, 64, fa.FA_F16, 0x10000, nb, None) == fa.FA_ERR_DEVICE
+    assert fa.fa_bwd_preprocess(P, P, P, 1, 1, 128, 64, fa.FA_F16, 0x10000, nb, None) == fa.FA_ERR_DEVICE
     assert fa.fa_bwd_dq(P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, 0x10000, nb,
                         None) == fa.FA_ERR_DEVICE
 

@@ -207,11 +207,16 @@ def test_repeatable_and_delta(fa):
     b = gpu_run(fa, inp, True, w.scale)
     for name in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(a[name], b[name]), f"{name} differs between runs"
-    # D = rowsum(dO * O) sits at the start of the workspace.
-    rows = 2 * 2 * 333
-    D = a["ws"][: 4 * rows].view(torch.float32).reshape(2, 2, 333)
+    # Workspace: D = rowsum(dO * O), then L2 = LSE log2(e), each [B, H, Np]
+    # with Np = 384 (333 rounded up to 64); padding rows hold D = 0, L2 = +inf.
+    Np = 384
+    ws = a["ws"][: 2 * 4 * 4 * Np].view(torch.float32).reshape(2, 2, 2, Np)
+    D, L2 = f64(ws[0]), f64(ws[1])
     expect = (f64(inp["do"]) * f64(a["o"])).sum(-1)
-    assert np.max(np.abs(f64(D) - expect)) <= 1e-4
+    assert np.max(np.abs(D[..., :333] - expect)) <= 1e-4
+    l2_expect = f64(a["lse"]) * 1.4426950408889634
+    assert np.max(np.abs(L2[..., :333] - l2_expect)) <= 1e-6 * max(1.0, np.max(np.abs(l2_expect)))
+    assert np.all(D[..., 333:] == 0) and np.all(np.isposinf(L2[..., 333:]))
 
 
 def test_non_default_stream(fa):
