@@ -32,9 +32,17 @@ COMMON = [
 ]
 
 
+# Per-file flags.  The 16-bit backward kernels keep their MFMA accumulators in
+# VGPRs (the VALU reads S and dP directly, no AGPR copies).
+EXTRA = {
+    f"fa_bwd_{t}_d{d}.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    for t in ("bf16", "f16") for d in (64, 128)
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
     err = "\n".join(line for line in (r.stderr or "").splitlines() if noise not in line)

@@ -590,6 +590,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     kf[ks] = load_frag<T>(K + (size_t)kg * D + ks * 16 + 8 * h);
     vf[ks] = load_frag<T>(V + (size_t)kg * D + ks * 16 + 8 * h);
   }
+  // K and V stay in AGPRs (MFMA reads its B operand from there); the VGPRs
+  // hold the accumulators, which the VALU reads directly.
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    asm volatile("" : "+a"(kf[ks]));
+    asm volatile("" : "+a"(vf[ks]));
+  }
   f32x16 dv[D / 32], dk[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
