@@ -521,6 +521,212 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ dQ (16-bit types)
+
+// Row of a 32-row block (queries or keys) that supplies result row m of an MFMA
+// whose A operand is read from a row-major tile (m = 8a + 4h + s -> 8a + 2s + h):
+// the 4 rows that one transposing read gathers for a later MFMA are then 2 apart.
+__device__ constexpr int dkv16_pi(int m) { return (m & ~7) | ((m & 3) << 1) | ((m >> 2) & 1); }
+
+// The dQ kernel for 16-bit types, on the same LDS layout as the 16-bit dK/dV
+// kernel (rows padded to D + 16 elements, 8-byte slot XOR (r >> 3) & 3):
+// K and V tiles are copied straight into LDS, three buffers deep; S^T = K Q^T
+// and dP^T = V dO^T take their A operand from K / V rows (two 8-byte reads,
+// rows in the order dkv16_pi) and Q / dO from registers; dQ^T += K^T dS^T takes
+// K^T through transposing reads.  8 waves x 32 queries per workgroup.
+template <int D>
+struct Dq16 {
+  static constexpr int NW = 8;
+  static constexpr int NT = 64 * NW;
+  static constexpr int BR = 32 * NW;             // queries per workgroup
+  static constexpr int BC = 64;                  // keys per tile
+  static constexpr int PB = 2 * (D + 16);        // row pitch in bytes
+  static constexpr int TILE = BC * PB;
+  static constexpr int BUF = 2 * TILE;           // K, V
+  static constexpr int NB = 3;
+  static constexpr bool HALF = D == 64;
+  static constexpr int NKS = D / 16;
+  static constexpr int NS = 2 * NKS;             // S/dP MFMAs per 32-key block
+  static constexpr int NQ = 2 * (D / 32);        // dQ MFMAs per 32-key block
+  static constexpr int NM = 2 * NS + 2 * NQ;     // MFMAs per tile
+  static constexpr int NLD = 2 * BC / NW;        // row copies per wave per tile
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
+  using C = Dq16<D>;
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, col = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = a.N;
+  const int ntq = gridDim.x;
+  const int lin = xcd_work_index();
+  // Under the causal mask the last query tiles see the most keys: start them first.
+  const int qt = CAUSAL ? ntq - 1 - (lin % ntq) : (lin % ntq);
+  const int q0 = qt * C::BR;
+  const size_t head = (size_t)(lin / ntq);
+  const T* Q = static_cast<const T*>(a.q) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head * N * D;
+  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  const T* dO = static_cast<const T*>(a.dout) + head * N * D;
+  T* dQ = static_cast<T*>(a.dq) + head * N * D;
+  const float c = a.scale * kLog2e;
+
+  const int qw = q0 + 32 * w;
+  const int myq = qw + col;
+  const int qrow = min(myq, N - 1);
+  // Q and dO operands (B of S^T = K Q^T and of dP^T = V dO^T) of this lane's
+  // query, held in registers for the whole kernel.
+  frag qf[C::NKS], gf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    qf[ks] = load_frag<T>(Q + (size_t)qrow * D + ks * 16 + 8 * h);
+    gf[ks] = load_frag<T>(dO + (size_t)qrow * D + ks * 16 + 8 * h);
+  }
+  const float l2 = a.l2[head * a.Np + qrow];       // LSE log2(e), +inf if no visible key
+  const float dl = a.delta[head * a.Np + qrow];
+  // Keys above klim are masked (causal and past N).
+  const int klim = CAUSAL ? min(myq, N - 1) : N - 1;
+
+  const int nkt_all = (N + C::BC - 1) / C::BC;
+  const int qlast = min(q0 + C::BR, N) - 1;
+  const int nkt = CAUSAL ? min(nkt_all, qlast / C::BC + 1) : nkt_all;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+  // Lane parts of the LDS addresses (bytes from the start of a buffer).
+  const int arow = dkv16_pi(col);
+  const int aA0 = arow * C::PB + 8 * ((2 * h) ^ (col >> 3));
+  const int aA1 = arow * C::PB + 8 * ((2 * h + 1) ^ (col >> 3));
+  const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
+  int aT[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) aT[x] = (2 * ts + h) * C::PB + 32 * tg + 8 * (ta ^ x);
+  int gofs[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) gofs[f] = 8 * ((lane >> 1) ^ f) + 4 * (lane & 1);
+  // Copy op j (0..15) of key tile kt into buffer b: waves 0-3 copy K, 4-7 copy
+  // V, rows 4 j + (w & 3).  Rows past N are clamped (masked through klim).
+  auto copy_op = [&](int b, int kt, int j) {
+    const uint32_t base = lds_address(smem) + b * C::BUF;
+    const int mat = w >> 2;
+    const int rr = 4 * j + (w & 3);
+    const int f = (j >> 1) & 3;                // slot XOR of row rr: (rr >> 3) & 3
+    const int rowg = min(kt * C::BC + rr, N - 1);
+    const char* src = reinterpret_cast<const char*>(mat ? V : K) + (size_t)rowg * (2 * D) + gofs[f];
+    copy_to_lds<C::HALF>(src, base + mat * C::TILE + rr * C::PB);
+  };
+
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+  for (int j = 0; j < C::NLD; ++j) copy_op(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < C::NLD; ++j) copy_op(1, 1, j);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+
+  // The MFMA stream of one key tile: S^T/dP^T of key blocks 0 and 1 (32 keys
+  // each), then dQ^T of blocks 0 and 1; the dS arithmetic of block 0 runs
+  // beside the S/dP MFMAs of block 1, that of block 1 beside dQ of block 0.
+  constexpr int NS = C::NS, NQ = C::NQ, NM = C::NM;
+  constexpr int PD = 4;
+  constexpr auto elem_slot = [](int b, int i) {
+    return b == 0 ? NS + 2 + (i * (NS - 2)) / 16 : 2 * NS + 1 + (i * (NQ - 2)) / 16;
+  };
+  constexpr auto copy_slot = [](int k) { return 1 + (k * (NM - 6)) / C::NLD; };
+  int bcur = 0;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int key0 = kt * C::BC;
+    const int b1 = bcur == 2 ? 0 : bcur + 1;
+    const int b2 = b1 == 2 ? 0 : b1 + 1;
+    const int boff = bcur * C::BUF;
+    const int pA0 = aA0 + boff, pA1 = aA1 + boff;
+    int pT[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) pT[x] = aT[x] + boff;
+    auto operand = [&](int m) -> frag {
+      if (m < 2 * NS) {
+        const int kb = m / NS, ks = (m % NS) / 2, mat = m & 1;   // K for S, V for dP
+        const int off = mat * C::TILE + kb * 32 * C::PB + 32 * ks;
+        const uint2 lo = *reinterpret_cast<const uint2*>(smem + pA0 + off);
+        const uint2 hi = *reinterpret_cast<const uint2*>(smem + pA1 + off);
+        return __builtin_bit_cast(frag, uint4{lo.x, lo.y, hi.x, hi.y});
+      }
+      const int r = m - 2 * NS, kb = r / NQ, u = (r % NQ) / (D / 32), db = r % (D / 32);
+      s16x4 v[2];
+#pragma unroll
+      for (int rp = 0; rp < 2; ++rp) {
+        const int off = (kb * 32 + 16 * u + 8 * rp) * C::PB + 64 * db;
+        v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(smem + pT[(2 * u + rp) & 3] + off));
+      }
+      return __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
+                                            v[1][0], v[1][1], v[1][2], v[1][3]});
+    };
+    f32x16 s[2], dp[2], ds[2];
+    frag sa[2][2];
+    frag opq[PD];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = f32x16{};
+      dp[b] = f32x16{};
+    }
+#pragma unroll
+    for (int m = 0; m < PD; ++m) opq[m] = operand(m);
+    static_for<0, NM>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+#pragma unroll
+      for (int k = 0; k < C::NLD; ++k)
+        if (m == copy_slot(k)) copy_op(b2, kt + 2, k);
+      const frag x = opq[m % PD];
+      if constexpr (m + PD < NM) opq[m % PD] = operand(m + PD);
+      if constexpr (m < 2 * NS) {
+        constexpr int kb = m / NS, ks = (m % NS) / 2;
+        if constexpr (m & 1) dp[kb] = M::mma(x, gf[ks], dp[kb]);
+        else s[kb] = M::mma(x, qf[ks], s[kb]);
+      } else {
+        constexpr int r = m - 2 * NS, kb = r / NQ, u = (r % NQ) / (D / 32), db = r % (D / 32);
+        acc[db] = M::mma(x, sa[kb][u], acc[db]);
+      }
+      // P = exp2(S c - L2), dS = P (dP - D); element i of lane half h is key
+      // 8 (i / 4) + 2 (i % 4) + h of its block.
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (m == elem_slot(b, i)) {
+            float e = exp2_fast(fmaf(s[b][i], c, -l2));
+            if (key0 + b * 32 + 8 * (i / 4) + 2 * (i % 4) + h > klim) e = 0.f;
+            ds[b][i] = e * (dp[b][i] - dl);
+            if ((i + 1) % 8 == 0) sa[b][i / 8] = pack_frag<T>(ds[b], i / 8);
+          }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
+    __syncthreads();
+    bcur = b1;
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  if (myq < N) {
+    // Lane (col = query, h) holds dQ^T rows d = 32 db + 8 (i / 4) + 4 h + i % 4.
+    T* orow = dQ + (size_t)myq * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        store4<T>(orow + db * 32 + 8 * r + 4 * h, acc[db][4 * r] * sc, acc[db][4 * r + 1] * sc,
+                  acc[db][4 * r + 2] * sc, acc[db][4 * r + 3] * sc);
+  }
+}
+
 // ------------------------------------------------------------------ dK, dV (16-bit types)
 
 // Layout of the 16-bit dK/dV kernel.  Query tiles (Q and dO, 64 rows) live in
@@ -549,10 +755,6 @@ struct Dkv16 {
   static constexpr int NM = 2 * NS + 2 * NV;     // MFMAs per tile
   static constexpr int NLD = 2 * BQ / 4 + 2;     // copies per wave per tile: Q, dO rows; L2, D
 };
-
-// Row of a 32-query block that supplies S row m (m = 8a + 4h + s -> 8a + 2s + h):
-// the 4 rows of one transposing read are then 2 apart.
-__device__ constexpr int dkv16_pi(int m) { return (m & ~7) | ((m & 3) << 1) | ((m >> 2) & 1); }
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
@@ -788,6 +990,9 @@ static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
       dim3 grid((a.N + DkvTile<T, D>::BKC - 1) / DkvTile<T, D>::BKC, a.H, a.B);
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
     }
+  } else if constexpr (sizeof(T) == 2) {
+    dim3 grid((a.N + Dq16<D>::BR - 1) / Dq16<D>::BR, a.H, a.B);
+    hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL>), grid, dim3(Dq16<D>::NT), 0, s, a);
   } else {
     dim3 grid((a.N + DqTile<T, D>::BR - 1) / DqTile<T, D>::BR, a.H, a.B);
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(DqTile<T, D>::NT), 0, s, a);
