@@ -32,12 +32,11 @@ COMMON = [
 ]
 
 
-# Per-file flags.  The 16-bit backward kernels keep their MFMA accumulators in
-# VGPRs (the VALU reads S and dP directly, no AGPR copies).
-EXTRA = {
-    f"fa_bwd_{t}_d{d}.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-    for t in ("bf16", "f16") for d in (64, 128)
-}
+# Per-file flags.  The 16-bit kernels keep their MFMA accumulators in VGPRs
+# (the VALU reads S and dP directly, no AGPR copies).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {f"fa_bwd_{t}_d{d}.hip": VGPR_FORM for t in ("bf16", "f16") for d in (64, 128)}
+EXTRA["fa_fwd.hip"] = VGPR_FORM
 
 
 def _compile(src: str) -> str:

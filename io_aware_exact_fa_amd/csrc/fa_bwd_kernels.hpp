@@ -72,15 +72,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long rows) {
   }
 }
 
-// Work index of this workgroup: workgroups are dealt to the 8 XCDs round-robin
-// by linear id; give each XCD a contiguous range so that the tiles of one head
-// share their K/V (or Q/dO) through one L2.
-__device__ inline int xcd_work_index() {
-  const int nwork = gridDim.x * gridDim.y * gridDim.z;
-  int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  if ((nwork & 7) == 0) lin = (lin & 7) * (nwork >> 3) + (lin >> 3);
-  return lin;
-}
 
 // ------------------------------------------------------------------ dQ
 
@@ -523,16 +514,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ dQ (16-bit types)
 
-// Row of a 32-row block (queries or keys) that supplies result row m of an MFMA
-// whose A operand is read from a row-major tile (m = 8a + 4h + s -> 8a + 2s + h):
-// the 4 rows that one transposing read gathers for a later MFMA are then 2 apart.
-__device__ constexpr int dkv16_pi(int m) { return (m & ~7) | ((m & 3) << 1) | ((m >> 2) & 1); }
 
 // The dQ kernel for 16-bit types, on the same LDS layout as the 16-bit dK/dV
 // kernel (rows padded to D + 16 elements, 8-byte slot XOR (r >> 3) & 3):
 // K and V tiles are copied straight into LDS, three buffers deep; S^T = K Q^T
 // and dP^T = V dO^T take their A operand from K / V rows (two 8-byte reads,
-// rows in the order dkv16_pi) and Q / dO from registers; dQ^T += K^T dS^T takes
+// rows in the order row_pi) and Q / dO from registers; dQ^T += K^T dS^T takes
 // K^T through transposing reads.  8 waves x 32 queries per workgroup.
 template <int D>
 struct Dq16 {
@@ -601,7 +588,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
-  const int arow = dkv16_pi(col);
+  const int arow = row_pi(col);
   const int aA0 = arow * C::PB + 8 * ((2 * h) ^ (col >> 3));
   const int aA1 = arow * C::PB + 8 * ((2 * h + 1) ^ (col >> 3));
   const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
@@ -619,8 +606,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
     const int rr = 4 * j + (w & 3);
     const int f = (j >> 1) & 3;                // slot XOR of row rr: (rr >> 3) & 3
     const int rowg = min(kt * C::BC + rr, N - 1);
-    const char* src = reinterpret_cast<const char*>(mat ? V : K) + (size_t)rowg * (2 * D) + gofs[f];
-    copy_to_lds<C::HALF>(src, base + mat * C::TILE + rr * C::PB);
+    const char* src = reinterpret_cast<const char*>(mat ? V : K) + (size_t)rowg * (2 * D);
+    copy_to_lds<C::HALF>(src, gofs[f], base + mat * C::TILE + rr * C::PB);
   };
 
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -809,7 +796,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   const int qt0 = CAUSAL ? k0 / C::BQ : 0;   // earlier tiles see none of these keys
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
-  const int arow = dkv16_pi(col);
+  const int arow = row_pi(col);
   const int aA0 = arow * C::PB + 8 * ((2 * h) ^ (col >> 3));
   const int aA1 = arow * C::PB + 8 * ((2 * h + 1) ^ (col >> 3));
   // Transposing reads: source lane (group g, a4, s) points at row 2s + h, columns
@@ -825,7 +812,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   for (int f = 0; f < 4; ++f) gofs[f] = 8 * ((lane >> 1) ^ f) + 4 * (lane & 1);
   // Copy op j of tile qt into buffer b: j < 32: wave w copies rows 4 jj + w
   // (jj = 0..15) of Q (j < 16) or dO; j = 32, 33: the tile's L2 and D, lane p
-  // holding query dkv16_pi(p) of the tile (the order of a lane half's P
+  // holding query row_pi(p) of the tile (the order of a lane half's P
   // elements).  Every wave copies the same L2 and D.  Rows past N are clamped
   // (their P is 0 through L2 = +inf), tiles past the end copy the last tile.
   auto copy_op = [&](int b, int qt, int j) {
@@ -835,11 +822,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
       const int rr = 4 * jj + w;
       const int f = (jj >> 1) & 3;             // slot XOR of row rr: (rr >> 3) & 3
       const int rowg = min(qt * C::BQ + rr, N - 1);
-      const char* src = reinterpret_cast<const char*>(mat ? dO : Q) + (size_t)rowg * (2 * D) + gofs[f];
-      copy_to_lds<C::HALF>(src, base + mat * C::TILE + rr * C::PB);
+      const char* src = reinterpret_cast<const char*>(mat ? dO : Q) + (size_t)rowg * (2 * D);
+      copy_to_lds<C::HALF>(src, gofs[f], base + mat * C::TILE + rr * C::PB);
     } else {
-      const int q = min(qt, nqt - 1) * C::BQ + dkv16_pi(lane);
-      copy_to_lds<false>((j == 32 ? L2 : Dl) + q, base + 2 * C::TILE + (j - 32) * C::BQ * 4);
+      const float* src = (j == 32 ? L2 : Dl) + min(qt, nqt - 1) * C::BQ;
+      copy_to_lds<false>(src, 4 * row_pi(lane), base + 2 * C::TILE + (j - 32) * C::BQ * 4);
     }
   };
 

@@ -288,6 +288,21 @@ struct TileStage {
   __device__ inline void store_transposed(T* dst, int tid) const;
 };
 
+// Work index of this workgroup: workgroups are dealt to the 8 XCDs round-robin
+// by linear id; give each XCD a contiguous range so that the tiles of one head
+// share their K/V (or Q/dO) through one L2.
+__device__ inline int xcd_work_index() {
+  const int nwork = gridDim.x * gridDim.y * gridDim.z;
+  int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  if ((nwork & 7) == 0) lin = (lin & 7) * (nwork >> 3) + (lin >> 3);
+  return lin;
+}
+
+// Row of a 32-row block (queries or keys) that supplies result row m of an MFMA
+// whose A operand is read from a row-major tile (m = 8a + 4h + s -> 8a + 2s + h):
+// the 4 rows that one transposing read gathers for a later MFMA are then 2 apart.
+__device__ constexpr int row_pi(int m) { return (m & ~7) | ((m & 3) << 1) | ((m >> 2) & 1); }
+
 // ---------------------------------------------------------------- copies into LDS
 
 // Byte address in LDS of a pointer into a __shared__ array.
@@ -295,26 +310,27 @@ __device__ inline uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Copy 4 bytes per lane from global memory straight into LDS: lane i's dword
-// lands at LDS byte address lds + 4 i (lds must be wave-uniform); with
-// HALF, only lanes 0..31 copy (128 bytes).  Issued as inline assembly so that
-// the compiler adds no waits of its own for it: the caller waits with
-// s_waitcnt vmcnt before the data is read, and before the barrier that hands
-// it to the other waves.  Expects every lane of the wave active.
+// Copy 4 bytes per lane from global memory straight into LDS: lane i reads the
+// dword at base + off_i (base wave-uniform, off_i a 32-bit byte offset) and it
+// lands at LDS byte address lds + 4 i (lds wave-uniform); with HALF, only lanes
+// 0..31 copy (128 bytes).  Issued as inline assembly so that the compiler adds
+// no waits of its own for it: the caller waits with s_waitcnt vmcnt before the
+// data is read, and before the barrier that hands it to the other waves.
+// Expects every lane of the wave active.
 template <bool HALF>
-__device__ inline void copy_to_lds(const void* src, uint32_t lds) {
+__device__ inline void copy_to_lds(const void* base, uint32_t off, uint32_t lds) {
   if constexpr (HALF) {
     uint64_t saved;
     asm volatile(
         "s_mov_b64 %0, exec\n\t"
         "s_mov_b32 exec_hi, 0\n\t"
-        "global_load_lds_dword %1, off\n\t"
+        "global_load_lds_dword %1, %2\n\t"
         "s_mov_b64 exec, %0"
         : "=&s"(saved)
-        : "v"(src), "{m0}"(lds)
+        : "v"(off), "s"(base), "{m0}"(lds)
         : "memory");
   } else {
-    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+    asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
   }
 }
 

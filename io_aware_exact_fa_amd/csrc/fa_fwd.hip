@@ -331,11 +331,274 @@ void fwd_kernel(FwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ 16-bit types
+
+
+// The forward for 16-bit types.  K and V tiles are copied from global memory
+// straight into LDS (global_load_lds), four buffers deep, into row-major tiles
+// whose rows are padded to D + 16 elements with the 8-byte slots of row r
+// XOR-ed in their low two bits by (r >> 3) & 3.  S^T = K Q^T takes its A
+// operand from K rows (two 8-byte reads, rows in the order row_pi) and Q from
+// registers; O^T += V^T P~^T takes V^T through transposing LDS reads
+// (ds_read_b64_tr_b16), which gather the 4 keys of each lane's P~ elements.
+// Each tile is one fixed MFMA stream: S of the next tile with the softmax of
+// this tile spread between its MFMAs, then P~ V of this tile; the accumulator
+// is rescaled in between, only when the max of some row of the wave grew.
+// 8 waves x 32 query rows per workgroup.
+template <int D>
+struct Fwd16 {
+  static constexpr int NW = 8;
+  static constexpr int NT = 64 * NW;
+  static constexpr int BR = 32 * NW;             // query rows per workgroup
+  static constexpr int BC = 64;                  // keys per tile
+  static constexpr int PB = 2 * (D + 16);        // row pitch in bytes
+  static constexpr int TILE = BC * PB;
+  static constexpr int BUF = 2 * TILE;           // K, V
+  static constexpr int NB = 4;                   // K runs one tile ahead of V
+  static constexpr bool HALF = D == 64;
+  static constexpr int NKS = D / 16;
+  static constexpr int NS = 2 * NKS;             // S MFMAs per tile (two 32-key blocks)
+  static constexpr int NV = 4 * (D / 32);        // P~V MFMAs per tile
+  static constexpr int NM = NS + NV;
+  static constexpr int NLD = 2 * BC / NW;        // row copies per wave per tile
+  static constexpr int NA = NS / 2;              // slots of the row max
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
+  using C = Fwd16<D>;
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, col = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = a.N;
+  const int ntq = gridDim.x;
+  const int lin = xcd_work_index();
+  const int qt = CAUSAL ? ntq - 1 - (lin % ntq) : (lin % ntq);
+  const int q0 = qt * C::BR;
+  const size_t head = (size_t)(lin / ntq);
+  const T* Q = static_cast<const T*>(a.q) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head * N * D;
+  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  T* O = static_cast<T*>(a.o) + head * N * D;
+  float* L = a.lse + head * N;
+
+  const int qw = q0 + 32 * w;
+  const int myq = qw + col;
+  // A negative scale is folded into Q (exact sign flip) so that c > 0.
+  const float c = fabsf(a.scale) * kLog2e;
+  frag qf[C::NKS];
+  {
+    const T* qrow = Q + (size_t)min(myq, N - 1) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const frag f = load_frag<T>(qrow + ks * 16);
+      qf[ks] = (a.scale < 0.f) ? neg_frag<T>(f) : f;
+    }
+  }
+  // Keys above klim are masked (causal and past N).
+  const int klim = CAUSAL ? min(myq, N - 1) : N - 1;
+  const int ntiles_all = (N + C::BC - 1) / C::BC;
+  const int qlast = min(q0 + C::BR, N) - 1;
+  const int ntiles = CAUSAL ? min(ntiles_all, qlast / C::BC + 1) : ntiles_all;
+
+  // Lane parts of the LDS addresses (bytes from the start of a buffer).
+  const int arow = row_pi(col);
+  const int aA0 = arow * C::PB + 8 * ((2 * h) ^ (col >> 3));
+  const int aA1 = arow * C::PB + 8 * ((2 * h + 1) ^ (col >> 3));
+  const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
+  int aT[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) aT[x] = C::TILE + (2 * ts + h) * C::PB + 32 * tg + 8 * (ta ^ x);
+  int gofs[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) gofs[f] = 8 * ((lane >> 1) ^ f) + 4 * (lane & 1);
+  // Copy op j (0..15) of key tile t into buffer b: waves 0-3 copy K, 4-7 copy V,
+  // rows 4 j + (w & 3); rows past N are clamped (masked through klim).
+  auto copy_op = [&](int b, int t, int j) {
+    const uint32_t base = lds_address(smem) + b * C::BUF;
+    const int mat = w >> 2;
+    const int rr = 4 * j + (w & 3);
+    const int f = (j >> 1) & 3;
+    const int rowg = min(t * C::BC + rr, N - 1);
+    const char* src = reinterpret_cast<const char*>(mat ? V : K) + (size_t)rowg * (2 * D);
+    copy_to_lds<C::HALF>(src, gofs[f], base + mat * C::TILE + rr * C::PB);
+  };
+  // S^T MFMA m of a tile (m < NS): key block kb = m & 1, k step ks = m >> 1.
+  auto opS = [&](int kboff, int m) -> frag {
+    const int off = kboff + (m & 1) * 32 * C::PB + 32 * (m >> 1);
+    const uint2 lo = *reinterpret_cast<const uint2*>(smem + aA0 + off);
+    const uint2 hi = *reinterpret_cast<const uint2*>(smem + aA1 + off);
+    return __builtin_bit_cast(frag, uint4{lo.x, lo.y, hi.x, hi.y});
+  };
+  // P~V MFMA r of a tile (r < NV): key block kb, 16-key step u, head-dim block db.
+  auto opV = [&](int vboff, int r) -> frag {
+    const int kb = r / (2 * (D / 32)), u = (r / (D / 32)) & 1, db = r % (D / 32);
+    s16x4 v[2];
+#pragma unroll
+    for (int rp = 0; rp < 2; ++rp) {
+      const int off = vboff + (kb * 32 + 16 * u + 8 * rp) * C::PB + 64 * db;
+      v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + aT[(2 * u + rp) & 3] + off));
+    }
+    return __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
+                                          v[1][0], v[1][1], v[1][2], v[1][3]});
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY;   // running max of c S (log2 units)
+  float l_run = 0.f;         // this lane's share of the running normalizer
+
+  // Prologue: tiles 0, 1, 2 into buffers 0, 1, 2; S of tile 0.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int j = 0; j < C::NLD; ++j) copy_op(t, t, j);
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // tile 2 may still be in flight
+  __syncthreads();
+  f32x16 sc[2];
+  sc[0] = f32x16{};
+  sc[1] = f32x16{};
+#pragma unroll
+  for (int m = 0; m < C::NS; ++m) sc[m & 1] = M::mma(opS(0, m), qf[m >> 1], sc[m & 1]);
+
+  constexpr int NS = C::NS, NV = C::NV, NM = C::NM, NA = C::NA;
+  constexpr int PD = 4;
+  // Slots of the softmax of the current tile (element e = 16 kb + i):
+  // row max over slots [0, NA), the exchange between lane halves at NA, the
+  // exponentials of key block 0 in (NA, NS) and of key block 1 in the first
+  // half of the P~V MFMAs (before its P~ operands are needed).
+  constexpr auto max_slot = [](int e) { return (e * NA) / 32; };
+  constexpr auto exp_slot = [](int kb, int i) {
+    return kb == 0 ? NA + 1 + (i * (NS - NA - 1)) / 16 : NS + (i * (NV / 2)) / 16;
+  };
+  constexpr auto copy_slot = [](int k) { return NS + (k * NV) / C::NLD; };
+
+  int b0 = 0;   // buffer of tile j
+  // One tile: S of tile j + 1 with the softmax of tile j, then P~V of tile j.
+  // MASK: some row of the wave crosses the causal diagonal or N in tile j.
+  auto iteration = [&](int j, auto maskc) {
+    const int key0 = j * C::BC;
+    const int bk = (b0 + 1) & 3, bc = (b0 + 3) & 3;
+    const int kboff = bk * C::BUF, vboff = b0 * C::BUF;
+    frag pf[2][2];
+    f32x16 sn[2];
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+    float mx = -INFINITY, m_new = m_run, nm = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    frag opq[PD];
+    auto operand = [&](int m) -> frag { return m < NS ? opS(kboff, m) : opV(vboff, m - NS); };
+#pragma unroll
+    for (int m = 0; m < PD; ++m) opq[m] = operand(m);
+    // One slot of the tile's stream: MFMA m (S of tile j + 1, or P~V of tile j)
+    // and the softmax / copy work placed on that slot.
+    auto slot = [&](auto mc, auto maskc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr bool MASK = decltype(maskc)::value;
+      const frag x = opq[m % PD];
+      if constexpr (m + PD < NM) opq[m % PD] = operand(m + PD);
+      if constexpr (m < NS) {
+        sn[m & 1] = M::mma(x, qf[m >> 1], sn[m & 1]);
+      } else {
+        constexpr int r = m - NS, kb = r / (2 * (D / 32)), u = (r / (D / 32)) & 1, db = r % (D / 32);
+        acc[db] = M::mma(x, pf[kb][u], acc[db]);
+      }
+#pragma unroll
+      for (int k = 0; k < C::NLD; ++k)
+        if (m == copy_slot(k)) copy_op(bc, j + 3, k);
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        if (m == max_slot(e)) {
+          const int kb = e >> 4, i = e & 15;
+          if constexpr (MASK)
+            if (key0 + kb * 32 + 8 * (i / 4) + 2 * (i % 4) + h > klim) sc[kb][i] = -INFINITY;
+          mx = fmaxf(mx, sc[kb][i]);
+        }
+      if constexpr (m == NA) {
+        mx = half_max(mx);
+        const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+        m_new = fmaxf(m_run, mt);
+        nm = (m_new == -INFINITY) ? 0.f : -m_new;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (m == exp_slot(kb, i)) {
+            const float xs = sc[kb][i];
+            float p = exp2_fast(fmaf(xs, c, nm));
+            if constexpr (MASK) p = (xs == -INFINITY) ? 0.f : p;
+            sc[kb][i] = p;
+            ps[i & 3] += p;
+            if ((i + 1) % 8 == 0) pf[kb][i / 8] = pack_frag<T>(sc[kb], i / 8);
+          }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto rescale = [&]() {
+      // Only when the max of some row of the wave grew; the max is tracked
+      // exactly so that the largest P~ of a row is exactly 1.
+      if (__any(m_new > m_run)) {
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      }
+      m_run = m_new;
+    };
+    static_for<0, NS>([&](auto mc) { slot(mc, maskc); });
+    rescale();
+    static_for<NS, NM>([&](auto mc) { slot(mc, maskc); });
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    sc[0] = sn[0];
+    sc[1] = sn[1];
+    // Tile j + 2 (copied during the previous tile) must have landed; the copies
+    // of tile j + 3 may still be in flight.
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
+    __syncthreads();
+    b0 = (b0 + 1) & 3;
+  };
+  // Tiles [0, jfull) need no mask in any row of the workgroup (they end at or
+  // before its first query and before N); the masked stream, a separate loop
+  // so that each loop body keeps its own register allocation, takes the rest.
+  const int jfull = min(min(ntiles, N / C::BC), CAUSAL ? (q0 + 1) / C::BC : ntiles);
+  int j = 0;
+  for (; j < jfull; ++j) iteration(j, std::false_type{});
+  for (; j < ntiles; ++j) iteration(j, std::true_type{});
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  const float l = half_sum(l_run);
+  if (myq < N) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    T* orow = O + (size_t)myq * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        store4<T>(orow + db * 32 + 8 * r + 4 * h, acc[db][4 * r] * inv, acc[db][4 * r + 1] * inv,
+                  acc[db][4 * r + 2] * inv, acc[db][4 * r + 3] * inv);
+    if (h == 0) L[myq] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-  using C = FwdTile<T, D>;
-  dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), grid, dim3(C::NT), 0, s, a);
+  // d = 64 keeps the register-staged kernel: with two head-dim blocks the
+  // stream of fwd16_kernel has too few independent accumulators to hide the
+  // MFMA latency.
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    dim3 grid((a.N + Fwd16<D>::BR - 1) / Fwd16<D>::BR, a.H, a.B);
+    hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL>), grid, dim3(Fwd16<D>::NT), 0, s, a);
+  } else {
+    using C = FwdTile<T, D>;
+    dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
+    hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), grid, dim3(C::NT), 0, s, a);
+  }
   return hipGetLastError();
 }
 
