@@ -37,7 +37,7 @@ METRIC = "attention fwd/bwd TFLOPS on 1 MI355X and % of bf16 MFMA peak"
 # (2516.6 = 256 CUs x 4096 flop/clk x 2.4 GHz), fp32 157.3.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
-DOMINANT = "bwd_dkdv_kernel"
+DOMINANT = "bwd_dkdv16_kernel"
 KERNEL_SOURCES = ("io_aware_exact_fa_amd/csrc/fa_bwd_kernels.hpp", "io_aware_exact_fa_amd/csrc/fa_common.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
