@@ -2,14 +2,17 @@
 //
 // Three launches on the caller's stream, no atomics and no fp32 accumulator
 // in device memory:
-//   1. bwd_pre_kernel:  D_i = rowsum(dO_i * O_i) in fp32 (HBM-bound).
-//   2. bwd_dkdv_kernel: one workgroup per (batch, head, 128-key tile); each wave
-//      owns 32 keys.  For every query tile, recompute
-//        S = Q K^T, P = 2^(c S - LSE log2 e), dP = dO V^T, dS = P (dP - D)
+//   1. bwd_pre_kernel: D_i = rowsum(dO_i * O_i) and L2_i = LSE_i log2(e) in
+//      fp32, padded per head to whole 64-row tiles (HBM-bound).
+//   2. dK, dV (bwd_dkdv16_kernel for 16-bit types, bwd_dkdv_kernel for fp32):
+//      one workgroup per (batch, head, 128-key tile); each wave owns 32 keys.
+//      For every query tile, recompute
+//        S = Q K^T, P = 2^(c S - L2), dP = dO V^T, dS = P (dP - D)
 //      and accumulate dV += P^T dO, dK += dS^T Q in registers; dk = scale dK.
-//   3. bwd_dq_kernel:   one workgroup per (batch, head, 128-query tile), the
-//      forward's loop order: for every key tile, recompute S^T, P, dP^T, dS and
-//      accumulate dQ^T += K^T dS^T in registers; dq = scale dQ at the end.
+//   3. dQ (bwd_dq16_kernel / bwd_dq_kernel): one workgroup per (batch, head,
+//      query tile), the forward's loop order: for every key tile, recompute
+//      S^T, P, dP^T, dS and accumulate dQ^T += K^T dS^T in registers;
+//      dq = scale dQ at the end.
 // dQ is computed by its own pass instead of being summed across key-tile
 // workgroups: the two GEMMs it recomputes cost less than the fp32 atomic
 // traffic they replace, and every output is written exactly once (bitwise
@@ -27,9 +30,11 @@
 // "forward가 끝난 뒤 backward는 무엇을 저장하고 무엇을 다시 계산하는가").
 //
 // Operands: every MFMA reads one operand from registers (a result tile of an
-// earlier MFMA, or rows held for the whole kernel) and the other with 16-byte
-// LDS reads, from a row-major tile or from a transposed, swizzled tile written
-// at load time (no transposing LDS reads).
+// earlier MFMA, or rows held for the whole kernel) and the other from LDS.
+// The 16-bit kernels keep each tile in LDS once, row-major and swizzled, copied
+// there straight from global memory, and read it two ways (8-byte reads of
+// rows, transposing reads of columns); the fp32 kernels stage tiles through
+// registers into a row-major and a transposed copy read with 16-byte reads.
 #pragma once
 
 #include "fa_common.hpp"

@@ -1,10 +1,14 @@
-// Forward attention kernel for gfx950.
+// Forward attention kernels for gfx950.
 //
-// One workgroup of 4 wavefronts computes a tile of BR = 128 query rows of one
-// (batch, head): each wave owns 32 rows (the queries are split across waves,
-// so the softmax of a row never leaves its wave).  The workgroup loops over
-// key/value tiles of BC = 64 keys, staged global -> registers -> LDS with the
-// next tile's global loads in flight while the current tile is computed.
+// One workgroup computes a tile of query rows of one (batch, head); each wave
+// owns 32 rows (the queries are split across waves, so the softmax of a row
+// never leaves its wave).  The workgroup loops over key/value tiles of 64 keys.
+// Two kernels:
+//   fwd16_kernel (16-bit types, d = 128): 8 waves (256 rows); tiles copied
+//     from global memory straight into LDS, read as 8-byte rows (K) and by
+//     transposing reads (V^T); each tile one fixed MFMA stream.
+//   fwd_kernel (fp32, and 16-bit d = 64): 8 waves for 16-bit, 4 for fp32;
+//     tiles staged global -> registers -> LDS, V stored transposed.
 // Per tile and wave:
 //   S^T = K_j Q^T            MFMA, fp32 accumulation (32 queries x 64 keys);
 //   mask                     only on tiles crossing the causal diagonal or N;
