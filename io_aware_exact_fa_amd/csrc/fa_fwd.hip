@@ -540,7 +540,14 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
             if constexpr (MASK) p = (xs == -INFINITY) ? 0.f : p;
             sc[kb][i] = p;
             ps[i & 3] += p;
-            if ((i + 1) % 8 == 0) pf[kb][i / 8] = pack_frag<T>(sc[kb], i / 8);
+            if ((i + 1) % 8 == 0) {
+              pf[kb][i / 8] = pack_frag<T>(sc[kb], i / 8);
+              // Pin the fragment (and the exponentials behind it) to this slot: the
+              // results are only used after the rescale branch, and the compiler
+              // would otherwise sink the whole computation past it.
+              asm volatile("" : "+v"(pf[kb][i / 8]));
+              asm volatile("" : "+v"(ps[0]), "+v"(ps[1]), "+v"(ps[2]), "+v"(ps[3]));
+            }
           }
       __builtin_amdgcn_sched_barrier(0);
     };
