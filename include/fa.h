@@ -39,7 +39,7 @@
  *    before any HIP call; on an argument error nothing is launched and no
  *    output is touched.  Checks: null pointers, B/H/N <= 0, element counts
  *    that overflow 64 bits, non-finite scale (FA_ERR_INVALID_ARGUMENT);
- *    unknown dtype, d outside {64, 128}, B or H above 65535, N above 2^30 or
+ *    unknown dtype, d outside {64, 128}, B or H above 65535, N above 2^23 or
  *    B*H*N above 2^34 (FA_ERR_UNSUPPORTED); workspace
  *    too small or not 256-byte aligned (FA_ERR_WORKSPACE); the current HIP
  *    device is not gfx950 or cannot be queried (FA_ERR_DEVICE); a launch

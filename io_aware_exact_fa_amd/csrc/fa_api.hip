@@ -15,7 +15,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxGridYZ = 65535;   // grid y (heads) and z (batch) limit
 constexpr int kMaxDevices = 64;
-constexpr int kMaxN = (1 << 30);                 // keeps tile index arithmetic in int
+constexpr int kMaxN = (1 << 23);   // keeps byte offsets inside one head matrix below 2^32
 constexpr uint64_t kMaxRows = (uint64_t)1 << 34;  // keeps 1-D row grids below 2^31 blocks
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

@@ -604,15 +604,15 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
 #pragma unroll
   for (int f = 0; f < 4; ++f) gofs[f] = 8 * ((lane >> 1) ^ f) + 4 * (lane & 1);
   // Copy op j (0..15) of key tile kt into buffer b: waves 0-3 copy K, 4-7 copy
-  // V, rows 4 j + (w & 3).  Rows past N are clamped (masked through klim).
+  // V, rows 4 j + (w & 3).  Rows past N read as zero (and are masked through klim).
+  const int mat = w >> 2;
+  const i32x4 rsrc = buffer_rsrc(mat ? V : K, (uint32_t)N * (2 * D));
   auto copy_op = [&](int b, int kt, int j) {
     const uint32_t base = lds_address(smem) + b * C::BUF;
-    const int mat = w >> 2;
     const int rr = 4 * j + (w & 3);
     const int f = (j >> 1) & 3;                // slot XOR of row rr: (rr >> 3) & 3
-    const int rowg = min(kt * C::BC + rr, N - 1);
-    const char* src = reinterpret_cast<const char*>(mat ? V : K) + (size_t)rowg * (2 * D);
-    copy_to_lds<C::HALF>(src, gofs[f], base + mat * C::TILE + rr * C::PB);
+    copy_to_lds<C::HALF>(rsrc, gofs[f], (uint32_t)(kt * C::BC + rr) * (2 * D),
+                         base + mat * C::TILE + rr * C::PB);
   };
 
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -818,20 +818,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // Copy op j of tile qt into buffer b: j < 32: wave w copies rows 4 jj + w
   // (jj = 0..15) of Q (j < 16) or dO; j = 32, 33: the tile's L2 and D, lane p
   // holding query row_pi(p) of the tile (the order of a lane half's P
-  // elements).  Every wave copies the same L2 and D.  Rows past N are clamped
-  // (their P is 0 through L2 = +inf), tiles past the end copy the last tile.
+  // elements).  Every wave copies the same L2 and D.  Rows past N read as zero
+  // (the padding rows of L2 are +inf, so their P is 0; past Np all of Q, dO,
+  // L2 and D read as zero, and P dO and P (dP - D) vanish with dO).
+  const i32x4 rsq = buffer_rsrc(Q, (uint32_t)N * (2 * D));
+  const i32x4 rsg = buffer_rsrc(dO, (uint32_t)N * (2 * D));
+  const i32x4 rsl = buffer_rsrc(L2, (uint32_t)a.Np * 4);
+  const i32x4 rsd = buffer_rsrc(Dl, (uint32_t)a.Np * 4);
   auto copy_op = [&](int b, int qt, int j) {
     const uint32_t base = lds_address(smem) + b * C::BUF;
     if (j < 32) {
       const int mat = j / 16, jj = j % 16;
       const int rr = 4 * jj + w;
       const int f = (jj >> 1) & 3;             // slot XOR of row rr: (rr >> 3) & 3
-      const int rowg = min(qt * C::BQ + rr, N - 1);
-      const char* src = reinterpret_cast<const char*>(mat ? dO : Q) + (size_t)rowg * (2 * D);
-      copy_to_lds<C::HALF>(src, gofs[f], base + mat * C::TILE + rr * C::PB);
+      copy_to_lds<C::HALF>(mat ? rsg : rsq, gofs[f], (uint32_t)(qt * C::BQ + rr) * (2 * D),
+                           base + mat * C::TILE + rr * C::PB);
     } else {
-      const float* src = (j == 32 ? L2 : Dl) + min(qt, nqt - 1) * C::BQ;
-      copy_to_lds<false>(src, 4 * row_pi(lane), base + 2 * C::TILE + (j - 32) * C::BQ * 4);
+      copy_to_lds<false>(j == 32 ? rsl : rsd, 4 * row_pi(lane), (uint32_t)(qt * C::BQ) * 4,
+                         base + 2 * C::TILE + (j - 32) * C::BQ * 4);
     }
   };
 

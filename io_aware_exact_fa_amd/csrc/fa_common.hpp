@@ -310,27 +310,46 @@ __device__ inline uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Copy 4 bytes per lane from global memory straight into LDS: lane i reads the
-// dword at base + off_i (base wave-uniform, off_i a 32-bit byte offset) and it
-// lands at LDS byte address lds + 4 i (lds wave-uniform); with HALF, only lanes
-// 0..31 copy (128 bytes).  Issued as inline assembly so that the compiler adds
-// no waits of its own for it: the caller waits with s_waitcnt vmcnt before the
-// data is read, and before the barrier that hands it to the other waves.
-// Expects every lane of the wave active.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource of the byte range [base, base + bytes): raw addressing
+// (stride 0), 32-bit elements, every access checked against the range.
+__device__ inline i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Copy 4 bytes per lane from a buffer straight into LDS: lane i reads the dword
+// at byte soff + voff_i of the range of rsrc (soff wave-uniform, voff_i per
+// lane) and it lands at LDS byte address lds + 4 i (lds wave-uniform).  A dword
+// at or past the end of the range is not read and lands as zero, so rows past
+// the end of a matrix need no clamping.  With HALF, only lanes 0..31 copy (128
+// bytes).  Issued as inline assembly so that the compiler adds no waits of its
+// own for it: the caller waits with s_waitcnt vmcnt before the data is read,
+// and before the barrier that hands it to the other waves.  The instruction
+// offset is left at zero: it would move the LDS address as well.  Expects every
+// lane of the wave active.
 template <bool HALF>
-__device__ inline void copy_to_lds(const void* base, uint32_t off, uint32_t lds) {
+__device__ inline void copy_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   if constexpr (HALF) {
     uint64_t saved;
     asm volatile(
         "s_mov_b64 %0, exec\n\t"
         "s_mov_b32 exec_hi, 0\n\t"
-        "global_load_lds_dword %1, %2\n\t"
+        "buffer_load_dword %1, %2, %3 offen lds\n\t"
         "s_mov_b64 exec, %0"
         : "=&s"(saved)
-        : "v"(off), "s"(base), "{m0}"(lds)
+        : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
         : "memory");
   } else {
-    asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+    asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+                 "{m0}"(lds)
+                 : "memory");
   }
 }
 

@@ -421,15 +421,15 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
 #pragma unroll
   for (int f = 0; f < 4; ++f) gofs[f] = 8 * ((lane >> 1) ^ f) + 4 * (lane & 1);
   // Copy op j (0..15) of key tile t into buffer b: waves 0-3 copy K, 4-7 copy V,
-  // rows 4 j + (w & 3); rows past N are clamped (masked through klim).
+  // rows 4 j + (w & 3).  Rows past N read as zero (and are masked through klim).
+  const int mat = w >> 2;
+  const i32x4 rsrc = buffer_rsrc(mat ? V : K, (uint32_t)N * (2 * D));
   auto copy_op = [&](int b, int t, int j) {
     const uint32_t base = lds_address(smem) + b * C::BUF;
-    const int mat = w >> 2;
     const int rr = 4 * j + (w & 3);
     const int f = (j >> 1) & 3;
-    const int rowg = min(t * C::BC + rr, N - 1);
-    const char* src = reinterpret_cast<const char*>(mat ? V : K) + (size_t)rowg * (2 * D);
-    copy_to_lds<C::HALF>(src, gofs[f], base + mat * C::TILE + rr * C::PB);
+    copy_to_lds<C::HALF>(rsrc, gofs[f], (uint32_t)(t * C::BC + rr) * (2 * D),
+                         base + mat * C::TILE + rr * C::PB);
   };
   // S^T MFMA m of a tile (m < NS): key block kb = m & 1, k step ks = m >> 1.
   auto opS = [&](int kboff, int m) -> frag {

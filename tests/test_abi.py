@@ -76,7 +76,7 @@ def test_fwd_null_pointer(name):
     (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=-1), fa.FA_ERR_UNSUPPORTED),
     (dict(H=70000), fa.FA_ERR_UNSUPPORTED),
-    (dict(N=2**30 + 1), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=2**23 + 1), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_fwd_rejects(kw, status):
     assert _fwd(**kw) == status
