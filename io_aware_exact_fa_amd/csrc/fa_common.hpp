@@ -154,6 +154,30 @@ __device__ inline f16x8 pack_frag<_Float16>(const f32x16& c, int u) {
   return r;
 }
 
+// ps[x] += elements 2x and 2x + 1 of a 16-bit fragment, as they stand in the
+// fragment (rounded): one dot-2 instruction against (1, 1) per pair, products
+// exact, accumulated in f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ inline void frag_sum4(const typename Mfma<T>::frag& f, float (&ps)[4]);
+
+template <>
+__device__ inline void frag_sum4<__bf16>(const bf16x8& f, float (&ps)[4]) {
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    ps[x] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[2 * x], f[2 * x + 1]}, one, ps[x], false);
+}
+
+template <>
+__device__ inline void frag_sum4<_Float16>(const f16x8& f, float (&ps)[4]) {
+  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    ps[x] = __builtin_amdgcn_fdot2(f16x2{f[2 * x], f[2 * x + 1]}, one, ps[x], false);
+}
+
 // Negate every element of a fragment (exact).
 template <typename T>
 __device__ inline typename Mfma<T>::frag neg_frag(typename Mfma<T>::frag a) { return -a; }

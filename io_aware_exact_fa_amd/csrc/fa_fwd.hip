@@ -349,6 +349,12 @@ void fwd_kernel(FwdArgs a) {
 // this tile spread between its MFMAs, then P~ V of this tile; the accumulator
 // is rescaled in between, only when the max of some row of the wave grew.
 // 8 waves x 32 query rows per workgroup.
+// Growth of a row max (log2 units) that fwd16_kernel absorbs without
+// rescaling its accumulator: the exponentials are taken against a reference
+// that may lag the true row max by up to this much, so P~ <= 2^8.  Softmax is
+// unchanged by the choice of reference (it cancels between O and l).
+constexpr float kMaxSlack = 8.f;
+
 template <int D>
 struct Fwd16 {
   static constexpr int NW = 8;
@@ -455,7 +461,9 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY;   // running max of c S (log2 units)
-  float l_run = 0.f;         // this lane's share of the running normalizer
+  // This lane's share of the running normalizer: the sum of P~ as rounded to T
+  // for the MFMA, so that the weights of O sum to 1 exactly as used.
+  float l_run = 0.f;
 
   // Prologue: tiles 0, 1, 2 into buffers 0, 1, 2; S of tile 0.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -465,11 +473,13 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
     for (int j = 0; j < C::NLD; ++j) copy_op(t, t, j);
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // tile 2 may still be in flight
   __syncthreads();
-  f32x16 sc[2];
-  sc[0] = f32x16{};
-  sc[1] = f32x16{};
+  // S of the current tile and of the next one; the two trade places every tile
+  // (the loops run two tiles per trip), so no tile copies them.
+  f32x16 sA[2], sB[2];
+  sA[0] = f32x16{};
+  sA[1] = f32x16{};
 #pragma unroll
-  for (int m = 0; m < C::NS; ++m) sc[m & 1] = M::mma(opS(0, m), qf[m >> 1], sc[m & 1]);
+  for (int m = 0; m < C::NS; ++m) sA[m & 1] = M::mma(opS(0, m), qf[m >> 1], sA[m & 1]);
 
   constexpr int NS = C::NS, NV = C::NV, NM = C::NM, NA = C::NA;
   constexpr int PD = 4;
@@ -484,17 +494,18 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
   constexpr auto copy_slot = [](int k) { return NS + (k * NV) / C::NLD; };
 
   int b0 = 0;   // buffer of tile j
-  // One tile: S of tile j + 1 with the softmax of tile j, then P~V of tile j.
-  // MASK: some row of the wave crosses the causal diagonal or N in tile j.
-  auto iteration = [&](int j, auto maskc) {
+  // One tile: S of tile j + 1 (into sn) with the softmax of tile j (S in sc),
+  // then P~V of tile j.  MASK: some row of the wave crosses the causal
+  // diagonal or N in tile j.
+  auto iteration = [&](int j, auto maskc, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     const int key0 = j * C::BC;
     const int bk = (b0 + 1) & 3, bc = (b0 + 3) & 3;
     const int kboff = bk * C::BUF, vboff = b0 * C::BUF;
     frag pf[2][2];
-    f32x16 sn[2];
     sn[0] = f32x16{};
     sn[1] = f32x16{};
     float mx = -INFINITY, m_new = m_run, nm = 0.f;
+    bool grow = false;
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
     frag opq[PD];
     auto operand = [&](int m) -> frag { return m < NS ? opS(kboff, m) : opV(vboff, m - NS); };
@@ -525,10 +536,15 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
           mx = fmaxf(mx, sc[kb][i]);
         }
       if constexpr (m == NA) {
+        // The reference max of the exponentials moves only when the max of
+        // some row of the wave grew by more than kMaxSlack (log2 units), so
+        // P~ <= 2^kMaxSlack and most tiles skip the rescale.
         mx = half_max(mx);
         const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
         m_new = fmaxf(m_run, mt);
-        nm = (m_new == -INFINITY) ? 0.f : -m_new;
+        grow = __any(m_new > m_run + kMaxSlack);
+        const float ref = grow ? m_new : m_run;
+        nm = (ref == -INFINITY) ? 0.f : -ref;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -539,9 +555,9 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
             float p = exp2_fast(fmaf(xs, c, nm));
             if constexpr (MASK) p = (xs == -INFINITY) ? 0.f : p;
             sc[kb][i] = p;
-            ps[i & 3] += p;
             if ((i + 1) % 8 == 0) {
               pf[kb][i / 8] = pack_frag<T>(sc[kb], i / 8);
+              frag_sum4<T>(pf[kb][i / 8], ps);
               // Pin the fragment (and the exponentials behind it) to this slot: the
               // results are only used after the rescale branch, and the compiler
               // would otherwise sink the whole computation past it.
@@ -552,22 +568,18 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
     auto rescale = [&]() {
-      // Only when the max of some row of the wave grew; the max is tracked
-      // exactly so that the largest P~ of a row is exactly 1.
-      if (__any(m_new > m_run)) {
+      if (grow) {
         const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+        m_run = m_new;
       }
-      m_run = m_new;
     };
     static_for<0, NS>([&](auto mc) { slot(mc, maskc); });
     rescale();
     static_for<NS, NM>([&](auto mc) { slot(mc, maskc); });
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    sc[0] = sn[0];
-    sc[1] = sn[1];
     // Tile j + 2 (copied during the previous tile) must have landed; the copies
     // of tile j + 3 may still be in flight.
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
@@ -579,8 +591,20 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
   // so that each loop body keeps its own register allocation, takes the rest.
   const int jfull = min(min(ntiles, N / C::BC), CAUSAL ? (q0 + 1) / C::BC : ntiles);
   int j = 0;
-  for (; j < jfull; ++j) iteration(j, std::false_type{});
-  for (; j < ntiles; ++j) iteration(j, std::true_type{});
+  for (; j + 1 < jfull; j += 2) {
+    iteration(j, std::false_type{}, sA, sB);
+    iteration(j + 1, std::false_type{}, sB, sA);
+  }
+  if (j < jfull) {
+    iteration(j++, std::false_type{}, sA, sB);
+    sA[0] = sB[0];
+    sA[1] = sB[1];
+  }
+  for (; j + 1 < ntiles; j += 2) {
+    iteration(j, std::true_type{}, sA, sB);
+    iteration(j + 1, std::true_type{}, sB, sA);
+  }
+  if (j < ntiles) iteration(j, std::true_type{}, sA, sB);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   const float l = half_sum(l_run);

@@ -18,10 +18,14 @@ from tests import pins
 
 pytestmark = pytest.mark.gpu
 
+# O and gradient bounds for fp16 / bf16 are the plan's.  LSE: the 16-bit
+# forward sums P~ as rounded to the input type (the values the P~V product
+# uses), so ln l carries up to that type's unit roundoff u: 2^-11 (fp16),
+# 2^-8 (bf16).  fp32: MFMA accumulation over a few thousand terms.
 TOL = {
     "f32": dict(o=1e-5, lse=1e-4, grad=1e-4),
     "f16": dict(o=2e-3, lse=1e-3, grad=5e-3),
-    "bf16": dict(o=1e-2, lse=1e-3, grad=2e-2),
+    "bf16": dict(o=1e-2, lse=4e-3, grad=2e-2),
 }
 TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
