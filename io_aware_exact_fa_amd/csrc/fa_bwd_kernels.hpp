@@ -670,14 +670,24 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
       dp[b] = f32x16{};
     }
 #pragma unroll
-    for (int m = 0; m < PD; ++m) opq[m] = operand(m);
+    for (int m = 0; m < PD; m += 2) {
+      opq[m + 1] = operand(m + 1);
+      asm volatile("" ::: "memory");   // keeps the two operands' reads apart
+      opq[m] = operand(m);
+    }
     static_for<0, NM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
 #pragma unroll
       for (int k = 0; k < C::NLD; ++k)
         if (m == copy_slot(k)) copy_op(b2, kt + 2, k);
+      // Operands are read in pairs at odd slots, the odd one first, so that the
+      // wait for the even one covers both.
       const frag x = opq[m % PD];
-      if constexpr (m + PD < NM) opq[m % PD] = operand(m + PD);
+      if constexpr ((m & 1) && m + PD - 1 < NM) {
+        opq[(m + PD) % PD] = operand(m + PD);
+        asm volatile("" ::: "memory");
+        opq[(m + PD - 1) % PD] = operand(m + PD - 1);
+      }
       if constexpr (m < 2 * NS) {
         constexpr int kb = m / NS, ks = (m % NS) / 2;
         if constexpr (m & 1) dp[kb] = M::mma(x, gf[ks], dp[kb]);
@@ -898,7 +908,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
       dp[b] = f32x16{};
     }
 #pragma unroll
-    for (int m = 0; m < PD; ++m) opq[m] = operand(m);
+    for (int m = 0; m < PD; m += 2) {
+      opq[m + 1] = operand(m + 1);
+      asm volatile("" ::: "memory");   // keeps the two operands' reads apart
+      opq[m] = operand(m);
+    }
     static_for<0, NM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
 #pragma unroll
@@ -914,8 +928,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
             l4[b][g] = *reinterpret_cast<const f32x4*>(&l2[b * 32 + 8 * g + 4 * h]);
             d4[b][g] = *reinterpret_cast<const f32x4*>(&l2[C::BQ + b * 32 + 8 * g + 4 * h]);
           }
+      // Operands are read in pairs at odd slots, the odd one first, so that the
+      // wait for the even one covers both.
       const frag x = opq[m % PD];
-      if constexpr (m + PD < NM) opq[m % PD] = operand(m + PD);
+      if constexpr ((m & 1) && m + PD - 1 < NM) {
+        opq[(m + PD) % PD] = operand(m + PD);
+        asm volatile("" ::: "memory");
+        opq[(m + PD - 1) % PD] = operand(m + PD - 1);
+      }
       if constexpr (m < 2 * NS) {
         constexpr int qb = m / NS, ks = (m % NS) / 2;
         if constexpr (m & 1) dp[qb] = M::mma(x, vf[ks], dp[qb]);

@@ -510,14 +510,24 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
     frag opq[PD];
     auto operand = [&](int m) -> frag { return m < NS ? opS(kboff, m) : opV(vboff, m - NS); };
 #pragma unroll
-    for (int m = 0; m < PD; ++m) opq[m] = operand(m);
+    for (int m = 0; m < PD; m += 2) {
+      opq[m + 1] = operand(m + 1);
+      asm volatile("" ::: "memory");
+      opq[m] = operand(m);
+    }
     // One slot of the tile's stream: MFMA m (S of tile j + 1, or P~V of tile j)
     // and the softmax / copy work placed on that slot.
     auto slot = [&](auto mc, auto maskc) {
       constexpr int m = decltype(mc)::value;
       constexpr bool MASK = decltype(maskc)::value;
+      // Operands are read in pairs at odd slots, the odd one first, so that the
+      // wait for the even one covers both.
       const frag x = opq[m % PD];
-      if constexpr (m + PD < NM) opq[m % PD] = operand(m + PD);
+      if constexpr ((m & 1) && m + PD - 1 < NM) {
+        opq[(m + PD) % PD] = operand(m + PD);
+        asm volatile("" ::: "memory");   // keeps the two operands' reads apart
+        opq[(m + PD - 1) % PD] = operand(m + PD - 1);
+      }
       if constexpr (m < NS) {
         sn[m & 1] = M::mma(x, qf[m >> 1], sn[m & 1]);
       } else {
