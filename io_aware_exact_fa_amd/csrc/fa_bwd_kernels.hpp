@@ -633,7 +633,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
   };
   constexpr auto copy_slot = [](int k) { return 1 + (k * (NM - 6)) / C::NLD; };
   int bcur = 0;
-  for (int kt = 0; kt < nkt; ++kt) {
+  // One key tile.  MASK: some key of the tile is past N or, under the causal
+  // mask, after some query of the workgroup.
+  auto tile = [&](int kt, auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value;
     const int key0 = kt * C::BC;
     const int b1 = bcur == 2 ? 0 : bcur + 1;
     const int b2 = b1 == 2 ? 0 : b1 + 1;
@@ -704,7 +707,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i)
           if (m == elem_slot(b, i)) {
             float e = exp2_fast(fmaf(s[b][i], c, -l2));
-            if (key0 + b * 32 + 8 * (i / 4) + 2 * (i % 4) + h > klim) e = 0.f;
+            if (MASK && key0 + b * 32 + 8 * (i / 4) + 2 * (i % 4) + h > klim) e = 0.f;
             ds[b][i] = e * (dp[b][i] - dl);
             if ((i + 1) % 8 == 0) sa[b][i / 8] = pack_frag<T>(ds[b], i / 8);
           }
@@ -713,7 +716,14 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
     __syncthreads();
     bcur = b1;
-  }
+  };
+  // Tiles [0, kfull) need no mask in any row (they end before N and at or
+  // before the first query of the workgroup); a separate loop, with its own
+  // register allocation, takes the rest.
+  const int kfull = min(min(nkt, N / C::BC), CAUSAL ? (q0 + 1) / C::BC : nkt);
+  int kt = 0;
+  for (; kt < kfull; ++kt) tile(kt, std::false_type{});
+  for (; kt < nkt; ++kt) tile(kt, std::true_type{});
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   if (myq < N) {
@@ -788,11 +798,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   const int myk = kw + col;      // this lane's key (column of S)
   const int kg = min(myk, N - 1);
   // K and V operands (B of S = Q K^T and of dP = dO V^T) of this lane's key.
+  // V is negated (exact): the dP accumulators start at D and end at D - dP,
+  // so dS = -P (D - dP) needs one multiply, and the sign goes into dK's scale.
   frag kf[C::NKS], vf[C::NKS];
 #pragma unroll
   for (int ks = 0; ks < C::NKS; ++ks) {
     kf[ks] = load_frag<T>(K + (size_t)kg * D + ks * 16 + 8 * h);
-    vf[ks] = load_frag<T>(V + (size_t)kg * D + ks * 16 + 8 * h);
+    vf[ks] = neg_frag<T>(load_frag<T>(V + (size_t)kg * D + ks * 16 + 8 * h));
   }
   // K and V stay in AGPRs (MFMA reads its B operand from there); the VGPRs
   // hold the accumulators, which the VALU reads directly.
@@ -869,7 +881,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // Slot of copy k of the next-but-one tile.
   constexpr auto copy_slot = [](int k) { return 1 + (k * (NM - 6)) / C::NLD; };
   int bcur = 0;
-  for (int qt = qt0; qt < nqt; ++qt) {
+  // One query tile.  MASK: under the causal mask, some query of the tile comes
+  // before some key of the workgroup.
+  auto tile = [&](int qt, auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value;
     const int qi0 = qt * C::BQ;
     const int b1 = bcur == 2 ? 0 : bcur + 1;
     const int b2 = b1 == 2 ? 0 : b1 + 1;
@@ -900,13 +915,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     };
     f32x16 s[2], dp[2], p[2], ds[2];
     frag pa[2][2], sa[2][2];
-    f32x4 l4[2][4], d4[2][4];
+    f32x4 l4[2][4];
     frag opq[PD];
+    // D of the 16 queries of this lane's elements of block b, in element order.
+    auto load_d = [&](int b) -> f32x16 {
+      const float* dl = reinterpret_cast<const float*>(smem + boff + 2 * C::TILE) + C::BQ + b * 32 + 4 * h;
+      f32x16 r;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = f32x16{};
-      dp[b] = f32x16{};
-    }
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 q = *reinterpret_cast<const f32x4*>(dl + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[4 * g + e] = q[e];
+      }
+      return r;
+    };
+    dp[0] = load_d(0);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) s[b] = f32x16{};
 #pragma unroll
     for (int m = 0; m < PD; m += 2) {
       opq[m + 1] = operand(m + 1);
@@ -918,7 +943,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
 #pragma unroll
       for (int k = 0; k < C::NLD; ++k)
         if (m == copy_slot(k)) copy_op(b2, qt + 2, k);
-      // L2 and D of 4 queries (one element group), PD slots before first use.
+      // L2 of 4 queries (one element group), PD slots before first use; D of
+      // block 1 well before its first dP MFMA.
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -926,8 +952,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
           if (m == elem_slot(b, 4 * g) - PD) {
             const float* l2 = reinterpret_cast<const float*>(smem + boff + 2 * C::TILE);
             l4[b][g] = *reinterpret_cast<const f32x4*>(&l2[b * 32 + 8 * g + 4 * h]);
-            d4[b][g] = *reinterpret_cast<const f32x4*>(&l2[C::BQ + b * 32 + 8 * g + 4 * h]);
           }
+      if constexpr (m == NS / 2) dp[1] = load_d(1);
       // Operands are read in pairs at odd slots, the odd one first, so that the
       // wait for the even one covers both.
       const frag x = opq[m % PD];
@@ -945,7 +971,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
         if constexpr (r & 1) dk[db] = M::mma(sa[qb][u], x, dk[db]);
         else dv[db] = M::mma(pa[qb][u], x, dv[db]);
       }
-      // P = exp2(S c - L2), dS = P (dP - D).  Element i of lane half h is
+      // P = exp2(S c - L2), -dS = P (D - dP).  Element i of lane half h is
       // query 8 (i / 4) + 2 (i % 4) + h of its block; keys past N need no mask
       // (their results are never stored).
 #pragma unroll
@@ -954,9 +980,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i)
           if (m == elem_slot(b, i)) {
             float e = exp2_fast(fmaf(s[b][i], c, -l4[b][i / 4][i % 4]));
-            if (CAUSAL && qi0 + b * 32 + 8 * (i / 4) + 2 * (i % 4) + h < myk) e = 0.f;
+            if (MASK && qi0 + b * 32 + 8 * (i / 4) + 2 * (i % 4) + h < myk) e = 0.f;
             p[b][i] = e;
-            ds[b][i] = e * (dp[b][i] - d4[b][i / 4][i % 4]);
+            ds[b][i] = e * dp[b][i];
             if ((i + 1) % 8 == 0) {
               pa[b][i / 8] = pack_frag<T>(p[b], i / 8);
               sa[b][i / 8] = pack_frag<T>(ds[b], i / 8);
@@ -969,7 +995,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
     __syncthreads();
     bcur = b1;
-  }
+  };
+  // Under the causal mask, tiles from qmask on start after the last key of the
+  // workgroup and need no mask; a separate loop, with its own register
+  // allocation, takes the diagonal tiles before them.
+  const int qmask = CAUSAL ? min(nqt, (k0 + C::BKC - 1) / C::BQ + 1) : qt0;
+  int qt = qt0;
+  for (; qt < qmask; ++qt) tile(qt, std::true_type{});
+  for (; qt < nqt; ++qt) tile(qt, std::false_type{});
   // No copy may still be writing LDS when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
@@ -983,7 +1016,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
       const int key = kw + 8 * (i >> 2) + 4 * h + (i & 3);
       if (key < N) {
         const size_t off = (size_t)key * D + db * 32 + col;
-        dK[off] = (T)(dk[db][i] * a.scale);
+        dK[off] = (T)(dk[db][i] * -a.scale);   // dk holds -dS^T Q
         dV[off] = (T)dv[db][i];
       }
     }
