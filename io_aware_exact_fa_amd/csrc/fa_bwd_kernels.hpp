@@ -594,15 +594,14 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const int arow = row_pi(col);
-  const int aA0 = arow * C::PB + 8 * ((2 * h) ^ (col >> 3));
-  const int aA1 = arow * C::PB + 8 * ((2 * h + 1) ^ (col >> 3));
+  const int aA = arow * C::PB + 16 * (h ^ ((col >> 3) & 1));
   const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
-  int aT[4];
+  int aT[2];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) aT[x] = (2 * ts + h) * C::PB + 32 * tg + 8 * (ta ^ x);
-  int gofs[4];
+  for (int x = 0; x < 2; ++x) aT[x] = (2 * ts + h) * C::PB + 16 * ((2 * tg + (ta >> 1)) ^ x) + 8 * (ta & 1);
+  int gofs[2];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) gofs[f] = 8 * ((lane >> 1) ^ f) + 4 * (lane & 1);
+  for (int f = 0; f < 2; ++f) gofs[f] = 16 * ((lane >> 2) ^ f) + 4 * (lane & 3);
   // Copy op j (0..15) of key tile kt into buffer b: waves 0-3 copy K, 4-7 copy
   // V, rows 4 j + (w & 3).  Rows past N read as zero (and are masked through klim).
   const int mat = w >> 2;
@@ -610,7 +609,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
   auto copy_op = [&](int b, int kt, int j) {
     const uint32_t base = lds_address(smem) + b * C::BUF;
     const int rr = 4 * j + (w & 3);
-    const int f = (j >> 1) & 3;                // slot XOR of row rr: (rr >> 3) & 3
+    const int f = (j >> 1) & 1;                // chunk XOR of row rr: (rr >> 3) & 1
     copy_to_lds<C::HALF>(rsrc, gofs[f], (uint32_t)(kt * C::BC + rr) * (2 * D),
                          base + mat * C::TILE + rr * C::PB);
   };
@@ -641,17 +640,15 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
     const int b1 = bcur == 2 ? 0 : bcur + 1;
     const int b2 = b1 == 2 ? 0 : b1 + 1;
     const int boff = bcur * C::BUF;
-    const int pA0 = aA0 + boff, pA1 = aA1 + boff;
-    int pT[4];
+    const int pA = aA + boff;
+    int pT[2];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) pT[x] = aT[x] + boff;
+    for (int x = 0; x < 2; ++x) pT[x] = aT[x] + boff;
     auto operand = [&](int m) -> frag {
       if (m < 2 * NS) {
         const int kb = m / NS, ks = (m % NS) / 2, mat = m & 1;   // K for S, V for dP
         const int off = mat * C::TILE + kb * 32 * C::PB + 32 * ks;
-        const uint2 lo = *reinterpret_cast<const uint2*>(smem + pA0 + off);
-        const uint2 hi = *reinterpret_cast<const uint2*>(smem + pA1 + off);
-        return __builtin_bit_cast(frag, uint4{lo.x, lo.y, hi.x, hi.y});
+        return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + pA + off));
       }
       const int r = m - 2 * NS, kb = r / NQ, u = (r % NQ) / (D / 32), db = r % (D / 32);
       s16x4 v[2];
@@ -659,7 +656,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
       for (int rp = 0; rp < 2; ++rp) {
         const int off = (kb * 32 + 16 * u + 8 * rp) * C::PB + 64 * db;
         v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(smem + pT[(2 * u + rp) & 3] + off));
+            (lds_s16x4*)(smem + pT[rp] + off));
       }
       return __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
                                             v[1][0], v[1][1], v[1][2], v[1][3]});
@@ -824,19 +821,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const int arow = row_pi(col);
-  const int aA0 = arow * C::PB + 8 * ((2 * h) ^ (col >> 3));
-  const int aA1 = arow * C::PB + 8 * ((2 * h + 1) ^ (col >> 3));
+  const int aA = arow * C::PB + 16 * (h ^ ((col >> 3) & 1));
   // Transposing reads: source lane (group g, a4, s) points at row 2s + h, columns
   // 16 g + 4 a4 .. + 3 of its 32-column block; x is the slot XOR of the row.
   const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
-  int aT[4];
+  int aT[2];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) aT[x] = (2 * ts + h) * C::PB + 32 * tg + 8 * (ta ^ x);
+  for (int x = 0; x < 2; ++x) aT[x] = (2 * ts + h) * C::PB + 16 * ((2 * tg + (ta >> 1)) ^ x) + 8 * (ta & 1);
   // Row copies (one dword per lane): byte offset inside a global row of the
   // data that lands on this lane's LDS dword, for slot XOR f.
-  int gofs[4];
+  int gofs[2];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) gofs[f] = 8 * ((lane >> 1) ^ f) + 4 * (lane & 1);
+  for (int f = 0; f < 2; ++f) gofs[f] = 16 * ((lane >> 2) ^ f) + 4 * (lane & 3);
   // Copy op j of tile qt into buffer b: j < 32: wave w copies rows 4 jj + w
   // (jj = 0..15) of Q (j < 16) or dO; j = 32, 33: the tile's L2 and D, lane p
   // holding query row_pi(p) of the tile (the order of a lane half's P
@@ -852,7 +848,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     if (j < 32) {
       const int mat = j / 16, jj = j % 16;
       const int rr = 4 * jj + w;
-      const int f = (jj >> 1) & 3;             // slot XOR of row rr: (rr >> 3) & 3
+      const int f = (jj >> 1) & 1;             // chunk XOR of row rr: (rr >> 3) & 1
       copy_to_lds<C::HALF>(mat ? rsg : rsq, gofs[f], (uint32_t)(qt * C::BQ + rr) * (2 * D),
                            base + mat * C::TILE + rr * C::PB);
     } else {
@@ -889,17 +885,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     const int b1 = bcur == 2 ? 0 : bcur + 1;
     const int b2 = b1 == 2 ? 0 : b1 + 1;
     const int boff = bcur * C::BUF;
-    const int pA0 = aA0 + boff, pA1 = aA1 + boff;
-    int pT[4];
+    const int pA = aA + boff;
+    int pT[2];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) pT[x] = aT[x] + boff;
+    for (int x = 0; x < 2; ++x) pT[x] = aT[x] + boff;
     auto operand = [&](int m) -> frag {
       if (m < 2 * NS) {
         const int qb = m / NS, ks = (m % NS) / 2, mat = m & 1;
         const int off = mat * C::TILE + qb * 32 * C::PB + 32 * ks;
-        const uint2 lo = *reinterpret_cast<const uint2*>(smem + pA0 + off);
-        const uint2 hi = *reinterpret_cast<const uint2*>(smem + pA1 + off);
-        return __builtin_bit_cast(frag, uint4{lo.x, lo.y, hi.x, hi.y});
+        return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + pA + off));
       }
       const int r = m - 2 * NS, qb = r / NV, u = (r % NV) / NVB, db = (r % NVB) / 2;
       const int mat = (r & 1) ? 0 : 1;         // dK reads Q, dV reads dO
@@ -908,7 +902,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
       for (int rp = 0; rp < 2; ++rp) {
         const int off = mat * C::TILE + (qb * 32 + 16 * u + 8 * rp) * C::PB + 64 * db;
         v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(smem + pT[(2 * u + rp) & 3] + off));
+            (lds_s16x4*)(smem + pT[rp] + off));
       }
       return __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
                                             v[1][0], v[1][1], v[1][2], v[1][3]});

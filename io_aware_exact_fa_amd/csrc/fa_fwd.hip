@@ -417,15 +417,15 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const int arow = row_pi(col);
-  const int aA0 = arow * C::PB + 8 * ((2 * h) ^ (col >> 3));
-  const int aA1 = arow * C::PB + 8 * ((2 * h + 1) ^ (col >> 3));
+  const int aA = arow * C::PB + 16 * (h ^ ((col >> 3) & 1));
   const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
-  int aT[4];
+  int aT[2];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) aT[x] = C::TILE + (2 * ts + h) * C::PB + 32 * tg + 8 * (ta ^ x);
-  int gofs[4];
+  for (int x = 0; x < 2; ++x)
+    aT[x] = C::TILE + (2 * ts + h) * C::PB + 16 * ((2 * tg + (ta >> 1)) ^ x) + 8 * (ta & 1);
+  int gofs[2];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) gofs[f] = 8 * ((lane >> 1) ^ f) + 4 * (lane & 1);
+  for (int f = 0; f < 2; ++f) gofs[f] = 16 * ((lane >> 2) ^ f) + 4 * (lane & 3);
   // Copy op j (0..15) of key tile t into buffer b: waves 0-3 copy K, 4-7 copy V,
   // rows 4 j + (w & 3).  Rows past N read as zero (and are masked through klim).
   const int mat = w >> 2;
@@ -433,16 +433,14 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
   auto copy_op = [&](int b, int t, int j) {
     const uint32_t base = lds_address(smem) + b * C::BUF;
     const int rr = 4 * j + (w & 3);
-    const int f = (j >> 1) & 3;
+    const int f = (j >> 1) & 1;                // chunk XOR of row rr: (rr >> 3) & 1
     copy_to_lds<C::HALF>(rsrc, gofs[f], (uint32_t)(t * C::BC + rr) * (2 * D),
                          base + mat * C::TILE + rr * C::PB);
   };
   // S^T MFMA m of a tile (m < NS): key block kb = m & 1, k step ks = m >> 1.
   auto opS = [&](int kboff, int m) -> frag {
     const int off = kboff + (m & 1) * 32 * C::PB + 32 * (m >> 1);
-    const uint2 lo = *reinterpret_cast<const uint2*>(smem + aA0 + off);
-    const uint2 hi = *reinterpret_cast<const uint2*>(smem + aA1 + off);
-    return __builtin_bit_cast(frag, uint4{lo.x, lo.y, hi.x, hi.y});
+    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + aA + off));
   };
   // P~V MFMA r of a tile (r < NV): key block kb, 16-key step u, head-dim block db.
   auto opV = [&](int vboff, int r) -> frag {
@@ -451,7 +449,7 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
 #pragma unroll
     for (int rp = 0; rp < 2; ++rp) {
       const int off = vboff + (kb * 32 + 16 * u + 8 * rp) * C::PB + 64 * db;
-      v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + aT[(2 * u + rp) & 3] + off));
+      v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + aT[rp] + off));
     }
     return __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
                                           v[1][0], v[1][1], v[1][2], v[1][3]});
