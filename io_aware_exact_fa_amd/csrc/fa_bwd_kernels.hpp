@@ -532,7 +532,7 @@ struct Dq16 {
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;             // queries per workgroup
   static constexpr int BC = 64;                  // keys per tile
-  static constexpr int PB = 2 * (D + 16);        // row pitch in bytes
+  static constexpr int PB = TileLds<D>::PB;      // bytes per row (4-row multiples)
   static constexpr int TILE = BC * PB;
   static constexpr int BUF = 2 * TILE;           // K, V
   static constexpr int NB = 3;
@@ -541,7 +541,7 @@ struct Dq16 {
   static constexpr int NS = 2 * NKS;             // S/dP MFMAs per 32-key block
   static constexpr int NQ = 2 * (D / 32);        // dQ MFMAs per 32-key block
   static constexpr int NM = 2 * NS + 2 * NQ;     // MFMAs per tile
-  static constexpr int NLD = 2 * BC / NW;        // row copies per wave per tile
+  static constexpr int NLD = 2 * BC / NW / TileLds<D>::ROWS_PER_COPY;   // copies per wave per tile
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -593,25 +593,24 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
-  const int arow = row_pi(col);
-  const int aA = arow * C::PB + 16 * (h ^ ((col >> 3) & 1));
-  const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
-  int aT[2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x) aT[x] = (2 * ts + h) * C::PB + 16 * ((2 * tg + (ta >> 1)) ^ x) + 8 * (ta & 1);
-  int gofs[2];
-#pragma unroll
-  for (int f = 0; f < 2; ++f) gofs[f] = 16 * ((lane >> 2) ^ f) + 4 * (lane & 3);
-  // Copy op j (0..15) of key tile kt into buffer b: waves 0-3 copy K, 4-7 copy
-  // V, rows 4 j + (w & 3).  Rows past N read as zero (and are masked through klim).
+  const TileLds<D> lay(lane);
+  // Copy op j of key tile kt into buffer b: waves 0-3 copy K, 4-7 copy V, wave
+  // w rows 16 (w & 3) + 4 j .. + 3 (d = 128: one 4-row group per copy) or row
+  // 4 j + (w & 3) (d = 64).  Rows past N read as zero (and are masked through
+  // klim).
   const int mat = w >> 2;
   const i32x4 rsrc = buffer_rsrc(mat ? V : K, (uint32_t)N * (2 * D));
   auto copy_op = [&](int b, int kt, int j) {
-    const uint32_t base = lds_address(smem) + b * C::BUF;
-    const int rr = 4 * j + (w & 3);
-    const int f = (j >> 1) & 1;                // chunk XOR of row rr: (rr >> 3) & 1
-    copy_to_lds<C::HALF>(rsrc, gofs[f], (uint32_t)(kt * C::BC + rr) * (2 * D),
-                         base + mat * C::TILE + rr * C::PB);
+    const uint32_t base = lds_address(smem) + b * C::BUF + mat * C::TILE;
+    if constexpr (D == 128) {
+      const int q = 4 * (w & 3) + j;
+      copy16_to_lds(rsrc, lay.c[(j >> 1) & 1], (uint32_t)(kt * C::BC + 4 * q) * (2 * D),
+                    base + q * 4 * C::PB);
+    } else {
+      const int rr = 4 * j + (w & 3);
+      copy_to_lds<C::HALF>(rsrc, lay.c[(j >> 1) & 1], (uint32_t)(kt * C::BC + rr) * (2 * D),
+                           base + rr * C::PB);
+    }
   };
 
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -640,23 +639,19 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
     const int b1 = bcur == 2 ? 0 : bcur + 1;
     const int b2 = b1 == 2 ? 0 : b1 + 1;
     const int boff = bcur * C::BUF;
-    const int pA = aA + boff;
-    int pT[2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) pT[x] = aT[x] + boff;
     auto operand = [&](int m) -> frag {
       if (m < 2 * NS) {
         const int kb = m / NS, ks = (m % NS) / 2, mat = m & 1;   // K for S, V for dP
-        const int off = mat * C::TILE + kb * 32 * C::PB + 32 * ks;
-        return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + pA + off));
+        const int off = boff + mat * C::TILE + kb * 32 * C::PB;
+        return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + lay.A(ks) + off));
       }
       const int r = m - 2 * NS, kb = r / NQ, u = (r % NQ) / (D / 32), db = r % (D / 32);
       s16x4 v[2];
 #pragma unroll
       for (int rp = 0; rp < 2; ++rp) {
-        const int off = (kb * 32 + 16 * u + 8 * rp) * C::PB + 64 * db;
+        const int off = boff + (kb * 32 + 16 * u + 8 * rp) * C::PB;
         v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(smem + pT[rp] + off));
+            (lds_s16x4*)(smem + lay.T(rp, db) + off));
       }
       return __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
                                             v[1][0], v[1][1], v[1][2], v[1][3]});
@@ -752,7 +747,7 @@ template <int D>
 struct Dkv16 {
   static constexpr int BKC = 128;                // keys per workgroup (32 per wave)
   static constexpr int BQ = 64;                  // queries per tile
-  static constexpr int PB = 2 * (D + 16);        // row pitch in bytes
+  static constexpr int PB = TileLds<D>::PB;      // bytes per row (4-row multiples)
   static constexpr int TILE = BQ * PB;           // bytes of one Q or dO tile
   static constexpr int BUF = 2 * TILE + 2 * BQ * 4;   // Q, dO, L2, D
   static constexpr int NB = 3;
@@ -762,7 +757,7 @@ struct Dkv16 {
   static constexpr int NVB = 2 * (D / 32);       // dV/dK MFMAs per 16 queries
   static constexpr int NV = 2 * NVB;             // dV/dK MFMAs per block
   static constexpr int NM = 2 * NS + 2 * NV;     // MFMAs per tile
-  static constexpr int NLD = 2 * BQ / 4 + 2;     // copies per wave per tile: Q, dO rows; L2, D
+  static constexpr int NLD = 2 * BQ / 4 / TileLds<D>::ROWS_PER_COPY + 2;   // copies per wave per tile: Q, dO; L2, D
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -820,40 +815,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   const int qt0 = CAUSAL ? k0 / C::BQ : 0;   // earlier tiles see none of these keys
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
-  const int arow = row_pi(col);
-  const int aA = arow * C::PB + 16 * (h ^ ((col >> 3) & 1));
-  // Transposing reads: source lane (group g, a4, s) points at row 2s + h, columns
-  // 16 g + 4 a4 .. + 3 of its 32-column block; x is the slot XOR of the row.
-  const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
-  int aT[2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x) aT[x] = (2 * ts + h) * C::PB + 16 * ((2 * tg + (ta >> 1)) ^ x) + 8 * (ta & 1);
-  // Row copies (one dword per lane): byte offset inside a global row of the
-  // data that lands on this lane's LDS dword, for slot XOR f.
-  int gofs[2];
-#pragma unroll
-  for (int f = 0; f < 2; ++f) gofs[f] = 16 * ((lane >> 2) ^ f) + 4 * (lane & 3);
-  // Copy op j of tile qt into buffer b: j < 32: wave w copies rows 4 jj + w
-  // (jj = 0..15) of Q (j < 16) or dO; j = 32, 33: the tile's L2 and D, lane p
-  // holding query row_pi(p) of the tile (the order of a lane half's P
-  // elements).  Every wave copies the same L2 and D.  Rows past N read as zero
-  // (the padding rows of L2 are +inf, so their P is 0; past Np all of Q, dO,
-  // L2 and D read as zero, and P dO and P (dP - D) vanish with dO).
+  const TileLds<D> lay(lane);
+  // Copy op j of tile qt into buffer b: j < NROW: rows of Q (first half of
+  // the ops) or dO, wave w taking rows 16 w .. 16 w + 15 (d = 128: 4-row groups
+  // 4 w + jj) or rows 4 jj + w (d = 64); j = NROW, NROW + 1: the tile's L2 and
+  // D, lane p holding query row_pi(p) of the tile (the order of a lane half's
+  // P elements).  Every wave copies the same L2 and D.  Rows past N read as
+  // zero (the padding rows of L2 are +inf, so their P is 0; past Np all of Q,
+  // dO, L2 and D read as zero, and P dO and P (dP - D) vanish with dO).
   const i32x4 rsq = buffer_rsrc(Q, (uint32_t)N * (2 * D));
   const i32x4 rsg = buffer_rsrc(dO, (uint32_t)N * (2 * D));
   const i32x4 rsl = buffer_rsrc(L2, (uint32_t)a.Np * 4);
   const i32x4 rsd = buffer_rsrc(Dl, (uint32_t)a.Np * 4);
+  constexpr int NROW = C::NLD - 2;
   auto copy_op = [&](int b, int qt, int j) {
     const uint32_t base = lds_address(smem) + b * C::BUF;
-    if (j < 32) {
-      const int mat = j / 16, jj = j % 16;
-      const int rr = 4 * jj + w;
-      const int f = (jj >> 1) & 1;             // chunk XOR of row rr: (rr >> 3) & 1
-      copy_to_lds<C::HALF>(mat ? rsg : rsq, gofs[f], (uint32_t)(qt * C::BQ + rr) * (2 * D),
-                           base + mat * C::TILE + rr * C::PB);
+    if (j < NROW) {
+      const int mat = j / (NROW / 2), jj = j % (NROW / 2);
+      if constexpr (D == 128) {
+        const int q = 4 * w + jj;
+        copy16_to_lds(mat ? rsg : rsq, lay.c[(jj >> 1) & 1], (uint32_t)(qt * C::BQ + 4 * q) * (2 * D),
+                      base + mat * C::TILE + q * 4 * C::PB);
+      } else {
+        const int rr = 4 * jj + w;
+        copy_to_lds<C::HALF>(mat ? rsg : rsq, lay.c[(jj >> 1) & 1], (uint32_t)(qt * C::BQ + rr) * (2 * D),
+                             base + mat * C::TILE + rr * C::PB);
+      }
     } else {
-      copy_to_lds<false>(j == 32 ? rsl : rsd, 4 * row_pi(lane), (uint32_t)(qt * C::BQ) * 4,
-                         base + 2 * C::TILE + (j - 32) * C::BQ * 4);
+      copy_to_lds<false>(j == NROW ? rsl : rsd, 4 * row_pi(lane), (uint32_t)(qt * C::BQ) * 4,
+                         base + 2 * C::TILE + (j - NROW) * C::BQ * 4);
     }
   };
 
@@ -885,24 +875,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     const int b1 = bcur == 2 ? 0 : bcur + 1;
     const int b2 = b1 == 2 ? 0 : b1 + 1;
     const int boff = bcur * C::BUF;
-    const int pA = aA + boff;
-    int pT[2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) pT[x] = aT[x] + boff;
     auto operand = [&](int m) -> frag {
       if (m < 2 * NS) {
         const int qb = m / NS, ks = (m % NS) / 2, mat = m & 1;
-        const int off = mat * C::TILE + qb * 32 * C::PB + 32 * ks;
-        return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + pA + off));
+        const int off = boff + mat * C::TILE + qb * 32 * C::PB;
+        return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + lay.A(ks) + off));
       }
       const int r = m - 2 * NS, qb = r / NV, u = (r % NV) / NVB, db = (r % NVB) / 2;
       const int mat = (r & 1) ? 0 : 1;         // dK reads Q, dV reads dO
       s16x4 v[2];
 #pragma unroll
       for (int rp = 0; rp < 2; ++rp) {
-        const int off = mat * C::TILE + (qb * 32 + 16 * u + 8 * rp) * C::PB + 64 * db;
+        const int off = boff + mat * C::TILE + (qb * 32 + 16 * u + 8 * rp) * C::PB;
         v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(smem + pT[rp] + off));
+            (lds_s16x4*)(smem + lay.T(rp, db) + off));
       }
       return __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
                                             v[1][0], v[1][1], v[1][2], v[1][3]});

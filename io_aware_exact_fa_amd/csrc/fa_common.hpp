@@ -377,6 +377,90 @@ __device__ inline void copy_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t so
   }
 }
 
+// Copy 16 bytes per lane from a buffer straight into LDS: lane i reads bytes
+// soff + voff_i .. + 15 of the range of rsrc and they land at LDS byte address
+// lds + 16 i, so one copy fills 1 KB of LDS.  Range checking, waits and the
+// instruction offset as for copy_to_lds.  Expects every lane active.
+__device__ inline void copy16_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+               "{m0}"(lds)
+               : "memory");
+}
+
+// ------------------------------------------------- tile layouts of the 16-bit kernels
+//
+// A tile holds rows of 2D bytes (D 16-bit elements) in LDS.  Two reads use it:
+// A-operand reads (16 bytes: 8 consecutive elements of one row; the 32 lanes of
+// a lane half read rows row_pi(0..31) of a 32-row block, all at the same
+// 16-byte chunk) and transposing reads (8 bytes per lane; a lane half reads
+// rows 2s + h, s = 0..3, of an 8-row step, 64 bytes each).  Both layouts below
+// keep every 16-lane quarter of an A read and every lane half of a
+// transposing read on distinct banks.  Offsets between rows that are a
+// multiple of 4 apart are (rows) * PB in both.
+//
+// d = 64: rows 160 bytes apart (128 + 32 of padding); 16-byte chunk c of row r
+// at chunk c ^ ((r >> 3) & 1).  Copied one row (32 lanes x 4 bytes) per copy.
+// d = 128: 4-row groups of 1 KB (rows 256 bytes apart), groups 1152 bytes
+// apart; chunk c of row r at chunk c ^ swz(r), swz(r) = r0 | r3 << 1 | r1 << 2
+// (bits of r).  Copied one group (64 lanes x 16 bytes) per copy.
+template <int D> struct TileLds;
+
+template <> struct TileLds<64> {
+  static constexpr int PB = 160;
+  static constexpr int ROWS_PER_COPY = 1;
+  // Lane offsets: A reads of k step ks at a + 32 ks; transposing reads of the
+  // 8-row step with bit 3 of its rows = rp, head-dim block db, at t[rp] + 64 db;
+  // row copies of rows with (r >> 3) & 1 = x from global byte offset c[x].
+  int a, t[2], c[2];
+  __device__ TileLds(int lane) {
+    const int col = lane & 31, h = lane >> 5;
+    const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
+    a = row_pi(col) * PB + 16 * (h ^ ((col >> 3) & 1));
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      t[x] = (2 * ts + h) * PB + 16 * ((2 * tg + (ta >> 1)) ^ x) + 8 * (ta & 1);
+      c[x] = 16 * ((lane >> 2) ^ x) + 4 * (lane & 3);
+    }
+  }
+  __device__ int A(int ks) const { return a + 32 * ks; }
+  __device__ int T(int rp, int db) const { return t[rp] + 64 * db; }
+};
+
+template <> struct TileLds<128> {
+  static constexpr int PB = 288;             // per row, for multiples of 4 rows
+  static constexpr int ROWS_PER_COPY = 4;
+  __device__ static constexpr int row(int r) { return (r >> 2) * 4 * PB + (r & 3) * 256; }
+  __device__ static constexpr int swz(int r) {
+    return (r & 1) | (((r >> 3) & 1) << 1) | (((r >> 1) & 1) << 2);
+  }
+  // Lane offsets: A reads of k step ks at a[ks & 3] + 128 (ks >> 2);
+  // transposing reads at t[rp][db & 1] + 128 (db >> 1); group copies of groups
+  // q with (q >> 1) & 1 = x from global byte offset c[x] (relative to the
+  // group's first row).
+  int a[4], t[2][2], c[2];
+  __device__ TileLds(int lane) {
+    const int col = lane & 31, h = lane >> 5;
+    const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
+    const int ra = row_pi(col);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = row(ra) + 16 * ((2 * k + h) ^ swz(ra));
+    // Rows 2 ts + h (+ 8 rp + multiples of 16): swz = h | rp << 1 | (ts & 1) << 2.
+#pragma unroll
+    for (int rp = 0; rp < 2; ++rp)
+#pragma unroll
+      for (int d0 = 0; d0 < 2; ++d0)
+        t[rp][d0] = row(2 * ts + h) + 16 * ((2 * tg + (ta >> 1)) ^ (2 * rp + h)) + 8 * (ta & 1) +
+                    64 * (d0 ^ (ts & 1));
+    // Lane i fills chunk i & 15 of row i >> 4 of the group.
+    const int gr = lane >> 4;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      c[x] = gr * 256 + 16 * ((lane & 15) ^ ((gr & 1) | (x << 1) | (((gr >> 1) & 1) << 2)));
+  }
+  __device__ int A(int ks) const { return a[ks & 3] + 128 * (ks >> 2); }
+  __device__ int T(int rp, int db) const { return t[rp][db & 1] + 128 * (db >> 1); }
+};
+
 // s_waitcnt operand that waits until at most n vector-memory loads are
 // outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt
 // left at their maxima).

@@ -361,7 +361,7 @@ struct Fwd16 {
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;             // query rows per workgroup
   static constexpr int BC = 64;                  // keys per tile
-  static constexpr int PB = 2 * (D + 16);        // row pitch in bytes
+  static constexpr int PB = TileLds<D>::PB;      // bytes per row (4-row multiples)
   static constexpr int TILE = BC * PB;
   static constexpr int BUF = 2 * TILE;           // K, V
   static constexpr int NB = 4;                   // K runs one tile ahead of V
@@ -370,7 +370,7 @@ struct Fwd16 {
   static constexpr int NS = 2 * NKS;             // S MFMAs per tile (two 32-key blocks)
   static constexpr int NV = 4 * (D / 32);        // P~V MFMAs per tile
   static constexpr int NM = NS + NV;
-  static constexpr int NLD = 2 * BC / NW;        // row copies per wave per tile
+  static constexpr int NLD = 2 * BC / NW / TileLds<D>::ROWS_PER_COPY;   // copies per wave per tile
   static constexpr int NA = NS / 2;              // slots of the row max
 };
 
@@ -416,31 +416,29 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
   const int ntiles = CAUSAL ? min(ntiles_all, qlast / C::BC + 1) : ntiles_all;
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
-  const int arow = row_pi(col);
-  const int aA = arow * C::PB + 16 * (h ^ ((col >> 3) & 1));
-  const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
-  int aT[2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-    aT[x] = C::TILE + (2 * ts + h) * C::PB + 16 * ((2 * tg + (ta >> 1)) ^ x) + 8 * (ta & 1);
-  int gofs[2];
-#pragma unroll
-  for (int f = 0; f < 2; ++f) gofs[f] = 16 * ((lane >> 2) ^ f) + 4 * (lane & 3);
-  // Copy op j (0..15) of key tile t into buffer b: waves 0-3 copy K, 4-7 copy V,
-  // rows 4 j + (w & 3).  Rows past N read as zero (and are masked through klim).
+  const TileLds<D> lay(lane);
+  // Copy op j of key tile t into buffer b: waves 0-3 copy K, 4-7 copy V, wave
+  // w rows 16 (w & 3) + 4 j .. + 3 (d = 128: one 4-row group per copy) or row
+  // 4 j + (w & 3) (d = 64).  Rows past N read as zero (and are masked through
+  // klim).
   const int mat = w >> 2;
   const i32x4 rsrc = buffer_rsrc(mat ? V : K, (uint32_t)N * (2 * D));
   auto copy_op = [&](int b, int t, int j) {
-    const uint32_t base = lds_address(smem) + b * C::BUF;
-    const int rr = 4 * j + (w & 3);
-    const int f = (j >> 1) & 1;                // chunk XOR of row rr: (rr >> 3) & 1
-    copy_to_lds<C::HALF>(rsrc, gofs[f], (uint32_t)(t * C::BC + rr) * (2 * D),
-                         base + mat * C::TILE + rr * C::PB);
+    const uint32_t base = lds_address(smem) + b * C::BUF + mat * C::TILE;
+    if constexpr (D == 128) {
+      const int q = 4 * (w & 3) + j;
+      copy16_to_lds(rsrc, lay.c[(j >> 1) & 1], (uint32_t)(t * C::BC + 4 * q) * (2 * D),
+                    base + q * 4 * C::PB);
+    } else {
+      const int rr = 4 * j + (w & 3);
+      copy_to_lds<C::HALF>(rsrc, lay.c[(j >> 1) & 1], (uint32_t)(t * C::BC + rr) * (2 * D),
+                           base + rr * C::PB);
+    }
   };
   // S^T MFMA m of a tile (m < NS): key block kb = m & 1, k step ks = m >> 1.
   auto opS = [&](int kboff, int m) -> frag {
-    const int off = kboff + (m & 1) * 32 * C::PB + 32 * (m >> 1);
-    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + aA + off));
+    const int off = kboff + (m & 1) * 32 * C::PB;
+    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + lay.A(m >> 1) + off));
   };
   // P~V MFMA r of a tile (r < NV): key block kb, 16-key step u, head-dim block db.
   auto opV = [&](int vboff, int r) -> frag {
@@ -448,8 +446,8 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
     s16x4 v[2];
 #pragma unroll
     for (int rp = 0; rp < 2; ++rp) {
-      const int off = vboff + (kb * 32 + 16 * u + 8 * rp) * C::PB + 64 * db;
-      v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + aT[rp] + off));
+      const int off = vboff + C::TILE + (kb * 32 + 16 * u + 8 * rp) * C::PB;
+      v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + lay.T(rp, db) + off));
     }
     return __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
                                           v[1][0], v[1][1], v[1][2], v[1][3]});
