@@ -355,16 +355,20 @@ void fwd_kernel(FwdArgs a) {
 // unchanged by the choice of reference (it cancels between O and l).
 constexpr float kMaxSlack = 8.f;
 
-template <int D>
+// NW = 8: one workgroup of 8 waves per CU, four K/V buffers, the K/V tiles
+// copied three tiles ahead (waves 0-3 copy K, 4-7 V).  NW = 4: two workgroups
+// of 4 waves per CU, two buffers, K copied two tiles and V one tile ahead by
+// every wave; 128 query rows per workgroup balance causal work better.
+template <int D, int NW_>
 struct Fwd16 {
-  static constexpr int NW = 8;
+  static constexpr int NW = NW_;
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;             // query rows per workgroup
   static constexpr int BC = 64;                  // keys per tile
   static constexpr int PB = TileLds<D>::PB;      // bytes per row (4-row multiples)
   static constexpr int TILE = BC * PB;
   static constexpr int BUF = 2 * TILE;           // K, V
-  static constexpr int NB = 4;                   // K runs one tile ahead of V
+  static constexpr int NB = NW == 8 ? 4 : 2;     // K/V buffers
   static constexpr bool HALF = D == 64;
   static constexpr int NKS = D / 16;
   static constexpr int NS = 2 * NKS;             // S MFMAs per tile (two 32-key blocks)
@@ -374,9 +378,10 @@ struct Fwd16 {
   static constexpr int NA = NS / 2;              // slots of the row max
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
-  using C = Fwd16<D>;
+template <typename T, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
+  using C = Fwd16<D, NW>;
+  static_assert(D == 128 && (NW == 4 || NW == 8), "fwd16_kernel is built for d = 128");
   using M = Mfma<T>;
   using frag = typename M::frag;
   __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF];
@@ -417,23 +422,14 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const TileLds<D> lay(lane);
-  // Copy op j of key tile t into buffer b: waves 0-3 copy K, 4-7 copy V, wave
-  // w rows 16 (w & 3) + 4 j .. + 3 (d = 128: one 4-row group per copy) or row
-  // 4 j + (w & 3) (d = 64).  Rows past N read as zero (and are masked through
-  // klim).
-  const int mat = w >> 2;
-  const i32x4 rsrc = buffer_rsrc(mat ? V : K, (uint32_t)N * (2 * D));
-  auto copy_op = [&](int b, int t, int j) {
+  // Copy of the 4-row group q of K (mat 0) or V (mat 1) of key tile t into
+  // buffer b.  Rows past N read as zero (and are masked through klim).
+  const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
+  const i32x4 rsv = buffer_rsrc(V, (uint32_t)N * (2 * D));
+  auto copy_group = [&](int b, int mat, int t, int q) {
     const uint32_t base = lds_address(smem) + b * C::BUF + mat * C::TILE;
-    if constexpr (D == 128) {
-      const int q = 4 * (w & 3) + j;
-      copy16_to_lds(rsrc, lay.c[(j >> 1) & 1], (uint32_t)(t * C::BC + 4 * q) * (2 * D),
-                    base + q * 4 * C::PB);
-    } else {
-      const int rr = 4 * j + (w & 3);
-      copy_to_lds<C::HALF>(rsrc, lay.c[(j >> 1) & 1], (uint32_t)(t * C::BC + rr) * (2 * D),
-                           base + rr * C::PB);
-    }
+    copy16_to_lds(mat ? rsv : rsk, lay.c[(q >> 1) & 1], (uint32_t)(t * C::BC + 4 * q) * (2 * D),
+                  base + q * 4 * C::PB);
   };
   // S^T MFMA m of a tile (m < NS): key block kb = m & 1, k step ks = m >> 1.
   auto opS = [&](int kboff, int m) -> frag {
@@ -461,13 +457,26 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
   // for the MFMA, so that the weights of O sum to 1 exactly as used.
   float l_run = 0.f;
 
-  // Prologue: tiles 0, 1, 2 into buffers 0, 1, 2; S of tile 0.
+  // Prologue: NW = 8: tiles 0, 1, 2 into buffers 0, 1, 2 (wave w copies groups
+  // 4 (w & 3) .. + 3 of K (w < 4) or V); NW = 4: K and V of tile 0 into buffer
+  // 0 and K of tile 1 into buffer 1 (wave w copies groups 4 w .. + 3 of each).
+  // Then S of tile 0.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if constexpr (NW == 8) {
 #pragma unroll
-  for (int t = 0; t < 3; ++t)
+    for (int t = 0; t < 3; ++t)
 #pragma unroll
-    for (int j = 0; j < C::NLD; ++j) copy_op(t, t, j);
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // tile 2 may still be in flight
+      for (int kk = 0; kk < 4; ++kk) copy_group(t, w >> 2, t, 4 * (w & 3) + kk);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // tile 2 may still be in flight
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      copy_group(0, 0, 0, 4 * w + kk);
+      copy_group(0, 1, 0, 4 * w + kk);
+      copy_group(1, 0, 1, 4 * w + kk);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
   __syncthreads();
   // S of the current tile and of the next one; the two trade places every tile
   // (the loops run two tiles per trip), so no tile copies them.
@@ -487,16 +496,21 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
   constexpr auto exp_slot = [](int kb, int i) {
     return kb == 0 ? NA + 1 + (i * (NS - NA - 1)) / 16 : NS + (i * (NV / 2)) / 16;
   };
-  constexpr auto copy_slot = [](int k) { return NS + (k * NV) / C::NLD; };
+  // NW = 8: the copies of tile j + 3 spread over the P~V MFMAs; NW = 4: the
+  // copies of iteration j (K of tile j + 2, V of tile j + 1) early in the
+  // stream, since they must land before its end.
+  constexpr auto copy_slot = [](int k) {
+    return NW == 8 ? NS + (k * NV) / C::NLD : 1 + 2 * k;
+  };
 
-  int b0 = 0;   // buffer of tile j
+  int b0 = 0;   // buffer of tile j (NW = 8)
   // One tile: S of tile j + 1 (into sn) with the softmax of tile j (S in sc),
   // then P~V of tile j.  MASK: some row of the wave crosses the causal
   // diagonal or N in tile j.
   auto iteration = [&](int j, auto maskc, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     const int key0 = j * C::BC;
-    const int bk = (b0 + 1) & 3, bc = (b0 + 3) & 3;
-    const int kboff = bk * C::BUF, vboff = b0 * C::BUF;
+    const int bk = NW == 8 ? (b0 + 1) & 3 : (j + 1) & 1, bc = (b0 + 3) & 3;
+    const int kboff = bk * C::BUF, vboff = (NW == 8 ? b0 : j & 1) * C::BUF;
     frag pf[2][2];
     sn[0] = f32x16{};
     sn[1] = f32x16{};
@@ -532,7 +546,11 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int k = 0; k < C::NLD; ++k)
-        if (m == copy_slot(k)) copy_op(bc, j + 3, k);
+        if (m == copy_slot(k)) {
+          if constexpr (NW == 8) copy_group(bc, w >> 2, j + 3, 4 * (w & 3) + k);
+          else if (k < 4) copy_group(j & 1, 0, j + 2, 4 * w + k);
+          else copy_group((j + 1) & 1, 1, j + 1, 4 * w + k - 4);
+        }
 #pragma unroll
       for (int e = 0; e < 32; ++e)
         if (m == max_slot(e)) {
@@ -586,9 +604,10 @@ __global__ __launch_bounds__(512, 2) void fwd16_kernel(FwdArgs a) {
     rescale();
     static_for<NS, NM>([&](auto mc) { slot(mc, maskc); });
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    // Tile j + 2 (copied during the previous tile) must have landed; the copies
-    // of tile j + 3 may still be in flight.
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
+    // NW = 8: tile j + 2 (copied during the previous tile) must have landed,
+    // the copies of tile j + 3 may still be in flight.  NW = 4: K of tile j + 2
+    // and V of tile j + 1 must have landed.
+    __builtin_amdgcn_s_waitcnt(NW == 8 ? wait_vmcnt(C::NLD) : kWaitVmcnt0);
     __syncthreads();
     b0 = (b0 + 1) & 3;
   };
@@ -632,9 +651,14 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   // d = 64 keeps the register-staged kernel: with two head-dim blocks the
   // stream of fwd16_kernel has too few independent accumulators to hide the
   // MFMA latency.
+  // Under the causal mask, 128 query rows per workgroup (two per CU) balance
+  // the triangle better; without it one 256-row workgroup per CU copies half
+  // as much.
   if constexpr (sizeof(T) == 2 && D == 128) {
-    dim3 grid((a.N + Fwd16<D>::BR - 1) / Fwd16<D>::BR, a.H, a.B);
-    hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL>), grid, dim3(Fwd16<D>::NT), 0, s, a);
+    constexpr int NW = CAUSAL ? 4 : 8;
+    using C = Fwd16<D, NW>;
+    dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
+    hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, NW>), grid, dim3(C::NT), 0, s, a);
   } else {
     using C = FwdTile<T, D>;
     dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
