@@ -526,16 +526,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 // and dP^T = V dO^T take their A operand from K / V rows (two 8-byte reads,
 // rows in the order row_pi) and Q / dO from registers; dQ^T += K^T dS^T takes
 // K^T through transposing reads.  8 waves x 32 queries per workgroup.
-template <int D>
+// NW = 8: one workgroup of 8 waves per CU, three K/V buffers, tiles copied two
+// ahead (waves 0-3 copy K, 4-7 V).  NW = 4 (d = 128): two workgroups of 4 waves
+// per CU, two buffers, each tile copied one ahead by every wave; 128 query rows
+// per workgroup balance causal work better.
+template <int D, int NW_>
 struct Dq16 {
-  static constexpr int NW = 8;
+  static constexpr int NW = NW_;
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;             // queries per workgroup
   static constexpr int BC = 64;                  // keys per tile
   static constexpr int PB = TileLds<D>::PB;      // bytes per row (4-row multiples)
   static constexpr int TILE = BC * PB;
   static constexpr int BUF = 2 * TILE;           // K, V
-  static constexpr int NB = 3;
+  static constexpr int NB = NW == 8 ? 3 : 2;
   static constexpr bool HALF = D == 64;
   static constexpr int NKS = D / 16;
   static constexpr int NS = 2 * NKS;             // S/dP MFMAs per 32-key block
@@ -544,9 +548,10 @@ struct Dq16 {
   static constexpr int NLD = 2 * BC / NW / TileLds<D>::ROWS_PER_COPY;   // copies per wave per tile
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
-  using C = Dq16<D>;
+template <typename T, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
+  using C = Dq16<D, NW>;
+  static_assert(NW == 8 || (NW == 4 && D == 128), "4-wave dQ workgroups copy 4-row groups");
   using M = Mfma<T>;
   using frag = typename M::frag;
   __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF];
@@ -594,17 +599,20 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const TileLds<D> lay(lane);
-  // Copy op j of key tile kt into buffer b: waves 0-3 copy K, 4-7 copy V, wave
-  // w rows 16 (w & 3) + 4 j .. + 3 (d = 128: one 4-row group per copy) or row
-  // 4 j + (w & 3) (d = 64).  Rows past N read as zero (and are masked through
-  // klim).
-  const int mat = w >> 2;
-  const i32x4 rsrc = buffer_rsrc(mat ? V : K, (uint32_t)N * (2 * D));
+  // Copy op j of key tile kt into buffer b.  NW = 8: waves 0-3 copy K, 4-7
+  // copy V, wave w rows 16 (w & 3) + 4 j .. + 3 (d = 128: one 4-row group per
+  // copy) or row 4 j + (w & 3) (d = 64).  NW = 4: wave w copies groups
+  // 4 w + j of K (j < 4) and 4 w + j - 4 of V.  Rows past N read as zero (and
+  // are masked through klim).
+  const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
+  const i32x4 rsv = buffer_rsrc(V, (uint32_t)N * (2 * D));
   auto copy_op = [&](int b, int kt, int j) {
+    const int mat = NW == 8 ? w >> 2 : j >> 2;
+    const i32x4& rsrc = mat ? rsv : rsk;
     const uint32_t base = lds_address(smem) + b * C::BUF + mat * C::TILE;
     if constexpr (D == 128) {
-      const int q = 4 * (w & 3) + j;
-      copy16_to_lds(rsrc, lay.c[(j >> 1) & 1], (uint32_t)(kt * C::BC + 4 * q) * (2 * D),
+      const int q = NW == 8 ? 4 * (w & 3) + j : 4 * w + (j & 3);
+      copy16_to_lds(rsrc, lay.c[(q >> 1) & 1], (uint32_t)(kt * C::BC + 4 * q) * (2 * D),
                     base + q * 4 * C::PB);
     } else {
       const int rr = 4 * j + (w & 3);
@@ -613,11 +621,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
     }
   };
 
+  // Prologue: tiles 0 and 1 (NW = 8) or tile 0 (NW = 4).
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
-  for (int j = 0; j < C::NLD; ++j) copy_op(0, 0, j);
+  for (int t = 0; t < C::NB - 1; ++t)
 #pragma unroll
-  for (int j = 0; j < C::NLD; ++j) copy_op(1, 1, j);
+    for (int j = 0; j < C::NLD; ++j) copy_op(t, t, j);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
@@ -629,15 +638,17 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
   constexpr auto elem_slot = [](int b, int i) {
     return b == 0 ? NS + 2 + (i * (NS - 2)) / 16 : 2 * NS + 1 + (i * (NQ - 2)) / 16;
   };
-  constexpr auto copy_slot = [](int k) { return 1 + (k * (NM - 6)) / C::NLD; };
+  // NW = 8: copies of tile kt + 2 spread over the stream; NW = 4: copies of
+  // tile kt + 1 early in the stream, since they must land before its end.
+  constexpr auto copy_slot = [](int k) { return NW == 8 ? 1 + (k * (NM - 6)) / C::NLD : 1 + 2 * k; };
   int bcur = 0;
   // One key tile.  MASK: some key of the tile is past N or, under the causal
   // mask, after some query of the workgroup.
   auto tile = [&](int kt, auto maskc) {
     constexpr bool MASK = decltype(maskc)::value;
     const int key0 = kt * C::BC;
-    const int b1 = bcur == 2 ? 0 : bcur + 1;
-    const int b2 = b1 == 2 ? 0 : b1 + 1;
+    const int b1 = bcur == C::NB - 1 ? 0 : bcur + 1;
+    const int b2 = b1 == C::NB - 1 ? 0 : b1 + 1;
     const int boff = bcur * C::BUF;
     auto operand = [&](int m) -> frag {
       if (m < 2 * NS) {
@@ -674,7 +685,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
       constexpr int m = decltype(mc)::value;
 #pragma unroll
       for (int k = 0; k < C::NLD; ++k)
-        if (m == copy_slot(k)) copy_op(b2, kt + 2, k);
+        if (m == copy_slot(k)) copy_op(C::NB == 3 ? b2 : b1, kt + C::NB - 1, k);
       // Operands are read in pairs at odd slots, the odd one first, so that the
       // wait for the even one covers both.
       const frag x = opq[m % PD];
@@ -705,7 +716,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dq16_kernel(BwdArgs a) {
           }
       __builtin_amdgcn_sched_barrier(0);
     });
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
+    // The tile copied during the previous tile (NW = 8) or this one (NW = 4)
+    // must have landed.
+    __builtin_amdgcn_s_waitcnt(NW == 8 ? wait_vmcnt(C::NLD) : kWaitVmcnt0);
     __syncthreads();
     bcur = b1;
   };
@@ -1020,8 +1033,11 @@ static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
     }
   } else if constexpr (sizeof(T) == 2) {
-    dim3 grid((a.N + Dq16<D>::BR - 1) / Dq16<D>::BR, a.H, a.B);
-    hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL>), grid, dim3(Dq16<D>::NT), 0, s, a);
+    // Causal d = 128: 128-row workgroups, two per CU, balance the triangle.
+    constexpr int NW = CAUSAL && D == 128 ? 4 : 8;
+    using C = Dq16<D, NW>;
+    dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
+    hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL, NW>), grid, dim3(C::NT), 0, s, a);
   } else {
     dim3 grid((a.N + DqTile<T, D>::BR - 1) / DqTile<T, D>::BR, a.H, a.B);
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(DqTile<T, D>::NT), 0, s, a);
