@@ -874,8 +874,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // P/dS arithmetic of a block fills the slots between its S/dP and dV/dK MFMAs.
   constexpr int NS = C::NS, NV = C::NV, NVB = C::NVB, NM = C::NM;
   constexpr int PD = 4;
+  // Element i of block b: the first 8 (P and dS for the first half of the
+  // block's dV/dK MFMAs) done before those start, the last 8 overlapping
+  // them, before the second half starts.
   constexpr auto elem_slot = [](int b, int i) {
-    return b == 0 ? NS + 2 + (i * (NS - 2)) / 16 : 2 * NS + 2 + (i * (NV - 2)) / 16;
+    return (b == 0 ? NS : 2 * NS) + 2 + (i * (NS + NVB - 2)) / 16;
   };
   // Slot of copy k of the next-but-one tile.
   constexpr auto copy_slot = [](int k) { return 1 + (k * (NM - 6)) / C::NLD; };
