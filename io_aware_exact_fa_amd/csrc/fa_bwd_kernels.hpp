@@ -250,12 +250,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int lane = tid & 63, w = tid >> 6, col = lane & 31, h = lane >> 5;
   const int N = a.N;
   const int ntk = gridDim.x;
-  const int lin = xcd_work_index();
+  int kt, hd;
   // Under the causal mask the key tiles near the start see the most queries and
-  // come first in each head's range.
-  const int kt = lin % ntk;
+  // come first.
+  work_item<CAUSAL>(ntk, kt, hd);
   const int k0 = kt * C::BKC;
-  const size_t head = (size_t)(lin / ntk);
+  const size_t head = (size_t)hd;
   const T* Q = static_cast<const T*>(a.q) + head * N * D;
   const T* K = static_cast<const T*>(a.k) + head * N * D;
   const T* V = static_cast<const T*>(a.v) + head * N * D;
@@ -561,11 +561,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = a.N;
   const int ntq = gridDim.x;
-  const int lin = xcd_work_index();
+  int rank, hd;
+  work_item<CAUSAL>(ntq, rank, hd);
   // Under the causal mask the last query tiles see the most keys: start them first.
-  const int qt = CAUSAL ? ntq - 1 - (lin % ntq) : (lin % ntq);
+  const int qt = CAUSAL ? ntq - 1 - rank : rank;
   const int q0 = qt * C::BR;
-  const size_t head = (size_t)(lin / ntq);
+  const size_t head = (size_t)hd;
   const T* Q = static_cast<const T*>(a.q) + head * N * D;
   const T* K = static_cast<const T*>(a.k) + head * N * D;
   const T* V = static_cast<const T*>(a.v) + head * N * D;
@@ -785,12 +786,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = a.N;
   const int ntk = gridDim.x;
-  const int lin = xcd_work_index();
+  int kt, hd;
   // Under the causal mask the key tiles near the start see the most queries and
-  // come first in each head's range.
-  const int kt = lin % ntk;
+  // come first.
+  work_item<CAUSAL>(ntk, kt, hd);
   const int k0 = kt * C::BKC;
-  const size_t head = (size_t)(lin / ntk);
+  const size_t head = (size_t)hd;
   const T* Q = static_cast<const T*>(a.q) + head * N * D;
   const T* K = static_cast<const T*>(a.k) + head * N * D;
   const T* V = static_cast<const T*>(a.v) + head * N * D;

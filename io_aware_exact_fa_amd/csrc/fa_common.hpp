@@ -322,6 +322,28 @@ __device__ inline int xcd_work_index() {
   return lin;
 }
 
+// Tile rank (position in its head's range) and head of this workgroup, for a
+// grid of nt tiles per head.  Without HEAVY_FIRST: xcd_work_index order.  With
+// it (causal launches, whose tiles differ in cost by rank): each XCD still
+// takes a contiguous range of heads, but walks their tiles rank-major, rank 0
+// (the heaviest) of every head first, so that the last workgroups it starts
+// are the shortest.
+template <bool HEAVY_FIRST>
+__device__ inline void work_item(int nt, int& rank, int& head) {
+  const int nwork = gridDim.x * gridDim.y * gridDim.z;
+  const int nheads = nwork / nt;
+  if (HEAVY_FIRST && (nheads & 7) == 0) {
+    const int id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int hpx = nheads >> 3, li = id >> 3;
+    head = (id & 7) * hpx + li % hpx;
+    rank = li / hpx;
+  } else {
+    const int lin = xcd_work_index();
+    head = lin / nt;
+    rank = lin % nt;
+  }
+}
+
 // Row of a 32-row block (queries or keys) that supplies result row m of an MFMA
 // whose A operand is read from a row-major tile (m = 8a + 4h + s -> 8a + 2s + h):
 // the 4 rows that one transposing read gathers for a later MFMA are then 2 apart.

@@ -391,10 +391,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = a.N;
   const int ntq = gridDim.x;
-  const int lin = xcd_work_index();
-  const int qt = CAUSAL ? ntq - 1 - (lin % ntq) : (lin % ntq);
+  int rank, hd;
+  work_item<CAUSAL>(ntq, rank, hd);   // causal: the last query tiles (most keys) first
+  const int qt = CAUSAL ? ntq - 1 - rank : rank;
   const int q0 = qt * C::BR;
-  const size_t head = (size_t)(lin / ntq);
+  const size_t head = (size_t)hd;
   const T* Q = static_cast<const T*>(a.q) + head * N * D;
   const T* K = static_cast<const T*>(a.k) + head * N * D;
   const T* V = static_cast<const T*>(a.v) + head * N * D;
