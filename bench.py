@@ -2,7 +2,9 @@
 
 One step = the whole path over one batch of seeded synthetic inputs already
 resident in HBM: fa_fwd, then fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq
-(the three steps of fa_bwd), all through the C ABI on one stream.  Throughput is counted with the method's FLOP formula: forward
+(the three steps of fa_bwd), all through the C ABI on one stream (called in
+their grouped-K/V forms, which are the plain ones when every query head has its
+own K/V head).  Throughput is counted with the method's FLOP formula: forward
 4*B*H*N^2*d (halved under the causal mask), backward 2.5x the forward.
 
 Prints ONE JSON line.  Besides the step throughput it reports:
@@ -100,26 +102,36 @@ def cpu_baseline(w, inp, gpu_out, budget_s: float = 10.0):
         cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:   # threadpoolctl missing: report the process's CPU affinity
         cores = len(os.sched_getaffinity(0))
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)][::-1]
+    # One K/V head and its G query heads at a time (G = 1 without grouped K/V):
+    # forward and backward of each query head, dK and dV summed over the group.
+    G = w.H // w.kv_heads
+    groups = [(b, j) for b in range(w.B) for j in range(w.kv_heads)][::-1]
     f64 = lambda t, b, h: t[b, h].to(dtype=torch.float64).numpy()
     rel = lambda a, r: float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-30))
     secs, done, check = 0.0, 0, None
-    for b, h in heads:
-        q, k, v, do = (f64(inp[n], b, h) for n in ("q", "k", "v", "do"))
+    for b, j in groups:
+        k, v = f64(inp["k"], b, j), f64(inp["v"], b, j)
+        res = []
         t0 = time.perf_counter()
-        o, lse = oracle.forward_head(q, k, v, w.scale, w.causal)
-        g = oracle.backward_head(q, k, v, do, w.scale, w.causal)
+        for h in range(j * G, (j + 1) * G):
+            q, do = f64(inp["q"], b, h), f64(inp["do"], b, h)
+            o, lse = oracle.forward_head(q, k, v, w.scale, w.causal)
+            res.append((h, o, lse, oracle.backward_head(q, k, v, do, w.scale, w.causal)))
         secs += time.perf_counter() - t0
-        done += 1
-        if check is None:   # GPU-vs-oracle error on the first sampled head
-            g64 = {n: gpu_out[n][b, h].double().numpy() for n in ("o", "lse", "dq", "dk", "dv")}
+        done += G
+        if check is None:   # GPU-vs-oracle error on the first sampled group
+            dk = sum(r[3]["dk"] for r in res)
+            dv = sum(r[3]["dv"] for r in res)
+            oerr = max(float(np.max(np.abs(gpu_out["o"][b, h].double().numpy() - o))) for h, o, _, _ in res)
+            lerr = max(float(np.max(np.abs(gpu_out["lse"][b, h].double().numpy() - l))) for h, _, l, _ in res)
+            dqerr = max(rel(gpu_out["dq"][b, h].double().numpy(), g["dq"]) for h, _, _, g in res)
             check = {
-                "head": [b, h],
-                "o_maxabs": float(np.max(np.abs(g64["o"] - o))),
-                "lse_maxabs": float(np.max(np.abs(g64["lse"] - lse))),
-                "dq_rel": rel(g64["dq"], g["dq"]),
-                "dk_rel": rel(g64["dk"], g["dk"]),
-                "dv_rel": rel(g64["dv"], g["dv"]),
+                "head": [b, j * G] if G == 1 else {"batch": b, "kv_head": j, "query_heads": [j * G, (j + 1) * G - 1]},
+                "o_maxabs": oerr,
+                "lse_maxabs": lerr,
+                "dq_rel": dqerr,
+                "dk_rel": rel(gpu_out["dk"][b, j].double().numpy(), dk),
+                "dv_rel": rel(gpu_out["dv"][b, j].double().numpy(), dv),
             }
         if secs >= budget_s:
             break
@@ -129,7 +141,7 @@ def cpu_baseline(w, inp, gpu_out, budget_s: float = 10.0):
         "unit": "TFLOPS",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"{done} of {w.B * w.H} heads (the last ones), forward + backward each, fp64 "
+        "sample": f"{done} of {w.B * w.H} query heads (the last ones), forward + backward each, fp64 "
                   f"numpy oracle with S and P materialized; {secs:.2f} s wall",
         "seconds": round(secs, 3),
         "parity_on_sample": check,
@@ -157,9 +169,10 @@ def main():
     inp = workloads.make_inputs(w)
     q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
     ws = fa.workspace(B, H, N, d, dev)
     code = fa.dtype_code(q.dtype)
     stream = torch.cuda.current_stream()
@@ -173,18 +186,19 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        check(fa.fa_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, N, d, w.causal, w.scale, code, sh), "fwd")
+        check(fa.fa_fwd_gqa(P(q), P(k), P(v), P(o), P(lse), B, H, Hkv, N, d, w.causal, w.scale, code,
+                            sh), "fwd")
         if ev is not None:
             ev[1].record(stream)
         check(fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, code, P(ws), ws.numel(), sh), "pre")
         if ev is not None:
             ev[2].record(stream)
-        check(fa.fa_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, N, d, w.causal,
-                             w.scale, code, P(ws), ws.numel(), sh), "dkdv")
+        check(fa.fa_bwd_dkdv_gqa(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, Hkv, N, d,
+                                 w.causal, w.scale, code, P(ws), ws.numel(), sh), "dkdv")
         if ev is not None:
             ev[3].record(stream)
-        check(fa.fa_bwd_dq(P(q), P(k), P(v), P(do), P(lse), P(dq), B, H, N, d, w.causal, w.scale,
-                           code, P(ws), ws.numel(), sh), "dq")
+        check(fa.fa_bwd_dq_gqa(P(q), P(k), P(v), P(do), P(lse), P(dq), B, H, Hkv, N, d, w.causal,
+                               w.scale, code, P(ws), ws.numel(), sh), "dq")
         if ev is not None:
             ev[4].record(stream)
 
@@ -229,7 +243,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded normal Q/K/V/dO of the workload's shape and distribution)",
         "config": {
-            "workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+            "workload": w.name, "B": B, "H": H, "H_kv": Hkv, "N": N, "d": d, "causal": w.causal,
             "step": "fa_fwd + fa_bwd (preprocess, dkdv, dq)",
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "bwd_pre_ms": round(pre_ms, 4), "bwd_dkdv_ms": round(dkdv_ms, 4),

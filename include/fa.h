@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -157,6 +157,45 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
                     int B, int H, int N, int d, int causal, float scale,
                     fa_dtype dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * Grouped key/value heads.  The page "Transformer 효율화 기법" (ailab.paldyn.com),
+ * section "v1에서 v3까지", lists grouped-query attention (GQA) among the
+ * features of FlashAttention-2 without defining it; the reading used here is
+ * the usual one: H query heads share H_kv key/value heads (H divisible by
+ * H_kv), query head h of a batch entry attends with key/value head
+ * h / (H / H_kv) of the same entry; H_kv = 1 is multi-query attention and
+ * H_kv = H is plain multi-head attention (the entry points above are exactly
+ * these with H_kv = H).  q, o, dout, dq: [B, H, N, d]; k, v, dk, dv:
+ * [B, H_kv, N, d]; lse [B, H, N]; the workspace is per query head
+ * (fa_bwd_workspace_size(B, H, N, d)) and is filled by fa_bwd_preprocess with
+ * H query heads.  dk and dv of a key/value head are the sums of the
+ * gradients through all of its query heads (one workgroup walks them in turn,
+ * no atomics).  Errors as above; in addition H_kv <= 0 or H not divisible by
+ * H_kv is FA_ERR_INVALID_ARGUMENT.
+ */
+fa_status fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int H_kv, int N, int d, int causal, float scale,
+                     fa_dtype dtype, void* stream);
+
+fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv,
+                     int B, int H, int H_kv, int N, int d, int causal, float scale,
+                     fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+fa_status fa_bwd_dkdv_gqa(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, void* dk, void* dv,
+                          int B, int H, int H_kv, int N, int d, int causal, float scale,
+                          fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+fa_status fa_bwd_dq_gqa(const void* q, const void* k, const void* v, const void* dout,
+                        const float* lse, void* dq,
+                        int B, int H, int H_kv, int N, int d, int causal, float scale,
+                        fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,8 @@ FA_F16 = 1
 FA_BF16 = 2
 
 EXPORTED = ("fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
-            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq")
+            "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
+            "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa")
 
 
 class FaError(RuntimeError):
@@ -71,6 +72,15 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_dq.restype = i
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_fwd_gqa.restype = i
+    lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_gqa.restype = i
+    lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz,
+                               vp]
+    lib.fa_bwd_dkdv_gqa.restype = i
+    lib.fa_bwd_dkdv_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dq_gqa.restype = i
+    lib.fa_bwd_dq_gqa.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     return lib
 
 
@@ -129,6 +139,29 @@ def fa_bwd_dq(q, k, v, dout, lse, dq, B, H, N, d, causal, scale, dtype,
                           int(dtype), workspace, workspace_bytes, stream)
 
 
+def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, dtype, stream) -> int:
+    return _lib.fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, int(causal), float(scale),
+                           int(dtype), stream)
+
+
+def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal, scale, dtype,
+               workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, int(causal),
+                           float(scale), int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_bwd_dkdv_gqa(q, k, v, dout, lse, dk, dv, B, H, H_kv, N, d, causal, scale, dtype,
+                    workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_dkdv_gqa(q, k, v, dout, lse, dk, dv, B, H, H_kv, N, d, int(causal),
+                                float(scale), int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_bwd_dq_gqa(q, k, v, dout, lse, dq, B, H, H_kv, N, d, causal, scale, dtype,
+                  workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_dq_gqa(q, k, v, dout, lse, dq, B, H, H_kv, N, d, int(causal), float(scale),
+                              int(dtype), workspace, workspace_bytes, stream)
+
+
 # ------------------------------------------------------------------ torch helpers
 
 
@@ -155,22 +188,24 @@ def _stream(stream):
 
 
 def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
-    """O, LSE for [B, H, N, d] tensors q, k, v (all one dtype, on the GPU)."""
+    """O, LSE for q [B, H, N, d] and k, v [B, H_kv, N, d] (H_kv divides H; all one
+    dtype, on the GPU)."""
     import torch
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
     _check("q", q, (B, H, N, d), q.dtype)
-    _check("k", k, (B, H, N, d), q.dtype)
-    _check("v", v, (B, H, N, d), q.dtype)
+    _check("k", k, (B, H_kv, N, d), q.dtype)
+    _check("v", v, (B, H_kv, N, d), q.dtype)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check("o", o, (B, H, N, d), q.dtype)
     _check("lse", lse, (B, H, N), torch.float32)
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                B, H, N, d, causal, scale, dtype_code(q.dtype), _stream(stream))
+    st = fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    B, H, H_kv, N, d, causal, scale, dtype_code(q.dtype), _stream(stream))
     if st != FA_OK:
-        raise FaError(st, "fa_fwd")
+        raise FaError(st, "fa_fwd_gqa")
     return o, lse
 
 
@@ -188,18 +223,23 @@ def backward(q, k, v, o, dout, lse, causal: bool, scale: float, dq=None, dk=None
     """dQ, dK, dV for the forward that produced o and lse."""
     import torch
     B, H, N, d = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+    H_kv = k.shape[1]
+    for name, t in (("q", q), ("o", o), ("dout", dout)):
         _check(name, t, (B, H, N, d), q.dtype)
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (B, H_kv, N, d), q.dtype)
     _check("lse", lse, (B, H, N), torch.float32)
     dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check(name, t, (B, H, N, d), q.dtype)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    _check("dq", dq, (B, H, N, d), q.dtype)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H_kv, N, d), q.dtype)
     ws = workspace(B, H, N, d, q.device) if ws is None else ws
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal,
-                scale, dtype_code(q.dtype), ws.data_ptr(), ws.numel(), _stream(stream))
+    st = fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d,
+                    causal, scale, dtype_code(q.dtype), ws.data_ptr(), ws.numel(),
+                    _stream(stream))
     if st != FA_OK:
-        raise FaError(st, "fa_bwd")
+        raise FaError(st, "fa_bwd_gqa")
     return dq, dk, dv

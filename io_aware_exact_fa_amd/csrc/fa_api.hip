@@ -66,8 +66,8 @@ fa::Dt to_dt(fa_dtype d) {
 fa_status launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
 // Shared checks of the backward entry points, then the workspace split.
-fa_status bwd_setup(int B, int H, int N, int d, float scale, fa_dtype dtype, void* workspace,
-                    size_t workspace_bytes, fa::BwdArgs* a);
+fa_status bwd_setup(int B, int H, int H_kv, int N, int d, float scale, fa_dtype dtype,
+                    void* workspace, size_t workspace_bytes, fa::BwdArgs* a);
 
 }  // namespace
 
@@ -87,15 +87,23 @@ const char* fa_status_string(fa_status status) {
   return "unknown status";
 }
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                 int N, int d, int causal, float scale, fa_dtype dtype, void* stream) {
+fa_status fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int H_kv, int N, int d, int causal, float scale, fa_dtype dtype,
+                     void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
   fa_status st = check_shape(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
+  if (H_kv <= 0 || H % H_kv != 0) return FA_ERR_INVALID_ARGUMENT;
   st = check_device();
   if (st != FA_OK) return st;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, scale};
+  a.G = H / H_kv;
   return launched(fa::launch_fwd(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream));
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, int causal, float scale, fa_dtype dtype, void* stream) {
+  return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
@@ -110,7 +118,7 @@ fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse, i
                             void* stream) {
   if (!o || !dout || !lse) return FA_ERR_INVALID_ARGUMENT;
   fa::BwdArgs a{};
-  fa_status st = bwd_setup(B, H, N, d, 1.0f, dtype, workspace, workspace_bytes, &a);
+  fa_status st = bwd_setup(B, H, H, N, d, 1.0f, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
   a.o = o;
   a.dout = dout;
@@ -118,13 +126,13 @@ fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse, i
   return launched(fa::launch_bwd_pre(to_dt(dtype), d, a, (hipStream_t)stream));
 }
 
-fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                      const float* lse, void* dk, void* dv, int B, int H, int N, int d, int causal,
-                      float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+fa_status fa_bwd_dkdv_gqa(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, void* dk, void* dv, int B, int H, int H_kv, int N,
+                          int d, int causal, float scale, fa_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !dout || !lse || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
   fa::BwdArgs a{};
-  fa_status st = bwd_setup(B, H, N, d, scale, dtype, workspace, workspace_bytes, &a);
+  fa_status st = bwd_setup(B, H, H_kv, N, d, scale, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
   a.q = q;
   a.k = k;
@@ -136,13 +144,21 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* d
   return launched(fa::launch_bwd_dkdv(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream));
 }
 
-fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                    const float* lse, void* dq, int B, int H, int N, int d, int causal,
-                    float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                      float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return fa_bwd_dkdv_gqa(q, k, v, dout, lse, dk, dv, B, H, H, N, d, causal, scale, dtype,
+                         workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_dq_gqa(const void* q, const void* k, const void* v, const void* dout,
+                        const float* lse, void* dq, int B, int H, int H_kv, int N, int d,
+                        int causal, float scale, fa_dtype dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !dout || !lse || !dq) return FA_ERR_INVALID_ARGUMENT;
   fa::BwdArgs a{};
-  fa_status st = bwd_setup(B, H, N, d, scale, dtype, workspace, workspace_bytes, &a);
+  fa_status st = bwd_setup(B, H, H_kv, N, d, scale, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
   a.q = q;
   a.k = k;
@@ -153,13 +169,21 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
   return launched(fa::launch_bwd_dq(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream));
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                 int causal, float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse, void* dq, int B, int H, int N, int d, int causal,
+                    float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return fa_bwd_dq_gqa(q, k, v, dout, lse, dq, B, H, H, N, d, causal, scale, dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv,
+                     int N, int d, int causal, float scale, fa_dtype dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
   fa::BwdArgs a{};
-  fa_status st = bwd_setup(B, H, N, d, scale, dtype, workspace, workspace_bytes, &a);
+  fa_status st = bwd_setup(B, H, H_kv, N, d, scale, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
   a.q = q;
   a.k = k;
@@ -179,14 +203,23 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   return launched(fa::launch_bwd_dq(dt, d, causal != 0, a, s));
 }
 
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                 int causal, float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, causal, scale, dtype,
+                    workspace, workspace_bytes, stream);
+}
+
 }  // extern "C"
 
 namespace {
 
-fa_status bwd_setup(int B, int H, int N, int d, float scale, fa_dtype dtype, void* workspace,
-                    size_t workspace_bytes, fa::BwdArgs* a) {
+fa_status bwd_setup(int B, int H, int H_kv, int N, int d, float scale, fa_dtype dtype,
+                    void* workspace, size_t workspace_bytes, fa::BwdArgs* a) {
   fa_status st = check_shape(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
+  if (H_kv <= 0 || H % H_kv != 0) return FA_ERR_INVALID_ARGUMENT;
   const size_t need = fa_bwd_workspace_size(B, H, N, d);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
     return FA_ERR_WORKSPACE;
@@ -199,6 +232,7 @@ fa_status bwd_setup(int B, int H, int N, int d, float scale, fa_dtype dtype, voi
   a->H = H;
   a->N = N;
   a->scale = scale;
+  a->G = H / H_kv;
   return FA_OK;
 }
 

@@ -117,8 +117,8 @@ void bwd_dq_kernel(BwdArgs a) {
   const int q0 = qt * C::BR;
   const size_t head = (size_t)(lin / ntq);
   const T* Q = static_cast<const T*>(a.q) + head * N * D;
-  const T* K = static_cast<const T*>(a.k) + head * N * D;
-  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head / a.G * N * D;   // the head's K/V head
+  const T* V = static_cast<const T*>(a.v) + head / a.G * N * D;
   const T* dO = static_cast<const T*>(a.dout) + head * N * D;
   T* dQ = static_cast<T*>(a.dq) + head * N * D;
   const float c = a.scale * kLog2e;
@@ -255,13 +255,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // come first.
   work_item<CAUSAL>(ntk, kt, hd);
   const int k0 = kt * C::BKC;
-  const size_t head = (size_t)hd;
-  const T* Q = static_cast<const T*>(a.q) + head * N * D;
-  const T* K = static_cast<const T*>(a.k) + head * N * D;
-  const T* V = static_cast<const T*>(a.v) + head * N * D;
-  const T* dO = static_cast<const T*>(a.dout) + head * N * D;
-  const float* LSE = a.lse + head * N;
-  const float* Dl = a.delta + head * a.Np;
+  // hd is a K/V head; its query heads hd G .. hd G + G - 1 run one after another.
+  const size_t kvhead = (size_t)hd;
+  const T* K = static_cast<const T*>(a.k) + kvhead * N * D;
+  const T* V = static_cast<const T*>(a.v) + kvhead * N * D;
+  const T *Q = nullptr, *dO = nullptr;
+  const float *LSE = nullptr, *Dl = nullptr;
   const float c = a.scale * kLog2e;
 
   const int kw = k0 + 32 * w;    // first key of this wave
@@ -386,13 +385,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       if (kind == 2) ld_op(qt_ld, j);
     }
   };
-  // The K/V fragments must have landed before the loop, whose waits then cover
-  // only the loads issued inside it.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // One query head of the group: stage its first tiles, then the tile loop.
+  auto use_head = [&](int g) {
+    const size_t head = kvhead * a.G + g;
+    Q = static_cast<const T*>(a.q) + head * N * D;
+    dO = static_cast<const T*>(a.dout) + head * N * D;
+    LSE = a.lse + head * N;
+    Dl = a.delta + head * a.Np;
+    // The K/V fragments must have landed before the loop, whose waits then
+    // cover only the loads issued inside it.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
-  for (int j = 0; j < NLD; ++j) ld_op(qt0, j);
-  stage_all(0, qt0, qt0 + 1);
-  __syncthreads();
+    for (int j = 0; j < NLD; ++j) ld_op(qt0, j);
+    stage_all(0, qt0, qt0 + 1);
+    __syncthreads();
+  };
 
   // One query tile is a fixed stream of NM MFMAs, in issue order:
   //   [0, NS)            S = Q K^T and dP = dO V^T of block 0 (32 queries)
@@ -427,6 +434,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     return load_frag<T>(&base[tr_index<T>(db * 32 + col, qofs)]);
   };
 
+  for (int g = 0; g < a.G; ++g) {
+  use_head(g);
   for (int qt = qt0; qt < nqt; ++qt) {
     const int qi0 = qt * C::BQ;
     const int buf = C::NBUF == 2 ? (qt - qt0) & 1 : 0;
@@ -500,10 +509,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       __syncthreads();
     }
   }
+  }
 
   // Epilogue: lane (col = d, h) holds keys kw + 8(i/4) + 4h + i%4.
-  T* dK = static_cast<T*>(a.dk) + head * N * D;
-  T* dV = static_cast<T*>(a.dv) + head * N * D;
+  T* dK = static_cast<T*>(a.dk) + kvhead * N * D;
+  T* dV = static_cast<T*>(a.dv) + kvhead * N * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -568,8 +578,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   const int q0 = qt * C::BR;
   const size_t head = (size_t)hd;
   const T* Q = static_cast<const T*>(a.q) + head * N * D;
-  const T* K = static_cast<const T*>(a.k) + head * N * D;
-  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head / a.G * N * D;   // the head's K/V head
+  const T* V = static_cast<const T*>(a.v) + head / a.G * N * D;
   const T* dO = static_cast<const T*>(a.dout) + head * N * D;
   T* dQ = static_cast<T*>(a.dq) + head * N * D;
   const float c = a.scale * kLog2e;
@@ -602,7 +612,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   const TileLds<D> lay(lane);
   // Copy op j of key tile kt into buffer b.  NW = 8: waves 0-3 copy K, 4-7
   // copy V, wave w rows 16 (w & 3) + 4 j .. + 3 (d = 128: one 4-row group per
-  // copy) or row 4 j + (w & 3) (d = 64).  NW = 4: wave w copies groups
+  // copy) or row 16 (w & 3) + j (d = 64).  NW = 4: wave w copies groups
   // 4 w + j of K (j < 4) and 4 w + j - 4 of V.  Rows past N read as zero (and
   // are masked through klim).
   const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
@@ -616,8 +626,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
       copy16_to_lds(rsrc, lay.c[(q >> 1) & 1], (uint32_t)(kt * C::BC + 4 * q) * (2 * D),
                     base + q * 4 * C::PB);
     } else {
-      const int rr = 4 * j + (w & 3);
-      copy_to_lds<C::HALF>(rsrc, lay.c[(j >> 1) & 1], (uint32_t)(kt * C::BC + rr) * (2 * D),
+      const int rr = 16 * (w & 3) + j;
+      copy_to_lds<C::HALF>(rsrc, lay.c[(j >> 3) & 1], (uint32_t)(kt * C::BC + rr) * (2 * D),
                            base + rr * C::PB);
     }
   };
@@ -791,13 +801,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // come first.
   work_item<CAUSAL>(ntk, kt, hd);
   const int k0 = kt * C::BKC;
-  const size_t head = (size_t)hd;
-  const T* Q = static_cast<const T*>(a.q) + head * N * D;
-  const T* K = static_cast<const T*>(a.k) + head * N * D;
-  const T* V = static_cast<const T*>(a.v) + head * N * D;
-  const T* dO = static_cast<const T*>(a.dout) + head * N * D;
-  const float* L2 = a.l2 + head * a.Np;
-  const float* Dl = a.delta + head * a.Np;
+  // hd is a K/V head; its query heads hd G .. hd G + G - 1 run one after another.
+  const size_t kvhead = (size_t)hd;
+  const T* K = static_cast<const T*>(a.k) + kvhead * N * D;
+  const T* V = static_cast<const T*>(a.v) + kvhead * N * D;
   const float c = a.scale * kLog2e;
 
   const int kw = k0 + 32 * w;    // first key of this wave
@@ -832,43 +839,61 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   const TileLds<D> lay(lane);
   // Copy op j of tile qt into buffer b: j < NROW: rows of Q (first half of
   // the ops) or dO, wave w taking rows 16 w .. 16 w + 15 (d = 128: 4-row groups
-  // 4 w + jj) or rows 4 jj + w (d = 64); j = NROW, NROW + 1: the tile's L2 and
+  // 4 w + jj; d = 64: row 16 w + jj); j = NROW, NROW + 1: the tile's L2 and
   // D, lane p holding query row_pi(p) of the tile (the order of a lane half's
   // P elements).  Every wave copies the same L2 and D.  Rows past N read as
   // zero (the padding rows of L2 are +inf, so their P is 0; past Np all of Q,
   // dO, L2 and D read as zero, and P dO and P (dP - D) vanish with dO).
-  const i32x4 rsq = buffer_rsrc(Q, (uint32_t)N * (2 * D));
-  const i32x4 rsg = buffer_rsrc(dO, (uint32_t)N * (2 * D));
-  const i32x4 rsl = buffer_rsrc(L2, (uint32_t)a.Np * 4);
-  const i32x4 rsd = buffer_rsrc(Dl, (uint32_t)a.Np * 4);
+  i32x4 rsq, rsg, rsl, rsd;   // Q, dO, L2 and D of the current query head
   constexpr int NROW = C::NLD - 2;
-  auto copy_op = [&](int b, int qt, int j) {
-    const uint32_t base = lds_address(smem) + b * C::BUF;
+  // Copies of one tile into one buffer.  Wave w's rows are 16 w .. 16 w + 15, so
+  // with the per-tile bases below (LDS address of the wave's first row, global
+  // byte offset of that row, LDS address of the buffer, byte offset of the
+  // tile's L2 and D) every copy adds only constants.  The bases pass through an
+  // empty asm so that the compiler computes them per tile instead of keeping one
+  // sum per copy live in scalar registers.
+  struct Bases { uint32_t row_lds, row_glb, buf_lds, ld_glb; };
+  auto bases = [&](int b, int qt) {
+    Bases x{lds_address(smem) + b * C::BUF + 16 * w * C::PB, (uint32_t)(qt * C::BQ + 16 * w) * (2 * D),
+            lds_address(smem) + b * C::BUF, (uint32_t)(qt * C::BQ) * 4};
+    asm volatile("" : "+s"(x.row_lds), "+s"(x.row_glb), "+s"(x.buf_lds), "+s"(x.ld_glb));
+    return x;
+  };
+  auto copy_op = [&](const Bases& x, int j) {
     if (j < NROW) {
       const int mat = j / (NROW / 2), jj = j % (NROW / 2);
       if constexpr (D == 128) {
-        const int q = 4 * w + jj;
-        copy16_to_lds(mat ? rsg : rsq, lay.c[(jj >> 1) & 1], (uint32_t)(qt * C::BQ + 4 * q) * (2 * D),
-                      base + mat * C::TILE + q * 4 * C::PB);
+        // Group 4 w + jj: rows 16 w + 4 jj .. + 3.
+        copy16_to_lds(mat ? rsg : rsq, lay.c[(jj >> 1) & 1], x.row_glb + 4 * jj * (2 * D),
+                      x.row_lds + mat * C::TILE + 4 * jj * C::PB);
       } else {
-        const int rr = 4 * jj + w;
-        copy_to_lds<C::HALF>(mat ? rsg : rsq, lay.c[(jj >> 1) & 1], (uint32_t)(qt * C::BQ + rr) * (2 * D),
-                             base + mat * C::TILE + rr * C::PB);
+        // Row 16 w + jj.
+        copy_to_lds<C::HALF>(mat ? rsg : rsq, lay.c[(jj >> 3) & 1], x.row_glb + jj * (2 * D),
+                             x.row_lds + mat * C::TILE + jj * C::PB);
       }
     } else {
-      copy_to_lds<false>(j == NROW ? rsl : rsd, 4 * row_pi(lane), (uint32_t)(qt * C::BQ) * 4,
-                         base + 2 * C::TILE + (j - NROW) * C::BQ * 4);
+      copy_to_lds<false>(j == NROW ? rsl : rsd, 4 * row_pi(lane), x.ld_glb,
+                         x.buf_lds + 2 * C::TILE + (j - NROW) * C::BQ * 4);
     }
   };
 
-  // Prologue: tiles qt0 and qt0 + 1 into buffers 0 and 1.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // Start query head g of the group: its resources, then tiles qt0 and qt0 + 1
+  // into buffers 0 and 1.
+  auto use_head = [&](int g) {
+    const size_t head = kvhead * a.G + g;
+    rsq = buffer_rsrc(static_cast<const T*>(a.q) + head * N * D, (uint32_t)N * (2 * D));
+    rsg = buffer_rsrc(static_cast<const T*>(a.dout) + head * N * D, (uint32_t)N * (2 * D));
+    rsl = buffer_rsrc(a.l2 + head * a.Np, (uint32_t)a.Np * 4);
+    rsd = buffer_rsrc(a.delta + head * a.Np, (uint32_t)a.Np * 4);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    const Bases x0 = bases(0, qt0), x1 = bases(1, qt0 + 1);
 #pragma unroll
-  for (int j = 0; j < C::NLD; ++j) copy_op(0, qt0, j);
+    for (int j = 0; j < C::NLD; ++j) copy_op(x0, j);
 #pragma unroll
-  for (int j = 0; j < C::NLD; ++j) copy_op(1, qt0 + 1, j);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
+    for (int j = 0; j < C::NLD; ++j) copy_op(x1, j);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  };
 
   // The MFMA stream of one tile: S/dP of blocks 0 and 1 (32 queries each), then
   // dV/dK of blocks 0 and 1; each LDS operand is read PD slots ahead, and the
@@ -935,11 +960,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
       asm volatile("" ::: "memory");   // keeps the two operands' reads apart
       opq[m] = operand(m);
     }
+    const Bases xc = bases(b2, qt + 2);
     static_for<0, NM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
 #pragma unroll
       for (int k = 0; k < C::NLD; ++k)
-        if (m == copy_slot(k)) copy_op(b2, qt + 2, k);
+        if (m == copy_slot(k)) copy_op(xc, k);
       // L2 of 4 queries (one element group), PD slots before first use; D of
       // block 1 well before its first dP MFMA.
 #pragma unroll
@@ -997,15 +1023,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // workgroup and need no mask; a separate loop, with its own register
   // allocation, takes the diagonal tiles before them.
   const int qmask = CAUSAL ? min(nqt, (k0 + C::BKC - 1) / C::BQ + 1) : qt0;
-  int qt = qt0;
-  for (; qt < qmask; ++qt) tile(qt, std::true_type{});
-  for (; qt < nqt; ++qt) tile(qt, std::false_type{});
-  // No copy may still be writing LDS when the workgroup ends.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  for (int g = 0; g < a.G; ++g) {
+    use_head(g);
+    bcur = 0;
+    int qt = qt0;
+    for (; qt < qmask; ++qt) tile(qt, std::true_type{});
+    for (; qt < nqt; ++qt) tile(qt, std::false_type{});
+    // No copy may still be writing LDS when the next head starts or the
+    // workgroup ends, and every wave is done with the buffers.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
 
   // Epilogue: lane (col = d, h) holds keys kw + 8(i/4) + 4h + i%4.
-  T* dK = static_cast<T*>(a.dk) + head * N * D;
-  T* dV = static_cast<T*>(a.dv) + head * N * D;
+  T* dK = static_cast<T*>(a.dk) + kvhead * N * D;
+  T* dV = static_cast<T*>(a.dv) + kvhead * N * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -1030,10 +1062,10 @@ static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, a, rows);
   } else if (step == BwdStep::dkdv) {
     if constexpr (sizeof(T) == 2) {
-      dim3 grid((a.N + Dkv16<D>::BKC - 1) / Dkv16<D>::BKC, a.H, a.B);
+      dim3 grid((a.N + Dkv16<D>::BKC - 1) / Dkv16<D>::BKC, a.H / a.G, a.B);
       hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
     } else {
-      dim3 grid((a.N + DkvTile<T, D>::BKC - 1) / DkvTile<T, D>::BKC, a.H, a.B);
+      dim3 grid((a.N + DkvTile<T, D>::BKC - 1) / DkvTile<T, D>::BKC, a.H / a.G, a.B);
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
     }
   } else if constexpr (sizeof(T) == 2) {

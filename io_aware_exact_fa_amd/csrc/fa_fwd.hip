@@ -103,8 +103,8 @@ void fwd_kernel(FwdArgs a) {
   const int q0 = qt * C::BR;
   const size_t head = (size_t)(lin / ntq);
   const T* Q = static_cast<const T*>(a.q) + head * N * D;
-  const T* K = static_cast<const T*>(a.k) + head * N * D;
-  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head / a.G * N * D;   // the head's K/V head
+  const T* V = static_cast<const T*>(a.v) + head / a.G * N * D;
   T* O = static_cast<T*>(a.o) + head * N * D;
   float* L = a.lse + head * N;
 
@@ -397,8 +397,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   const int q0 = qt * C::BR;
   const size_t head = (size_t)hd;
   const T* Q = static_cast<const T*>(a.q) + head * N * D;
-  const T* K = static_cast<const T*>(a.k) + head * N * D;
-  const T* V = static_cast<const T*>(a.v) + head * N * D;
+  const T* K = static_cast<const T*>(a.k) + head / a.G * N * D;   // the head's K/V head
+  const T* V = static_cast<const T*>(a.v) + head / a.G * N * D;
   T* O = static_cast<T*>(a.o) + head * N * D;
   float* L = a.lse + head * N;
 

@@ -14,8 +14,9 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int B, H, N;
+  int B, H, N;    // H query heads; K and V have H / G heads
   float scale;
+  int G = 1;      // query heads per K/V head
 };
 
 struct BwdArgs {
@@ -33,6 +34,7 @@ struct BwdArgs {
   int B, H, N;
   int Np;         // N rounded up to a multiple of 64
   float scale;
+  int G = 1;      // query heads per K/V head (K, V, dK, dV have H / G heads)
 };
 
 enum class Dt { f32 = 0, f16 = 1, bf16 = 2 };

@@ -9,7 +9,8 @@ the seeded input tensors from ``workloads.py``.
 
 Contents
 --------
-``attention``   the plain definition: S and P materialized, analytic backward.
+``attention``   the plain definition: S and P materialized, analytic backward;
+                also with grouped key/value heads (forward_gqa, backward_gqa).
 ``recurrence``  the online-softmax tile recurrence and the two-tile merge,
                 written in the pages' order; used only to pin that the
                 recurrence is exact, never as the reference for the GPU path.
@@ -20,9 +21,11 @@ differences (``tests/test_oracle.py``).  No function here is parity-unpinned.
 """
 from .attention import (  # noqa: F401
     backward,
+    backward_gqa,
     backward_head,
     causal_visible,
     forward,
+    forward_gqa,
     forward_head,
     probabilities,
     row_softmax,

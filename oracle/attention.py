@@ -134,3 +134,52 @@ def backward(q, k, v, do, scale: float, causal: bool, heads=None):
         g = backward_head(q[idx], k[idx], v[idx], do[idx], scale, causal)
         dq[idx], dk[idx], dv[idx], D[idx] = g["dq"], g["dk"], g["dv"], g["D"]
     return dq, dk, dv, D
+
+
+# ---------------------------------------------------------------- grouped K/V heads
+#
+# Grouped-query attention: the page "Transformer 효율화 기법" (ailab.paldyn.com),
+# section "v1에서 v3까지", names GQA among FlashAttention-2's features but does
+# not define it.  Reading: H query heads share H_kv key/value heads (H_kv
+# divides H); query head h attends with key/value head h // (H // H_kv) of the
+# same batch entry.  Each query head is the plain definition above; the
+# gradient of a shared K or V head is the sum over the query heads that use it
+# (the chain rule through every use).
+
+
+def _group(h_q: int, h_kv: int) -> int:
+    if h_kv <= 0 or h_q % h_kv:
+        raise ValueError(f"{h_q} query heads cannot share {h_kv} key/value heads")
+    return h_q // h_kv
+
+
+def forward_gqa(q, k, v, scale: float, causal: bool):
+    """q [B, H, N, d], k [B, H_kv, N, d], v [B, H_kv, N, dv] -> (O [B, H, N, dv],
+    LSE [B, H, N])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H = q.shape[:2]
+    g = _group(H, k.shape[1])
+    o = np.empty((B, H, q.shape[2], v.shape[-1]))
+    lse = np.empty((B, H, q.shape[2]))
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h // g], v[b, h // g], scale, causal)
+    return o, lse
+
+
+def backward_gqa(q, k, v, do, scale: float, causal: bool):
+    """Gradients of sum(O * dO) for forward_gqa: (dQ [B, H, N, d], dK [B, H_kv, N, d],
+    dV [B, H_kv, N, dv])."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H = q.shape[:2]
+    g = _group(H, k.shape[1])
+    dq = np.empty(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            r = backward_head(q[b, h], k[b, h // g], v[b, h // g], do[b, h], scale, causal)
+            dq[b, h] = r["dq"]
+            dk[b, h // g] += r["dk"]
+            dv[b, h // g] += r["dv"]
+    return dq, dk, dv

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
     for st in range(6):
         assert fa.fa_status_string(st) and fa.fa_status_string(st) != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -119,6 +119,24 @@ def test_split_backward_rejects():
                         None) == fa.FA_ERR_WORKSPACE
 
 
+def test_grouped_kv_rejects():
+    ws, nb = 0x10000, fa.fa_bwd_workspace_size(1, 8, 128, 64)
+    fwd = lambda H, H_kv: fa.fa_fwd_gqa(P, P, P, P, P, 1, H, H_kv, 128, 64, 0, 0.1, fa.FA_F16, None)
+    for H, H_kv in ((8, 0), (8, -2), (8, 3), (8, 16), (6, 4)):
+        assert fwd(H, H_kv) == fa.FA_ERR_INVALID_ARGUMENT, (H, H_kv)
+        assert fa.fa_bwd_gqa(P, P, P, P, P, P, P, P, P, 1, H, H_kv, 128, 64, 0, 0.1, fa.FA_F16,
+                             ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
+        assert fa.fa_bwd_dkdv_gqa(P, P, P, P, P, P, P, 1, H, H_kv, 128, 64, 0, 0.1, fa.FA_F16,
+                                  ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
+        assert fa.fa_bwd_dq_gqa(P, P, P, P, P, P, 1, H, H_kv, 128, 64, 0, 0.1, fa.FA_F16,
+                                ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
+    # The other checks are those of the plain entry points.
+    assert fa.fa_fwd_gqa(P, None, P, P, P, 1, 8, 2, 128, 64, 0, 0.1, fa.FA_F16, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_fwd_gqa(P, P, P, P, P, 1, 8, 2, 128, 96, 0, 0.1, fa.FA_F16, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_gqa(P, P, P, P, P, P, P, P, P, 1, 8, 2, 128, 64, 0, 0.1, fa.FA_F16,
+                         ws, nb - 1, None) == fa.FA_ERR_WORKSPACE
+
+
 def test_workspace_size():
     # Two float32 arrays [B, H, Np], Np = N rounded up to a multiple of 64.
     up = lambda x: (x + 255) // 256 * 256
@@ -138,6 +156,10 @@ def _has_gpu():
 def test_valid_arguments_without_gpu_report_device_error():
     assert _fwd() == fa.FA_ERR_DEVICE
     assert _bwd() == fa.FA_ERR_DEVICE
+    ws, nb = 0x10000, fa.fa_bwd_workspace_size(1, 8, 128, 64)
+    assert fa.fa_fwd_gqa(P, P, P, P, P, 1, 8, 2, 128, 64, 0, 0.1, fa.FA_F16, None) == fa.FA_ERR_DEVICE
+    assert fa.fa_bwd_gqa(P, P, P, P, P, P, P, P, P, 1, 8, 2, 128, 64, 0, 0.1, fa.FA_F16,
+                         ws, nb, None) == fa.FA_ERR_DEVICE
     nb = fa.fa_bwd_workspace_size(1, 1, 128, 64)
     assert fa.fa_bwd_preprocess(P, P, P, 1, 1, 128, 64, fa.FA_F16, 0x10000, nb, None) == fa.FA_ERR_DEVICE
     assert fa.fa_bwd_dq(P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, 0x10000, nb,

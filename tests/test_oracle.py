@@ -225,3 +225,91 @@ def test_batched_wrappers_match_heads():
     o_s, _ = oracle.forward(q, k, v, 0.5, True, heads=[(1, 2)])
     np.testing.assert_array_equal(o_s[1, 2], o[1, 2])
     assert np.isnan(o_s[0, 0]).all()
+
+
+# ----------------------------------------------------------- grouped K/V heads
+
+
+def _gqa_inputs(B=2, H=6, H_kv=2, n=5, d=3, dv=4, seed=11):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((B, H, n, d)), r.standard_normal((B, H_kv, n, d)),
+            r.standard_normal((B, H_kv, n, dv)), r.standard_normal((B, H, n, dv)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_with_one_query_head_per_kv_head_is_plain_attention(causal):
+    q, k, v, do = _gqa_inputs(H=3, H_kv=3)
+    o, lse = oracle.forward_gqa(q, k, v, 0.6, causal)
+    for b in range(2):
+        for h in range(3):
+            o1, l1 = oracle.forward_head(q[b, h], k[b, h], v[b, h], 0.6, causal)
+            np.testing.assert_array_equal(o[b, h], o1)
+            np.testing.assert_array_equal(lse[b, h], l1)
+
+
+def test_gqa_head_mapping():
+    """Key/value head j holds values equal to j + 1 in every entry, so every output
+    row of query head h is exactly 1 + (the K/V head it reads): h // (H / H_kv)."""
+    q, k, _, _ = _gqa_inputs(H=6, H_kv=3)
+    v = np.broadcast_to(np.arange(1.0, 4.0)[None, :, None, None], (2, 3, 5, 4)).copy()
+    o, _ = oracle.forward_gqa(q, k, v, 0.9, False)
+    for h in range(6):
+        np.testing.assert_allclose(o[:, h], 1.0 + h // 2, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_zero_query(causal):
+    """Q = 0: every query head's rows are means of the (visible) rows of its shared V."""
+    _, k, v, _ = _gqa_inputs(H=4, H_kv=2, n=7)
+    o, lse = oracle.forward_gqa(np.zeros((2, 4, 7, 3)), k, v, 0.4, causal)
+    for b in range(2):
+        for h in range(4):
+            for i in range(7):
+                vis = i + 1 if causal else 7
+                np.testing.assert_allclose(o[b, h, i], v[b, h // 2, :vis].mean(axis=0), atol=1e-13)
+                np.testing.assert_allclose(lse[b, h, i], math.log(vis), atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_finite_differences(causal):
+    """Central differences of L = sum(O * dO) with respect to the shared K and V
+    (each element feeds several query heads) and to Q."""
+    q, k, v, do = _gqa_inputs(B=1, H=4, H_kv=2, n=4, d=3, dv=2)
+    scale, hstep = 0.8, 1e-6
+    dq, dk, dv = oracle.backward_gqa(q, k, v, do, scale, causal)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.forward_gqa(qq, kk, vv, scale, causal)
+        return float((o * do).sum())
+
+    for which, (x, g) in enumerate(zip((q, k, v), (dq, dk, dv))):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += hstep
+            xm[idx] -= hstep
+            ap, am = [q, k, v], [q, k, v]
+            ap[which], am[which] = xp, xm
+            fd[idx] = (loss(*ap) - loss(*am)) / (2 * hstep)
+        np.testing.assert_allclose(g, fd, rtol=0, atol=1e-7, err_msg="qkv"[which])
+
+
+def test_gqa_query_head_order_within_a_group():
+    """Swapping two query heads of one group swaps their outputs and dQ and leaves
+    the shared dK, dV unchanged."""
+    q, k, v, do = _gqa_inputs(H=4, H_kv=2)
+    perm = [1, 0, 2, 3]
+    o, _ = oracle.forward_gqa(q, k, v, 0.5, True)
+    o2, _ = oracle.forward_gqa(q[:, perm], k, v, 0.5, True)
+    np.testing.assert_allclose(o2, o[:, perm], atol=1e-14)
+    g = oracle.backward_gqa(q, k, v, do, 0.5, True)
+    g2 = oracle.backward_gqa(q[:, perm], k, v, do[:, perm], 0.5, True)
+    np.testing.assert_allclose(g2[0], g[0][:, perm], atol=1e-13)
+    np.testing.assert_allclose(g2[1], g[1], atol=1e-13)
+    np.testing.assert_allclose(g2[2], g[2], atol=1e-13)
+
+
+def test_gqa_rejects_uneven_groups():
+    q, k, v, _ = _gqa_inputs(H=6, H_kv=4)
+    with pytest.raises(ValueError):
+        oracle.forward_gqa(q, k, v, 0.5, False)

@@ -269,3 +269,79 @@ def test_large_workloads_sampled_heads(fa, w):
     assert (dv - do).abs().max().item() <= tol * scale_dv
     assert dk.abs().max().item() <= tol * scale_dk
     assert torch.isfinite(out["lse"]).all() and torch.isfinite(out["o"]).all()
+
+
+# ------------------------------------------------------------------ grouped K/V heads
+
+
+def compare_gqa(out, inp, causal, scale, dtype, tag="", groups=None):
+    """Compare with the grouped-K/V oracle; ``groups`` restricts the check to a list of
+    (b, kv head) pairs (their query heads and the shared dK, dV)."""
+    tol = TOL[dtype]
+    q, k, v, do = (f64(inp[n]) for n in ("q", "k", "v", "do"))
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    G = H // Hkv
+    if groups is not None:
+        # The oracle on just those groups: one batch entry and K/V head at a time.
+        sel_q = [(b, j * G + g) for b, j in groups for g in range(G)]
+        qi = tuple(np.array(x) for x in zip(*sel_q))
+        ki = tuple(np.array(x) for x in zip(*groups))
+    if groups is None:
+        o_ref, lse_ref = oracle.forward_gqa(q, k, v, scale, causal)
+        err_o = float(np.max(np.abs(f64(out["o"]) - o_ref)))
+        err_l = float(np.max(np.abs(f64(out["lse"]) - lse_ref)))
+        dq_ref, dk_ref, dv_ref = oracle.backward_gqa(q, k, v, do, scale, causal)
+        got = {n: f64(out[n]) for n in ("dq", "dk", "dv")}
+        refs = {"dq": dq_ref, "dk": dk_ref, "dv": dv_ref}
+    else:
+        fw = [oracle.forward_gqa(q[b:b + 1, j * G:(j + 1) * G], k[b:b + 1, j:j + 1],
+                                 v[b:b + 1, j:j + 1], scale, causal) for b, j in groups]
+        bw = [oracle.backward_gqa(q[b:b + 1, j * G:(j + 1) * G], k[b:b + 1, j:j + 1],
+                                  v[b:b + 1, j:j + 1], do[b:b + 1, j * G:(j + 1) * G], scale, causal)
+              for b, j in groups]
+        o_ref = np.concatenate([f[0][0] for f in fw])
+        lse_ref = np.concatenate([f[1][0] for f in fw])
+        err_o = float(np.max(np.abs(f64(out["o"])[qi] - o_ref)))
+        err_l = float(np.max(np.abs(f64(out["lse"])[qi] - lse_ref)))
+        got = {"dq": f64(out["dq"])[qi], "dk": f64(out["dk"])[ki], "dv": f64(out["dv"])[ki]}
+        refs = {"dq": np.concatenate([x[0][0] for x in bw]),
+                "dk": np.concatenate([x[1][0] for x in bw]),
+                "dv": np.concatenate([x[2][0] for x in bw])}
+    say(f"  {tag} O max-abs {err_o:.3e} (tol {tol['o']}), LSE max-abs {err_l:.3e}")
+    assert err_o <= tol["o"], f"O error {err_o}"
+    assert err_l <= tol["lse"], f"LSE error {err_l}"
+    for name in ("dq", "dk", "dv"):
+        e = rel_err(got[name], refs[name])
+        say(f"  {tag} {name} rel-to-max {e:.3e} (tol {tol['grad']})")
+        assert e <= tol["grad"], f"{name} error {e}"
+
+
+def gqa_cases():
+    for dtype in ("bf16", "f16", "f32"):
+        for d in (64, 128):
+            for causal in (False, True):
+                for H, Hkv in ((8, 2), (6, 1)):
+                    yield dtype, d, causal, H, Hkv
+
+
+@pytest.mark.parametrize("dtype,d,causal,H,Hkv", list(gqa_cases()))
+def test_grouped_kv_heads(fa, dtype, d, causal, H, Hkv):
+    """H query heads over Hkv shared K/V heads (Hkv = 1: multi-query), N = 200 (three
+    64-row tiles and a tail of 8), two batch entries."""
+    w = workloads.Workload(f"gqa-{dtype}-d{d}-h{H}kv{Hkv}", 2, H, 200, d, dtype, causal,
+                           seed=41 + H + Hkv + d, H_kv=Hkv)
+    inp = workloads.make_inputs(w)
+    say(f"case {w.name} causal={causal}")
+    compare_gqa(gpu_run(fa, inp, causal, w.scale), inp, causal, w.scale, dtype, tag=w.name)
+
+
+@pytest.mark.parametrize("w", workloads.GQA, ids=lambda w: w.name)
+def test_large_gqa_sampled_groups(fa, w):
+    """The grouped-K/V workloads at full size, in the launch the benchmark times; the
+    oracle on the first and last K/V group."""
+    inp = workloads.make_inputs(w)
+    say(f"case {w.name}")
+    out = gpu_run(fa, inp, w.causal, w.scale)
+    groups = [(0, 0), (w.B - 1, w.kv_heads - 1)]
+    compare_gqa(out, inp, w.causal, w.scale, w.dtype, tag=w.name, groups=groups)

@@ -6,7 +6,8 @@ and the fp64 oracle under ``oracle/`` recomputes it for checking.  Both sides
 receive the very same rounded tensors from here.
 
 Every workload is Q, K, V and an upstream gradient dO, each [B, H, N, d] and
-contiguous with d fastest, plus the softmax scale (1/sqrt(d)).  Draw order for
+contiguous with d fastest (K and V [B, H_kv, N, d] when H_kv key/value heads are
+shared by the H query heads), plus the softmax scale (1/sqrt(d)).  Draw order for
 one workload, from a CPU ``torch.Generator`` seeded with the workload's seed:
 [the per-head offset, only when ``offset`` is set], Q, K, V, dO, all as fp32
 standard normals.  Q and K are then multiplied by ``qk_std``; with ``offset``
@@ -36,6 +37,11 @@ class Workload:
     seed: int
     qk_std: float = 1.0
     offset: bool = False
+    H_kv: int = 0       # key/value heads (0: one per query head)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
 
     @property
     def scale(self) -> float:
@@ -68,17 +74,28 @@ PEAKED_BF16 = Workload("b2h32n8192d128-bf16-offset", 2, 32, 8192, 128, "bf16", F
                        offset=True)
 
 ALL = (SINGLE_HEAD_F32, SHORT_F16, CAUSAL_BF16, LONG_CAUSAL_F16, PEAKED_BF16)
-BY_NAME = {w.name: w for w in ALL}
+
+# Grouped key/value heads (32 query heads over 8 or 4 K/V heads) at the shapes of
+# the two d = 128 workloads above.
+GQA_BF16 = Workload("b2h32kv8n8192d128-bf16-gqa", 2, 32, 8192, 128, "bf16", False, 1006, H_kv=8)
+GQA_CAUSAL_BF16 = Workload("b4h32kv4n4096d128-bf16-causal-gqa", 4, 32, 4096, 128, "bf16", True,
+                           1007, H_kv=4)
+GQA = (GQA_BF16, GQA_CAUSAL_BF16)
+
+BY_NAME = {w.name: w for w in ALL + GQA}
 
 
 def make_inputs(w: Workload) -> dict:
     """Return {"q","k","v","do"} as contiguous CPU tensors in the workload dtype."""
     g = torch.Generator(device="cpu").manual_seed(w.seed)
     shape = (w.B, w.H, w.N, w.d)
+    kv_shape = (w.B, w.kv_heads, w.N, w.d)
+    if w.offset and w.kv_heads != w.H:
+        raise ValueError("the per-head offset is defined for one K/V head per query head")
     c = torch.randn((w.H, w.d), generator=g, dtype=torch.float32) if w.offset else None
     q = torch.randn(shape, generator=g, dtype=torch.float32)
-    k = torch.randn(shape, generator=g, dtype=torch.float32)
-    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(kv_shape, generator=g, dtype=torch.float32)
+    v = torch.randn(kv_shape, generator=g, dtype=torch.float32)
     do = torch.randn(shape, generator=g, dtype=torch.float32)
     if w.qk_std != 1.0:
         q.mul_(w.qk_std)
