@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=sorted(workloads.BY_NAME) + sorted(workloads.VARLEN_BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="step", choices=["step", "copy"])
     return ap.parse_args()
@@ -164,6 +165,9 @@ def main():
         copy_calibration(args.steps)
         return
 
+    if args.workload in workloads.VARLEN_BY_NAME:
+        bench_varlen(args, workloads.VARLEN_BY_NAME[args.workload])
+        return
     w = workloads.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     inp = workloads.make_inputs(w)
@@ -267,6 +271,154 @@ def main():
     if not args.no_cpu_baseline:
         gpu_out = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
         out["cpu_baseline"] = cpu_baseline(w, inp, gpu_out)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_varlen(w, inp, gpu_out, budget_s: float = 10.0):
+    """The fp64 oracle on whole sequences (all heads), shortest first, until about
+    ``budget_s`` seconds of CPU work; GPU-vs-oracle error on the first one."""
+    import numpy as np
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    cu = inp["cu_seqlens"].tolist()
+    order = sorted((b for b in range(w.B) if w.lens[b] > 0), key=lambda b: w.lens[b])
+    f64 = lambda t: t.to(dtype=torch.float64).numpy()
+    q, k, v, do = (f64(inp[n]) for n in ("q", "k", "v", "do"))
+    secs, flops, done, check = 0.0, 0.0, 0, None
+    for b in order:
+        s0, s1 = cu[b], cu[b + 1]
+        n = s1 - s0
+        one = [0, n]   # the sequence alone, as a packed batch of one
+        t0 = time.perf_counter()
+        o, lse = oracle.forward_varlen(q[:, s0:s1], k[:, s0:s1], v[:, s0:s1], one, n, w.scale,
+                                       w.causal)
+        dq, dk, dv = oracle.backward_varlen(q[:, s0:s1], k[:, s0:s1], v[:, s0:s1], do[:, s0:s1],
+                                            one, n, w.scale, w.causal)
+        secs += time.perf_counter() - t0
+        flops += 3.5 * 4.0 * w.H * n * n * w.d / (2 if w.causal else 1)
+        done += 1
+        if check is None:
+            rel = lambda a, r: float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-30))
+            check = {
+                "sequence": b, "length": n,
+                "o_maxabs": float(np.max(np.abs(f64(gpu_out["o"][:, s0:s1]) - o))),
+                "lse_maxabs": float(np.max(np.abs(f64(gpu_out["lse"][b, :, :n]) - lse[0]))),
+                "dq_rel": rel(f64(gpu_out["dq"][:, s0:s1]), dq),
+                "dk_rel": rel(f64(gpu_out["dk"][:, s0:s1]), dk),
+                "dv_rel": rel(f64(gpu_out["dv"][:, s0:s1]), dv),
+            }
+        if secs >= budget_s:
+            break
+    return {
+        "value": flops / secs / 1e12,
+        "unit": "TFLOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B} sequences (shortest first), all {w.H} query heads, forward + "
+                  f"backward, fp64 numpy oracle; {secs:.2f} s wall",
+        "seconds": round(secs, 3),
+        "parity_on_sample": check,
+    }
+
+
+def bench_varlen(args, w):
+    """A packed variable-length batch: fa_fwd_varlen then fa_bwd_varlen per step."""
+    import torch
+    import io_aware_exact_fa_amd as fa
+    dev = torch.device("cuda:0")
+    inp = workloads.make_varlen_inputs(w)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    cu = inp["cu_seqlens"].to(dev)
+    H, total, d = q.shape
+    Hkv = k.shape[0]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, H, w.max_s), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+    ws = fa.workspace(w.B, H, w.max_s, d, dev)
+    code = fa.dtype_code(q.dtype)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    P = lambda t: t.data_ptr()
+
+    def check(st, where):
+        if st != fa.FA_OK:
+            raise fa.FaError(st, where)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        check(fa.fa_fwd_varlen(P(q), P(k), P(v), P(o), P(lse), P(cu), w.B, w.max_s, total, H, Hkv,
+                               d, w.causal, w.scale, code, sh), "fwd_varlen")
+        if ev is not None:
+            ev[1].record(stream)
+        check(fa.fa_bwd_varlen(P(q), P(k), P(v), P(o), P(do), P(lse), P(dq), P(dk), P(dv), P(cu),
+                               w.B, w.max_s, total, H, Hkv, d, w.causal, w.scale, code, P(ws),
+                               ws.numel(), sh), "bwd_varlen")
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = lambda a, b_: sum(e[a].elapsed_time(e[b_]) for e in events) / args.steps
+    fwd_ms, bwd_ms = ms(0, 1), ms(1, 2)
+    ms_per_step = wall * 1e3 / args.steps
+    fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
+    peak = PEAK_TFLOPS[w.dtype]
+    value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = fwd_f / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal Q/K/V/dO, packed sequences of the workload's lengths)",
+        "config": {
+            "workload": w.name, "B": w.B, "H": H, "H_kv": Hkv, "total": total, "max_s": w.max_s,
+            "d": d, "causal": w.causal, "lens": list(w.lens),
+            "step": "fa_fwd_varlen + fa_bwd_varlen",
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
+            "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),
+            "bwd_pct_of_peak": round(100 * bwd_tf / peak, 2),
+            "step_pct_of_peak": round(100 * value / peak, 2),
+            "peak_tflops": peak,
+        },
+        # The backward call (three launches) timed as one, at the method's FLOP count.
+        "roofline": {
+            "kernel": "fa_bwd_varlen (preprocess, dK/dV, dQ)",
+            "bound": "mfma",
+            "achieved": round(bwd_tf, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(bwd_tf / peak, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        gpu_out = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+        out["cpu_baseline"] = cpu_baseline_varlen(w, inp, gpu_out)
     print(json.dumps(out), flush=True)
 
 

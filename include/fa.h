@@ -39,8 +39,8 @@
  *    before any HIP call; on an argument error nothing is launched and no
  *    output is touched.  Checks: null pointers, B/H/N <= 0, element counts
  *    that overflow 64 bits, non-finite scale (FA_ERR_INVALID_ARGUMENT);
- *    unknown dtype, d outside {64, 128}, B or H above 65535, N above 2^23 or
- *    B*H*N above 2^34 (FA_ERR_UNSUPPORTED); workspace
+ *    unknown dtype, d outside {64, 128}, B or H above 65535, B*H above 2^24,
+ *    N above 2^23 or B*H*N above 2^34 (FA_ERR_UNSUPPORTED); workspace
  *    too small or not 256-byte aligned (FA_ERR_WORKSPACE); the current HIP
  *    device is not gfx950 or cannot be queried (FA_ERR_DEVICE); a launch
  *    reported an error (FA_ERR_LAUNCH, outputs then undefined).
@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -194,6 +194,47 @@ fa_status fa_bwd_dkdv_gqa(const void* q, const void* k, const void* v, const voi
 fa_status fa_bwd_dq_gqa(const void* q, const void* k, const void* v, const void* dout,
                         const float* lse, void* dq,
                         int B, int H, int H_kv, int N, int d, int causal, float scale,
+                        fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * Padding-free variable-length batches.  The 2022 interface described on
+ * "FlashAttention 원 논문 해부" (section "내부 구조와 실제 실행 흐름", items 2 and 3)
+ * drops padding tokens, packs the valid tokens of all sequences one after
+ * another and passes cu_seqlens, the cumulative token offsets, and max_s, the
+ * longest length, keeping the softmax statistics per (batch, head, max_s).
+ * Sequence b owns the packed rows cu_seqlens[b] <= t < cu_seqlens[b + 1] and
+ * attends to its own tokens only (under the causal mask, key j is visible to
+ * query i of the same sequence iff j <= i, counted from the sequence's first
+ * token).
+ *
+ *  - q, o, dout, dq: [H, total, d]; k, v, dk, dv: [H_kv, total, d] (dtype, d
+ *    fastest, 16-byte aligned): one packed slab per head, so that every
+ *    (sequence, head) pair is one contiguous block of rows.  Callers holding
+ *    [total, H, d] transpose once.  Grouped heads as for the _gqa entry points.
+ *  - cu_seqlens: DEVICE pointer to B + 1 int32 offsets, cu_seqlens[0] = 0,
+ *    non-decreasing, every length at most max_s, cu_seqlens[B] <= total.
+ *    Read by the kernels, so it cannot be checked before the launch: offsets
+ *    outside [0, total] are clamped and lengths cut to max_s, which keeps every
+ *    access inside the tensors, but the results are then unspecified.
+ *  - lse: [B, H, max_s] float32; entries past a sequence's length are not
+ *    written.  Rows of o, dq, dk, dv outside every sequence are not written.
+ *  - Empty sequences are allowed (nothing is written for them).
+ *  - Workspace: fa_bwd_workspace_size(B, H, max_s, d), same layout as the
+ *    dense backward with N = max_s, rewritten by every call.
+ *  - Errors as for the dense entry points with N = max_s; in addition
+ *    cu_seqlens == NULL or total <= 0 is FA_ERR_INVALID_ARGUMENT.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens, int B, int max_s, int total,
+                        int H, int H_kv, int d, int causal, float scale,
+                        fa_dtype dtype, void* stream);
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse,
+                        void* dq, void* dk, void* dv,
+                        const int* cu_seqlens, int B, int max_s, int total,
+                        int H, int H_kv, int d, int causal, float scale,
                         fa_dtype dtype, void* workspace, size_t workspace_bytes,
                         void* stream);
 

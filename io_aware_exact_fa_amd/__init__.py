@@ -10,7 +10,8 @@ Two layers:
     / ``fa_abi_version``: the C entry points with the same names and the same
     arguments (device pointers as Python ints, sizes, dtype code, stream
     handle); they return the status code.
-  * ``forward`` / ``backward``: torch tensors in, torch tensors out; they
+  * ``forward`` / ``backward`` (and ``forward_varlen`` / ``backward_varlen``
+    for packed variable-length batches): torch tensors in, torch tensors out; they
     check shapes, allocate outputs (and the backward workspace) with torch
     and raise ``FaError`` on a non-zero status.
 """
@@ -35,7 +36,7 @@ FA_BF16 = 2
 
 EXPORTED = ("fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
             "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
-            "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa")
+            "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa", "fa_fwd_varlen", "fa_bwd_varlen")
 
 
 class FaError(RuntimeError):
@@ -81,6 +82,11 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_dkdv_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_dq_gqa.restype = i
     lib.fa_bwd_dq_gqa.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_fwd_varlen.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_varlen.restype = i
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
+                                  i, vp, sz, vp]
     return lib
 
 
@@ -160,6 +166,19 @@ def fa_bwd_dq_gqa(q, k, v, dout, lse, dq, B, H, H_kv, N, d, causal, scale, dtype
                   workspace, workspace_bytes, stream) -> int:
     return _lib.fa_bwd_dq_gqa(q, k, v, dout, lse, dq, B, H, H_kv, N, d, int(causal), float(scale),
                               int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, max_s, total, H, H_kv, d, causal, scale, dtype,
+                  stream) -> int:
+    return _lib.fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, max_s, total, H, H_kv, d,
+                              int(causal), float(scale), int(dtype), stream)
+
+
+def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, B, max_s, total, H, H_kv, d,
+                  causal, scale, dtype, workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, B, max_s, total, H,
+                              H_kv, d, int(causal), float(scale), int(dtype), workspace,
+                              workspace_bytes, stream)
 
 
 # ------------------------------------------------------------------ torch helpers
@@ -242,4 +261,66 @@ def backward(q, k, v, o, dout, lse, causal: bool, scale: float, dq=None, dk=None
                     _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_gqa")
+    return dq, dk, dv
+
+
+def _check_cu(cu_seqlens, device):
+    import torch
+    if (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2
+            or not cu_seqlens.is_contiguous() or cu_seqlens.device != device):
+        raise ValueError("cu_seqlens: expected a contiguous 1-D int32 tensor of B + 1 offsets on "
+                         f"{device}, got {cu_seqlens.dtype} {tuple(cu_seqlens.shape)} on "
+                         f"{cu_seqlens.device}")
+    return cu_seqlens.numel() - 1
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_s: int, causal: bool, scale: float, o=None, lse=None,
+                   stream=None):
+    """O [H, total, d], LSE [B, H, max_s] for packed q [H, total, d], k, v
+    [H_kv, total, d] and device int32 cu_seqlens [B + 1] (offsets are read on the
+    device, not checked here)."""
+    import torch
+    H, total, d = q.shape
+    H_kv = k.shape[0]
+    B = _check_cu(cu_seqlens, q.device)
+    _check("q", q, (H, total, d), q.dtype)
+    _check("k", k, (H_kv, total, d), q.dtype)
+    _check("v", v, (H_kv, total, d), q.dtype)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, max_s), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check("o", o, (H, total, d), q.dtype)
+    _check("lse", lse, (B, H, max_s), torch.float32)
+    st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       cu_seqlens.data_ptr(), B, max_s, total, H, H_kv, d, causal, scale,
+                       dtype_code(q.dtype), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_varlen")
+    return o, lse
+
+
+def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_s: int, causal: bool, scale: float,
+                    dq=None, dk=None, dv=None, ws=None, stream=None):
+    """dQ, dK, dV for the packed forward that produced o and lse."""
+    import torch
+    H, total, d = q.shape
+    H_kv = k.shape[0]
+    B = _check_cu(cu_seqlens, q.device)
+    for name, t in (("q", q), ("o", o), ("dout", dout)):
+        _check(name, t, (H, total, d), q.dtype)
+    for name, t in (("k", k), ("v", v)):
+        _check(name, t, (H_kv, total, d), q.dtype)
+    _check("lse", lse, (B, H, max_s), torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    _check("dq", dq, (H, total, d), q.dtype)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check(name, t, (H_kv, total, d), q.dtype)
+    ws = workspace(B, H, max_s, d, q.device) if ws is None else ws
+    st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       cu_seqlens.data_ptr(), B, max_s, total, H, H_kv, d, causal, scale,
+                       dtype_code(q.dtype), ws.data_ptr(), ws.numel(), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_varlen")
     return dq, dk, dv

@@ -17,6 +17,7 @@ constexpr int kMaxGridYZ = 65535;   // grid y (heads) and z (batch) limit
 constexpr int kMaxDevices = 64;
 constexpr int kMaxN = (1 << 23);   // keeps byte offsets inside one head matrix below 2^32
 constexpr uint64_t kMaxRows = (uint64_t)1 << 34;  // keeps 1-D row grids below 2^31 blocks
+constexpr uint64_t kMaxHeads = (uint64_t)1 << 24;  // B*H: with kMaxRows keeps tile grids below 2^31
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Rows per head of the workspace arrays: N rounded up to whole 64-row tiles.
@@ -38,6 +39,20 @@ fa_status check_shape(int B, int H, int N, int d, float scale, fa_dtype dtype) {
   if (B > kMaxGridYZ || H > kMaxGridYZ) return FA_ERR_UNSUPPORTED;
   if (N > kMaxN) return FA_ERR_UNSUPPORTED;
   if ((uint64_t)B * H * N > kMaxRows) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)B * H > kMaxHeads) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// Packed variable-length batch: B sequences of at most max_s tokens, `total`
+// rows per head.  The per-(sequence, head) limits are those of the dense shape
+// [B, H, max_s]; in addition the packed tensors must be addressable.
+fa_status check_varlen(const int* cu_seqlens, int B, int max_s, int total, int H, int H_kv, int d,
+                       float scale, fa_dtype dtype) {
+  if (!cu_seqlens || total <= 0) return FA_ERR_INVALID_ARGUMENT;
+  fa_status st = check_shape(B, H, max_s, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (H_kv <= 0 || H % H_kv != 0) return FA_ERR_INVALID_ARGUMENT;
+  if (elements(1, H, total, d) == 0) return FA_ERR_INVALID_ARGUMENT;
   return FA_OK;
 }
 
@@ -68,6 +83,10 @@ fa_status launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNC
 // Shared checks of the backward entry points, then the workspace split.
 fa_status bwd_setup(int B, int H, int H_kv, int N, int d, float scale, fa_dtype dtype,
                     void* workspace, size_t workspace_bytes, fa::BwdArgs* a);
+// Sets the tensor pointers and enqueues preprocess, dK/dV and dQ.
+fa_status bwd_all(fa::BwdArgs& a, const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv, int d,
+                  int causal, fa_dtype dtype, void* stream);
 
 }  // namespace
 
@@ -104,6 +123,21 @@ fa_status fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, int causal, float scale, fa_dtype dtype, void* stream) {
   return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens, int B, int max_s, int total, int H, int H_kv,
+                        int d, int causal, float scale, fa_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
+  fa_status st = check_varlen(cu_seqlens, B, max_s, total, H, H_kv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, max_s, scale};
+  a.G = H / H_kv;
+  a.cu_seqlens = cu_seqlens;
+  a.total = total;
+  return launched(fa::launch_fwd(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream));
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
@@ -185,23 +219,25 @@ fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
   fa::BwdArgs a{};
   fa_status st = bwd_setup(B, H, H_kv, N, d, scale, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.dout = dout;
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  const fa::Dt dt = to_dt(dtype);
-  hipStream_t s = (hipStream_t)stream;
-  st = launched(fa::launch_bwd_pre(dt, d, a, s));
-  if (st != FA_OK) return st;
-  st = launched(fa::launch_bwd_dkdv(dt, d, causal != 0, a, s));
-  if (st != FA_OK) return st;
-  return launched(fa::launch_bwd_dq(dt, d, causal != 0, a, s));
+  return bwd_all(a, q, k, v, o, dout, lse, dq, dk, dv, d, causal, dtype, stream);
 }
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        const int* cu_seqlens, int B, int max_s, int total, int H, int H_kv,
+                        int d, int causal, float scale, fa_dtype dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
+  fa_status st = check_varlen(cu_seqlens, B, max_s, total, H, H_kv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  fa::BwdArgs a{};
+  st = bwd_setup(B, H, H_kv, max_s, d, scale, dtype, workspace, workspace_bytes, &a);
+  if (st != FA_OK) return st;
+  a.cu_seqlens = cu_seqlens;
+  a.total = total;
+  return bwd_all(a, q, k, v, o, dout, lse, dq, dk, dv, d, causal, dtype, stream);
+}
+
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
@@ -234,6 +270,28 @@ fa_status bwd_setup(int B, int H, int H_kv, int N, int d, float scale, fa_dtype 
   a->scale = scale;
   a->G = H / H_kv;
   return FA_OK;
+}
+
+fa_status bwd_all(fa::BwdArgs& a, const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv, int d,
+                  int causal, fa_dtype dtype, void* stream) {
+  fa_status st;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const fa::Dt dt = to_dt(dtype);
+  hipStream_t s = (hipStream_t)stream;
+  st = launched(fa::launch_bwd_pre(dt, d, a, s));
+  if (st != FA_OK) return st;
+  st = launched(fa::launch_bwd_dkdv(dt, d, causal != 0, a, s));
+  if (st != FA_OK) return st;
+  return launched(fa::launch_bwd_dq(dt, d, causal != 0, a, s));
 }
 
 }  // namespace

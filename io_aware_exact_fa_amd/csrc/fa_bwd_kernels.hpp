@@ -54,11 +54,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long rows) {
   const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
   const long head = row / a.Np;
   const int q = (int)(row - head * a.Np);
-  const bool live = row < rows && q < a.N;
-  const size_t src = (size_t)head * a.N + q;
+  const Span sp = row < rows ? span_of(a, (int)head) : Span{0, 0, 0, 0};
+  const bool live = q < sp.n;
   float part = 0.f;
   if (live) {
-    const size_t off = src * D + sub * E16;
+    const size_t off = (sp.q + q) * D + sub * E16;
     const T* o = static_cast<const T*>(a.o) + off;
     const T* g = static_cast<const T*>(a.dout) + off;
 #pragma unroll
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long rows) {
   if (row < rows && sub == 0) {
     float l2 = INFINITY;   // P = exp2(-inf) = 0 on padding rows and rows that see no key
     if (live) {
-      const float lse = a.lse[src];
+      const float lse = a.lse[(size_t)head * a.N + q];
       if (lse != -INFINITY) l2 = lse * kLog2e;
     }
     a.delta[row] = part;
@@ -110,17 +110,20 @@ void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, col = lane & 31, h = lane >> 5;
-  const int N = a.N;
   const int ntq = gridDim.x;
   const int lin = xcd_work_index();
-  const int qt = CAUSAL ? ntq - 1 - (lin % ntq) : (lin % ntq);
+  const size_t head = (size_t)packed_head(a, lin / ntq, a.H);
+  const Span sp = span_of(a, (int)head);
+  const int N = sp.n;
+  const int ntq_own = (N + C::BR - 1) / C::BR;
+  const int qt = CAUSAL ? ntq_own - 1 - (lin % ntq) : (lin % ntq);
+  if (qt < 0 || qt >= ntq_own) return;   // a tile past the end of a shorter sequence
   const int q0 = qt * C::BR;
-  const size_t head = (size_t)(lin / ntq);
-  const T* Q = static_cast<const T*>(a.q) + head * N * D;
-  const T* K = static_cast<const T*>(a.k) + head / a.G * N * D;   // the head's K/V head
-  const T* V = static_cast<const T*>(a.v) + head / a.G * N * D;
-  const T* dO = static_cast<const T*>(a.dout) + head * N * D;
-  T* dQ = static_cast<T*>(a.dq) + head * N * D;
+  const T* Q = static_cast<const T*>(a.q) + sp.q * D;
+  const T* K = static_cast<const T*>(a.k) + sp.kv * D;   // the head's K/V head
+  const T* V = static_cast<const T*>(a.v) + sp.kv * D;
+  const T* dO = static_cast<const T*>(a.dout) + sp.q * D;
+  T* dQ = static_cast<T*>(a.dq) + sp.q * D;
   const float c = a.scale * kLog2e;
 
   const int qw = q0 + 32 * w;
@@ -135,7 +138,7 @@ void bwd_dq_kernel(BwdArgs a) {
   }
   // Row statistics of this lane's query.  A row with no visible key (LSE = -inf)
   // has P = 0: use +inf as its log2-domain LSE.
-  const float lse = a.lse[head * N + qrow];
+  const float lse = a.lse[head * a.N + qrow];
   const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
   const float dl = a.delta[head * a.Np + qrow];
 
@@ -248,17 +251,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, col = lane & 31, h = lane >> 5;
-  const int N = a.N;
   const int ntk = gridDim.x;
   int kt, hd;
   // Under the causal mask the key tiles near the start see the most queries and
   // come first.
   work_item<CAUSAL>(ntk, kt, hd);
+  hd = packed_head(a, hd, a.H / a.G);
   const int k0 = kt * C::BKC;
   // hd is a K/V head; its query heads hd G .. hd G + G - 1 run one after another.
   const size_t kvhead = (size_t)hd;
-  const T* K = static_cast<const T*>(a.k) + kvhead * N * D;
-  const T* V = static_cast<const T*>(a.v) + kvhead * N * D;
+  const Span sp = span_of(a, hd * a.G);
+  const int N = sp.n;
+  if (k0 >= N) return;   // a tile past the end of a shorter sequence
+  const T* K = static_cast<const T*>(a.k) + sp.kv * D;
+  const T* V = static_cast<const T*>(a.v) + sp.kv * D;
   const T *Q = nullptr, *dO = nullptr;
   const float *LSE = nullptr, *Dl = nullptr;
   const float c = a.scale * kLog2e;
@@ -388,9 +394,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // One query head of the group: stage its first tiles, then the tile loop.
   auto use_head = [&](int g) {
     const size_t head = kvhead * a.G + g;
-    Q = static_cast<const T*>(a.q) + head * N * D;
-    dO = static_cast<const T*>(a.dout) + head * N * D;
-    LSE = a.lse + head * N;
+    Q = static_cast<const T*>(a.q) + (sp.q + g * sp.hs) * D;
+    dO = static_cast<const T*>(a.dout) + (sp.q + g * sp.hs) * D;
+    LSE = a.lse + head * a.N;
     Dl = a.delta + head * a.Np;
     // The K/V fragments must have landed before the loop, whose waits then
     // cover only the loads issued inside it.
@@ -512,8 +518,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // Epilogue: lane (col = d, h) holds keys kw + 8(i/4) + 4h + i%4.
-  T* dK = static_cast<T*>(a.dk) + kvhead * N * D;
-  T* dV = static_cast<T*>(a.dv) + kvhead * N * D;
+  T* dK = static_cast<T*>(a.dk) + sp.kv * D;
+  T* dV = static_cast<T*>(a.dv) + sp.kv * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -569,19 +575,24 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int N = a.N;
   const int ntq = gridDim.x;
   int rank, hd;
   work_item<CAUSAL>(ntq, rank, hd);
-  // Under the causal mask the last query tiles see the most keys: start them first.
-  const int qt = CAUSAL ? ntq - 1 - rank : rank;
-  const int q0 = qt * C::BR;
+  hd = packed_head(a, hd, a.H);
   const size_t head = (size_t)hd;
-  const T* Q = static_cast<const T*>(a.q) + head * N * D;
-  const T* K = static_cast<const T*>(a.k) + head / a.G * N * D;   // the head's K/V head
-  const T* V = static_cast<const T*>(a.v) + head / a.G * N * D;
-  const T* dO = static_cast<const T*>(a.dout) + head * N * D;
-  T* dQ = static_cast<T*>(a.dq) + head * N * D;
+  const Span sp = span_of(a, hd);
+  const int N = sp.n;
+  // Under the causal mask the last query tiles see the most keys: start them
+  // first (counted in this sequence's tiles).
+  const int ntq_own = (N + C::BR - 1) / C::BR;
+  const int qt = CAUSAL ? ntq_own - 1 - rank : rank;
+  if (qt < 0 || qt >= ntq_own) return;   // a tile past the end of a shorter sequence
+  const int q0 = qt * C::BR;
+  const T* Q = static_cast<const T*>(a.q) + sp.q * D;
+  const T* K = static_cast<const T*>(a.k) + sp.kv * D;   // the head's K/V head
+  const T* V = static_cast<const T*>(a.v) + sp.kv * D;
+  const T* dO = static_cast<const T*>(a.dout) + sp.q * D;
+  T* dQ = static_cast<T*>(a.dq) + sp.q * D;
   const float c = a.scale * kLog2e;
 
   const int qw = q0 + 32 * w;
@@ -794,17 +805,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int N = a.N;
   const int ntk = gridDim.x;
   int kt, hd;
   // Under the causal mask the key tiles near the start see the most queries and
   // come first.
   work_item<CAUSAL>(ntk, kt, hd);
+  hd = packed_head(a, hd, a.H / a.G);
   const int k0 = kt * C::BKC;
   // hd is a K/V head; its query heads hd G .. hd G + G - 1 run one after another.
   const size_t kvhead = (size_t)hd;
-  const T* K = static_cast<const T*>(a.k) + kvhead * N * D;
-  const T* V = static_cast<const T*>(a.v) + kvhead * N * D;
+  const Span sp = span_of(a, hd * a.G);
+  const int N = sp.n;
+  if (k0 >= N) return;   // a tile past the end of a shorter sequence
+  const T* K = static_cast<const T*>(a.k) + sp.kv * D;
+  const T* V = static_cast<const T*>(a.v) + sp.kv * D;
   const float c = a.scale * kLog2e;
 
   const int kw = k0 + 32 * w;    // first key of this wave
@@ -881,8 +895,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // into buffers 0 and 1.
   auto use_head = [&](int g) {
     const size_t head = kvhead * a.G + g;
-    rsq = buffer_rsrc(static_cast<const T*>(a.q) + head * N * D, (uint32_t)N * (2 * D));
-    rsg = buffer_rsrc(static_cast<const T*>(a.dout) + head * N * D, (uint32_t)N * (2 * D));
+    rsq = buffer_rsrc(static_cast<const T*>(a.q) + (sp.q + g * sp.hs) * D, (uint32_t)N * (2 * D));
+    rsg = buffer_rsrc(static_cast<const T*>(a.dout) + (sp.q + g * sp.hs) * D, (uint32_t)N * (2 * D));
     rsl = buffer_rsrc(a.l2 + head * a.Np, (uint32_t)a.Np * 4);
     rsd = buffer_rsrc(a.delta + head * a.Np, (uint32_t)a.Np * 4);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -1036,8 +1050,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   }
 
   // Epilogue: lane (col = d, h) holds keys kw + 8(i/4) + 4h + i%4.
-  T* dK = static_cast<T*>(a.dk) + kvhead * N * D;
-  T* dV = static_cast<T*>(a.dv) + kvhead * N * D;
+  T* dK = static_cast<T*>(a.dk) + sp.kv * D;
+  T* dV = static_cast<T*>(a.dv) + sp.kv * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll

@@ -89,7 +89,6 @@ void fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, col = lane & 31, h = lane >> 5;
-  const int N = a.N;
 
   // Workgroup -> (head, query tile).  Workgroups are dealt to the 8 XCDs
   // round-robin by linear id; give each XCD a contiguous range of (head, tile)
@@ -99,14 +98,19 @@ void fwd_kernel(FwdArgs a) {
   const int nwork = ntq * gridDim.y * gridDim.z;
   int lin = blockIdx.x + ntq * (blockIdx.y + gridDim.y * blockIdx.z);
   if ((nwork & 7) == 0) lin = (lin & 7) * (nwork >> 3) + (lin >> 3);
-  const int qt = CAUSAL ? ntq - 1 - (lin % ntq) : (lin % ntq);
+  const size_t head = (size_t)packed_head(a, lin / ntq, a.H);
+  const Span sp = span_of(a, (int)head);
+  const int N = sp.n;
+  // Causal: the tile with the most keys first (counted in this sequence's tiles).
+  const int ntq_own = (N + C::BR - 1) / C::BR;
+  const int qt = CAUSAL ? ntq_own - 1 - (lin % ntq) : (lin % ntq);
+  if (qt < 0 || qt >= ntq_own) return;   // a tile past the end of a shorter sequence
   const int q0 = qt * C::BR;
-  const size_t head = (size_t)(lin / ntq);
-  const T* Q = static_cast<const T*>(a.q) + head * N * D;
-  const T* K = static_cast<const T*>(a.k) + head / a.G * N * D;   // the head's K/V head
-  const T* V = static_cast<const T*>(a.v) + head / a.G * N * D;
-  T* O = static_cast<T*>(a.o) + head * N * D;
-  float* L = a.lse + head * N;
+  const T* Q = static_cast<const T*>(a.q) + sp.q * D;
+  const T* K = static_cast<const T*>(a.k) + sp.kv * D;   // the head's K/V head
+  const T* V = static_cast<const T*>(a.v) + sp.kv * D;
+  T* O = static_cast<T*>(a.o) + sp.q * D;
+  float* L = a.lse + head * a.N;
 
   const int qw = q0 + 32 * w;   // first query row of this wave
   const int myq = qw + col;     // the query row of this lane
@@ -389,18 +393,23 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int N = a.N;
   const int ntq = gridDim.x;
   int rank, hd;
-  work_item<CAUSAL>(ntq, rank, hd);   // causal: the last query tiles (most keys) first
-  const int qt = CAUSAL ? ntq - 1 - rank : rank;
-  const int q0 = qt * C::BR;
+  work_item<CAUSAL>(ntq, rank, hd);
+  hd = packed_head(a, hd, a.H);
   const size_t head = (size_t)hd;
-  const T* Q = static_cast<const T*>(a.q) + head * N * D;
-  const T* K = static_cast<const T*>(a.k) + head / a.G * N * D;   // the head's K/V head
-  const T* V = static_cast<const T*>(a.v) + head / a.G * N * D;
-  T* O = static_cast<T*>(a.o) + head * N * D;
-  float* L = a.lse + head * N;
+  const Span sp = span_of(a, hd);
+  const int N = sp.n;
+  // Causal: the last query tiles (most keys) first, counted in this sequence's tiles.
+  const int ntq_own = (N + C::BR - 1) / C::BR;
+  const int qt = CAUSAL ? ntq_own - 1 - rank : rank;
+  if (qt < 0 || qt >= ntq_own) return;   // a tile past the end of a shorter sequence
+  const int q0 = qt * C::BR;
+  const T* Q = static_cast<const T*>(a.q) + sp.q * D;
+  const T* K = static_cast<const T*>(a.k) + sp.kv * D;   // the head's K/V head
+  const T* V = static_cast<const T*>(a.v) + sp.kv * D;
+  T* O = static_cast<T*>(a.o) + sp.q * D;
+  float* L = a.lse + head * a.N;
 
   const int qw = q0 + 32 * w;
   const int myq = qw + col;

@@ -17,6 +17,11 @@ struct FwdArgs {
   int B, H, N;    // H query heads; K and V have H / G heads
   float scale;
   int G = 1;      // query heads per K/V head
+  // Packed variable-length batch when non-null: [B + 1] token offsets of the
+  // sequences in tensors laid out [heads, total, d]; N is then the longest
+  // length (the grid and the LSE rows per (sequence, head)).
+  const int* cu_seqlens = nullptr;
+  int total = 0;
 };
 
 struct BwdArgs {
@@ -35,7 +40,41 @@ struct BwdArgs {
   int Np;         // N rounded up to a multiple of 64
   float scale;
   int G = 1;      // query heads per K/V head (K, V, dK, dV have H / G heads)
+  const int* cu_seqlens = nullptr;   // as in FwdArgs; workspace and LSE rows per
+  int total = 0;                     // (sequence, head) stay Np and N
 };
+
+// Rows of the (sequence, query head) pair hd = b H + h in the row-major
+// tensors: the first row of its query slab (q, o, dout, dq), of its K/V head's
+// slab (k, v, dk, dv), the row distance between consecutive query heads, and
+// the number of rows.  Dense: slab hd of N rows.  Packed: rows cu[b] .. cu[b+1]
+// of head h's slab of `total` rows; offsets are clamped into [0, total] and the
+// length to N, so any offsets stay inside the tensors.
+struct Span {
+  size_t q, kv, hs;
+  int n;
+};
+// Packed batches: the work order's linear head index is taken head-major
+// (lin = h B + b), so that the contiguous range of heads that one XCD receives
+// spans every sequence and the XCDs get equal shares of long and short ones;
+// returns the (sequence, head) index b Hx + h.  Dense launches keep lin.
+template <class Args>
+__device__ inline int packed_head(const Args& a, int lin, int Hx) {
+  if (!a.cu_seqlens) return lin;
+  const int h = lin / a.B;
+  return (lin - h * a.B) * Hx + h;
+}
+
+template <class Args>
+__device__ inline Span span_of(const Args& a, int hd) {
+  if (!a.cu_seqlens)
+    return Span{(size_t)hd * a.N, (size_t)(hd / a.G) * a.N, (size_t)a.N, a.N};
+  const int b = hd / a.H, h = hd - b * a.H;
+  const int s0 = min(max(a.cu_seqlens[b], 0), a.total);
+  const int s1 = min(max(a.cu_seqlens[b + 1], s0), a.total);
+  return Span{(size_t)h * a.total + s0, (size_t)(h / a.G) * a.total + s0, (size_t)a.total,
+              min(s1 - s0, a.N)};
+}
 
 enum class Dt { f32 = 0, f16 = 1, bf16 = 2 };
 

@@ -10,7 +10,9 @@ the seeded input tensors from ``workloads.py``.
 Contents
 --------
 ``attention``   the plain definition: S and P materialized, analytic backward;
-                also with grouped key/value heads (forward_gqa, backward_gqa).
+                also with grouped key/value heads (forward_gqa, backward_gqa)
+                and padding-free variable-length batches (forward_varlen,
+                backward_varlen).
 ``recurrence``  the online-softmax tile recurrence and the two-tile merge,
                 written in the pages' order; used only to pin that the
                 recurrence is exact, never as the reference for the GPU path.
@@ -22,10 +24,12 @@ differences (``tests/test_oracle.py``).  No function here is parity-unpinned.
 from .attention import (  # noqa: F401
     backward,
     backward_gqa,
+    backward_varlen,
     backward_head,
     causal_visible,
     forward,
     forward_gqa,
+    forward_varlen,
     forward_head,
     probabilities,
     row_softmax,

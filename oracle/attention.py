@@ -183,3 +183,74 @@ def backward_gqa(q, k, v, do, scale: float, causal: bool):
             dk[b, h // g] += r["dk"]
             dv[b, h // g] += r["dv"]
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- variable-length batches
+#
+# Padding-free batches: the 2022 interface described on "FlashAttention 원 논문
+# 해부" (section "내부 구조와 실제 실행 흐름", items 2 and 3) packs the valid tokens
+# of all sequences one after another and passes cu_seqlens (the cumulative token
+# offset of each sequence, B + 1 entries from 0 to the token total) and max_s
+# (the longest length); the softmax statistics stay [B, heads, max_s].
+# Reading: sequence b owns packed rows cu[b] <= t < cu[b + 1]; its attention is
+# the plain definition over its own tokens only (the causal mask top-left
+# aligned at its first token), so tokens of different sequences never see one
+# another.  Layout here: one packed slab per head, q [H, total, d],
+# k and v [H_kv, total, d] (grouped heads as above); rows outside every
+# sequence and LSE entries past a sequence's length are left as NaN.
+
+
+def _spans(cu_seqlens, total: int, max_s: int):
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    if len(cu) < 2 or cu[0] != 0 or cu[-1] > total:
+        raise ValueError("cu_seqlens must start at 0 and end at most at the token total")
+    for b in range(len(cu) - 1):
+        if not 0 <= cu[b + 1] - cu[b] <= max_s:
+            raise ValueError(f"sequence {b} has length {cu[b + 1] - cu[b]} outside [0, {max_s}]")
+    return cu
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_s: int, scale: float, causal: bool, seqs=None):
+    """q [H, total, d], k [H_kv, total, d], v [H_kv, total, dv] -> (O [H, total, dv],
+    LSE [B, H, max_s]).  ``seqs`` optionally restricts the work to some sequences."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H, total = q.shape[:2]
+    g = _group(H, k.shape[0])
+    cu = _spans(cu_seqlens, total, max_s)
+    B = len(cu) - 1
+    o = np.full((H, total, v.shape[-1]), np.nan)
+    lse = np.full((B, H, max_s), np.nan)
+    for b in (seqs if seqs is not None else range(B)):
+        s0, s1 = cu[b], cu[b + 1]
+        if s1 == s0:
+            continue   # an empty sequence has no rows
+        for h in range(H):
+            o[h, s0:s1], lse[b, h, : s1 - s0] = forward_head(
+                q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], scale, causal)
+    return o, lse
+
+
+def backward_varlen(q, k, v, do, cu_seqlens, max_s: int, scale: float, causal: bool, seqs=None):
+    """Gradients of sum(O * dO) for forward_varlen: (dQ [H, total, d],
+    dK [H_kv, total, d], dV [H_kv, total, dv]); rows outside the computed
+    sequences are NaN."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    H, total = q.shape[:2]
+    g = _group(H, k.shape[0])
+    cu = _spans(cu_seqlens, total, max_s)
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    for b in (seqs if seqs is not None else range(len(cu) - 1)):
+        s0, s1 = cu[b], cu[b + 1]
+        if s1 == s0:
+            continue
+        dk[:, s0:s1] = 0.0
+        dv[:, s0:s1] = 0.0
+        for h in range(H):
+            r = backward_head(q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], do[h, s0:s1],
+                              scale, causal)
+            dq[h, s0:s1] = r["dq"]
+            dk[h // g, s0:s1] += r["dk"]
+            dv[h // g, s0:s1] += r["dv"]
+    return dq, dk, dv

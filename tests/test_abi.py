@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 3
+    assert fa.fa_abi_version() == 4
     for st in range(6):
         assert fa.fa_status_string(st) and fa.fa_status_string(st) != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -137,6 +137,46 @@ def test_grouped_kv_rejects():
                          ws, nb - 1, None) == fa.FA_ERR_WORKSPACE
 
 
+def _fwd_varlen(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, cu_seqlens=P, B=3, max_s=128, total=300, H=8, H_kv=2,
+                d=64, causal=0, scale=0.125, dtype=fa.FA_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_varlen(**args)
+
+
+def _bwd_varlen(**kw):
+    args = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, cu_seqlens=P, B=3, max_s=128,
+                total=300, H=8, H_kv=2, d=64, causal=0, scale=0.125, dtype=fa.FA_BF16,
+                workspace=0x10000, workspace_bytes=fa.fa_bwd_workspace_size(3, 8, 128, 64),
+                stream=None)
+    args.update(kw)
+    return fa.fa_bwd_varlen(**args)
+
+
+def test_varlen_rejects():
+    E = fa.FA_ERR_INVALID_ARGUMENT
+    for call in (_fwd_varlen, _bwd_varlen):
+        assert call(cu_seqlens=None) == E
+        assert call(q=None) == E
+        assert call(total=0) == E and call(total=-5) == E
+        assert call(B=0) == E and call(max_s=0) == E
+        assert call(H_kv=3) == E and call(H_kv=0) == E
+        assert call(scale=math.inf) == E
+        assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+        assert call(dtype=7) == fa.FA_ERR_UNSUPPORTED
+        assert call(max_s=2**23 + 1) == fa.FA_ERR_UNSUPPORTED
+        assert call(B=65536) == fa.FA_ERR_UNSUPPORTED
+    assert _bwd_varlen(workspace_bytes=fa.fa_bwd_workspace_size(3, 8, 128, 64) - 1) == fa.FA_ERR_WORKSPACE
+    assert _bwd_varlen(workspace=0x10008) == fa.FA_ERR_WORKSPACE
+    assert _bwd_varlen(dk=None) == E
+
+
+def test_too_many_heads_rejected():
+    """B*H above 2^24 would overflow the tile grids' 32-bit work index."""
+    assert _fwd(B=65535, H=257, N=1) == fa.FA_ERR_UNSUPPORTED
+    assert _fwd(B=4097, H=4096, N=1) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_workspace_size():
     # Two float32 arrays [B, H, Np], Np = N rounded up to a multiple of 64.
     up = lambda x: (x + 255) // 256 * 256
@@ -160,6 +200,8 @@ def test_valid_arguments_without_gpu_report_device_error():
     assert fa.fa_fwd_gqa(P, P, P, P, P, 1, 8, 2, 128, 64, 0, 0.1, fa.FA_F16, None) == fa.FA_ERR_DEVICE
     assert fa.fa_bwd_gqa(P, P, P, P, P, P, P, P, P, 1, 8, 2, 128, 64, 0, 0.1, fa.FA_F16,
                          ws, nb, None) == fa.FA_ERR_DEVICE
+    assert _fwd_varlen() == fa.FA_ERR_DEVICE
+    assert _bwd_varlen() == fa.FA_ERR_DEVICE
     nb = fa.fa_bwd_workspace_size(1, 1, 128, 64)
     assert fa.fa_bwd_preprocess(P, P, P, 1, 1, 128, 64, fa.FA_F16, 0x10000, nb, None) == fa.FA_ERR_DEVICE
     assert fa.fa_bwd_dq(P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, 0x10000, nb,

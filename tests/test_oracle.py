@@ -313,3 +313,128 @@ def test_gqa_rejects_uneven_groups():
     q, k, v, _ = _gqa_inputs(H=6, H_kv=4)
     with pytest.raises(ValueError):
         oracle.forward_gqa(q, k, v, 0.5, False)
+
+
+# ----------------------------------------------------------- variable-length batches
+
+
+def _varlen_inputs(lens=(3, 0, 5, 1), H=4, H_kv=2, d=3, dv=4, seed=21, extra=0):
+    """Packed [H, total, d] inputs for the given sequence lengths (plus ``extra``
+    trailing rows that belong to no sequence)."""
+    r = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1]) + extra
+    return (cu, r.standard_normal((H, total, d)), r.standard_normal((H_kv, total, d)),
+            r.standard_normal((H_kv, total, dv)), r.standard_normal((H, total, dv)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equal_lengths_is_the_padded_batch(causal):
+    """B sequences of one length N packed head-major are the [B, H, N, d] batch."""
+    B, H, H_kv, N = 3, 4, 2, 6
+    cu, q, k, v, do = _varlen_inputs(lens=(N,) * B, H=H, H_kv=H_kv)
+    to_batch = lambda x: x.reshape(x.shape[0], B, N, x.shape[-1]).transpose(1, 0, 2, 3)
+    o, lse = oracle.forward_varlen(q, k, v, cu, N, 0.7, causal)
+    ob, lseb = oracle.forward_gqa(to_batch(q), to_batch(k), to_batch(v), 0.7, causal)
+    np.testing.assert_allclose(to_batch(o), ob, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lseb, rtol=0, atol=1e-14)
+    g = oracle.backward_varlen(q, k, v, do, cu, N, 0.7, causal)
+    gb = oracle.backward_gqa(to_batch(q), to_batch(k), to_batch(v), to_batch(do), 0.7, causal)
+    for x, y in zip(g, gb):
+        np.testing.assert_allclose(to_batch(x), y, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_is_block_diagonal_attention(causal):
+    """The packed batch equals one attention over all packed tokens in which
+    token t sees token u only inside its own sequence (and u <= t if causal):
+    a mask-based formulation with no per-sequence slicing."""
+    cu, q, k, v, _ = _varlen_inputs(lens=(3, 0, 5, 1, 4), H=2, H_kv=1)
+    total = q.shape[1]
+    seq = np.searchsorted(cu, np.arange(total), side="right") - 1
+    pos = np.arange(total)
+    visible = seq[:, None] == seq[None, :]
+    if causal:
+        visible &= pos[None, :] <= pos[:, None]
+    o, lse = oracle.forward_varlen(q, k, v, cu, 5, 0.9, causal)
+    for h in range(2):
+        s = np.where(visible, 0.9 * q[h] @ k[0].T, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        p = e / e.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(o[h], p @ v[0], rtol=0, atol=1e-13)
+        ref_lse = (m[:, 0] + np.log(e.sum(axis=1)))
+        for b in range(len(cu) - 1):
+            n = cu[b + 1] - cu[b]
+            np.testing.assert_allclose(lse[b, h, :n], ref_lse[cu[b]:cu[b + 1]], atol=1e-13)
+            assert np.isnan(lse[b, h, n:]).all()
+
+
+def test_varlen_sequences_do_not_interact():
+    """Changing every input of one sequence changes no output or gradient of
+    another sequence."""
+    cu, q, k, v, do = _varlen_inputs(lens=(4, 3, 5))
+    base = oracle.forward_varlen(q, k, v, cu, 5, 0.5, True)
+    gbase = oracle.backward_varlen(q, k, v, do, cu, 5, 0.5, True)
+    s0, s1 = cu[1], cu[2]
+    q2, k2, v2, do2 = q.copy(), k.copy(), v.copy(), do.copy()
+    for x in (q2, k2, v2, do2):
+        x[:, s0:s1] = np.random.default_rng(5).standard_normal(x[:, s0:s1].shape)
+    o2, lse2 = oracle.forward_varlen(q2, k2, v2, cu, 5, 0.5, True)
+    g2 = oracle.backward_varlen(q2, k2, v2, do2, cu, 5, 0.5, True)
+    keep = np.r_[0:s0, s1:q.shape[1]]
+    np.testing.assert_array_equal(o2[:, keep], base[0][:, keep])
+    np.testing.assert_array_equal(lse2[[0, 2]], base[1][[0, 2]])
+    assert not np.allclose(o2[:, s0:s1], base[0][:, s0:s1])
+    for x, y in zip(g2, gbase):
+        np.testing.assert_array_equal(x[:, keep], y[:, keep])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_zero_query(causal):
+    """Q = 0: each row is the mean of the visible V rows of its own sequence and
+    LSE = ln(number visible); empty sequences and unowned rows are untouched."""
+    cu, _, k, v, _ = _varlen_inputs(lens=(3, 0, 5, 1), extra=2)
+    q = np.zeros((4,) + k.shape[1:])
+    o, lse = oracle.forward_varlen(q, k, v, cu, 6, 0.4, causal)
+    for b in range(4):
+        for h in range(4):
+            for i in range(cu[b + 1] - cu[b]):
+                vis = i + 1 if causal else cu[b + 1] - cu[b]
+                np.testing.assert_allclose(o[h, cu[b] + i], v[h // 2, cu[b]:cu[b] + vis].mean(axis=0),
+                                           atol=1e-13)
+                np.testing.assert_allclose(lse[b, h, i], math.log(vis), atol=1e-13)
+    assert np.isnan(lse[1]).all() and np.isnan(o[:, cu[-1]:]).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_finite_differences(causal):
+    """Central differences of L = sum(O * dO) over every packed input element,
+    with an empty sequence and a row that belongs to no sequence (gradient 0)."""
+    cu, q, k, v, do = _varlen_inputs(lens=(2, 0, 3), H=2, H_kv=1, d=2, dv=2, extra=1)
+    scale, hstep = 0.8, 1e-6
+    dq, dk, dv = oracle.backward_varlen(q, k, v, do, cu, 3, scale, causal)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.forward_varlen(qq, kk, vv, cu, 3, scale, causal)
+        return float(np.nansum(o * do))
+
+    for which, (x, g) in enumerate(zip((q, k, v), (dq, dk, dv))):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += hstep
+            xm[idx] -= hstep
+            ap, am = [q, k, v], [q, k, v]
+            ap[which], am[which] = xp, xm
+            fd[idx] = (loss(*ap) - loss(*am)) / (2 * hstep)
+        owned = np.nan_to_num(g, nan=0.0)
+        np.testing.assert_allclose(owned, fd, rtol=0, atol=1e-7, err_msg="qkv"[which])
+        assert np.isnan(g[:, -1]).all()
+
+
+def test_varlen_rejects_bad_offsets():
+    cu, q, k, v, _ = _varlen_inputs(lens=(3, 4))
+    for bad, max_s in (([1, 3, 7], 4), ([0, 4, 3], 4), ([0, 3, 8], 5), ([0, 3, 7], 3)):
+        with pytest.raises(ValueError):
+            oracle.forward_varlen(q, k, v, np.array(bad), max_s, 0.5, False)

@@ -107,6 +107,99 @@ def make_inputs(w: Workload) -> dict:
     return {name: t.to(dt).contiguous() for name, t in (("q", q), ("k", k), ("v", v), ("do", do))}
 
 
+# ----------------------------------------------------------- packed variable-length batches
+#
+# A padding-free batch: sequences of different lengths packed one after another,
+# one slab per head: Q and dO [H, total, d], K and V [H_kv, total, d], with
+# cu_seqlens the B + 1 cumulative offsets.  Draw order from a CPU generator
+# seeded with the workload's seed: Q, K, V, dO (fp32 standard normals, rounded
+# to the dtype).  The lengths are part of the workload's definition.
+
+
+@dataclasses.dataclass(frozen=True)
+class Varlen:
+    name: str
+    lens: tuple         # sequence lengths (zeros allowed)
+    H: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+    H_kv: int = 0
+
+    @property
+    def B(self) -> int:
+        return len(self.lens)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
+
+    @property
+    def total(self) -> int:
+        return int(sum(self.lens))
+
+    @property
+    def max_s(self) -> int:
+        return max(max(self.lens), 1)
+
+    @property
+    def cu_seqlens(self) -> torch.Tensor:
+        cu = [0]
+        for n in self.lens:
+            cu.append(cu[-1] + int(n))
+        return torch.tensor(cu, dtype=torch.int32)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPES[self.dtype]
+
+    def fwd_flops(self) -> float:
+        """4*H*n^2*d per sequence of length n (halved under the causal mask)."""
+        f = sum(4.0 * self.H * n * n * self.d for n in self.lens)
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        return 2.5 * self.fwd_flops()
+
+
+def uniform_lengths(B: int, lo: int, hi: int, seed: int) -> tuple:
+    """B lengths drawn uniformly from [lo, hi] with a seeded CPU generator."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return tuple(int(x) for x in torch.randint(lo, hi + 1, (B,), generator=g))
+
+
+# 16 sequences of 512 to 8192 tokens (uniform), 32 query heads, d = 128: the
+# token budget of the dense b2h32n8192d128 workloads spread over a realistic
+# length mix; one full-mask and one causal with grouped K/V heads.
+VARLEN_BF16 = Varlen("varlen16-512to8192-h32d128-bf16", uniform_lengths(16, 512, 8192, 1008), 32,
+                     128, "bf16", False, 1008)
+VARLEN_CAUSAL_BF16 = Varlen("varlen16-512to8192-h32kv8d128-bf16-causal",
+                            uniform_lengths(16, 512, 8192, 1009), 32, 128, "bf16", True, 1009,
+                            H_kv=8)
+VARLEN = (VARLEN_BF16, VARLEN_CAUSAL_BF16)
+VARLEN_BY_NAME = {w.name: w for w in VARLEN}
+
+
+def make_varlen_inputs(w: Varlen, extra_rows: int = 0) -> dict:
+    """{"q","k","v","do"} packed per head ([H or H_kv, total + extra_rows, d]) and
+    "cu_seqlens" (int32, B + 1); ``extra_rows`` trailing rows belong to no sequence."""
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    rows = w.total + extra_rows
+    q = torch.randn((w.H, rows, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.kv_heads, rows, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.kv_heads, rows, w.d), generator=g, dtype=torch.float32)
+    do = torch.randn((w.H, rows, w.d), generator=g, dtype=torch.float32)
+    dt = w.torch_dtype
+    out = {name: t.to(dt).contiguous() for name, t in (("q", q), ("k", k), ("v", v), ("do", do))}
+    out["cu_seqlens"] = w.cu_seqlens
+    return out
+
+
 def make_random(shape, dtype: str, seed: int, std: float = 1.0) -> torch.Tensor:
     """One seeded N(0, std^2) tensor rounded to ``dtype`` (for edge-case tests)."""
     g = torch.Generator(device="cpu").manual_seed(seed)
