@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -237,6 +237,51 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         int H, int H_kv, int d, int causal, float scale,
                         fa_dtype dtype, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * Local windows, and one description of a call for every feature.
+ *
+ * Local attention keeps, for query i, only the keys j with
+ * i - window_left <= j <= i + window_right ("어텐션 비용 줄이기: 희소 어텐션에서
+ * FlashAttention과 SSM까지", ailab.paldyn.com, sections "지역 윈도와 글로벌
+ * 토큰", w keys on each side, and "슬라이딩 윈도와 수용 영역", the most recent W
+ * keys: causal with window_left = W - 1).  Positions count inside each
+ * sequence.  Tiles outside every row's window are skipped, so the work and the
+ * traffic shrink with the window.  The causal mask still applies when causal
+ * != 0 (it acts as window_right = 0).
+ *
+ * fa_attn fields:
+ *   B, H, H_kv, N, d  batch entries (packed: sequences), query heads, key/value
+ *                     heads (H_kv divides H), sequence length (packed: max_s),
+ *                     head dimension;
+ *   causal            as above;
+ *   window_left,      >= 0: the window's extent on that side; -1: open.  Every
+ *   window_right      row sees at least its own key;
+ *   scale, dtype      as above;
+ *   cu_seqlens, total NULL for the dense layout [B, H(_kv), N, d]; otherwise a
+ *                     packed batch exactly as for fa_fwd_varlen.
+ * Tensors, workspace (fa_bwd_workspace_size(B, H, N, d)), ownership and errors
+ * as for the entry points above (dense or packed); in addition p == NULL or a
+ * window value below -1 is FA_ERR_INVALID_ARGUMENT.  fa_bwd_ex needs the o and
+ * lse that fa_fwd_ex wrote for the same description.
+ */
+typedef struct fa_attn {
+  int B, H, H_kv, N, d;
+  int causal;
+  int window_left, window_right;
+  float scale;
+  fa_dtype dtype;
+  const int* cu_seqlens;
+  int total;
+} fa_attn;
+
+fa_status fa_fwd_ex(const fa_attn* p, const void* q, const void* k, const void* v, void* o,
+                    float* lse, void* stream);
+
+fa_status fa_bwd_ex(const fa_attn* p, const void* q, const void* k, const void* v,
+                    const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

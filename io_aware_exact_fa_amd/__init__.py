@@ -36,7 +36,17 @@ FA_BF16 = 2
 
 EXPORTED = ("fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
             "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
-            "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa", "fa_fwd_varlen", "fa_bwd_varlen")
+            "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_ex",
+            "fa_bwd_ex")
+
+
+class FaAttn(ctypes.Structure):
+    """struct fa_attn of include/fa.h: one call's shape, mask, window and packing."""
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("H_kv", ctypes.c_int),
+                ("N", ctypes.c_int), ("d", ctypes.c_int), ("causal", ctypes.c_int),
+                ("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
+                ("cu_seqlens", ctypes.c_void_p), ("total", ctypes.c_int)]
 
 
 class FaError(RuntimeError):
@@ -87,6 +97,11 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_varlen.restype = i
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
                                   i, vp, sz, vp]
+    pa = ctypes.POINTER(FaAttn)
+    lib.fa_fwd_ex.restype = i
+    lib.fa_fwd_ex.argtypes = [pa, vp, vp, vp, vp, vp, vp]
+    lib.fa_bwd_ex.restype = i
+    lib.fa_bwd_ex.argtypes = [pa, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     return lib
 
 
@@ -181,6 +196,22 @@ def fa_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, B, max_s, total
                               workspace_bytes, stream)
 
 
+def fa_fwd_ex(p, q, k, v, o, lse, stream) -> int:
+    return _lib.fa_fwd_ex(ctypes.byref(p) if p is not None else None, q, k, v, o, lse, stream)
+
+
+def fa_bwd_ex(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_ex(ctypes.byref(p) if p is not None else None, q, k, v, o, dout, lse, dq,
+                          dk, dv, workspace, workspace_bytes, stream)
+
+
+def attn(B, H, H_kv, N, d, causal, scale, dtype, window=(-1, -1), cu_seqlens=None,
+         total=0) -> FaAttn:
+    """Fill an fa_attn (window sides -1 = open; cu_seqlens a device address or None)."""
+    return FaAttn(B, H, H_kv, N, d, int(causal), int(window[0]), int(window[1]), float(scale),
+                  int(dtype), cu_seqlens, int(total))
+
+
 # ------------------------------------------------------------------ torch helpers
 
 
@@ -206,9 +237,9 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
+def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, window=None):
     """O, LSE for q [B, H, N, d] and k, v [B, H_kv, N, d] (H_kv divides H; all one
-    dtype, on the GPU)."""
+    dtype, on the GPU).  ``window`` = (left, right), -1 = open side."""
     import torch
     B, H, N, d = q.shape
     H_kv = k.shape[1]
@@ -221,6 +252,13 @@ def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check("o", o, (B, H, N, d), q.dtype)
     _check("lse", lse, (B, H, N), torch.float32)
+    if window is not None:
+        p = attn(B, H, H_kv, N, d, causal, scale, dtype_code(q.dtype), window)
+        st = fa_fwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       _stream(stream))
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_ex")
+        return o, lse
     st = fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     B, H, H_kv, N, d, causal, scale, dtype_code(q.dtype), _stream(stream))
     if st != FA_OK:
@@ -238,7 +276,7 @@ def workspace(B, H, N, d, device):
 
 
 def backward(q, k, v, o, dout, lse, causal: bool, scale: float, dq=None, dk=None, dv=None,
-             ws=None, stream=None):
+             ws=None, stream=None, window=None):
     """dQ, dK, dV for the forward that produced o and lse."""
     import torch
     B, H, N, d = q.shape
@@ -255,6 +293,14 @@ def backward(q, k, v, o, dout, lse, causal: bool, scale: float, dq=None, dk=None
     for name, t in (("dk", dk), ("dv", dv)):
         _check(name, t, (B, H_kv, N, d), q.dtype)
     ws = workspace(B, H, N, d, q.device) if ws is None else ws
+    if window is not None:
+        p = attn(B, H, H_kv, N, d, causal, scale, dtype_code(q.dtype), window)
+        st = fa_bwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                       ws.numel(), _stream(stream))
+        if st != FA_OK:
+            raise FaError(st, "fa_bwd_ex")
+        return dq, dk, dv
     st = fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d,
                     causal, scale, dtype_code(q.dtype), ws.data_ptr(), ws.numel(),
@@ -275,7 +321,7 @@ def _check_cu(cu_seqlens, device):
 
 
 def forward_varlen(q, k, v, cu_seqlens, max_s: int, causal: bool, scale: float, o=None, lse=None,
-                   stream=None):
+                   stream=None, window=None):
     """O [H, total, d], LSE [B, H, max_s] for packed q [H, total, d], k, v
     [H_kv, total, d] and device int32 cu_seqlens [B + 1] (offsets are read on the
     device, not checked here)."""
@@ -290,16 +336,22 @@ def forward_varlen(q, k, v, cu_seqlens, max_s: int, causal: bool, scale: float, 
     lse = torch.empty((B, H, max_s), dtype=torch.float32, device=q.device) if lse is None else lse
     _check("o", o, (H, total, d), q.dtype)
     _check("lse", lse, (B, H, max_s), torch.float32)
-    st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                       cu_seqlens.data_ptr(), B, max_s, total, H, H_kv, d, causal, scale,
-                       dtype_code(q.dtype), _stream(stream))
+    if window is not None:
+        p = attn(B, H, H_kv, max_s, d, causal, scale, dtype_code(q.dtype), window,
+                 cu_seqlens.data_ptr(), total)
+        st = fa_fwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       _stream(stream))
+    else:
+        st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           cu_seqlens.data_ptr(), B, max_s, total, H, H_kv, d, causal, scale,
+                           dtype_code(q.dtype), _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_fwd_varlen")
     return o, lse
 
 
 def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_s: int, causal: bool, scale: float,
-                    dq=None, dk=None, dv=None, ws=None, stream=None):
+                    dq=None, dk=None, dv=None, ws=None, stream=None, window=None):
     """dQ, dK, dV for the packed forward that produced o and lse."""
     import torch
     H, total, d = q.shape
@@ -317,10 +369,18 @@ def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_s: int, causal: bool,
     for name, t in (("dk", dk), ("dv", dv)):
         _check(name, t, (H_kv, total, d), q.dtype)
     ws = workspace(B, H, max_s, d, q.device) if ws is None else ws
-    st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                       cu_seqlens.data_ptr(), B, max_s, total, H, H_kv, d, causal, scale,
-                       dtype_code(q.dtype), ws.data_ptr(), ws.numel(), _stream(stream))
+    if window is not None:
+        p = attn(B, H, H_kv, max_s, d, causal, scale, dtype_code(q.dtype), window,
+                 cu_seqlens.data_ptr(), total)
+        st = fa_bwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                       ws.numel(), _stream(stream))
+    else:
+        st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                           dv.data_ptr(), cu_seqlens.data_ptr(), B, max_s, total, H, H_kv, d,
+                           causal, scale, dtype_code(q.dtype), ws.data_ptr(), ws.numel(),
+                           _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_varlen")
     return dq, dk, dv

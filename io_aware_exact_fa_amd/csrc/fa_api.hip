@@ -56,6 +56,30 @@ fa_status check_varlen(const int* cu_seqlens, int B, int max_s, int total, int H
   return FA_OK;
 }
 
+// Checks of a call description; then its grouping, packing and window into
+// the kernel arguments.
+fa_status check_attn(const fa_attn* p) {
+  if (!p) return FA_ERR_INVALID_ARGUMENT;
+  if (p->window_left < -1 || p->window_right < -1) return FA_ERR_INVALID_ARGUMENT;
+  if (p->cu_seqlens)
+    return check_varlen(p->cu_seqlens, p->B, p->N, p->total, p->H, p->H_kv, p->d, p->scale,
+                        p->dtype);
+  const fa_status st = check_shape(p->B, p->H, p->N, p->d, p->scale, p->dtype);
+  if (st != FA_OK) return st;
+  if (p->H_kv <= 0 || p->H % p->H_kv != 0) return FA_ERR_INVALID_ARGUMENT;
+  return FA_OK;
+}
+
+template <class Args>
+void apply_attn(const fa_attn* p, Args* a) {
+  a->G = p->H / p->H_kv;
+  a->cu_seqlens = p->cu_seqlens;
+  a->total = p->cu_seqlens ? p->total : 0;
+  // A side wider than the longest sequence is open (this also keeps i + w in range).
+  a->wl = (p->window_left < 0 || p->window_left >= p->N) ? fa::kNoLimit : p->window_left;
+  a->wr = (p->window_right < 0 || p->window_right >= p->N) ? fa::kNoLimit : p->window_right;
+}
+
 // 1 = gfx950, 2 = something else; 0 = not yet known.
 std::atomic<int> g_device_ok[kMaxDevices];
 
@@ -209,6 +233,32 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
                     void* stream) {
   return fa_bwd_dq_gqa(q, k, v, dout, lse, dq, B, H, H, N, d, causal, scale, dtype, workspace,
                        workspace_bytes, stream);
+}
+
+fa_status fa_fwd_ex(const fa_attn* p, const void* q, const void* k, const void* v, void* o,
+                    float* lse, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
+  fa_status st = check_attn(p);
+  if (st != FA_OK) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, p->B, p->H, p->N, p->scale};
+  apply_attn(p, &a);
+  return launched(fa::launch_fwd(to_dt(p->dtype), p->d, p->causal != 0, a, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_ex(const fa_attn* p, const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
+  fa_status st = check_attn(p);
+  if (st != FA_OK) return st;
+  fa::BwdArgs a{};
+  st = bwd_setup(p->B, p->H, p->H_kv, p->N, p->d, p->scale, p->dtype, workspace, workspace_bytes,
+                 &a);
+  if (st != FA_OK) return st;
+  apply_attn(p, &a);
+  return bwd_all(a, q, k, v, o, dout, lse, dq, dk, dv, p->d, p->causal, p->dtype, stream);
 }
 
 fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -142,10 +142,13 @@ void bwd_dq_kernel(BwdArgs a) {
   const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
   const float dl = a.delta[head * a.Np + qrow];
 
-  const int ntiles_all = (N + C::BC - 1) / C::BC;
-  const int qlast = min(q0 + C::BR, N) - 1;
-  const int ntiles = CAUSAL ? min(ntiles_all, qlast / C::BC + 1) : ntiles_all;
-  const int wlast = (qw >= N) ? -1 : (CAUSAL ? min(qw + 31, N - 1) / C::BC : ntiles - 1);
+  // Window: keys [myq - wl, myq + wr] of this lane's row are visible.
+  const int wl = a.wl, wr = CAUSAL ? min(a.wr, 0) : a.wr;
+  const TileRange tr = tile_range(q0, min(q0 + C::BR, N) - 1, N, wl, wr, C::BC, false);
+  const int j0 = tr.lo, ntiles = tr.hi;
+  // Tiles this wave needs: [wfirst, wlast] (none if it holds no row below N).
+  const int wfirst = max(0, qw - wl) / C::BC;
+  const int wlast = (qw >= N) ? -1 : min(qw + 31 + wr, N - 1) / C::BC;
   const int krow = kPerm ? perm16(col) : col;
   const int hoff = kPerm ? 8 * h : 4 * h;
   auto key0_of = [](int i) {
@@ -158,9 +161,9 @@ void bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
   TileStage<T, D, C::NT> ks_stage, vs_stage;
-  ks_stage.load(K, 0, N, tid);
-  vs_stage.load(V, 0, N, tid);
-  for (int j = 0; j < ntiles; ++j) {
+  ks_stage.load(K, j0 * C::BC, N, tid);
+  vs_stage.load(V, j0 * C::BC, N, tid);
+  for (int j = j0; j < ntiles; ++j) {
     ks_stage.store_rows(Ks, C::KP, tid);
     ks_stage.store_transposed(Kt, tid);
     vs_stage.store_rows(Vs, C::KP, tid);
@@ -169,7 +172,7 @@ void bwd_dq_kernel(BwdArgs a) {
       ks_stage.load(K, (j + 1) * C::BC, N, tid);
       vs_stage.load(V, (j + 1) * C::BC, N, tid);
     }
-    if (j <= wlast) {
+    if (j >= wfirst && j <= wlast) {
       const int key0 = j * C::BC;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -183,12 +186,12 @@ void bwd_dq_kernel(BwdArgs a) {
           dp = M::mma(load_frag<T>(vr + ks * C::KM), gf[ks], dp);
         }
         const int kb0 = key0 + kb * 32;
-        const bool masked = (CAUSAL && kb0 + 31 > qw) || (kb0 + 32 > N);
-        const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kb0 - hoff;
+        const bool masked = (kb0 + 31 > qw + wr) || (kb0 < qw + 31 - wl) || (kb0 + 32 > N);
+        const int lim = min(myq + wr, N - 1) - kb0 - hoff, low = myq - wl - kb0 - hoff;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float p = exp2_fast(fmaf(s[i], c, -l2));
-          if (masked && key0_of(i) > lim) p = 0.f;
+          if (masked && (key0_of(i) > lim || key0_of(i) < low)) p = 0.f;
           s[i] = p * (dp[i] - dl);                     // dS
         }
         // dQ^T += K^T dS^T: A operand = 8 consecutive keys of one head-dim row of K^T.
@@ -294,9 +297,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     return kPerm ? perm16(r) : r;
   };
 
-  const int nqt = (N + C::BQ - 1) / C::BQ;
-  // Earlier query tiles see none of these keys (qt0 < nqt because k0 < N).
-  const int qt0 = CAUSAL ? k0 / C::BQ : 0;
+  // Window: queries [myk - wr, myk + wl] see this lane's key.  Query tiles of
+  // the workgroup: [qt0, nqt) (qt0 < nqt because k0 < N).
+  const int wl = a.wl, wr = CAUSAL ? min(a.wr, 0) : a.wr;
+  const TileRange tr = tile_range(k0, k0 + C::BKC - 1, N, wr, wl, C::BQ, true);
+  const int qt0 = tr.lo, nqt = tr.hi;
   // Staging of a query tile (Q and dO, 64 rows each) through registers, as
   // 2 NGM units of 4 rows x 16 bytes: thread tid owns units tid + 256 u, which
   // belong to Q (mat 0) or dO (mat 1).  The work is split into single
@@ -497,7 +502,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           if (m == elem_slot(b, i)) {
             const int qo = b * 32 + qoff_of(i) + hoff;
             float e = exp2_fast(fmaf(s[b][i], c, -l4[b][i / 4][i % 4]));
-            if (CAUSAL && qi0 + qo < myk) e = 0.f;
+            if (qi0 + qo < myk - wr || qi0 + qo > myk + wl) e = 0.f;
             p[b][i] = e;
             ds[b][i] = e * (dp[b][i] - d4[b][i / 4][i % 4]);
             if ((i + 1) % EPU == 0) {
@@ -608,12 +613,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   }
   const float l2 = a.l2[head * a.Np + qrow];       // LSE log2(e), +inf if no visible key
   const float dl = a.delta[head * a.Np + qrow];
-  // Keys above klim are masked (causal and past N).
-  const int klim = CAUSAL ? min(myq, N - 1) : N - 1;
-
-  const int nkt_all = (N + C::BC - 1) / C::BC;
-  const int qlast = min(q0 + C::BR, N) - 1;
-  const int nkt = CAUSAL ? min(nkt_all, qlast / C::BC + 1) : nkt_all;
+  // Visible keys of this lane's row: klo .. khi (window, causal and N).
+  const int wr = CAUSAL ? min(a.wr, 0) : a.wr;
+  const int khi = min(myq + wr, N - 1), klo = myq - a.wl;
+  // Key tiles of the workgroup: [lo, hi), of which [ml, mu) need no mask.
+  const TileRange tr = tile_range(q0, min(q0 + C::BR, N) - 1, N, a.wl, wr, C::BC, false);
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -625,7 +629,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   // copy V, wave w rows 16 (w & 3) + 4 j .. + 3 (d = 128: one 4-row group per
   // copy) or row 16 (w & 3) + j (d = 64).  NW = 4: wave w copies groups
   // 4 w + j of K (j < 4) and 4 w + j - 4 of V.  Rows past N read as zero (and
-  // are masked through klim).
+  // are masked through khi).
   const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
   const i32x4 rsv = buffer_rsrc(V, (uint32_t)N * (2 * D));
   auto copy_op = [&](int b, int kt, int j) {
@@ -643,12 +647,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
     }
   };
 
-  // Prologue: tiles 0 and 1 (NW = 8) or tile 0 (NW = 4).
+  // Prologue: tiles lo and lo + 1 (NW = 8) or tile lo (NW = 4).
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
   for (int t = 0; t < C::NB - 1; ++t)
 #pragma unroll
-    for (int j = 0; j < C::NLD; ++j) copy_op(t, t, j);
+    for (int j = 0; j < C::NLD; ++j) copy_op(t, tr.lo + t, j);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
@@ -669,6 +673,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   auto tile = [&](int kt, auto maskc) {
     constexpr bool MASK = decltype(maskc)::value;
     const int key0 = kt * C::BC;
+    const int rlo = klo - key0 - h;                 // masked tiles: offsets rlo ..
+    const uint32_t rspan = (uint32_t)(khi - klo);   // rlo + rspan are visible
     const int b1 = bcur == C::NB - 1 ? 0 : bcur + 1;
     const int b2 = b1 == C::NB - 1 ? 0 : b1 + 1;
     const int boff = bcur * C::BUF;
@@ -732,7 +738,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i)
           if (m == elem_slot(b, i)) {
             float e = exp2_fast(fmaf(s[b][i], c, -l2));
-            if (MASK && key0 + b * 32 + 8 * (i / 4) + 2 * (i % 4) + h > klim) e = 0.f;
+            if (MASK) {
+              // Visible iff klo <= key <= khi, as one unsigned compare.
+              const int ke = b * 32 + 8 * (i / 4) + 2 * (i % 4);   // key - key0 - h
+              if ((uint32_t)(ke - rlo) > rspan) e = 0.f;
+            }
             ds[b][i] = e * (dp[b][i] - dl);
             if ((i + 1) % 8 == 0) sa[b][i / 8] = pack_frag<T>(ds[b], i / 8);
           }
@@ -744,13 +754,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
     __syncthreads();
     bcur = b1;
   };
-  // Tiles [0, kfull) need no mask in any row (they end before N and at or
-  // before the first query of the workgroup); a separate loop, with its own
-  // register allocation, takes the rest.
-  const int kfull = min(min(nkt, N / C::BC), CAUSAL ? (q0 + 1) / C::BC : nkt);
-  int kt = 0;
-  for (; kt < kfull; ++kt) tile(kt, std::false_type{});
-  for (; kt < nkt; ++kt) tile(kt, std::true_type{});
+  // Tiles [lo, ml) and [mu, hi) need masks in some row (the window's edges,
+  // the causal diagonal, N); [ml, mu) none.  Separate loops, each with its own
+  // register allocation.
+  int kt = tr.lo;
+  for (; kt < tr.ml; ++kt) tile(kt, std::true_type{});
+  for (; kt < tr.mu; ++kt) tile(kt, std::false_type{});
+  for (; kt < tr.hi; ++kt) tile(kt, std::true_type{});
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   if (myq < N) {
@@ -846,8 +856,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     dv[db] = f32x16{};
     dk[db] = f32x16{};
   }
-  const int nqt = (N + C::BQ - 1) / C::BQ;
-  const int qt0 = CAUSAL ? k0 / C::BQ : 0;   // earlier tiles see none of these keys
+  // Window: queries [myk - wr, myk + wl] see this lane's key.  Query tiles of
+  // the workgroup: [lo, hi), of which [ml, mu) need no mask.
+  const int wl = a.wl, wr = CAUSAL ? min(a.wr, 0) : a.wr;
+  const TileRange tr = tile_range(k0, k0 + C::BKC - 1, N, wr, wl, C::BQ, true);
+  const int qt0 = tr.lo;
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const TileLds<D> lay(lane);
@@ -928,6 +941,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   auto tile = [&](int qt, auto maskc) {
     constexpr bool MASK = decltype(maskc)::value;
     const int qi0 = qt * C::BQ;
+    // Masked tiles: query offsets (q - qi0 - h) rlo .. rlo + rspan see this
+    // lane's key (sides of kNoLimit keep the sums below 2^31).
+    const int rlo = myk - wr - qi0 - h;
+    const uint32_t rspan = (uint32_t)wl + (uint32_t)wr;
     const int b1 = bcur == 2 ? 0 : bcur + 1;
     const int b2 = b1 == 2 ? 0 : b1 + 1;
     const int boff = bcur * C::BUF;
@@ -1017,7 +1034,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i)
           if (m == elem_slot(b, i)) {
             float e = exp2_fast(fmaf(s[b][i], c, -l4[b][i / 4][i % 4]));
-            if (MASK && qi0 + b * 32 + 8 * (i / 4) + 2 * (i % 4) + h < myk) e = 0.f;
+            if (MASK) {
+              // Visible iff myk - wr <= q <= myk + wl, as one unsigned compare.
+              const int qe = b * 32 + 8 * (i / 4) + 2 * (i % 4);   // q - qi0 - h
+              if ((uint32_t)(qe - rlo) > rspan) e = 0.f;
+            }
             p[b][i] = e;
             ds[b][i] = e * dp[b][i];
             if ((i + 1) % 8 == 0) {
@@ -1033,16 +1054,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     __syncthreads();
     bcur = b1;
   };
-  // Under the causal mask, tiles from qmask on start after the last key of the
-  // workgroup and need no mask; a separate loop, with its own register
-  // allocation, takes the diagonal tiles before them.
-  const int qmask = CAUSAL ? min(nqt, (k0 + C::BKC - 1) / C::BQ + 1) : qt0;
+  // Tiles [lo, ml) and [mu, hi) need masks in some key column (the causal
+  // diagonal and the window's near edge, its far edge); [ml, mu) none, rows past
+  // N included (their L2 is +inf).  Separate loops, each with its own register
+  // allocation.
   for (int g = 0; g < a.G; ++g) {
     use_head(g);
     bcur = 0;
     int qt = qt0;
-    for (; qt < qmask; ++qt) tile(qt, std::true_type{});
-    for (; qt < nqt; ++qt) tile(qt, std::false_type{});
+    for (; qt < tr.ml; ++qt) tile(qt, std::true_type{});
+    for (; qt < tr.mu; ++qt) tile(qt, std::false_type{});
+    for (; qt < tr.hi; ++qt) tile(qt, std::true_type{});
     // No copy may still be writing LDS when the next head starts or the
     // workgroup ends, and every wave is done with the buffers.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

@@ -129,11 +129,15 @@ void fwd_kernel(FwdArgs a) {
     }
   }
 
-  const int ntiles_all = (N + C::BC - 1) / C::BC;
-  const int qlast = min(q0 + C::BR, N) - 1;
-  const int ntiles = CAUSAL ? min(ntiles_all, qlast / C::BC + 1) : ntiles_all;
-  // Last tile this wave needs; -1 if the wave holds no row below N.
-  const int wlast = (qw >= N) ? -1 : (CAUSAL ? min(qw + 31, N - 1) / C::BC : ntiles - 1);
+  // Window: keys [myq - wl, myq + wr] of this lane's row are visible.
+  const int wl = a.wl, wr = CAUSAL ? min(a.wr, 0) : a.wr;
+  // Key tiles of the workgroup: [j0, ntiles).
+  const TileRange tr = tile_range(q0, min(q0 + C::BR, N) - 1, N, wl, wr, C::BC, false);
+  const int j0 = tr.lo, ntiles = tr.hi;
+  // Tiles this wave needs: [wfirst, wlast]; wlast = -1 if the wave holds no
+  // row below N.
+  const int wfirst = max(0, qw - wl) / C::BC;
+  const int wlast = (qw >= N) ? -1 : min(qw + 31 + wr, N - 1) / C::BC;
 
   // This lane's K row inside each 32-key block (permuted for 16-bit types, so
   // that lane half h ends up holding keys 16u + 8h + t of the P~ operand).
@@ -242,25 +246,27 @@ void fwd_kernel(FwdArgs a) {
   // issued.  K therefore runs one tile ahead of V in LDS (two buffers each, one
   // barrier per iteration): iteration j reads K_{j+1} and V_j and writes
   // K_{j+2} and V_{j+1}.
-  gload_k(0);
-  gload_v(0);
-  sstore_k(0);
-  sstore_v(0);
-  if (ntiles > 1) {
-    gload_k(1);
-    sstore_k(1);
+  gload_k(j0);
+  gload_v(j0);
+  sstore_k(j0 & 1);
+  sstore_v(j0 & 1);
+  if (j0 + 1 < ntiles) {
+    gload_k(j0 + 1);
+    sstore_k((j0 + 1) & 1);
   }
   __syncthreads();
   f32x16 sc[2];
-  if (wlast >= 0) s_tile(0, sc);
-  // Iteration 0 overwrites K buffer 0 (read just above) with K_2.
+  if (wlast >= 0 && wfirst == j0) s_tile(j0 & 1, sc);
+  // Iteration j0 overwrites the K buffer read just above with K of tile j0 + 2.
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
+  for (int j = j0; j < ntiles; ++j) {
     if (j + 2 < ntiles) gload_k(j + 2);
     if (j + 1 < ntiles) gload_v(j + 1);
-    if (j <= wlast) {
+    // A wave whose first tile is the next one computes its S now.
+    if (j + 1 == wfirst && wfirst <= wlast) s_tile((j + 1) & 1, sc);
+    if (j >= wfirst && j <= wlast) {
       const int key0 = j * C::BC;
-      const bool masked = (CAUSAL && key0 + C::BC - 1 > qw) || (key0 + C::BC > N);
+      const bool masked = (key0 + C::BC - 1 > qw + wr) || (key0 < qw + 31 - wl) || (key0 + C::BC > N);
       f32x16 sn[2];
       float m_new, lsum;
       if (!masked) {
@@ -280,13 +286,13 @@ void fwd_kernel(FwdArgs a) {
           }
         }
       } else {
-        // Visible keys of this lane's row: key <= myq (causal) and key < N.
-        const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - key0 - hoff;
+        // Visible keys of this lane's row: [myq - wl, myq + wr] and below N.
+        const int lim = min(myq + wr, N - 1) - key0 - hoff, low = myq - wl - key0 - hoff;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (kb * 32 + key0_of(i) > lim) sc[kb][i] = -INFINITY;
+            if (kb * 32 + key0_of(i) > lim || kb * 32 + key0_of(i) < low) sc[kb][i] = -INFINITY;
         const float mt = tile_max(sc);
         m_new = (mt == -INFINITY) ? m_run : fmaxf(m_run, mt);
         lsum = exp_tile(sc, (m_new == -INFINITY) ? 0.f : m_new, true);
@@ -424,16 +430,16 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
       qf[ks] = (a.scale < 0.f) ? neg_frag<T>(f) : f;
     }
   }
-  // Keys above klim are masked (causal and past N).
-  const int klim = CAUSAL ? min(myq, N - 1) : N - 1;
-  const int ntiles_all = (N + C::BC - 1) / C::BC;
-  const int qlast = min(q0 + C::BR, N) - 1;
-  const int ntiles = CAUSAL ? min(ntiles_all, qlast / C::BC + 1) : ntiles_all;
+  // Visible keys of this lane's row: klo .. khi (window, causal and N).
+  const int wr = CAUSAL ? min(a.wr, 0) : a.wr;
+  const int khi = min(myq + wr, N - 1), klo = myq - a.wl;
+  // Key tiles of the workgroup: [lo, hi), of which [ml, mu) need no mask.
+  const TileRange tr = tile_range(q0, min(q0 + C::BR, N) - 1, N, a.wl, wr, C::BC, false);
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const TileLds<D> lay(lane);
   // Copy of the 4-row group q of K (mat 0) or V (mat 1) of key tile t into
-  // buffer b.  Rows past N read as zero (and are masked through klim).
+  // buffer b.  Rows past N read as zero (and are masked through khi).
   const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
   const i32x4 rsv = buffer_rsrc(V, (uint32_t)N * (2 * D));
   auto copy_group = [&](int b, int mat, int t, int q) {
@@ -467,23 +473,24 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   // for the MFMA, so that the weights of O sum to 1 exactly as used.
   float l_run = 0.f;
 
-  // Prologue: NW = 8: tiles 0, 1, 2 into buffers 0, 1, 2 (wave w copies groups
-  // 4 (w & 3) .. + 3 of K (w < 4) or V); NW = 4: K and V of tile 0 into buffer
-  // 0 and K of tile 1 into buffer 1 (wave w copies groups 4 w .. + 3 of each).
-  // Then S of tile 0.
+  // Prologue (first tile j0 = tr.lo): NW = 8: tiles j0, j0 + 1, j0 + 2 into
+  // buffers 0, 1, 2 (wave w copies groups 4 (w & 3) .. + 3 of K (w < 4) or V);
+  // NW = 4: K and V of tile j0 into buffer j0 & 1 and K of tile j0 + 1 into the
+  // other (wave w copies groups 4 w .. + 3 of each).  Then S of tile j0.
+  const int j0 = tr.lo;
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if constexpr (NW == 8) {
 #pragma unroll
     for (int t = 0; t < 3; ++t)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) copy_group(t, w >> 2, t, 4 * (w & 3) + kk);
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // tile 2 may still be in flight
+      for (int kk = 0; kk < 4; ++kk) copy_group(t, w >> 2, j0 + t, 4 * (w & 3) + kk);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // tile j0 + 2 may still be in flight
   } else {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      copy_group(0, 0, 0, 4 * w + kk);
-      copy_group(0, 1, 0, 4 * w + kk);
-      copy_group(1, 0, 1, 4 * w + kk);
+      copy_group(j0 & 1, 0, j0, 4 * w + kk);
+      copy_group(j0 & 1, 1, j0, 4 * w + kk);
+      copy_group((j0 + 1) & 1, 0, j0 + 1, 4 * w + kk);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
@@ -493,8 +500,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   f32x16 sA[2], sB[2];
   sA[0] = f32x16{};
   sA[1] = f32x16{};
+  {
+    const int kb0 = NW == 8 ? 0 : (j0 & 1) * C::BUF;
 #pragma unroll
-  for (int m = 0; m < C::NS; ++m) sA[m & 1] = M::mma(opS(0, m), qf[m >> 1], sA[m & 1]);
+    for (int m = 0; m < C::NS; ++m) sA[m & 1] = M::mma(opS(kb0, m), qf[m >> 1], sA[m & 1]);
+  }
 
   constexpr int NS = C::NS, NV = C::NV, NM = C::NM, NA = C::NA;
   constexpr int PD = 4;
@@ -526,6 +536,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
     sn[1] = f32x16{};
     float mx = -INFINITY, m_new = m_run, nm = 0.f;
     bool grow = false;
+    // Masked tiles: visible element offsets (key - key0 - h) of this lane's row.
+    const int rlo = klo - key0 - h;
+    const uint32_t rspan = (uint32_t)(khi - klo);   // khi >= klo for rows below N
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
     frag opq[PD];
     auto operand = [&](int m) -> frag { return m < NS ? opS(kboff, m) : opV(vboff, m - NS); };
@@ -565,8 +578,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
       for (int e = 0; e < 32; ++e)
         if (m == max_slot(e)) {
           const int kb = e >> 4, i = e & 15;
-          if constexpr (MASK)
-            if (key0 + kb * 32 + 8 * (i / 4) + 2 * (i % 4) + h > klim) sc[kb][i] = -INFINITY;
+          if constexpr (MASK) {
+            // Visible iff rlo <= ke <= rhi, as one unsigned compare.
+            const int ke = kb * 32 + 8 * (i / 4) + 2 * (i % 4);   // key - key0 - h
+            if ((uint32_t)(ke - rlo) > rspan) sc[kb][i] = -INFINITY;
+          }
           mx = fmaxf(mx, sc[kb][i]);
         }
       if constexpr (m == NA) {
@@ -621,25 +637,34 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
     __syncthreads();
     b0 = (b0 + 1) & 3;
   };
-  // Tiles [0, jfull) need no mask in any row of the workgroup (they end at or
-  // before its first query and before N); the masked stream, a separate loop
-  // so that each loop body keeps its own register allocation, takes the rest.
-  const int jfull = min(min(ntiles, N / C::BC), CAUSAL ? (q0 + 1) / C::BC : ntiles);
-  int j = 0;
-  for (; j + 1 < jfull; j += 2) {
+  // Tiles [lo, ml) and [mu, hi) need masks in some row of the workgroup (the
+  // window's edges, the causal diagonal, N); [ml, mu) none.  Each range runs in
+  // a loop of its own, so that each loop body keeps its own register
+  // allocation; after an odd tile the S registers are handed over by copy.
+  int j = j0;
+  for (; j + 1 < tr.ml; j += 2) {
+    iteration(j, std::true_type{}, sA, sB);
+    iteration(j + 1, std::true_type{}, sB, sA);
+  }
+  if (j < tr.ml) {
+    iteration(j++, std::true_type{}, sA, sB);
+    sA[0] = sB[0];
+    sA[1] = sB[1];
+  }
+  for (; j + 1 < tr.mu; j += 2) {
     iteration(j, std::false_type{}, sA, sB);
     iteration(j + 1, std::false_type{}, sB, sA);
   }
-  if (j < jfull) {
+  if (j < tr.mu) {
     iteration(j++, std::false_type{}, sA, sB);
     sA[0] = sB[0];
     sA[1] = sB[1];
   }
-  for (; j + 1 < ntiles; j += 2) {
+  for (; j + 1 < tr.hi; j += 2) {
     iteration(j, std::true_type{}, sA, sB);
     iteration(j + 1, std::true_type{}, sB, sA);
   }
-  if (j < ntiles) iteration(j, std::true_type{}, sA, sB);
+  if (j < tr.hi) iteration(j, std::true_type{}, sA, sB);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   const float l = half_sum(l_run);

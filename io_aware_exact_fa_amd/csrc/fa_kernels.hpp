@@ -8,6 +8,9 @@
 
 namespace fa {
 
+// An open side of the attention window (no limit on j - i or i - j).
+constexpr int kNoLimit = 1 << 30;
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -22,6 +25,9 @@ struct FwdArgs {
   // length (the grid and the LSE rows per (sequence, head)).
   const int* cu_seqlens = nullptr;
   int total = 0;
+  // Window: key j is visible to query i iff i - wl <= j <= i + wr (positions in
+  // the sequence; wl, wr >= 0 or kNoLimit).  Causal launches take wr = 0.
+  int wl = kNoLimit, wr = kNoLimit;
 };
 
 struct BwdArgs {
@@ -42,7 +48,33 @@ struct BwdArgs {
   int G = 1;      // query heads per K/V head (K, V, dK, dV have H / G heads)
   const int* cu_seqlens = nullptr;   // as in FwdArgs; workspace and LSE rows per
   int total = 0;                     // (sequence, head) stay Np and N
+  int wl = kNoLimit, wr = kNoLimit;  // as in FwdArgs
 };
+
+// Tile ranges of one workgroup under the window: rows [ra, rb] of the outer
+// operand (queries in the forward and dQ, keys in dK/dV) need inner tiles
+// (BI rows each, `n` rows in all) [lo, hi); of these, [ml, mu) need no mask in
+// any outer row (every element inside the window and below n), [lo, ml) and
+// [mu, hi) do.  The inner rows visible to outer row r are [r - back, r + fwd],
+// with back >= 0 and fwd >= 0 (or kNoLimit).  `full_tail`: inner rows past n
+// need no mask (the dK/dV kernels, whose padding rows contribute zero).
+struct TileRange {
+  int lo, ml, mu, hi;
+};
+__device__ inline TileRange tile_range(int ra, int rb, int n, int back, int fwd, int BI,
+                                       bool full_tail) {
+  TileRange t;
+  const int first = max(0, ra - back), last = min(n - 1, rb + fwd);
+  t.lo = first / BI;
+  t.hi = last / BI + 1;
+  // [ml, mu): tiles whose first row is >= rb - back and whose last row is <= ra + fwd.
+  t.ml = rb - back <= 0 ? t.lo : min(t.hi, (rb - back + BI - 1) / BI);
+  t.ml = max(t.ml, t.lo);
+  int mu = min(t.hi, (ra + fwd + 1) / BI);
+  if (!full_tail) mu = min(mu, n / BI);
+  t.mu = max(mu, t.ml);
+  return t;
+}
 
 // Rows of the (sequence, query head) pair hd = b H + h in the row-major
 // tensors: the first row of its query slab (q, o, dout, dq), of its K/V head's

@@ -12,7 +12,8 @@ Contents
 ``attention``   the plain definition: S and P materialized, analytic backward;
                 also with grouped key/value heads (forward_gqa, backward_gqa)
                 and padding-free variable-length batches (forward_varlen,
-                backward_varlen).
+                backward_varlen); every function takes an optional local
+                window (window_visible).
 ``recurrence``  the online-softmax tile recurrence and the two-tile merge,
                 written in the pages' order; used only to pin that the
                 recurrence is exact, never as the reference for the GPU path.
@@ -34,5 +35,6 @@ from .attention import (  # noqa: F401
     probabilities,
     row_softmax,
     scores,
+    window_visible,
 )
 from .recurrence import merge_tile, online_forward_head  # noqa: F401

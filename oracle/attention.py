@@ -49,12 +49,32 @@ def causal_visible(n_q: int, n_k: int) -> np.ndarray:
     return j <= i
 
 
-def scores(q, k, scale: float, causal: bool) -> np.ndarray:
-    """S = scale * Q K^T for one head, with -inf where the causal mask hides a key."""
+def window_visible(n_q: int, n_k: int, window) -> np.ndarray:
+    """Boolean [n_q, n_k]: key j is inside the window (left, right) of query i iff
+    i - left <= j <= i + right; a side given as None or a negative number is
+    open.  Local attention: "어텐션 비용 줄이기" (ailab.paldyn.com), sections
+    "지역 윈도와 글로벌 토큰" (w keys on each side) and "슬라이딩 윈도와 수용 영역"
+    (the most recent W keys: causal with left = W - 1)."""
+    left, right = window
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    vis = np.ones((n_q, n_k), dtype=bool)
+    if left is not None and left >= 0:
+        vis &= j >= i - left
+    if right is not None and right >= 0:
+        vis &= j <= i + right
+    return vis
+
+
+def scores(q, k, scale: float, causal: bool, window=None) -> np.ndarray:
+    """S = scale * Q K^T for one head, with -inf where the causal mask or the
+    window hides a key."""
     q, k = _f64(q), _f64(k)
     s = float(scale) * (q @ k.T)
     if causal:
         s = np.where(causal_visible(q.shape[0], k.shape[0]), s, -np.inf)
+    if window is not None:
+        s = np.where(window_visible(q.shape[0], k.shape[0], window), s, -np.inf)
     return s
 
 
@@ -74,26 +94,26 @@ def row_softmax(s) -> tuple[np.ndarray, np.ndarray]:
     return p, lse
 
 
-def probabilities(q, k, scale: float, causal: bool) -> np.ndarray:
+def probabilities(q, k, scale: float, causal: bool, window=None) -> np.ndarray:
     """P = softmax(scale * Q K^T + mask) for one head."""
-    p, _ = row_softmax(scores(q, k, scale, causal))
+    p, _ = row_softmax(scores(q, k, scale, causal, window))
     return p
 
 
-def forward_head(q, k, v, scale: float, causal: bool) -> tuple[np.ndarray, np.ndarray]:
+def forward_head(q, k, v, scale: float, causal: bool, window=None) -> tuple[np.ndarray, np.ndarray]:
     """O = P V and LSE for one head (q: [N,d], k: [N,d], v: [N,dv])."""
-    p, lse = row_softmax(scores(q, k, scale, causal))
+    p, lse = row_softmax(scores(q, k, scale, causal, window))
     o = p @ _f64(v)
     return o, lse
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool) -> dict:
+def backward_head(q, k, v, do, scale: float, causal: bool, window=None) -> dict:
     """Analytic gradients of sum(O * dO) for one head.
 
     Returns dict(dq, dk, dv, D, p, dp, ds); D is computed as rowsum(P * dP).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    p, _ = row_softmax(scores(q, k, scale, causal))
+    p, _ = row_softmax(scores(q, k, scale, causal, window))
     dv = p.T @ do                          # dV = P^T dO
     dp = do @ v.T                          # dP = dO V^T
     D = (p * dp).sum(axis=1)               # D_i = sum_j P_ij dP_ij
@@ -107,7 +127,7 @@ def _heads(shape):
     return np.ndindex(*shape[:-2])
 
 
-def forward(q, k, v, scale: float, causal: bool, heads=None):
+def forward(q, k, v, scale: float, causal: bool, heads=None, window=None):
     """Batched forward over leading axes ([..., N, d]); returns (O, LSE).
 
     ``heads`` optionally restricts the work to a list of leading-index tuples;
@@ -118,11 +138,11 @@ def forward(q, k, v, scale: float, causal: bool, heads=None):
     o = np.full(lead + (q.shape[-2], v.shape[-1]), np.nan)
     lse = np.full(lead + (q.shape[-2],), np.nan)
     for idx in (heads if heads is not None else _heads(q.shape)):
-        o[idx], lse[idx] = forward_head(q[idx], k[idx], v[idx], scale, causal)
+        o[idx], lse[idx] = forward_head(q[idx], k[idx], v[idx], scale, causal, window)
     return o, lse
 
 
-def backward(q, k, v, do, scale: float, causal: bool, heads=None):
+def backward(q, k, v, do, scale: float, causal: bool, heads=None, window=None):
     """Batched backward over leading axes; returns (dQ, dK, dV, D)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     lead = q.shape[:-2]
@@ -131,7 +151,7 @@ def backward(q, k, v, do, scale: float, causal: bool, heads=None):
     dv = np.full(v.shape, np.nan)
     D = np.full(lead + (q.shape[-2],), np.nan)
     for idx in (heads if heads is not None else _heads(q.shape)):
-        g = backward_head(q[idx], k[idx], v[idx], do[idx], scale, causal)
+        g = backward_head(q[idx], k[idx], v[idx], do[idx], scale, causal, window)
         dq[idx], dk[idx], dv[idx], D[idx] = g["dq"], g["dk"], g["dv"], g["D"]
     return dq, dk, dv, D
 
@@ -153,7 +173,7 @@ def _group(h_q: int, h_kv: int) -> int:
     return h_q // h_kv
 
 
-def forward_gqa(q, k, v, scale: float, causal: bool):
+def forward_gqa(q, k, v, scale: float, causal: bool, window=None):
     """q [B, H, N, d], k [B, H_kv, N, d], v [B, H_kv, N, dv] -> (O [B, H, N, dv],
     LSE [B, H, N])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -163,11 +183,12 @@ def forward_gqa(q, k, v, scale: float, causal: bool):
     lse = np.empty((B, H, q.shape[2]))
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h // g], v[b, h // g], scale, causal)
+            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h // g], v[b, h // g], scale, causal,
+                                              window)
     return o, lse
 
 
-def backward_gqa(q, k, v, do, scale: float, causal: bool):
+def backward_gqa(q, k, v, do, scale: float, causal: bool, window=None):
     """Gradients of sum(O * dO) for forward_gqa: (dQ [B, H, N, d], dK [B, H_kv, N, d],
     dV [B, H_kv, N, dv])."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
@@ -178,7 +199,7 @@ def backward_gqa(q, k, v, do, scale: float, causal: bool):
     dv = np.zeros(v.shape)
     for b in range(B):
         for h in range(H):
-            r = backward_head(q[b, h], k[b, h // g], v[b, h // g], do[b, h], scale, causal)
+            r = backward_head(q[b, h], k[b, h // g], v[b, h // g], do[b, h], scale, causal, window)
             dq[b, h] = r["dq"]
             dk[b, h // g] += r["dk"]
             dv[b, h // g] += r["dv"]
@@ -210,7 +231,8 @@ def _spans(cu_seqlens, total: int, max_s: int):
     return cu
 
 
-def forward_varlen(q, k, v, cu_seqlens, max_s: int, scale: float, causal: bool, seqs=None):
+def forward_varlen(q, k, v, cu_seqlens, max_s: int, scale: float, causal: bool, seqs=None,
+                   window=None):
     """q [H, total, d], k [H_kv, total, d], v [H_kv, total, dv] -> (O [H, total, dv],
     LSE [B, H, max_s]).  ``seqs`` optionally restricts the work to some sequences."""
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -226,11 +248,12 @@ def forward_varlen(q, k, v, cu_seqlens, max_s: int, scale: float, causal: bool, 
             continue   # an empty sequence has no rows
         for h in range(H):
             o[h, s0:s1], lse[b, h, : s1 - s0] = forward_head(
-                q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], scale, causal)
+                q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], scale, causal, window)
     return o, lse
 
 
-def backward_varlen(q, k, v, do, cu_seqlens, max_s: int, scale: float, causal: bool, seqs=None):
+def backward_varlen(q, k, v, do, cu_seqlens, max_s: int, scale: float, causal: bool, seqs=None,
+                    window=None):
     """Gradients of sum(O * dO) for forward_varlen: (dQ [H, total, d],
     dK [H_kv, total, d], dV [H_kv, total, dv]); rows outside the computed
     sequences are NaN."""
@@ -249,7 +272,7 @@ def backward_varlen(q, k, v, do, cu_seqlens, max_s: int, scale: float, causal: b
         dv[:, s0:s1] = 0.0
         for h in range(H):
             r = backward_head(q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], do[h, s0:s1],
-                              scale, causal)
+                              scale, causal, window)
             dq[h, s0:s1] = r["dq"]
             dk[h // g, s0:s1] += r["dk"]
             dv[h // g, s0:s1] += r["dv"]

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 4
+    assert fa.fa_abi_version() == 5
     for st in range(6):
         assert fa.fa_status_string(st) and fa.fa_status_string(st) != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -171,6 +171,32 @@ def test_varlen_rejects():
     assert _bwd_varlen(dk=None) == E
 
 
+def test_attn_struct_layout():
+    """ctypes mirror of struct fa_attn: natural alignment on x86-64 (the pointer at
+    byte 40, the whole 56 bytes)."""
+    assert ctypes.sizeof(fa.FaAttn) == 56
+    assert fa.FaAttn.cu_seqlens.offset == 40 and fa.FaAttn.total.offset == 48
+    assert fa.FaAttn.window_left.offset == 24 and fa.FaAttn.scale.offset == 32
+
+
+def test_ex_rejects():
+    E = fa.FA_ERR_INVALID_ARGUMENT
+    good = dict(B=1, H=8, H_kv=2, N=128, d=64, causal=1, scale=0.1, dtype=fa.FA_F16)
+    ws, nb = 0x10000, fa.fa_bwd_workspace_size(1, 8, 128, 64)
+    fwd = lambda p: fa.fa_fwd_ex(p, P, P, P, P, P, None)
+    bwd = lambda p, nb=nb: fa.fa_bwd_ex(p, P, P, P, P, P, P, P, P, P, ws, nb, None)
+    assert fwd(None) == E and bwd(None) == E
+    for window in ((-2, -1), (-1, -7)):
+        assert fwd(fa.attn(**good, window=window)) == E
+        assert bwd(fa.attn(**good, window=window)) == E
+    assert fwd(fa.attn(**{**good, "H_kv": 3})) == E
+    assert fwd(fa.attn(**{**good, "d": 96})) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(fa.attn(**good), nb - 1) == fa.FA_ERR_WORKSPACE
+    # Packed batch through the description: total must be positive.
+    assert fwd(fa.attn(**good, cu_seqlens=P, total=0)) == E
+    assert fa.fa_fwd_ex(fa.attn(**good), P, None, P, P, P, None) == E
+
+
 def test_too_many_heads_rejected():
     """B*H above 2^24 would overflow the tile grids' 32-bit work index."""
     assert _fwd(B=65535, H=257, N=1) == fa.FA_ERR_UNSUPPORTED
@@ -202,6 +228,10 @@ def test_valid_arguments_without_gpu_report_device_error():
                          ws, nb, None) == fa.FA_ERR_DEVICE
     assert _fwd_varlen() == fa.FA_ERR_DEVICE
     assert _bwd_varlen() == fa.FA_ERR_DEVICE
+    p = fa.attn(1, 8, 2, 128, 64, 1, 0.1, fa.FA_F16, window=(16, 0))
+    assert fa.fa_fwd_ex(p, P, P, P, P, P, None) == fa.FA_ERR_DEVICE
+    assert fa.fa_bwd_ex(p, P, P, P, P, P, P, P, P, P, 0x10000,
+                        fa.fa_bwd_workspace_size(1, 8, 128, 64), None) == fa.FA_ERR_DEVICE
     nb = fa.fa_bwd_workspace_size(1, 1, 128, 64)
     assert fa.fa_bwd_preprocess(P, P, P, 1, 1, 128, 64, fa.FA_F16, 0x10000, nb, None) == fa.FA_ERR_DEVICE
     assert fa.fa_bwd_dq(P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, 0x10000, nb,

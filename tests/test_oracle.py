@@ -438,3 +438,95 @@ def test_varlen_rejects_bad_offsets():
     for bad, max_s in (([1, 3, 7], 4), ([0, 4, 3], 4), ([0, 3, 8], 5), ([0, 3, 7], 3)):
         with pytest.raises(ValueError):
             oracle.forward_varlen(q, k, v, np.array(bad), max_s, 0.5, False)
+
+
+# ----------------------------------------------------------- local windows
+
+
+def _win_inputs(n=9, d=3, dv=2, seed=31):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((n, d)), r.standard_normal((n, d)), r.standard_normal((n, dv)),
+            r.standard_normal((n, dv)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_wider_than_the_sequence_changes_nothing(causal):
+    q, k, v, do = _win_inputs()
+    o, lse = oracle.forward_head(q, k, v, 0.7, causal)
+    for window in ((-1, -1), (None, None), (8, 8), (100, 3 if causal else 100)):
+        o2, lse2 = oracle.forward_head(q, k, v, 0.7, causal, window)
+        np.testing.assert_array_equal(o2, o)
+        np.testing.assert_array_equal(lse2, lse)
+
+
+def test_window_of_one_key_is_the_value_row():
+    """Window (0, 0): each query sees only its own key, so O_i = v_i exactly and
+    LSE_i = scale q_i . k_i; dQ and dK vanish (a softmax over one key is constant)."""
+    q, k, v, do = _win_inputs()
+    o, lse = oracle.forward_head(q, k, v, 0.7, False, (0, 0))
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.7 * (q * k).sum(axis=1), rtol=0, atol=1e-14)
+    g = oracle.backward_head(q, k, v, do, 0.7, False, (0, 0))
+    np.testing.assert_allclose(g["dv"], do, atol=1e-15)
+    assert np.abs(g["dq"]).max() < 1e-14 and np.abs(g["dk"]).max() < 1e-14
+
+
+@pytest.mark.parametrize("W", [1, 2, 4])
+def test_sliding_window_brute_force(W):
+    """The most recent W keys (causal, left = W - 1), written as a per-row loop over
+    an explicit key list with math.exp: no mask matrix, no numpy softmax."""
+    q, k, v, _ = _win_inputs(n=7)
+    o, lse = oracle.forward_head(q, k, v, 0.8, True, (W - 1, -1))
+    for i in range(7):
+        keys = list(range(max(0, i - W + 1), i + 1))
+        sc = [0.8 * sum(q[i, t] * k[j, t] for t in range(3)) for j in keys]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        tot = sum(w)
+        for c in range(2):
+            assert abs(o[i, c] - sum(wj * v[j, c] for wj, j in zip(w, keys)) / tot) < 1e-13
+        assert abs(lse[i] - (mx + math.log(tot))) < 1e-13
+
+
+@pytest.mark.parametrize("left,right", [(2, 2), (3, 1), (0, 4), (5, 0)])
+def test_local_window_zero_query(left, right):
+    """Q = 0: row i is the mean of v over keys max(0, i - left) .. min(n - 1, i + right)
+    and LSE = ln(their number); an asymmetric window pins which side is which."""
+    _, k, v, _ = _win_inputs(n=10)
+    o, lse = oracle.forward_head(np.zeros((10, 3)), k, v, 0.5, False, (left, right))
+    for i in range(10):
+        lo, hi = max(0, i - left), min(9, i + right)
+        np.testing.assert_allclose(o[i], v[lo:hi + 1].mean(axis=0), atol=1e-14)
+        np.testing.assert_allclose(lse[i], math.log(hi - lo + 1), atol=1e-14)
+
+
+def test_window_cell_count_matches_the_page():
+    """The efficiency page counts N = 4096 with a 512-wide window (256 on each side) as
+    4096 x 512 = 2,097,152 cells, one eighth of full attention; the mask's count
+    differs from that only by the rows whose window is cut at the sequence ends."""
+    n, half = 4096, 256
+    cells = int(oracle.window_visible(n, n, (half, half - 1)).sum())
+    edge = half * (half + 1) // 2 + half * (half - 1) // 2   # keys cut at both ends
+    assert cells == n * 2 * half - edge
+    assert abs(cells / (n * n) - 1 / 8) < 0.01
+
+
+@pytest.mark.parametrize("causal,window", [(False, (2, 1)), (True, (2, -1)), (False, (0, 3))])
+def test_window_finite_differences(causal, window):
+    q, k, v, do = _win_inputs(n=6, d=2, dv=2)
+    scale, hstep = 0.9, 1e-6
+    g = oracle.backward_head(q, k, v, do, scale, causal, window)
+
+    def loss(qq, kk, vv):
+        return float((oracle.forward_head(qq, kk, vv, scale, causal, window)[0] * do).sum())
+
+    for which, (x, gg) in enumerate(zip((q, k, v), (g["dq"], g["dk"], g["dv"]))):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += hstep
+            xm[idx] -= hstep
+            ap, am = [q, k, v], [q, k, v]
+            ap[which], am[which] = xp, xm
+            fd[idx] = (loss(*ap) - loss(*am)) / (2 * hstep)
+        np.testing.assert_allclose(gg, fd, rtol=0, atol=1e-7, err_msg="qkv"[which])

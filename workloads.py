@@ -38,10 +38,15 @@ class Workload:
     qk_std: float = 1.0
     offset: bool = False
     H_kv: int = 0       # key/value heads (0: one per query head)
+    window: tuple = (-1, -1)   # local window (left, right); -1: open side
 
     @property
     def kv_heads(self) -> int:
         return self.H_kv or self.H
+
+    @property
+    def windowed(self) -> bool:
+        return tuple(self.window) != (-1, -1)
 
     @property
     def scale(self) -> float:
@@ -52,7 +57,10 @@ class Workload:
         return _TORCH_DTYPES[self.dtype]
 
     def fwd_flops(self) -> float:
-        """Forward FLOPs counted as 4*B*H*N^2*d, halved under the causal mask."""
+        """Forward FLOPs counted as 4*B*H*N^2*d, halved under the causal mask; with a
+        local window, 4*B*H*d per visible (query, key) pair."""
+        if self.windowed:
+            return 4.0 * self.B * self.H * self.d * visible_pairs(self.N, self.causal, self.window)
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
@@ -62,6 +70,18 @@ class Workload:
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
+
+
+def visible_pairs(n: int, causal: bool, window) -> int:
+    """Number of (query, key) pairs with max(0, i - left) <= j <= min(n - 1, i + right)
+    (right = 0 under the causal mask; -1 = open side), summed row by row."""
+    left, right = window
+    left = n if left < 0 else left
+    right = (n if right < 0 else right) if not causal else min(0 if right < 0 else right, 0)
+    total = 0
+    for i in range(n):   # n is at most a few tens of thousands
+        total += min(n - 1, i + right) - max(0, i - left) + 1
+    return total
 
 
 # The five workloads of the method's measurement plan, named by what they are.
@@ -82,7 +102,14 @@ GQA_CAUSAL_BF16 = Workload("b4h32kv4n4096d128-bf16-causal-gqa", 4, 32, 4096, 128
                            1007, H_kv=4)
 GQA = (GQA_BF16, GQA_CAUSAL_BF16)
 
-BY_NAME = {w.name: w for w in ALL + GQA}
+# Sliding-window attention: each query sees its 4096 most recent keys (window
+# left 4095, causal), with grouped K/V heads: the local-attention configuration of
+# the efficiency page's sliding-window section, at N = 16384.
+WINDOW_BF16 = Workload("b2h32kv8n16384d128-bf16-causal-window4096", 2, 32, 16384, 128, "bf16",
+                       True, 1010, H_kv=8, window=(4095, -1))
+WINDOWED = (WINDOW_BF16,)
+
+BY_NAME = {w.name: w for w in ALL + GQA + WINDOWED}
 
 
 def make_inputs(w: Workload) -> dict:
