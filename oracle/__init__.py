@@ -14,6 +14,7 @@ Contents
                 and padding-free variable-length batches (forward_varlen,
                 backward_varlen); every function takes an optional local
                 window (window_visible).
+``philox``      Philox4x32-10 and the dropout keep mask built from it.
 ``recurrence``  the online-softmax tile recurrence and the two-tile merge,
                 written in the pages' order; used only to pin that the
                 recurrence is exact, never as the reference for the GPU path.
@@ -26,6 +27,8 @@ from .attention import (  # noqa: F401
     backward,
     backward_gqa,
     backward_varlen,
+    dropped,
+    head_drop,
     backward_head,
     causal_visible,
     forward,
@@ -38,3 +41,4 @@ from .attention import (  # noqa: F401
     window_visible,
 )
 from .recurrence import merge_tile, online_forward_head  # noqa: F401
+from . import philox  # noqa: F401

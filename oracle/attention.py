@@ -37,6 +37,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import philox
+
 
 def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
@@ -100,22 +102,35 @@ def probabilities(q, k, scale: float, causal: bool, window=None) -> np.ndarray:
     return p
 
 
-def forward_head(q, k, v, scale: float, causal: bool, window=None) -> tuple[np.ndarray, np.ndarray]:
-    """O = P V and LSE for one head (q: [N,d], k: [N,d], v: [N,dv])."""
+def dropped(p, drop):
+    """Dropout applied to P: drop = (keep mask [n_q, n_k], scale) or None.  Kept
+    entries are multiplied by the scale (the inverse keep probability), so the
+    expectation over masks is P itself."""
+    if drop is None:
+        return p
+    mask, sc = drop
+    return np.where(mask, p * float(sc), 0.0)
+
+
+def forward_head(q, k, v, scale: float, causal: bool, window=None,
+                 drop=None) -> tuple[np.ndarray, np.ndarray]:
+    """O = dropout(P) V and LSE for one head (q: [N,d], k: [N,d], v: [N,dv]).  LSE
+    is that of the undropped softmax (it is what the backward recomputes P from)."""
     p, lse = row_softmax(scores(q, k, scale, causal, window))
-    o = p @ _f64(v)
+    o = dropped(p, drop) @ _f64(v)
     return o, lse
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool, window=None) -> dict:
+def backward_head(q, k, v, do, scale: float, causal: bool, window=None, drop=None) -> dict:
     """Analytic gradients of sum(O * dO) for one head.
 
     Returns dict(dq, dk, dv, D, p, dp, ds); D is computed as rowsum(P * dP).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     p, _ = row_softmax(scores(q, k, scale, causal, window))
-    dv = p.T @ do                          # dV = P^T dO
-    dp = do @ v.T                          # dP = dO V^T
+    dv = dropped(p, drop).T @ do           # dV = dropout(P)^T dO
+    dp = dropped(do @ v.T, drop)           # dP = dropout'(dO V^T): the chain rule
+                                           # through the kept entries and the scale
     D = (p * dp).sum(axis=1)               # D_i = sum_j P_ij dP_ij
     ds = p * (dp - D[:, None])             # dS_ij = P_ij (dP_ij - D_i)
     dq = float(scale) * (ds @ k)           # dQ = tau dS K
@@ -127,7 +142,23 @@ def _heads(shape):
     return np.ndindex(*shape[:-2])
 
 
-def forward(q, k, v, scale: float, causal: bool, heads=None, window=None):
+def head_drop(dropout, hd: int, n: int):
+    """The (mask, scale) of attention head hd = b H + h for dropout = (p_drop, seed,
+    offset), or None.  The scale is 2^16 / threshold, the inverse of the keep
+    probability the 16-bit threshold realizes (0 when everything is dropped)."""
+    if dropout is None:
+        return None
+    p_drop, seed, offset = dropout
+    t = philox.keep_threshold(p_drop)
+    return philox.keep_mask(hd, n, n, p_drop, seed, offset), (65536.0 / t if t > 0 else 0.0)
+
+
+def _hd(idx, shape):
+    """Head index b H + h of a [B, H, ...] leading index."""
+    return int(idx[0]) * int(shape[1]) + int(idx[1])
+
+
+def forward(q, k, v, scale: float, causal: bool, heads=None, window=None, dropout=None):
     """Batched forward over leading axes ([..., N, d]); returns (O, LSE).
 
     ``heads`` optionally restricts the work to a list of leading-index tuples;
@@ -138,11 +169,12 @@ def forward(q, k, v, scale: float, causal: bool, heads=None, window=None):
     o = np.full(lead + (q.shape[-2], v.shape[-1]), np.nan)
     lse = np.full(lead + (q.shape[-2],), np.nan)
     for idx in (heads if heads is not None else _heads(q.shape)):
-        o[idx], lse[idx] = forward_head(q[idx], k[idx], v[idx], scale, causal, window)
+        drop = head_drop(dropout, _hd(idx, q.shape), q.shape[-2])
+        o[idx], lse[idx] = forward_head(q[idx], k[idx], v[idx], scale, causal, window, drop)
     return o, lse
 
 
-def backward(q, k, v, do, scale: float, causal: bool, heads=None, window=None):
+def backward(q, k, v, do, scale: float, causal: bool, heads=None, window=None, dropout=None):
     """Batched backward over leading axes; returns (dQ, dK, dV, D)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     lead = q.shape[:-2]
@@ -151,7 +183,8 @@ def backward(q, k, v, do, scale: float, causal: bool, heads=None, window=None):
     dv = np.full(v.shape, np.nan)
     D = np.full(lead + (q.shape[-2],), np.nan)
     for idx in (heads if heads is not None else _heads(q.shape)):
-        g = backward_head(q[idx], k[idx], v[idx], do[idx], scale, causal, window)
+        drop = head_drop(dropout, _hd(idx, q.shape), q.shape[-2])
+        g = backward_head(q[idx], k[idx], v[idx], do[idx], scale, causal, window, drop)
         dq[idx], dk[idx], dv[idx], D[idx] = g["dq"], g["dk"], g["dv"], g["D"]
     return dq, dk, dv, D
 
@@ -173,7 +206,7 @@ def _group(h_q: int, h_kv: int) -> int:
     return h_q // h_kv
 
 
-def forward_gqa(q, k, v, scale: float, causal: bool, window=None):
+def forward_gqa(q, k, v, scale: float, causal: bool, window=None, dropout=None):
     """q [B, H, N, d], k [B, H_kv, N, d], v [B, H_kv, N, dv] -> (O [B, H, N, dv],
     LSE [B, H, N])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -183,12 +216,13 @@ def forward_gqa(q, k, v, scale: float, causal: bool, window=None):
     lse = np.empty((B, H, q.shape[2]))
     for b in range(B):
         for h in range(H):
+            drop = head_drop(dropout, b * H + h, q.shape[2])
             o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h // g], v[b, h // g], scale, causal,
-                                              window)
+                                              window, drop)
     return o, lse
 
 
-def backward_gqa(q, k, v, do, scale: float, causal: bool, window=None):
+def backward_gqa(q, k, v, do, scale: float, causal: bool, window=None, dropout=None):
     """Gradients of sum(O * dO) for forward_gqa: (dQ [B, H, N, d], dK [B, H_kv, N, d],
     dV [B, H_kv, N, dv])."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
@@ -199,7 +233,9 @@ def backward_gqa(q, k, v, do, scale: float, causal: bool, window=None):
     dv = np.zeros(v.shape)
     for b in range(B):
         for h in range(H):
-            r = backward_head(q[b, h], k[b, h // g], v[b, h // g], do[b, h], scale, causal, window)
+            drop = head_drop(dropout, b * H + h, q.shape[2])
+            r = backward_head(q[b, h], k[b, h // g], v[b, h // g], do[b, h], scale, causal, window,
+                              drop)
             dq[b, h] = r["dq"]
             dk[b, h // g] += r["dk"]
             dv[b, h // g] += r["dv"]
@@ -207,6 +243,10 @@ def backward_gqa(q, k, v, do, scale: float, causal: bool, window=None):
 
 
 # ---------------------------------------------------------------- variable-length batches
+#
+# Dropout (every batched function's `dropout` = (p_drop, seed, offset)): the
+# keep mask of head b H + h is philox.keep_mask; in a packed batch, b is the
+# sequence and positions count inside it.
 #
 # Padding-free batches: the 2022 interface described on "FlashAttention 원 논문
 # 해부" (section "내부 구조와 실제 실행 흐름", items 2 and 3) packs the valid tokens
@@ -232,7 +272,7 @@ def _spans(cu_seqlens, total: int, max_s: int):
 
 
 def forward_varlen(q, k, v, cu_seqlens, max_s: int, scale: float, causal: bool, seqs=None,
-                   window=None):
+                   window=None, dropout=None):
     """q [H, total, d], k [H_kv, total, d], v [H_kv, total, dv] -> (O [H, total, dv],
     LSE [B, H, max_s]).  ``seqs`` optionally restricts the work to some sequences."""
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -247,13 +287,14 @@ def forward_varlen(q, k, v, cu_seqlens, max_s: int, scale: float, causal: bool, 
         if s1 == s0:
             continue   # an empty sequence has no rows
         for h in range(H):
+            drop = head_drop(dropout, b * H + h, s1 - s0)
             o[h, s0:s1], lse[b, h, : s1 - s0] = forward_head(
-                q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], scale, causal, window)
+                q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], scale, causal, window, drop)
     return o, lse
 
 
 def backward_varlen(q, k, v, do, cu_seqlens, max_s: int, scale: float, causal: bool, seqs=None,
-                    window=None):
+                    window=None, dropout=None):
     """Gradients of sum(O * dO) for forward_varlen: (dQ [H, total, d],
     dK [H_kv, total, d], dV [H_kv, total, dv]); rows outside the computed
     sequences are NaN."""
@@ -271,8 +312,9 @@ def backward_varlen(q, k, v, do, cu_seqlens, max_s: int, scale: float, causal: b
         dk[:, s0:s1] = 0.0
         dv[:, s0:s1] = 0.0
         for h in range(H):
+            drop = head_drop(dropout, b * H + h, s1 - s0)
             r = backward_head(q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], do[h, s0:s1],
-                              scale, causal, window)
+                              scale, causal, window, drop)
             dq[h, s0:s1] = r["dq"]
             dk[h // g, s0:s1] += r["dk"]
             dv[h // g, s0:s1] += r["dv"]

@@ -530,3 +530,126 @@ def test_window_finite_differences(causal, window):
             ap[which], am[which] = xp, xm
             fd[idx] = (loss(*ap) - loss(*am)) / (2 * hstep)
         np.testing.assert_allclose(gg, fd, rtol=0, atol=1e-7, err_msg="qkv"[which])
+
+
+# ----------------------------------------------------------- dropout
+
+
+def test_philox_known_answers():
+    """Philox4x32-10 against the generator's published known-answer vectors."""
+    from oracle import philox
+    path = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden",
+                                      "philox4x32_10_kat.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    assert len(rows) == 3
+    for r in rows:
+        v = [int(x, 16) for x in r]
+        out = philox.philox4x32(*v[:4], v[4], v[5])
+        assert [int(x) for x in out] == v[6:], r
+
+
+def test_uniform_layout_of_one_call():
+    """One call (query i, group g, parity p) feeds keys 16 g + p + 2 t, t = 0..7, with
+    its eight 16-bit halves in order (low half of word 0 first)."""
+    from oracle import philox
+    u = philox.uniforms16(5, 4, 48, seed=0x1234_5678_9abc_def0, offset=77)
+    for i, g, par in ((0, 0, 0), (3, 2, 1), (2, 1, 0)):
+        w = philox.philox4x32(i, 2 * g + par, 5, 77, 0x9abcdef0, 0x12345678)
+        halves = []
+        for x in w:
+            halves += [int(x) & 0xFFFF, int(x) >> 16]
+        assert [int(u[i, 16 * g + par + 2 * t]) for t in range(8)] == halves
+
+
+def test_keep_rate_and_uniformity():
+    """Over 2^20 draws the keep fraction is within 5 sigma of threshold / 2^16, and the
+    16-bit uniforms fill 16 equal bins evenly (chi-square below 50 at 15 dof)."""
+    from oracle import philox
+    u = philox.uniforms16(3, 1024, 1024, seed=42, offset=0).astype(np.int64)
+    for p in (0.1, 0.5, 0.9):
+        t = philox.keep_threshold(p)
+        rate = (u < t).mean()
+        q = t / 65536
+        assert abs(rate - q) < 5 * math.sqrt(q * (1 - q) / u.size), (p, rate, q)
+    hist = np.bincount(u.reshape(-1) >> 12, minlength=16)
+    exp = u.size / 16
+    assert ((hist - exp) ** 2 / exp).sum() < 50
+
+
+def test_masks_depend_on_head_seed_and_offset():
+    from oracle import philox
+    base = philox.keep_mask(1, 64, 64, 0.5, 9, 0)
+    assert np.array_equal(base, philox.keep_mask(1, 64, 64, 0.5, 9, 0))
+    for other in (philox.keep_mask(2, 64, 64, 0.5, 9, 0), philox.keep_mask(1, 64, 64, 0.5, 10, 0),
+                  philox.keep_mask(1, 64, 64, 0.5, 9, 1), philox.keep_mask(1, 64, 64, 0.5, 9 + (1 << 32), 0)):
+        assert 0.4 < (other != base).mean() < 0.6
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_probability_zero_is_no_dropout(causal):
+    q, k, v, do = _gqa_inputs(H=4, H_kv=2, n=9)
+    o, lse = oracle.forward_gqa(q, k, v, 0.6, causal)
+    o2, lse2 = oracle.forward_gqa(q, k, v, 0.6, causal, dropout=(0.0, 5, 0))
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    for a, b in zip(oracle.backward_gqa(q, k, v, do, 0.6, causal),
+                    oracle.backward_gqa(q, k, v, do, 0.6, causal, dropout=(0.0, 5, 0))):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_dropout_zero_query_closed_form():
+    """Q = 0, causal: row i averages the i + 1 visible rows of V, so with dropout it is
+    (scale / (i + 1)) times the sum of the kept visible rows; LSE = ln(i + 1)."""
+    _, k, v, _ = _win_inputs(n=12)
+    from oracle import philox
+    p_drop, seed, offset, hd = 0.3, 123, 4, 7
+    mask = philox.keep_mask(hd, 12, 12, p_drop, seed, offset)
+    sc = 65536.0 / philox.keep_threshold(p_drop)
+    o, lse = oracle.forward_head(np.zeros((12, 3)), k, v, 0.5, True, drop=(mask, sc))
+    for i in range(12):
+        want = sc / (i + 1) * v[:i + 1][mask[i, :i + 1]].sum(axis=0)
+        np.testing.assert_allclose(o[i], want, atol=1e-14)
+        assert abs(lse[i] - math.log(i + 1)) < 1e-14
+
+
+def test_dropout_is_unbiased():
+    """Averaged over 400 seeds, dropout(P) V approaches P V (the scale is the inverse
+    keep probability): the mean error shrinks like 1 / sqrt(seeds)."""
+    q, k, v, _ = _win_inputs(n=8)
+    o_ref, _ = oracle.forward_head(q, k, v, 0.9, False)
+    acc = np.zeros_like(o_ref)
+    from oracle import philox
+    n = 400
+    for seed in range(n):
+        mask = philox.keep_mask(0, 8, 8, 0.5, seed, 0)
+        acc += oracle.forward_head(q, k, v, 0.9, False, drop=(mask, 2.0))[0]
+    err = np.abs(acc / n - o_ref).max()
+    assert err < 4 * np.abs(v).max() / math.sqrt(n)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_finite_differences(causal):
+    """With the mask fixed, the gradients of sum(O * dO) match central differences,
+    and D = rowsum(dO * O) (the dropped O) equals rowsum(P * dP)."""
+    from oracle import philox
+    q, k, v, do = _win_inputs(n=6, d=2, dv=2)
+    mask = philox.keep_mask(3, 6, 6, 0.4, 99, 1)
+    drop = (mask, 65536.0 / philox.keep_threshold(0.4))
+    scale, hstep = 0.9, 1e-6
+    g = oracle.backward_head(q, k, v, do, scale, causal, drop=drop)
+    o, _ = oracle.forward_head(q, k, v, scale, causal, drop=drop)
+    np.testing.assert_allclose(g["D"], (do * o).sum(axis=1), atol=1e-13)
+
+    def loss(qq, kk, vv):
+        return float((oracle.forward_head(qq, kk, vv, scale, causal, drop=drop)[0] * do).sum())
+
+    for which, (x, gg) in enumerate(zip((q, k, v), (g["dq"], g["dk"], g["dv"]))):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += hstep
+            xm[idx] -= hstep
+            ap, am = [q, k, v], [q, k, v]
+            ap[which], am[which] = xp, xm
+            fd[idx] = (loss(*ap) - loss(*am)) / (2 * hstep)
+        np.testing.assert_allclose(gg, fd, rtol=0, atol=1e-7, err_msg="qkv"[which])
