@@ -117,8 +117,9 @@ def cpu_baseline(w, inp, gpu_out, budget_s: float = 10.0):
         for h in range(j * G, (j + 1) * G):
             q, do = f64(inp["q"], b, h), f64(inp["do"], b, h)
             t0 = time.perf_counter()
-            o, lse = oracle.forward_head(q, k, v, w.scale, w.causal, win)
-            res.append((h, o, lse, oracle.backward_head(q, k, v, do, w.scale, w.causal, win)))
+            drop = oracle.head_drop(w.dropout or None, b * w.H + h, w.N)
+            o, lse = oracle.forward_head(q, k, v, w.scale, w.causal, win, drop)
+            res.append((h, o, lse, oracle.backward_head(q, k, v, do, w.scale, w.causal, win, drop)))
             secs += time.perf_counter() - t0
             done += 1
             if secs >= budget_s:
@@ -190,7 +191,7 @@ def main():
         if st != fa.FA_OK:
             raise fa.FaError(st, where)
 
-    if w.windowed:
+    if w.windowed or w.dropout:
         bench_windowed(args, w, fa, inp, q, k, v, do, o, lse, dq, dk, dv, ws, code, stream)
         return
 
@@ -343,10 +344,10 @@ def time_two_calls(args, step):
 
 
 def bench_windowed(args, w, fa, inp, q, k, v, do, o, lse, dq, dk, dv, ws, code, stream):
-    """A local-window workload: fa_fwd_ex then fa_bwd_ex per step."""
+    """A local-window or dropout workload: fa_fwd_ex then fa_bwd_ex per step."""
     B, H, N, d = q.shape
     Hkv = k.shape[1]
-    p = fa.attn(B, H, Hkv, N, d, w.causal, w.scale, code, w.window)
+    p = fa.attn(B, H, Hkv, N, d, w.causal, w.scale, code, w.window, dropout=w.dropout or None)
     sh = stream.cuda_stream
     P = lambda t: t.data_ptr()
 
@@ -367,7 +368,7 @@ def bench_windowed(args, w, fa, inp, q, k, v, do, o, lse, dq, dk, dv, ws, code, 
 
     events, wall = time_two_calls(args, step)
     config = {"workload": w.name, "B": B, "H": H, "H_kv": Hkv, "N": N, "d": d, "causal": w.causal,
-              "window": list(w.window), "step": "fa_fwd_ex + fa_bwd_ex",
+              "window": list(w.window), "dropout": list(w.dropout), "step": "fa_fwd_ex + fa_bwd_ex",
               "visible_pairs_per_head": workloads.visible_pairs(N, w.causal, w.window)}
     out = two_call_result(args, w, events, wall, w.dtype, config,
                           "synthetic (seeded normal Q/K/V/dO of the workload's shape and "

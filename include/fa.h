@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -259,10 +259,27 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  *   window_right      row sees at least its own key;
  *   scale, dtype      as above;
  *   cu_seqlens, total NULL for the dense layout [B, H(_kv), N, d]; otherwise a
- *                     packed batch exactly as for fa_fwd_varlen.
+ *                     packed batch exactly as for fa_fwd_varlen;
+ *   dropout_p, seed,  dropout on P (0 <= dropout_p <= 1; 0: none), below.
+ *   rng_offset
+ *
+ * Dropout.  The forward computes O = dropout(P) V: element (i, j) of P is kept
+ * with probability keep = K / 65536, K = round((1 - dropout_p) 65536), and kept
+ * elements are multiplied by 1 / keep; LSE is that of the undropped softmax.
+ * The backward regenerates the same mask tile by tile from (seed, rng_offset)
+ * ("FlashAttention 원 논문 해부", sections "forward가 끝난 뒤 backward는 무엇을
+ * 저장하고 무엇을 다시 계산하는가" and "내부 구조와 실제 실행 흐름": the generator
+ * state is kept from the forward, the mask is never stored), so fa_bwd_ex must
+ * get the seed, offset and dropout_p of the forward.  The mask: element (i, j)
+ * of attention head b H + h (b the sequence of a packed batch, i and j
+ * positions in it) is kept iff u < K, u = 16-bit half number (j mod 16) / 2
+ * (low half of word 0 first) of Philox4x32-10 (Salmon et al., "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011) with counter (i, 2 floor(j / 16) +
+ * (j mod 2), b H + h, rng_offset) and key (seed mod 2^32, seed / 2^32).  A
+ * caller advances rng_offset (or the seed) between steps.
  * Tensors, workspace (fa_bwd_workspace_size(B, H, N, d)), ownership and errors
- * as for the entry points above (dense or packed); in addition p == NULL or a
- * window value below -1 is FA_ERR_INVALID_ARGUMENT.  fa_bwd_ex needs the o and
+ * as for the entry points above (dense or packed); in addition p == NULL, a
+ * window value below -1 or dropout_p outside [0, 1] is FA_ERR_INVALID_ARGUMENT.  fa_bwd_ex needs the o and
  * lse that fa_fwd_ex wrote for the same description.
  */
 typedef struct fa_attn {
@@ -273,6 +290,9 @@ typedef struct fa_attn {
   fa_dtype dtype;
   const int* cu_seqlens;
   int total;
+  float dropout_p;
+  unsigned long long seed;
+  unsigned int rng_offset;
 } fa_attn;
 
 fa_status fa_fwd_ex(const fa_attn* p, const void* q, const void* k, const void* v, void* o,

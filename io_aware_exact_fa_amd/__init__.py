@@ -46,7 +46,9 @@ class FaAttn(ctypes.Structure):
                 ("N", ctypes.c_int), ("d", ctypes.c_int), ("causal", ctypes.c_int),
                 ("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
-                ("cu_seqlens", ctypes.c_void_p), ("total", ctypes.c_int)]
+                ("cu_seqlens", ctypes.c_void_p), ("total", ctypes.c_int),
+                ("dropout_p", ctypes.c_float), ("seed", ctypes.c_ulonglong),
+                ("rng_offset", ctypes.c_uint)]
 
 
 class FaError(RuntimeError):
@@ -206,10 +208,12 @@ def fa_bwd_ex(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, 
 
 
 def attn(B, H, H_kv, N, d, causal, scale, dtype, window=(-1, -1), cu_seqlens=None,
-         total=0) -> FaAttn:
-    """Fill an fa_attn (window sides -1 = open; cu_seqlens a device address or None)."""
+         total=0, dropout=None) -> FaAttn:
+    """Fill an fa_attn (window sides -1 = open; cu_seqlens a device address or None;
+    dropout = (p, seed, offset) or None)."""
+    p, seed, offset = dropout if dropout is not None else (0.0, 0, 0)
     return FaAttn(B, H, H_kv, N, d, int(causal), int(window[0]), int(window[1]), float(scale),
-                  int(dtype), cu_seqlens, int(total))
+                  int(dtype), cu_seqlens, int(total), float(p), int(seed), int(offset))
 
 
 # ------------------------------------------------------------------ torch helpers
@@ -237,9 +241,11 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, window=None):
+def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, window=None,
+            dropout=None):
     """O, LSE for q [B, H, N, d] and k, v [B, H_kv, N, d] (H_kv divides H; all one
-    dtype, on the GPU).  ``window`` = (left, right), -1 = open side."""
+    dtype, on the GPU).  ``window`` = (left, right), -1 = open side; ``dropout`` =
+    (p, seed, offset)."""
     import torch
     B, H, N, d = q.shape
     H_kv = k.shape[1]
@@ -252,8 +258,9 @@ def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, 
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check("o", o, (B, H, N, d), q.dtype)
     _check("lse", lse, (B, H, N), torch.float32)
-    if window is not None:
-        p = attn(B, H, H_kv, N, d, causal, scale, dtype_code(q.dtype), window)
+    if window is not None or dropout is not None:
+        p = attn(B, H, H_kv, N, d, causal, scale, dtype_code(q.dtype), window or (-1, -1),
+                 dropout=dropout)
         st = fa_fwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        _stream(stream))
         if st != FA_OK:
@@ -276,7 +283,7 @@ def workspace(B, H, N, d, device):
 
 
 def backward(q, k, v, o, dout, lse, causal: bool, scale: float, dq=None, dk=None, dv=None,
-             ws=None, stream=None, window=None):
+             ws=None, stream=None, window=None, dropout=None):
     """dQ, dK, dV for the forward that produced o and lse."""
     import torch
     B, H, N, d = q.shape
@@ -293,8 +300,9 @@ def backward(q, k, v, o, dout, lse, causal: bool, scale: float, dq=None, dk=None
     for name, t in (("dk", dk), ("dv", dv)):
         _check(name, t, (B, H_kv, N, d), q.dtype)
     ws = workspace(B, H, N, d, q.device) if ws is None else ws
-    if window is not None:
-        p = attn(B, H, H_kv, N, d, causal, scale, dtype_code(q.dtype), window)
+    if window is not None or dropout is not None:
+        p = attn(B, H, H_kv, N, d, causal, scale, dtype_code(q.dtype), window or (-1, -1),
+                 dropout=dropout)
         st = fa_bwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
                        ws.numel(), _stream(stream))
@@ -321,7 +329,7 @@ def _check_cu(cu_seqlens, device):
 
 
 def forward_varlen(q, k, v, cu_seqlens, max_s: int, causal: bool, scale: float, o=None, lse=None,
-                   stream=None, window=None):
+                   stream=None, window=None, dropout=None):
     """O [H, total, d], LSE [B, H, max_s] for packed q [H, total, d], k, v
     [H_kv, total, d] and device int32 cu_seqlens [B + 1] (offsets are read on the
     device, not checked here)."""
@@ -336,9 +344,9 @@ def forward_varlen(q, k, v, cu_seqlens, max_s: int, causal: bool, scale: float, 
     lse = torch.empty((B, H, max_s), dtype=torch.float32, device=q.device) if lse is None else lse
     _check("o", o, (H, total, d), q.dtype)
     _check("lse", lse, (B, H, max_s), torch.float32)
-    if window is not None:
-        p = attn(B, H, H_kv, max_s, d, causal, scale, dtype_code(q.dtype), window,
-                 cu_seqlens.data_ptr(), total)
+    if window is not None or dropout is not None:
+        p = attn(B, H, H_kv, max_s, d, causal, scale, dtype_code(q.dtype), window or (-1, -1),
+                 cu_seqlens.data_ptr(), total, dropout)
         st = fa_fwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        _stream(stream))
     else:
@@ -351,7 +359,7 @@ def forward_varlen(q, k, v, cu_seqlens, max_s: int, causal: bool, scale: float, 
 
 
 def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_s: int, causal: bool, scale: float,
-                    dq=None, dk=None, dv=None, ws=None, stream=None, window=None):
+                    dq=None, dk=None, dv=None, ws=None, stream=None, window=None, dropout=None):
     """dQ, dK, dV for the packed forward that produced o and lse."""
     import torch
     H, total, d = q.shape
@@ -369,9 +377,9 @@ def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_s: int, causal: bool,
     for name, t in (("dk", dk), ("dv", dv)):
         _check(name, t, (H_kv, total, d), q.dtype)
     ws = workspace(B, H, max_s, d, q.device) if ws is None else ws
-    if window is not None:
-        p = attn(B, H, H_kv, max_s, d, causal, scale, dtype_code(q.dtype), window,
-                 cu_seqlens.data_ptr(), total)
+    if window is not None or dropout is not None:
+        p = attn(B, H, H_kv, max_s, d, causal, scale, dtype_code(q.dtype), window or (-1, -1),
+                 cu_seqlens.data_ptr(), total, dropout)
         st = fa_bwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
                        ws.numel(), _stream(stream))

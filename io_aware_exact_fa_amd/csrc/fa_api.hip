@@ -61,6 +61,7 @@ fa_status check_varlen(const int* cu_seqlens, int B, int max_s, int total, int H
 fa_status check_attn(const fa_attn* p) {
   if (!p) return FA_ERR_INVALID_ARGUMENT;
   if (p->window_left < -1 || p->window_right < -1) return FA_ERR_INVALID_ARGUMENT;
+  if (!(p->dropout_p >= 0.f && p->dropout_p <= 1.f)) return FA_ERR_INVALID_ARGUMENT;   // NaN too
   if (p->cu_seqlens)
     return check_varlen(p->cu_seqlens, p->B, p->N, p->total, p->H, p->H_kv, p->d, p->scale,
                         p->dtype);
@@ -78,6 +79,13 @@ void apply_attn(const fa_attn* p, Args* a) {
   // A side wider than the longest sequence is open (this also keeps i + w in range).
   a->wl = (p->window_left < 0 || p->window_left >= p->N) ? fa::kNoLimit : p->window_left;
   a->wr = (p->window_right < 0 || p->window_right >= p->N) ? fa::kNoLimit : p->window_right;
+  // Keep iff the 16-bit uniform is below keep_t = round((1 - p) 2^16) (nearest, ties to even).
+  const uint32_t keep_t = (uint32_t)lrint((1.0 - (double)p->dropout_p) * 65536.0);
+  a->drop.keep_t = keep_t;
+  a->drop.scale = keep_t > 0 ? (float)(65536.0 / keep_t) : 0.f;
+  a->drop.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFu);
+  a->drop.seed_hi = (uint32_t)(p->seed >> 32);
+  a->drop.offset = p->rng_offset;
 }
 
 // 1 = gfx950, 2 = something else; 0 = not yet known.

@@ -97,7 +97,7 @@ struct DqTile {
   static constexpr int KP = D + E16;             // row pitch of the K and V tiles
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__((DqTile<T, D>::NT), (DqTile<T, D>::WAVES_PER_SIMD))
 void bwd_dq_kernel(BwdArgs a) {
   using C = DqTile<T, D>;
@@ -192,7 +192,10 @@ void bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) {
           float p = exp2_fast(fmaf(s[i], c, -l2));
           if (masked && (key0_of(i) > lim || key0_of(i) < low)) p = 0.f;
-          s[i] = p * (dp[i] - dl);                     // dS
+          float dpi = dp[i];
+          if constexpr (DROP)   // dP through the kept entries and their scale
+            dpi = drop_keep(a.drop, (int)head, myq, kb0 + key0_of(i) + hoff) ? dpi * a.drop.scale : 0.f;
+          s[i] = p * (dpi - dl);                       // dS
         }
         // dQ^T += K^T dS^T: A operand = 8 consecutive keys of one head-dim row of K^T.
 #pragma unroll
@@ -237,7 +240,7 @@ struct DkvTile {
   static constexpr int NBUF = 2 * BUF_BYTES <= 160 * 1024 ? 2 : 1;
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkvTile<T, D>;
   using M = Mfma<T>;
@@ -270,6 +273,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const T* V = static_cast<const T*>(a.v) + sp.kv * D;
   const T *Q = nullptr, *dO = nullptr;
   const float *LSE = nullptr, *Dl = nullptr;
+  int qhead = 0;   // query head of the current pass (dropout's generator counter)
   const float c = a.scale * kLog2e;
 
   const int kw = k0 + 32 * w;    // first key of this wave
@@ -399,6 +403,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // One query head of the group: stage its first tiles, then the tile loop.
   auto use_head = [&](int g) {
     const size_t head = kvhead * a.G + g;
+    qhead = (int)head;
     Q = static_cast<const T*>(a.q) + (sp.q + g * sp.hs) * D;
     dO = static_cast<const T*>(a.dout) + (sp.q + g * sp.hs) * D;
     LSE = a.lse + head * a.N;
@@ -503,8 +508,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
             const int qo = b * 32 + qoff_of(i) + hoff;
             float e = exp2_fast(fmaf(s[b][i], c, -l4[b][i / 4][i % 4]));
             if (qi0 + qo < myk - wr || qi0 + qo > myk + wl) e = 0.f;
-            p[b][i] = e;
-            ds[b][i] = e * (dp[b][i] - d4[b][i / 4][i % 4]);
+            float pe = e, dpi = dp[b][i];
+            if constexpr (DROP) {   // dV's P and dP through the kept entries
+              const bool keep = drop_keep(a.drop, qhead, qi0 + qo, myk);
+              pe = keep ? e * a.drop.scale : 0.f;
+              dpi = keep ? dpi * a.drop.scale : 0.f;
+            }
+            p[b][i] = pe;
+            ds[b][i] = e * (dpi - d4[b][i / 4][i % 4]);
             if ((i + 1) % EPU == 0) {
               pa[b][i / EPU] = pack_frag<T>(p[b], i / EPU);
               sa[b][i / EPU] = pack_frag<T>(ds[b], i / EPU);
@@ -569,7 +580,7 @@ struct Dq16 {
   static constexpr int NLD = 2 * BC / NW / TileLds<D>::ROWS_PER_COPY;   // copies per wave per tile
 };
 
-template <typename T, int D, bool CAUSAL, int NW>
+template <typename T, int D, bool CAUSAL, int NW, bool DROP>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   using C = Dq16<D, NW>;
   static_assert(NW == 8 || (NW == 4 && D == 128), "4-wave dQ workgroups copy 4-row groups");
@@ -675,6 +686,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
     const int key0 = kt * C::BC;
     const int rlo = klo - key0 - h;                 // masked tiles: offsets rlo ..
     const uint32_t rspan = (uint32_t)(khi - klo);   // rlo + rspan are visible
+    uint32_t kbits[2] = {0u, 0u};                   // dropout: keep bit of element i of block b
     const int b1 = bcur == C::NB - 1 ? 0 : bcur + 1;
     const int b2 = b1 == C::NB - 1 ? 0 : b1 + 1;
     const int boff = bcur * C::BUF;
@@ -743,7 +755,22 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
               const int ke = b * 32 + 8 * (i / 4) + 2 * (i % 4);   // key - key0 - h
               if ((uint32_t)(ke - rlo) > rspan) e = 0.f;
             }
-            ds[b][i] = e * (dp[b][i] - dl);
+            float dpi = dp[b][i];
+            if constexpr (DROP) {
+              // Elements 8 u .. 8 u + 7 are keys key0 + 32 b + 16 u + h + 2 t: one
+              // generator call, made at the first of them.
+              if (i % 8 == 0) {
+                uint32_t wv[4];
+                drop_call(a.drop, hd, myq, (key0 + 32 * b) / 16 + i / 8, h, wv);
+                uint32_t bits = 0;
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                  bits |= (((t & 1) ? (wv[t >> 1] >> 16) : (wv[t >> 1] & 0xFFFFu)) < a.drop.keep_t ? 1u : 0u) << t;
+                kbits[b] = (kbits[b] & ~(0xFFu << i)) | (bits << i);
+              }
+              dpi = ((kbits[b] >> i) & 1u) ? dpi * a.drop.scale : 0.f;
+            }
+            ds[b][i] = e * (dpi - dl);
             if ((i + 1) % 8 == 0) sa[b][i / 8] = pack_frag<T>(ds[b], i / 8);
           }
       __builtin_amdgcn_sched_barrier(0);
@@ -805,12 +832,15 @@ struct Dkv16 {
   static constexpr int NLD = 2 * BQ / 4 / TileLds<D>::ROWS_PER_COPY + 2;   // copies per wave per tile: Q, dO; L2, D
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   using C = Dkv16<D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
-  __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF];
+  // Dropout: per wave and 32-query block, the 16-bit uniforms of its 32 x 32
+  // (query, key) elements, 2 KB, after the tile buffers.
+  constexpr int DSCR = 2048;
+  __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF + (DROP ? 8 * DSCR : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, h = lane >> 5;
@@ -872,6 +902,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // zero (the padding rows of L2 are +inf, so their P is 0; past Np all of Q,
   // dO, L2 and D read as zero, and P dO and P (dP - D) vanish with dO).
   i32x4 rsq, rsg, rsl, rsd;   // Q, dO, L2 and D of the current query head
+  int qhead = 0;              // its index b H + h (dropout's generator counter)
   constexpr int NROW = C::NLD - 2;
   // Copies of one tile into one buffer.  Wave w's rows are 16 w .. 16 w + 15, so
   // with the per-tile bases below (LDS address of the wave's first row, global
@@ -908,6 +939,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // into buffers 0 and 1.
   auto use_head = [&](int g) {
     const size_t head = kvhead * a.G + g;
+    qhead = (int)head;
     rsq = buffer_rsrc(static_cast<const T*>(a.q) + (sp.q + g * sp.hs) * D, (uint32_t)N * (2 * D));
     rsg = buffer_rsrc(static_cast<const T*>(a.dout) + (sp.q + g * sp.hs) * D, (uint32_t)N * (2 * D));
     rsl = buffer_rsrc(a.l2 + head * a.Np, (uint32_t)a.Np * 4);
@@ -992,6 +1024,38 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
       opq[m] = operand(m);
     }
     const Bases xc = bases(b2, qt + 2);
+    // Dropout keep bits of this lane's key column, bit i of block b for query
+    // 8 (i / 4) + 2 (i % 4) + h of the block.  A generator call serves the 8
+    // keys 16 p + par + 2 t of one query, which sit in 8 lanes here: lane (col,
+    // h) makes the calls of query col and key half p = h (both parities) into
+    // the wave's LDS area, then reads the uniforms of its own key back.
+    uint32_t kbits[2] = {0u, 0u};
+    float d4[2][4][4];   // D of 4 queries per element group (dropout only)
+    if constexpr (DROP) {
+      const int kgrp = (kw >> 4) + h;   // 16-key group of the calls this lane makes
+      char* scr = smem + C::NB * C::BUF + w * 2 * DSCR;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+          uint32_t wv[4];
+          drop_call(a.drop, qhead, qi0 + 32 * b + col, kgrp, par, wv);
+          *reinterpret_cast<uint4*>(scr + b * DSCR + ((col * 2 + h) * 2 + par) * 16) =
+              uint4{wv[0], wv[1], wv[2], wv[3]};
+        }
+      __builtin_amdgcn_wave_barrier();
+      const int kp = col >> 4, kpar = col & 1, kt = (col & 15) >> 1;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ql = 8 * (i / 4) + 2 * (i % 4) + h;
+          const uint16_t u = *reinterpret_cast<const uint16_t*>(
+              scr + b * DSCR + ((ql * 2 + kp) * 2 + kpar) * 16 + 2 * kt);
+          kbits[b] |= ((uint32_t)u < a.drop.keep_t ? 1u : 0u) << i;
+        }
+      __builtin_amdgcn_wave_barrier();
+    }
     static_for<0, NM>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
 #pragma unroll
@@ -1006,6 +1070,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
           if (m == elem_slot(b, 4 * g) - PD) {
             const float* l2 = reinterpret_cast<const float*>(smem + boff + 2 * C::TILE);
             l4[b][g] = *reinterpret_cast<const f32x4*>(&l2[b * 32 + 8 * g + 4 * h]);
+            if constexpr (DROP) {
+              const f32x4 dd = *reinterpret_cast<const f32x4*>(&l2[C::BQ + b * 32 + 8 * g + 4 * h]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) d4[b][g][e] = dd[e];
+            }
           }
       if constexpr (m == NS / 2) dp[1] = load_d(1);
       // Operands are read in pairs at odd slots, the odd one first, so that the
@@ -1039,8 +1108,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
               const int qe = b * 32 + 8 * (i / 4) + 2 * (i % 4);   // q - qi0 - h
               if ((uint32_t)(qe - rlo) > rspan) e = 0.f;
             }
-            p[b][i] = e;
-            ds[b][i] = e * dp[b][i];
+            if constexpr (DROP) {
+              // dV takes the kept P scaled; -dS = P (D - dP') with dP' the kept,
+              // scaled dP = D - (accumulator), as the accumulator holds D - dP.
+              const bool keep = (kbits[b] >> i) & 1u;
+              const float dd = d4[b][i / 4][i % 4];
+              p[b][i] = keep ? e * a.drop.scale : 0.f;
+              ds[b][i] = e * (keep ? fmaf(a.drop.scale, dp[b][i] - dd, dd) : dd);
+            } else {
+              p[b][i] = e;
+              ds[b][i] = e * dp[b][i];
+            }
             if ((i + 1) % 8 == 0) {
               pa[b][i / 8] = pack_frag<T>(p[b], i / 8);
               sa[b][i / 8] = pack_frag<T>(ds[b], i / 8);
@@ -1089,7 +1167,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ launchers
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP>
 static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
   const long rows = (long)a.B * a.H * a.Np;
   if (step == BwdStep::pre) {
@@ -1099,27 +1177,29 @@ static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
   } else if (step == BwdStep::dkdv) {
     if constexpr (sizeof(T) == 2) {
       dim3 grid((a.N + Dkv16<D>::BKC - 1) / Dkv16<D>::BKC, a.H / a.G, a.B);
-      hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL, DROP>), grid, dim3(256), 0, s, a);
     } else {
       dim3 grid((a.N + DkvTile<T, D>::BKC - 1) / DkvTile<T, D>::BKC, a.H / a.G, a.B);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, DROP>), grid, dim3(256), 0, s, a);
     }
   } else if constexpr (sizeof(T) == 2) {
     // Causal d = 128: 128-row workgroups, two per CU, balance the triangle.
     constexpr int NW = CAUSAL && D == 128 ? 4 : 8;
     using C = Dq16<D, NW>;
     dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
-    hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL, NW>), grid, dim3(C::NT), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL, NW, DROP>), grid, dim3(C::NT), 0, s, a);
   } else {
     dim3 grid((a.N + DqTile<T, D>::BR - 1) / DqTile<T, D>::BR, a.H, a.B);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), grid, dim3(DqTile<T, D>::NT), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, DROP>), grid, dim3(DqTile<T, D>::NT), 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_bwd_inst(BwdStep st, bool causal, const BwdArgs& a, hipStream_t s) {
-  return causal ? launch_bwd_t<T, D, true>(st, a, s) : launch_bwd_t<T, D, false>(st, a, s);
+  if (a.drop.keep_t < 65536)
+    return causal ? launch_bwd_t<T, D, true, true>(st, a, s) : launch_bwd_t<T, D, false, true>(st, a, s);
+  return causal ? launch_bwd_t<T, D, true, false>(st, a, s) : launch_bwd_t<T, D, false, false>(st, a, s);
 }
 
 }  // namespace fa

@@ -348,6 +348,59 @@ __device__ inline void work_item(int nt, int& rank, int& head) {
   }
 }
 
+// ---------------------------------------------------------------- dropout
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): ten rounds of two 32 x 32 -> 64-bit products mixed
+// with the other counter words and the key, the key bumped by two Weyl
+// constants between rounds.
+__device__ inline void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                     uint32_t k0, uint32_t k1, uint32_t (&w)[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  w[0] = c0;
+  w[1] = c1;
+  w[2] = c2;
+  w[3] = c3;
+}
+
+// The eight 16-bit uniforms of one call (query q, 16-key group g, key parity
+// par): those of keys 16 g + par + 2 t, t = 0..7, half t of the output.
+template <class Drop>
+__device__ inline void drop_call(const Drop& d, int head, int q, int g, int par, uint32_t (&w)[4]) {
+  philox4x32_10((uint32_t)q, (uint32_t)(2 * g + par), (uint32_t)head, d.offset, d.seed_lo,
+                d.seed_hi, w);
+}
+
+// Keep decision of one element (query q, key k) from its own call.
+template <class Drop>
+__device__ inline bool drop_keep(const Drop& d, int head, int q, int k) {
+  uint32_t w[4];
+  drop_call(d, head, q, k >> 4, k & 1, w);
+  const int t = (k & 15) >> 1;
+  const uint32_t x = (t >> 1) == 0 ? w[0] : (t >> 1) == 1 ? w[1] : (t >> 1) == 2 ? w[2] : w[3];
+  return ((t & 1) ? (x >> 16) : (x & 0xFFFFu)) < d.keep_t;
+}
+
+// Keep masks of the halves of 4 packed dwords (element 2 k in the low half of
+// dword k, 2 k + 1 in the high half) from one call: 0xFFFF where kept.
+template <class Drop>
+__device__ inline void drop_masks(const Drop& d, const uint32_t (&w)[4], uint32_t (&m)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    m[k] = ((w[k] & 0xFFFFu) < d.keep_t ? 0xFFFFu : 0u) | ((w[k] >> 16) < d.keep_t ? 0xFFFF0000u : 0u);
+}
+
 // Row of a 32-row block (queries or keys) that supplies result row m of an MFMA
 // whose A operand is read from a row-major tile (m = 8a + 4h + s -> 8a + 2s + h):
 // the 4 rows that one transposing read gathers for a later MFMA are then 2 apart.

@@ -77,7 +77,7 @@ __device__ inline int vt_index(int d, int key) {
   return ((key / KPC) ^ swz) * KPC + (key % KPC);
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__((FwdTile<T, D>::NT), (FwdTile<T, D>::WAVES_PER_SIMD))
 void fwd_kernel(FwdArgs a) {
   using C = FwdTile<T, D>;
@@ -216,7 +216,9 @@ void fwd_kernel(FwdArgs a) {
     }
   };
   // P~ = 2^(c S - m) for the tile with reference max m_use, row-sum partials.
-  auto exp_tile = [&](f32x16 (&sc)[2], float m_use, bool masked) {
+  // DROP: the sum takes every P~, the P~V operand only the kept ones (each
+  // element's keep bit from its own generator call).
+  auto exp_tile = [&](f32x16 (&sc)[2], float m_use, bool masked, int key0) {
     const float nm = -m_use;
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -226,8 +228,10 @@ void fwd_kernel(FwdArgs a) {
         const float x = sc[kb][i];
         float p = exp2_fast(fmaf(x, c, nm));
         if (masked) p = (x == -INFINITY) ? 0.f : p;   // exact also for c == 0
-        sc[kb][i] = p;
         ps[i & 3] += p;
+        if constexpr (DROP)
+          if (!drop_keep(a.drop, (int)head, myq, key0 + kb * 32 + key0_of(i) + hoff)) p = 0.f;
+        sc[kb][i] = p;
       }
     return (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
@@ -275,7 +279,7 @@ void fwd_kernel(FwdArgs a) {
         // the reads stay inside the LDS buffers.)
         s_tile((j + 1) & 1, sn);
         m_new = fmaxf(m_run, tile_max(sc));
-        lsum = exp_tile(sc, m_new, false);
+        lsum = exp_tile(sc, m_new, false, key0);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // 8 LDS reads (K operands)
@@ -295,7 +299,7 @@ void fwd_kernel(FwdArgs a) {
             if (kb * 32 + key0_of(i) > lim || kb * 32 + key0_of(i) < low) sc[kb][i] = -INFINITY;
         const float mt = tile_max(sc);
         m_new = (mt == -INFINITY) ? m_run : fmaxf(m_run, mt);
-        lsum = exp_tile(sc, (m_new == -INFINITY) ? 0.f : m_new, true);
+        lsum = exp_tile(sc, (m_new == -INFINITY) ? 0.f : m_new, true, key0);
         s_tile((j + 1) & 1, sn);
       }
       // Rescale the accumulator only when the max of some row of the wave grew.  The
@@ -333,7 +337,8 @@ void fwd_kernel(FwdArgs a) {
 
   const float l = half_sum(l_run);
   if (myq < N) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    // Dropout scales the kept weights by the inverse keep probability.
+    const float inv = l > 0.f ? (DROP ? a.drop.scale : 1.f) / l : 0.f;
     T* orow = O + (size_t)myq * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -388,7 +393,7 @@ struct Fwd16 {
   static constexpr int NA = NS / 2;              // slots of the row max
 };
 
-template <typename T, int D, bool CAUSAL, int NW>
+template <typename T, int D, bool CAUSAL, int NW, bool DROP>
 __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   using C = Fwd16<D, NW>;
   static_assert(D == 128 && (NW == 4 || NW == 8), "fwd16_kernel is built for d = 128");
@@ -608,6 +613,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
             if ((i + 1) % 8 == 0) {
               pf[kb][i / 8] = pack_frag<T>(sc[kb], i / 8);
               frag_sum4<T>(pf[kb][i / 8], ps);
+              if constexpr (DROP) {
+                // The 8 keys of this fragment, key0 + 32 kb + 16 (i / 8) + h + 2 t,
+                // are exactly the keys of one generator call: the row sum above
+                // took them all, the P~V operand keeps the kept ones.
+                uint32_t wv[4], mk[4];
+                drop_call(a.drop, hd, myq, (key0 + 32 * kb) / 16 + i / 8, h, wv);
+                drop_masks(a.drop, wv, mk);
+                i32x4 pv = __builtin_bit_cast(i32x4, pf[kb][i / 8]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) pv[k] &= (int)mk[k];
+                pf[kb][i / 8] = __builtin_bit_cast(frag, pv);
+              }
               // Pin the fragment (and the exponentials behind it) to this slot: the
               // results are only used after the rescale branch, and the compiler
               // would otherwise sink the whole computation past it.
@@ -669,7 +686,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
 
   const float l = half_sum(l_run);
   if (myq < N) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    // Dropout scales the kept weights by the inverse keep probability.
+    const float inv = l > 0.f ? (DROP ? a.drop.scale : 1.f) / l : 0.f;
     T* orow = O + (size_t)myq * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -689,15 +707,22 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   // Under the causal mask, 128 query rows per workgroup (two per CU) balance
   // the triangle better; without it one 256-row workgroup per CU copies half
   // as much.
+  const bool drop = a.drop.keep_t < 65536;
   if constexpr (sizeof(T) == 2 && D == 128) {
     constexpr int NW = CAUSAL ? 4 : 8;
     using C = Fwd16<D, NW>;
     dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
-    hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, NW>), grid, dim3(C::NT), 0, s, a);
+    if (drop)
+      hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, NW, true>), grid, dim3(C::NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, NW, false>), grid, dim3(C::NT), 0, s, a);
   } else {
     using C = FwdTile<T, D>;
     dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
-    hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), grid, dim3(C::NT), 0, s, a);
+    if (drop)
+      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, true>), grid, dim3(C::NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, false>), grid, dim3(C::NT), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -11,6 +11,17 @@ namespace fa {
 // An open side of the attention window (no limit on j - i or i - j).
 constexpr int kNoLimit = 1 << 30;
 
+// Dropout on P: element (query i, key j) of head b H + h is kept iff its 16-bit
+// uniform is below keep_t (keep_t = 65536: no dropout); kept elements are
+// scaled by `scale` = 65536 / keep_t.  The uniform of (i, j) is half number
+// (j % 16) / 2 (low half of word 0 first) of Philox4x32-10 with counter
+// (i, 2 (j / 16) + j % 2, b H + h, offset) and key (seed_lo, seed_hi).
+struct Dropout {
+  uint32_t keep_t = 65536;
+  float scale = 1.f;
+  uint32_t seed_lo = 0, seed_hi = 0, offset = 0;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -28,6 +39,7 @@ struct FwdArgs {
   // Window: key j is visible to query i iff i - wl <= j <= i + wr (positions in
   // the sequence; wl, wr >= 0 or kNoLimit).  Causal launches take wr = 0.
   int wl = kNoLimit, wr = kNoLimit;
+  Dropout drop;
 };
 
 struct BwdArgs {
@@ -49,6 +61,7 @@ struct BwdArgs {
   const int* cu_seqlens = nullptr;   // as in FwdArgs; workspace and LSE rows per
   int total = 0;                     // (sequence, head) stay Np and N
   int wl = kNoLimit, wr = kNoLimit;  // as in FwdArgs
+  Dropout drop;                      // as in FwdArgs
 };
 
 // Tile ranges of one workgroup under the window: rows [ra, rb] of the outer

@@ -39,6 +39,7 @@ class Workload:
     offset: bool = False
     H_kv: int = 0       # key/value heads (0: one per query head)
     window: tuple = (-1, -1)   # local window (left, right); -1: open side
+    dropout: tuple = ()        # (p, seed, offset): dropout on P, regenerated in the backward
 
     @property
     def kv_heads(self) -> int:
@@ -109,7 +110,14 @@ WINDOW_BF16 = Workload("b2h32kv8n16384d128-bf16-causal-window4096", 2, 32, 16384
                        True, 1010, H_kv=8, window=(4095, -1))
 WINDOWED = (WINDOW_BF16,)
 
-BY_NAME = {w.name: w for w in ALL + GQA + WINDOWED}
+# Training-time dropout at the rate of the original paper's runtime benchmark
+# (p = 0.1: "FlashAttention 원 논문 해부", section "원 논문 benchmark는 조건을
+# 떼지 않고 읽는다"), at the shape of the offset workload.
+DROPOUT_BF16 = Workload("b2h32n8192d128-bf16-dropout0.1", 2, 32, 8192, 128, "bf16", False, 1011,
+                        dropout=(0.1, 0x5EED_0001_2345_6789, 7))
+DROPOUT = (DROPOUT_BF16,)
+
+BY_NAME = {w.name: w for w in ALL + GQA + WINDOWED + DROPOUT}
 
 
 def make_inputs(w: Workload) -> dict:
