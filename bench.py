@@ -111,6 +111,7 @@ def cpu_baseline(w, inp, gpu_out, budget_s: float = 10.0):
     rel = lambda a, r: float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-30))
     secs, done, check = 0.0, 0, None
     win = w.window if w.windowed else None
+    bmask = workloads.block_mask(w).numpy() if w.sparse else None
     for b, j in groups:
         k, v = f64(inp["k"], b, j), f64(inp["v"], b, j)
         res = []
@@ -118,8 +119,10 @@ def cpu_baseline(w, inp, gpu_out, budget_s: float = 10.0):
             q, do = f64(inp["q"], b, h), f64(inp["do"], b, h)
             t0 = time.perf_counter()
             drop = oracle.head_drop(w.dropout or None, b * w.H + h, w.N)
-            o, lse = oracle.forward_head(q, k, v, w.scale, w.causal, win, drop)
-            res.append((h, o, lse, oracle.backward_head(q, k, v, do, w.scale, w.causal, win, drop)))
+            blk = bmask[h] if bmask is not None else None
+            o, lse = oracle.forward_head(q, k, v, w.scale, w.causal, win, drop, blk)
+            res.append((h, o, lse,
+                        oracle.backward_head(q, k, v, do, w.scale, w.causal, win, drop, blk)))
             secs += time.perf_counter() - t0
             done += 1
             if secs >= budget_s:
@@ -191,7 +194,7 @@ def main():
         if st != fa.FA_OK:
             raise fa.FaError(st, where)
 
-    if w.windowed or w.dropout:
+    if w.windowed or w.dropout or w.sparse:
         bench_windowed(args, w, fa, inp, q, k, v, do, o, lse, dq, dk, dv, ws, code, stream)
         return
 
@@ -344,10 +347,14 @@ def time_two_calls(args, step):
 
 
 def bench_windowed(args, w, fa, inp, q, k, v, do, o, lse, dq, dk, dv, ws, code, stream):
-    """A local-window or dropout workload: fa_fwd_ex then fa_bwd_ex per step."""
+    """A local-window, dropout or block-sparse workload: fa_fwd_ex then fa_bwd_ex per
+    step."""
     B, H, N, d = q.shape
     Hkv = k.shape[1]
-    p = fa.attn(B, H, Hkv, N, d, w.causal, w.scale, code, w.window, dropout=w.dropout or None)
+    bm = workloads.block_mask(w).to(q.device) if w.sparse else None
+    p = fa.attn(B, H, Hkv, N, d, w.causal, w.scale, code, w.window, dropout=w.dropout or None,
+                block_mask=bm.data_ptr() if bm is not None else None,
+                block_mask_heads=H if bm is not None else 1)
     sh = stream.cuda_stream
     P = lambda t: t.data_ptr()
 
@@ -368,7 +375,8 @@ def bench_windowed(args, w, fa, inp, q, k, v, do, o, lse, dq, dk, dv, ws, code, 
 
     events, wall = time_two_calls(args, step)
     config = {"workload": w.name, "B": B, "H": H, "H_kv": Hkv, "N": N, "d": d, "causal": w.causal,
-              "window": list(w.window), "dropout": list(w.dropout), "step": "fa_fwd_ex + fa_bwd_ex",
+              "window": list(w.window), "dropout": list(w.dropout),
+              "block_density": w.block_density, "step": "fa_fwd_ex + fa_bwd_ex",
               "visible_pairs_per_head": workloads.visible_pairs(N, w.causal, w.window)}
     out = two_call_result(args, w, events, wall, w.dtype, config,
                           "synthetic (seeded normal Q/K/V/dO of the workload's shape and "

@@ -54,7 +54,11 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
+
+/* Block sizes (queries x keys) of the block-sparse mask of fa_attn. */
+#define FA_BLOCK_Q 256
+#define FA_BLOCK_K 128
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -262,7 +266,23 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  *                     packed batch exactly as for fa_fwd_varlen;
  *   dropout_p, seed,  dropout on P (0 <= dropout_p <= 1; 0: none), below.
  *   rng_offset
+ *   block_mask,       NULL, or a block-sparse mask, below.
+ *   block_mask_heads
  *
+ * Block-sparse attention ("FlashAttention 원 논문 해부", section "대안, 비교와
+ * 선택 기준": block-sparse FlashAttention skips the zero blocks of a given
+ * block mask, so its IO shrinks with the mask's density; it approximates
+ * attention by design).  block_mask is a DEVICE array of
+ * uint8, [block_mask_heads, ceil(N / FA_BLOCK_Q), ceil(N / FA_BLOCK_K)] row
+ * major (N: the sequence length, or max_s of a packed batch); block (qb, kb)
+ * covers queries qb FA_BLOCK_Q .. + FA_BLOCK_Q - 1 and keys kb FA_BLOCK_K ..
+ * + FA_BLOCK_K - 1 (positions in the sequence), nonzero = computed.
+ * block_mask_heads is 1 (one mask for every head) or H (one per query head,
+ * shared by the batch entries / sequences).  Key j is visible to query i iff
+ * its block is kept and the causal mask and the window allow it; a row that
+ * sees no key gets O = 0 and LSE = -inf, and no gradient.  The mask is read by
+ * the kernels, which skip the tiles of blocks it drops (the register-staged
+ * fp32 kernels and the d = 64 forward test them one by one). *
  * Dropout.  The forward computes O = dropout(P) V: element (i, j) of P is kept
  * with probability keep = K / 65536, K = round((1 - dropout_p) 65536), and kept
  * elements are multiplied by 1 / keep; LSE is that of the undropped softmax.
@@ -277,9 +297,12 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  * numbers: as easy as 1, 2, 3", SC 2011) with counter (i, 2 floor(j / 16) +
  * (j mod 2), b H + h, rng_offset) and key (seed mod 2^32, seed / 2^32).  A
  * caller advances rng_offset (or the seed) between steps.
+ * Currently switched off: dropout_p > 0 returns FA_ERR_UNSUPPORTED while a
+ * memory fault seen in a run of the dropout kernel instances is investigated.
  * Tensors, workspace (fa_bwd_workspace_size(B, H, N, d)), ownership and errors
  * as for the entry points above (dense or packed); in addition p == NULL, a
- * window value below -1 or dropout_p outside [0, 1] is FA_ERR_INVALID_ARGUMENT.  fa_bwd_ex needs the o and
+ * window value below -1, dropout_p outside [0, 1] or block_mask_heads other
+ * than 1 or H (with a mask) is FA_ERR_INVALID_ARGUMENT.  fa_bwd_ex needs the o and
  * lse that fa_fwd_ex wrote for the same description.
  */
 typedef struct fa_attn {
@@ -293,6 +316,8 @@ typedef struct fa_attn {
   float dropout_p;
   unsigned long long seed;
   unsigned int rng_offset;
+  const unsigned char* block_mask;
+  int block_mask_heads;
 } fa_attn;
 
 fa_status fa_fwd_ex(const fa_attn* p, const void* q, const void* k, const void* v, void* o,

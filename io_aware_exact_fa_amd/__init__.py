@@ -48,7 +48,11 @@ class FaAttn(ctypes.Structure):
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
                 ("cu_seqlens", ctypes.c_void_p), ("total", ctypes.c_int),
                 ("dropout_p", ctypes.c_float), ("seed", ctypes.c_ulonglong),
-                ("rng_offset", ctypes.c_uint)]
+                ("rng_offset", ctypes.c_uint), ("block_mask", ctypes.c_void_p),
+                ("block_mask_heads", ctypes.c_int)]
+
+FA_BLOCK_Q = 256
+FA_BLOCK_K = 128
 
 
 class FaError(RuntimeError):
@@ -208,12 +212,13 @@ def fa_bwd_ex(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, 
 
 
 def attn(B, H, H_kv, N, d, causal, scale, dtype, window=(-1, -1), cu_seqlens=None,
-         total=0, dropout=None) -> FaAttn:
-    """Fill an fa_attn (window sides -1 = open; cu_seqlens a device address or None;
-    dropout = (p, seed, offset) or None)."""
+         total=0, dropout=None, block_mask=None, block_mask_heads=1) -> FaAttn:
+    """Fill an fa_attn (window sides -1 = open; cu_seqlens and block_mask device
+    addresses or None; dropout = (p, seed, offset) or None)."""
     p, seed, offset = dropout if dropout is not None else (0.0, 0, 0)
     return FaAttn(B, H, H_kv, N, d, int(causal), int(window[0]), int(window[1]), float(scale),
-                  int(dtype), cu_seqlens, int(total), float(p), int(seed), int(offset))
+                  int(dtype), cu_seqlens, int(total), float(p), int(seed), int(offset),
+                  block_mask, int(block_mask_heads))
 
 
 # ------------------------------------------------------------------ torch helpers
@@ -242,7 +247,7 @@ def _stream(stream):
 
 
 def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, window=None,
-            dropout=None):
+            dropout=None, block_mask=None):
     """O, LSE for q [B, H, N, d] and k, v [B, H_kv, N, d] (H_kv divides H; all one
     dtype, on the GPU).  ``window`` = (left, right), -1 = open side; ``dropout`` =
     (p, seed, offset)."""
@@ -258,9 +263,9 @@ def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, 
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check("o", o, (B, H, N, d), q.dtype)
     _check("lse", lse, (B, H, N), torch.float32)
-    if window is not None or dropout is not None:
+    if window is not None or dropout is not None or block_mask is not None:
         p = attn(B, H, H_kv, N, d, causal, scale, dtype_code(q.dtype), window or (-1, -1),
-                 dropout=dropout)
+                 dropout=dropout, **_bm(block_mask, H, N, q.device))
         st = fa_fwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        _stream(stream))
         if st != FA_OK:
@@ -283,7 +288,7 @@ def workspace(B, H, N, d, device):
 
 
 def backward(q, k, v, o, dout, lse, causal: bool, scale: float, dq=None, dk=None, dv=None,
-             ws=None, stream=None, window=None, dropout=None):
+             ws=None, stream=None, window=None, dropout=None, block_mask=None):
     """dQ, dK, dV for the forward that produced o and lse."""
     import torch
     B, H, N, d = q.shape
@@ -300,9 +305,9 @@ def backward(q, k, v, o, dout, lse, causal: bool, scale: float, dq=None, dk=None
     for name, t in (("dk", dk), ("dv", dv)):
         _check(name, t, (B, H_kv, N, d), q.dtype)
     ws = workspace(B, H, N, d, q.device) if ws is None else ws
-    if window is not None or dropout is not None:
+    if window is not None or dropout is not None or block_mask is not None:
         p = attn(B, H, H_kv, N, d, causal, scale, dtype_code(q.dtype), window or (-1, -1),
-                 dropout=dropout)
+                 dropout=dropout, **_bm(block_mask, H, N, q.device))
         st = fa_bwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
                        ws.numel(), _stream(stream))
@@ -318,6 +323,21 @@ def backward(q, k, v, o, dout, lse, causal: bool, scale: float, dq=None, dk=None
     return dq, dk, dv
 
 
+def _bm(block_mask, H, N, device):
+    """fa_attn fields of a block mask: a contiguous uint8 device tensor
+    [1 or H, ceil(N / FA_BLOCK_Q), ceil(N / FA_BLOCK_K)]."""
+    import torch
+    if block_mask is None:
+        return {}
+    nbq, nbk = -(-N // FA_BLOCK_Q), -(-N // FA_BLOCK_K)
+    if (block_mask.dtype != torch.uint8 or block_mask.dim() != 3 or block_mask.shape[0] not in (1, H)
+            or tuple(block_mask.shape[1:]) != (nbq, nbk) or not block_mask.is_contiguous()
+            or block_mask.device != device):
+        raise ValueError(f"block_mask: expected a contiguous uint8 tensor [1 or {H}, {nbq}, {nbk}] "
+                         f"on {device}, got {block_mask.dtype} {tuple(block_mask.shape)}")
+    return {"block_mask": block_mask.data_ptr(), "block_mask_heads": block_mask.shape[0]}
+
+
 def _check_cu(cu_seqlens, device):
     import torch
     if (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2
@@ -329,7 +349,7 @@ def _check_cu(cu_seqlens, device):
 
 
 def forward_varlen(q, k, v, cu_seqlens, max_s: int, causal: bool, scale: float, o=None, lse=None,
-                   stream=None, window=None, dropout=None):
+                   stream=None, window=None, dropout=None, block_mask=None):
     """O [H, total, d], LSE [B, H, max_s] for packed q [H, total, d], k, v
     [H_kv, total, d] and device int32 cu_seqlens [B + 1] (offsets are read on the
     device, not checked here)."""
@@ -344,9 +364,9 @@ def forward_varlen(q, k, v, cu_seqlens, max_s: int, causal: bool, scale: float, 
     lse = torch.empty((B, H, max_s), dtype=torch.float32, device=q.device) if lse is None else lse
     _check("o", o, (H, total, d), q.dtype)
     _check("lse", lse, (B, H, max_s), torch.float32)
-    if window is not None or dropout is not None:
+    if window is not None or dropout is not None or block_mask is not None:
         p = attn(B, H, H_kv, max_s, d, causal, scale, dtype_code(q.dtype), window or (-1, -1),
-                 cu_seqlens.data_ptr(), total, dropout)
+                 cu_seqlens.data_ptr(), total, dropout, **_bm(block_mask, H, max_s, q.device))
         st = fa_fwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        _stream(stream))
     else:
@@ -359,7 +379,8 @@ def forward_varlen(q, k, v, cu_seqlens, max_s: int, causal: bool, scale: float, 
 
 
 def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_s: int, causal: bool, scale: float,
-                    dq=None, dk=None, dv=None, ws=None, stream=None, window=None, dropout=None):
+                    dq=None, dk=None, dv=None, ws=None, stream=None, window=None, dropout=None,
+                    block_mask=None):
     """dQ, dK, dV for the packed forward that produced o and lse."""
     import torch
     H, total, d = q.shape
@@ -377,9 +398,9 @@ def backward_varlen(q, k, v, o, dout, lse, cu_seqlens, max_s: int, causal: bool,
     for name, t in (("dk", dk), ("dv", dv)):
         _check(name, t, (H_kv, total, d), q.dtype)
     ws = workspace(B, H, max_s, d, q.device) if ws is None else ws
-    if window is not None or dropout is not None:
+    if window is not None or dropout is not None or block_mask is not None:
         p = attn(B, H, H_kv, max_s, d, causal, scale, dtype_code(q.dtype), window or (-1, -1),
-                 cu_seqlens.data_ptr(), total, dropout)
+                 cu_seqlens.data_ptr(), total, dropout, **_bm(block_mask, H, max_s, q.device))
         st = fa_bwd_ex(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
                        ws.numel(), _stream(stream))

@@ -172,7 +172,7 @@ void bwd_dq_kernel(BwdArgs a) {
       ks_stage.load(K, (j + 1) * C::BC, N, tid);
       vs_stage.load(V, (j + 1) * C::BC, N, tid);
     }
-    if (j >= wfirst && j <= wlast) {
+    if (j >= wfirst && j <= wlast && block_on(a, (int)head, q0, j * C::BC)) {
       const int key0 = j * C::BC;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -454,6 +454,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   use_head(g);
   for (int qt = qt0; qt < nqt; ++qt) {
     const int qi0 = qt * C::BQ;
+    const bool tact = block_on(a, qhead, qi0, k0);   // block of a block mask computed
     const int buf = C::NBUF == 2 ? (qt - qt0) & 1 : 0;
     f32x16 s[2], dp[2], p[2], ds[2];
     frag pa[2][C::NU], sa[2][C::NU];
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
           if (m == elem_slot(b, i)) {
             const int qo = b * 32 + qoff_of(i) + hoff;
             float e = exp2_fast(fmaf(s[b][i], c, -l4[b][i / 4][i % 4]));
-            if (qi0 + qo < myk - wr || qi0 + qo > myk + wl) e = 0.f;
+            if (!tact || qi0 + qo < myk - wr || qi0 + qo > myk + wl) e = 0.f;
             float pe = e, dpi = dp[b][i];
             if constexpr (DROP) {   // dV's P and dP through the kept entries
               const bool keep = drop_keep(a.drop, qhead, qi0 + qo, myk);
@@ -629,6 +630,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   const int khi = min(myq + wr, N - 1), klo = myq - a.wl;
   // Key tiles of the workgroup: [lo, hi), of which [ml, mu) need no mask.
   const TileRange tr = tile_range(q0, min(q0 + C::BR, N) - 1, N, a.wl, wr, C::BC, false);
+  // The key tiles to visit: consecutive, or the active ones of the
+  // workgroup's row of a block mask.
+  BlockSkip sk = block_row(a, hd, q0 / kBlockQ, C::BC);
+  TileQueue tq;
+  tq.start(sk, tr.lo, tr.hi, lane);
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -658,12 +664,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
     }
   };
 
-  // Prologue: tiles lo and lo + 1 (NW = 8) or tile lo (NW = 4).
+  // Prologue: queue tiles t0 and t1 (NW = 8) or t0 (NW = 4).
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
   for (int t = 0; t < C::NB - 1; ++t)
 #pragma unroll
-    for (int j = 0; j < C::NLD; ++j) copy_op(t, tr.lo + t, j);
+    for (int j = 0; j < C::NLD; ++j) copy_op(t, tq.t[t], j);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
@@ -675,13 +681,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   constexpr auto elem_slot = [](int b, int i) {
     return b == 0 ? NS + 2 + (i * (NS - 2)) / 16 : 2 * NS + 1 + (i * (NQ - 2)) / 16;
   };
-  // NW = 8: copies of tile kt + 2 spread over the stream; NW = 4: copies of
-  // tile kt + 1 early in the stream, since they must land before its end.
+  // NW = 8: copies of queue tile t2 spread over the stream; NW = 4: copies of
+  // t1 early in the stream, since they must land before its end.
   constexpr auto copy_slot = [](int k) { return NW == 8 ? 1 + (k * (NM - 6)) / C::NLD : 1 + 2 * k; };
   int bcur = 0;
   // One key tile.  MASK: some key of the tile is past N or, under the causal
   // mask, after some query of the workgroup.
-  auto tile = [&](int kt, auto maskc) {
+  auto tile = [&](int kt, int tnext, auto maskc) {
     constexpr bool MASK = decltype(maskc)::value;
     const int key0 = kt * C::BC;
     const int rlo = klo - key0 - h;                 // masked tiles: offsets rlo ..
@@ -725,7 +731,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
       constexpr int m = decltype(mc)::value;
 #pragma unroll
       for (int k = 0; k < C::NLD; ++k)
-        if (m == copy_slot(k)) copy_op(C::NB == 3 ? b2 : b1, kt + C::NB - 1, k);
+        if (m == copy_slot(k)) copy_op(C::NB == 3 ? b2 : b1, tnext, k);
       // Operands are read in pairs at odd slots, the odd one first, so that the
       // wait for the even one covers both.
       const frag x = opq[m % PD];
@@ -784,10 +790,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   // Tiles [lo, ml) and [mu, hi) need masks in some row (the window's edges,
   // the causal diagonal, N); [ml, mu) none.  Separate loops, each with its own
   // register allocation.
-  int kt = tr.lo;
-  for (; kt < tr.ml; ++kt) tile(kt, std::true_type{});
-  for (; kt < tr.mu; ++kt) tile(kt, std::false_type{});
-  for (; kt < tr.hi; ++kt) tile(kt, std::true_type{});
+  // The queue skips the inactive tiles of a block mask; tnext is the tile copied
+  // during this one.
+  for (; tq.t[0] < tr.ml; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[C::NB - 1], std::true_type{});
+  for (; tq.t[0] < tr.mu; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[C::NB - 1], std::false_type{});
+  for (; tq.t[0] < tr.hi; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[C::NB - 1], std::true_type{});
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   if (myq < N) {
@@ -890,7 +897,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // the workgroup: [lo, hi), of which [ml, mu) need no mask.
   const int wl = a.wl, wr = CAUSAL ? min(a.wr, 0) : a.wr;
   const TileRange tr = tile_range(k0, k0 + C::BKC - 1, N, wr, wl, C::BQ, true);
-  const int qt0 = tr.lo;
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const TileLds<D> lay(lane);
@@ -935,17 +941,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     }
   };
 
-  // Start query head g of the group: its resources, then tiles qt0 and qt0 + 1
-  // into buffers 0 and 1.
+  // The query tiles to visit for the current query head: consecutive, or the
+  // active ones of the workgroup's column of its block mask.
+  BlockSkip sk;
+  TileQueue tq;
+  // Start query head g of the group: its resources and tile queue, then queue
+  // tiles t0 and t1 into buffers 0 and 1.
   auto use_head = [&](int g) {
     const size_t head = kvhead * a.G + g;
     qhead = (int)head;
+    sk = block_col(a, qhead, k0 / kBlockK, C::BQ);
+    tq.start(sk, tr.lo, tr.hi, lane);
     rsq = buffer_rsrc(static_cast<const T*>(a.q) + (sp.q + g * sp.hs) * D, (uint32_t)N * (2 * D));
     rsg = buffer_rsrc(static_cast<const T*>(a.dout) + (sp.q + g * sp.hs) * D, (uint32_t)N * (2 * D));
     rsl = buffer_rsrc(a.l2 + head * a.Np, (uint32_t)a.Np * 4);
     rsd = buffer_rsrc(a.delta + head * a.Np, (uint32_t)a.Np * 4);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    const Bases x0 = bases(0, qt0), x1 = bases(1, qt0 + 1);
+    const Bases x0 = bases(0, tq.t[0]), x1 = bases(1, tq.t[1]);
 #pragma unroll
     for (int j = 0; j < C::NLD; ++j) copy_op(x0, j);
 #pragma unroll
@@ -968,9 +980,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // Slot of copy k of the next-but-one tile.
   constexpr auto copy_slot = [](int k) { return 1 + (k * (NM - 6)) / C::NLD; };
   int bcur = 0;
-  // One query tile.  MASK: under the causal mask, some query of the tile comes
-  // before some key of the workgroup.
-  auto tile = [&](int qt, auto maskc) {
+  // One query tile (tnext: the tile copied meanwhile).  MASK: some query of the
+  // tile lies outside the window of some key of the workgroup.
+  auto tile = [&](int qt, int tnext, auto maskc) {
     constexpr bool MASK = decltype(maskc)::value;
     const int qi0 = qt * C::BQ;
     // Masked tiles: query offsets (q - qi0 - h) rlo .. rlo + rspan see this
@@ -1023,7 +1035,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
       asm volatile("" ::: "memory");   // keeps the two operands' reads apart
       opq[m] = operand(m);
     }
-    const Bases xc = bases(b2, qt + 2);
+    const Bases xc = bases(b2, tnext);
     // Dropout keep bits of this lane's key column, bit i of block b for query
     // 8 (i / 4) + 2 (i % 4) + h of the block.  A generator call serves the 8
     // keys 16 p + par + 2 t of one query, which sit in 8 lanes here: lane (col,
@@ -1127,7 +1139,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     });
     // Tile qt + 1 (copied during the previous tile) must have landed; the
-    // copies of tile qt + 2 may still be in flight.
+    // copies of tile tnext may still be in flight.
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
     __syncthreads();
     bcur = b1;
@@ -1139,10 +1151,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   for (int g = 0; g < a.G; ++g) {
     use_head(g);
     bcur = 0;
-    int qt = qt0;
-    for (; qt < tr.ml; ++qt) tile(qt, std::true_type{});
-    for (; qt < tr.mu; ++qt) tile(qt, std::false_type{});
-    for (; qt < tr.hi; ++qt) tile(qt, std::true_type{});
+    // The queue skips the inactive tiles of a block mask; the tile copied during
+    // tile t0 is t2.
+    for (; tq.t[0] < tr.ml; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[2], std::true_type{});
+    for (; tq.t[0] < tr.mu; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[2], std::false_type{});
+    for (; tq.t[0] < tr.hi; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[2], std::true_type{});
     // No copy may still be writing LDS when the next head starts or the
     // workgroup ends, and every wave is done with the buffers.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

@@ -259,16 +259,22 @@ void fwd_kernel(FwdArgs a) {
     sstore_k((j0 + 1) & 1);
   }
   __syncthreads();
+  // Tiles this wave computes: inside its range and in an active block of a block
+  // mask (the whole workgroup lies in one block row).
+  auto proc = [&](int j) {
+    return j < ntiles && j >= wfirst && j <= wlast && block_on(a, (int)head, q0, j * C::BC);
+  };
   f32x16 sc[2];
-  if (wlast >= 0 && wfirst == j0) s_tile(j0 & 1, sc);
+  if (proc(j0)) s_tile(j0 & 1, sc);
   // Iteration j0 overwrites the K buffer read just above with K of tile j0 + 2.
   __syncthreads();
   for (int j = j0; j < ntiles; ++j) {
     if (j + 2 < ntiles) gload_k(j + 2);
     if (j + 1 < ntiles) gload_v(j + 1);
-    // A wave whose first tile is the next one computes its S now.
-    if (j + 1 == wfirst && wfirst <= wlast) s_tile((j + 1) & 1, sc);
-    if (j >= wfirst && j <= wlast) {
+    // A wave that skips this tile but computes the next one takes its S now.
+    const bool pj = proc(j);
+    if (!pj && proc(j + 1)) s_tile((j + 1) & 1, sc);
+    if (pj) {
       const int key0 = j * C::BC;
       const bool masked = (key0 + C::BC - 1 > qw + wr) || (key0 < qw + 31 - wl) || (key0 + C::BC > N);
       f32x16 sn[2];
@@ -440,6 +446,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   const int khi = min(myq + wr, N - 1), klo = myq - a.wl;
   // Key tiles of the workgroup: [lo, hi), of which [ml, mu) need no mask.
   const TileRange tr = tile_range(q0, min(q0 + C::BR, N) - 1, N, a.wl, wr, C::BC, false);
+  // The tiles to visit, in order: consecutive, or the active ones of the
+  // workgroup's row of a block mask.
+  BlockSkip sk = block_row(a, hd, q0 / kBlockQ, C::BC);
+  TileQueue tq;
+  tq.start(sk, tr.lo, tr.hi, lane);
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const TileLds<D> lay(lane);
@@ -478,24 +489,23 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   // for the MFMA, so that the weights of O sum to 1 exactly as used.
   float l_run = 0.f;
 
-  // Prologue (first tile j0 = tr.lo): NW = 8: tiles j0, j0 + 1, j0 + 2 into
-  // buffers 0, 1, 2 (wave w copies groups 4 (w & 3) .. + 3 of K (w < 4) or V);
-  // NW = 4: K and V of tile j0 into buffer j0 & 1 and K of tile j0 + 1 into the
-  // other (wave w copies groups 4 w .. + 3 of each).  Then S of tile j0.
-  const int j0 = tr.lo;
+  // Prologue (queue tiles t0, t1, t2): NW = 8: t0, t1, t2 into buffers 0, 1, 2
+  // (wave w copies groups 4 (w & 3) .. + 3 of K (w < 4) or V); NW = 4: K and V
+  // of t0 into buffer 0 and K of t1 into buffer 1 (wave w copies groups
+  // 4 w .. + 3 of each).  Then S of t0.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if constexpr (NW == 8) {
 #pragma unroll
     for (int t = 0; t < 3; ++t)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) copy_group(t, w >> 2, j0 + t, 4 * (w & 3) + kk);
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // tile j0 + 2 may still be in flight
+      for (int kk = 0; kk < 4; ++kk) copy_group(t, w >> 2, tq.t[t], 4 * (w & 3) + kk);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // t2 may still be in flight
   } else {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      copy_group(j0 & 1, 0, j0, 4 * w + kk);
-      copy_group(j0 & 1, 1, j0, 4 * w + kk);
-      copy_group((j0 + 1) & 1, 0, j0 + 1, 4 * w + kk);
+      copy_group(0, 0, tq.t[0], 4 * w + kk);
+      copy_group(0, 1, tq.t[0], 4 * w + kk);
+      copy_group(1, 0, tq.t[1], 4 * w + kk);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
@@ -505,11 +515,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   f32x16 sA[2], sB[2];
   sA[0] = f32x16{};
   sA[1] = f32x16{};
-  {
-    const int kb0 = NW == 8 ? 0 : (j0 & 1) * C::BUF;
 #pragma unroll
-    for (int m = 0; m < C::NS; ++m) sA[m & 1] = M::mma(opS(kb0, m), qf[m >> 1], sA[m & 1]);
-  }
+  for (int m = 0; m < C::NS; ++m) sA[m & 1] = M::mma(opS(0, m), qf[m >> 1], sA[m & 1]);
 
   constexpr int NS = C::NS, NV = C::NV, NM = C::NM, NA = C::NA;
   constexpr int PD = 4;
@@ -521,21 +528,21 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   constexpr auto exp_slot = [](int kb, int i) {
     return kb == 0 ? NA + 1 + (i * (NS - NA - 1)) / 16 : NS + (i * (NV / 2)) / 16;
   };
-  // NW = 8: the copies of tile j + 3 spread over the P~V MFMAs; NW = 4: the
-  // copies of iteration j (K of tile j + 2, V of tile j + 1) early in the
-  // stream, since they must land before its end.
+  // NW = 8: the copies of queue tile t3 spread over the P~V MFMAs; NW = 4: the
+  // copies of the step (K of t2, V of t1) early in the stream, since they must
+  // land before its end.
   constexpr auto copy_slot = [](int k) {
     return NW == 8 ? NS + (k * NV) / C::NLD : 1 + 2 * k;
   };
 
-  int b0 = 0;   // buffer of tile j (NW = 8)
-  // One tile: S of tile j + 1 (into sn) with the softmax of tile j (S in sc),
-  // then P~V of tile j.  MASK: some row of the wave crosses the causal
-  // diagonal or N in tile j.
-  auto iteration = [&](int j, auto maskc, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    const int key0 = j * C::BC;
-    const int bk = NW == 8 ? (b0 + 1) & 3 : (j + 1) & 1, bc = (b0 + 3) & 3;
-    const int kboff = bk * C::BUF, vboff = (NW == 8 ? b0 : j & 1) * C::BUF;
+  int b0 = 0;   // buffer of tile t0 (NW = 8)
+  // One step: S of queue tile t1 (into sn) with the softmax of t0 (S in sc),
+  // then P~V of t0.  MASK: some row of the wave crosses an edge of the window,
+  // the causal diagonal or N in t0.  NW = 4 buffers alternate by step.
+  auto iteration = [&](const TileQueue& q, auto maskc, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    const int key0 = q.t[0] * C::BC;
+    const int bk = NW == 8 ? (b0 + 1) & 3 : (q.s + 1) & 1, bc = (b0 + 3) & 3;
+    const int kboff = bk * C::BUF, vboff = (NW == 8 ? b0 : q.s & 1) * C::BUF;
     frag pf[2][2];
     sn[0] = f32x16{};
     sn[1] = f32x16{};
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
       asm volatile("" ::: "memory");
       opq[m] = operand(m);
     }
-    // One slot of the tile's stream: MFMA m (S of tile j + 1, or P~V of tile j)
+    // One slot of the tile's stream: MFMA m (S of tile t1, or P~V of tile t0)
     // and the softmax / copy work placed on that slot.
     auto slot = [&](auto mc, auto maskc) {
       constexpr int m = decltype(mc)::value;
@@ -575,9 +582,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
 #pragma unroll
       for (int k = 0; k < C::NLD; ++k)
         if (m == copy_slot(k)) {
-          if constexpr (NW == 8) copy_group(bc, w >> 2, j + 3, 4 * (w & 3) + k);
-          else if (k < 4) copy_group(j & 1, 0, j + 2, 4 * w + k);
-          else copy_group((j + 1) & 1, 1, j + 1, 4 * w + k - 4);
+          if constexpr (NW == 8) copy_group(bc, w >> 2, q.t[3], 4 * (w & 3) + k);
+          else if (k < 4) copy_group(q.s & 1, 0, q.t[2], 4 * w + k);
+          else copy_group((q.s + 1) & 1, 1, q.t[1], 4 * w + k - 4);
         }
 #pragma unroll
       for (int e = 0; e < 32; ++e)
@@ -647,9 +654,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
     rescale();
     static_for<NS, NM>([&](auto mc) { slot(mc, maskc); });
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    // NW = 8: tile j + 2 (copied during the previous tile) must have landed,
-    // the copies of tile j + 3 may still be in flight.  NW = 4: K of tile j + 2
-    // and V of tile j + 1 must have landed.
+    // NW = 8: t2 (copied during the previous step) must have landed, the copies
+    // of t3 may still be in flight.  NW = 4: K of t2 and V of t1 must have landed.
     __builtin_amdgcn_s_waitcnt(NW == 8 ? wait_vmcnt(C::NLD) : kWaitVmcnt0);
     __syncthreads();
     b0 = (b0 + 1) & 3;
@@ -658,30 +664,34 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   // window's edges, the causal diagonal, N); [ml, mu) none.  Each range runs in
   // a loop of its own, so that each loop body keeps its own register
   // allocation; after an odd tile the S registers are handed over by copy.
-  int j = j0;
-  for (; j + 1 < tr.ml; j += 2) {
-    iteration(j, std::true_type{}, sA, sB);
-    iteration(j + 1, std::true_type{}, sB, sA);
+  // The queue skips the inactive tiles of a block mask.
+  auto step = [&](auto maskc, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    iteration(tq, maskc, sc, sn);
+    tq.advance(sk, tr.hi, lane);
+  };
+  while (tq.t[1] < tr.ml) {
+    step(std::true_type{}, sA, sB);
+    step(std::true_type{}, sB, sA);
   }
-  if (j < tr.ml) {
-    iteration(j++, std::true_type{}, sA, sB);
+  if (tq.t[0] < tr.ml) {
+    step(std::true_type{}, sA, sB);
     sA[0] = sB[0];
     sA[1] = sB[1];
   }
-  for (; j + 1 < tr.mu; j += 2) {
-    iteration(j, std::false_type{}, sA, sB);
-    iteration(j + 1, std::false_type{}, sB, sA);
+  while (tq.t[1] < tr.mu) {
+    step(std::false_type{}, sA, sB);
+    step(std::false_type{}, sB, sA);
   }
-  if (j < tr.mu) {
-    iteration(j++, std::false_type{}, sA, sB);
+  if (tq.t[0] < tr.mu) {
+    step(std::false_type{}, sA, sB);
     sA[0] = sB[0];
     sA[1] = sB[1];
   }
-  for (; j + 1 < tr.hi; j += 2) {
-    iteration(j, std::true_type{}, sA, sB);
-    iteration(j + 1, std::true_type{}, sB, sA);
+  while (tq.t[1] < tr.hi) {
+    step(std::true_type{}, sA, sB);
+    step(std::true_type{}, sB, sA);
   }
-  if (j < tr.hi) iteration(j, std::true_type{}, sA, sB);
+  if (tq.t[0] < tr.hi) step(std::true_type{}, sA, sB);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   const float l = half_sum(l_run);

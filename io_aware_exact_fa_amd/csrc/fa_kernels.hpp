@@ -22,6 +22,16 @@ struct Dropout {
   uint32_t seed_lo = 0, seed_hi = 0, offset = 0;
 };
 
+// Block-sparse mask: blocks of kBlockQ queries x kBlockK keys (positions in the
+// sequence); block (qb, kb) of query head h is mask[(h % heads) * nbq * nbk +
+// qb * nbk + kb], nonzero = computed.  Every workgroup of every kernel lies in
+// one block row (at most kBlockQ query rows) or one block column (kBlockK keys).
+constexpr int kBlockQ = 256, kBlockK = 128;
+struct BlockMask {
+  const uint8_t* mask = nullptr;   // null: every block is computed
+  int heads = 1, nbq = 0, nbk = 0;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -40,6 +50,7 @@ struct FwdArgs {
   // the sequence; wl, wr >= 0 or kNoLimit).  Causal launches take wr = 0.
   int wl = kNoLimit, wr = kNoLimit;
   Dropout drop;
+  BlockMask bm;
 };
 
 struct BwdArgs {
@@ -62,7 +73,90 @@ struct BwdArgs {
   int total = 0;                     // (sequence, head) stay Np and N
   int wl = kNoLimit, wr = kNoLimit;  // as in FwdArgs
   Dropout drop;                      // as in FwdArgs
+  BlockMask bm;                      // as in FwdArgs
 };
+
+// Active tiles along one block row (forward, dQ: key tiles of one query block)
+// or block column (dK/dV: query tiles of one key block) of a block mask, tpb
+// tiles per block.  Blocks are scanned 64 at a time, one byte load per lane and
+// a ballot; everything else is uniform (scalar).
+struct BlockSkip {
+  const uint8_t* base = nullptr;   // block x of the row/column at base[x * stride]; null: all
+  int stride = 1, nblk = 0, tpb = 1;
+  int chunk = -1;
+  uint64_t bits = 0;
+  // The first active tile >= t, or some tile >= end if there is none below end.
+  __device__ int next(int t, int end, int lane) {
+    if (!base) return t;
+    while (t < end) {
+      const int blk = t / tpb, c = blk >> 6;
+      if (c != chunk) {
+        chunk = c;
+        const int x = (c << 6) + lane;
+        bits = __ballot(x < nblk && base[(size_t)x * stride] != 0);
+      }
+      const uint64_t m = bits >> (blk & 63);
+      if (m & 1ull) return t;
+      t = m ? (blk + __builtin_ctzll(m)) * tpb : ((c + 1) << 6) * tpb;
+    }
+    return t;
+  }
+};
+
+// Whether block (q / kBlockQ, k / kBlockK) of query head `head` is computed
+// (the register-staged kernels test tiles one by one instead of skipping).
+template <class Args>
+__device__ inline bool block_on(const Args& a, int head, int q, int k) {
+  if (!a.bm.mask) return true;
+  return a.bm.mask[(size_t)((head % a.H) % a.bm.heads) * a.bm.nbq * a.bm.nbk +
+                   (size_t)(q / kBlockQ) * a.bm.nbk + k / kBlockK] != 0;
+}
+
+// The workgroup's next tiles: t[0] the current one, t[1..3] the following active
+// ones (copied ahead), s the step count (buffer parity of the 4-wave kernels).
+struct TileQueue {
+  int t[4];
+  int s;
+  __device__ void start(BlockSkip& sk, int lo, int end, int lane) {
+    t[0] = sk.next(lo, end, lane);
+#pragma unroll
+    for (int k = 1; k < 4; ++k) t[k] = sk.next(t[k - 1] + 1, end, lane);
+    s = 0;
+  }
+  __device__ void advance(BlockSkip& sk, int end, int lane) {
+    t[0] = t[1];
+    t[1] = t[2];
+    t[2] = t[3];
+    t[3] = sk.next(t[3] + 1, end, lane);
+    ++s;
+  }
+};
+
+// The skip of one workgroup: a row of the mask (forward, dQ: query block qb,
+// key tiles of `tile` keys) or a column (dK/dV: key block kb, query tiles).
+template <class Args>
+__device__ inline BlockSkip block_row(const Args& a, int head, int qb, int tile) {
+  BlockSkip sk;
+  if (a.bm.mask) {
+    sk.base = a.bm.mask + (size_t)((head % a.H) % a.bm.heads) * a.bm.nbq * a.bm.nbk +
+              (size_t)qb * a.bm.nbk;
+    sk.stride = 1;
+    sk.nblk = a.bm.nbk;
+    sk.tpb = kBlockK / tile;
+  }
+  return sk;
+}
+template <class Args>
+__device__ inline BlockSkip block_col(const Args& a, int head, int kb, int tile) {
+  BlockSkip sk;
+  if (a.bm.mask) {
+    sk.base = a.bm.mask + (size_t)((head % a.H) % a.bm.heads) * a.bm.nbq * a.bm.nbk + kb;
+    sk.stride = a.bm.nbk;
+    sk.nblk = a.bm.nbq;
+    sk.tpb = kBlockQ / tile;
+  }
+  return sk;
+}
 
 // Tile ranges of one workgroup under the window: rows [ra, rb] of the outer
 // operand (queries in the forward and dQ, keys in dK/dV) need inner tiles

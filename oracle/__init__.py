@@ -13,7 +13,8 @@ Contents
                 also with grouped key/value heads (forward_gqa, backward_gqa)
                 and padding-free variable-length batches (forward_varlen,
                 backward_varlen); every function takes an optional local
-                window (window_visible).
+                window (window_visible) and a block-sparse mask
+                (block_visible).
 ``philox``      Philox4x32-10 and the dropout keep mask built from it.
 ``recurrence``  the online-softmax tile recurrence and the two-tile merge,
                 written in the pages' order; used only to pin that the
@@ -27,6 +28,7 @@ from .attention import (  # noqa: F401
     backward,
     backward_gqa,
     backward_varlen,
+    block_visible,
     dropped,
     head_drop,
     backward_head,

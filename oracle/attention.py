@@ -68,15 +68,30 @@ def window_visible(n_q: int, n_k: int, window) -> np.ndarray:
     return vis
 
 
-def scores(q, k, scale: float, causal: bool, window=None) -> np.ndarray:
-    """S = scale * Q K^T for one head, with -inf where the causal mask or the
-    window hides a key."""
+BLOCK_Q, BLOCK_K = 256, 128
+
+
+def block_visible(n_q: int, n_k: int, blocks) -> np.ndarray:
+    """Boolean [n_q, n_k] from a block mask [ceil(n_q / BLOCK_Q), ceil(n_k / BLOCK_K)]:
+    key j is visible to query i iff block (i // BLOCK_Q, j // BLOCK_K) is nonzero.
+    Block-sparse attention skips the zero blocks of a given mask ("FlashAttention 원
+    논문 해부", section "대안, 비교와 선택 기준"); the dense attention with this
+    element mask is its exact result."""
+    b = np.asarray(blocks) != 0
+    return b[np.arange(n_q)[:, None] // BLOCK_Q, np.arange(n_k)[None, :] // BLOCK_K]
+
+
+def scores(q, k, scale: float, causal: bool, window=None, blocks=None) -> np.ndarray:
+    """S = scale * Q K^T for one head, with -inf where the causal mask, the window
+    or a block mask hides a key."""
     q, k = _f64(q), _f64(k)
     s = float(scale) * (q @ k.T)
     if causal:
         s = np.where(causal_visible(q.shape[0], k.shape[0]), s, -np.inf)
     if window is not None:
         s = np.where(window_visible(q.shape[0], k.shape[0], window), s, -np.inf)
+    if blocks is not None:
+        s = np.where(block_visible(q.shape[0], k.shape[0], blocks), s, -np.inf)
     return s
 
 
@@ -113,21 +128,22 @@ def dropped(p, drop):
 
 
 def forward_head(q, k, v, scale: float, causal: bool, window=None,
-                 drop=None) -> tuple[np.ndarray, np.ndarray]:
+                 drop=None, blocks=None) -> tuple[np.ndarray, np.ndarray]:
     """O = dropout(P) V and LSE for one head (q: [N,d], k: [N,d], v: [N,dv]).  LSE
     is that of the undropped softmax (it is what the backward recomputes P from)."""
-    p, lse = row_softmax(scores(q, k, scale, causal, window))
+    p, lse = row_softmax(scores(q, k, scale, causal, window, blocks))
     o = dropped(p, drop) @ _f64(v)
     return o, lse
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool, window=None, drop=None) -> dict:
+def backward_head(q, k, v, do, scale: float, causal: bool, window=None, drop=None,
+                  blocks=None) -> dict:
     """Analytic gradients of sum(O * dO) for one head.
 
     Returns dict(dq, dk, dv, D, p, dp, ds); D is computed as rowsum(P * dP).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    p, _ = row_softmax(scores(q, k, scale, causal, window))
+    p, _ = row_softmax(scores(q, k, scale, causal, window, blocks))
     dv = dropped(p, drop).T @ do           # dV = dropout(P)^T dO
     dp = dropped(do @ v.T, drop)           # dP = dropout'(dO V^T): the chain rule
                                            # through the kept entries and the scale
@@ -206,7 +222,16 @@ def _group(h_q: int, h_kv: int) -> int:
     return h_q // h_kv
 
 
-def forward_gqa(q, k, v, scale: float, causal: bool, window=None, dropout=None):
+def _blocks(block_mask, h):
+    """Block mask of query head h from [1 or H, nbq, nbk], or None."""
+    if block_mask is None:
+        return None
+    bm = np.asarray(block_mask)
+    return bm[h % bm.shape[0]]
+
+
+def forward_gqa(q, k, v, scale: float, causal: bool, window=None, dropout=None,
+                block_mask=None):
     """q [B, H, N, d], k [B, H_kv, N, d], v [B, H_kv, N, dv] -> (O [B, H, N, dv],
     LSE [B, H, N])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -218,11 +243,12 @@ def forward_gqa(q, k, v, scale: float, causal: bool, window=None, dropout=None):
         for h in range(H):
             drop = head_drop(dropout, b * H + h, q.shape[2])
             o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h // g], v[b, h // g], scale, causal,
-                                              window, drop)
+                                              window, drop, _blocks(block_mask, h))
     return o, lse
 
 
-def backward_gqa(q, k, v, do, scale: float, causal: bool, window=None, dropout=None):
+def backward_gqa(q, k, v, do, scale: float, causal: bool, window=None, dropout=None,
+                 block_mask=None):
     """Gradients of sum(O * dO) for forward_gqa: (dQ [B, H, N, d], dK [B, H_kv, N, d],
     dV [B, H_kv, N, dv])."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
@@ -235,7 +261,7 @@ def backward_gqa(q, k, v, do, scale: float, causal: bool, window=None, dropout=N
         for h in range(H):
             drop = head_drop(dropout, b * H + h, q.shape[2])
             r = backward_head(q[b, h], k[b, h // g], v[b, h // g], do[b, h], scale, causal, window,
-                              drop)
+                              drop, _blocks(block_mask, h))
             dq[b, h] = r["dq"]
             dk[b, h // g] += r["dk"]
             dv[b, h // g] += r["dv"]
@@ -272,7 +298,7 @@ def _spans(cu_seqlens, total: int, max_s: int):
 
 
 def forward_varlen(q, k, v, cu_seqlens, max_s: int, scale: float, causal: bool, seqs=None,
-                   window=None, dropout=None):
+                   window=None, dropout=None, block_mask=None):
     """q [H, total, d], k [H_kv, total, d], v [H_kv, total, dv] -> (O [H, total, dv],
     LSE [B, H, max_s]).  ``seqs`` optionally restricts the work to some sequences."""
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -289,12 +315,13 @@ def forward_varlen(q, k, v, cu_seqlens, max_s: int, scale: float, causal: bool, 
         for h in range(H):
             drop = head_drop(dropout, b * H + h, s1 - s0)
             o[h, s0:s1], lse[b, h, : s1 - s0] = forward_head(
-                q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], scale, causal, window, drop)
+                q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], scale, causal, window, drop,
+                _blocks(block_mask, h))
     return o, lse
 
 
 def backward_varlen(q, k, v, do, cu_seqlens, max_s: int, scale: float, causal: bool, seqs=None,
-                    window=None, dropout=None):
+                    window=None, dropout=None, block_mask=None):
     """Gradients of sum(O * dO) for forward_varlen: (dQ [H, total, d],
     dK [H_kv, total, d], dV [H_kv, total, dv]); rows outside the computed
     sequences are NaN."""
@@ -314,7 +341,7 @@ def backward_varlen(q, k, v, do, cu_seqlens, max_s: int, scale: float, causal: b
         for h in range(H):
             drop = head_drop(dropout, b * H + h, s1 - s0)
             r = backward_head(q[h, s0:s1], k[h // g, s0:s1], v[h // g, s0:s1], do[h, s0:s1],
-                              scale, causal, window, drop)
+                              scale, causal, window, drop, _blocks(block_mask, h))
             dq[h, s0:s1] = r["dq"]
             dk[h // g, s0:s1] += r["dk"]
             dv[h // g, s0:s1] += r["dv"]

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 6
+    assert fa.fa_abi_version() == 7
     for st in range(6):
         assert fa.fa_status_string(st) and fa.fa_status_string(st) != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -173,11 +173,12 @@ def test_varlen_rejects():
 
 def test_attn_struct_layout():
     """ctypes mirror of struct fa_attn: natural alignment on x86-64 (the pointer at
-    byte 40, the seed at 56, the whole 72 bytes)."""
-    assert ctypes.sizeof(fa.FaAttn) == 72
+    byte 40, the seed at 56, the block mask at 72, the whole 88 bytes)."""
+    assert ctypes.sizeof(fa.FaAttn) == 88
     assert fa.FaAttn.cu_seqlens.offset == 40 and fa.FaAttn.total.offset == 48
     assert fa.FaAttn.dropout_p.offset == 52 and fa.FaAttn.seed.offset == 56
-    assert fa.FaAttn.rng_offset.offset == 64
+    assert fa.FaAttn.rng_offset.offset == 64 and fa.FaAttn.block_mask.offset == 72
+    assert fa.FaAttn.block_mask_heads.offset == 80
     assert fa.FaAttn.window_left.offset == 24 and fa.FaAttn.scale.offset == 32
 
 
@@ -192,6 +193,11 @@ def test_ex_rejects():
         assert fwd(fa.attn(**good, window=window)) == E
         assert bwd(fa.attn(**good, window=window)) == E
     assert fwd(fa.attn(**{**good, "H_kv": 3})) == E
+    # Dropout instances are switched off for now.
+    assert fwd(fa.attn(**good, dropout=(0.25, 1, 0))) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(fa.attn(**good, dropout=(0.25, 1, 0))) == fa.FA_ERR_UNSUPPORTED
+    for heads in (0, 3, 9):   # a mask needs 1 or H (= 8) heads
+        assert fwd(fa.attn(**good, block_mask=P, block_mask_heads=heads)) == E
     for pd in (-0.1, 1.5, float("nan")):
         assert fwd(fa.attn(**good, dropout=(pd, 1, 0))) == E
         assert bwd(fa.attn(**good, dropout=(pd, 1, 0))) == E

@@ -653,3 +653,75 @@ def test_dropout_finite_differences(causal):
             ap[which], am[which] = xp, xm
             fd[idx] = (loss(*ap) - loss(*am)) / (2 * hstep)
         np.testing.assert_allclose(gg, fd, rtol=0, atol=1e-7, err_msg="qkv"[which])
+
+
+# ----------------------------------------------------------- block-sparse masks
+
+
+def test_full_block_mask_changes_nothing():
+    q, k, v, do = _win_inputs(n=300)
+    o, lse = oracle.forward_head(q, k, v, 0.5, True)
+    o2, lse2 = oracle.forward_head(q, k, v, 0.5, True, blocks=np.ones((2, 3)))
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_diagonal_mask_is_a_packed_batch(causal):
+    """Query block b sees key blocks 2 b and 2 b + 1 only (256 queries x 2 x 128 keys):
+    exactly a packed batch of sequences of 256 tokens, a formulation by slicing."""
+    r = np.random.default_rng(3)
+    n, H = 768, 2
+    q, k, v, do = (r.standard_normal((1, H, n, 3)) for _ in range(4))
+    bm = np.zeros((1, 3, 6), dtype=np.uint8)
+    for b in range(3):
+        bm[0, b, 2 * b:2 * b + 2] = 1
+    o, lse = oracle.forward_gqa(q, k, v, 0.7, causal, block_mask=bm)
+    ov, lsev = oracle.forward_varlen(q[0], k[0], v[0], [0, 256, 512, 768], 256, 0.7, causal)
+    np.testing.assert_allclose(o[0], ov, rtol=0, atol=1e-13)
+    for b in range(3):
+        np.testing.assert_allclose(lse[0, :, 256 * b:256 * b + 256], lsev[b], rtol=0, atol=1e-13)
+    g = oracle.backward_gqa(q, k, v, do, 0.7, causal, block_mask=bm)
+    gv = oracle.backward_varlen(q[0], k[0], v[0], do[0], [0, 256, 512, 768], 256, 0.7, causal)
+    for x, y in zip(g, gv):
+        np.testing.assert_allclose(x[0], y, rtol=0, atol=1e-12)
+
+
+def test_block_mask_empty_rows_and_zero_query():
+    """A query block with no kept key block: O = 0, LSE = -inf, no gradient; the
+    other rows with Q = 0 average V over exactly the kept key blocks."""
+    r = np.random.default_rng(4)
+    n = 300
+    k, v, do = (r.standard_normal((n, 3)) for _ in range(3))
+    blocks = np.array([[1, 0, 1], [0, 0, 0]])
+    o, lse = oracle.forward_head(np.zeros((n, 3)), k, v, 0.5, False, blocks=blocks)
+    keep = np.r_[0:128, 256:300]
+    np.testing.assert_allclose(o[:256], np.broadcast_to(v[keep].mean(axis=0), (256, 3)), atol=1e-14)
+    np.testing.assert_allclose(lse[:256], math.log(len(keep)), atol=1e-14)
+    assert (o[256:] == 0).all() and np.isneginf(lse[256:]).all()
+    g = oracle.backward_head(r.standard_normal((n, 3)), k, v, do, 0.5, False, blocks=blocks)
+    assert (g["dq"][256:] == 0).all()
+    assert (g["dk"][128:256] == 0).all() and (g["dv"][128:256] == 0).all()
+
+
+def test_block_mask_finite_differences():
+    r = np.random.default_rng(5)
+    n = 260
+    q, k, v, do = (r.standard_normal((n, 2)) for _ in range(4))
+    blocks = np.array([[1, 0, 1], [0, 1, 1]])
+    scale, hstep = 0.9, 1e-6
+    g = oracle.backward_head(q, k, v, do, scale, True, blocks=blocks)
+
+    def loss(qq, kk, vv):
+        return float((oracle.forward_head(qq, kk, vv, scale, True, blocks=blocks)[0] * do).sum())
+
+    for which, (x, gg) in enumerate(zip((q, k, v), (g["dq"], g["dk"], g["dv"]))):
+        idxs = [(i, c) for i in (0, 5, 127, 128, 200, 255, 256, 259) for c in range(2)]
+        for idx in idxs:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += hstep
+            xm[idx] -= hstep
+            ap, am = [q, k, v], [q, k, v]
+            ap[which], am[which] = xp, xm
+            fd = (loss(*ap) - loss(*am)) / (2 * hstep)
+            assert abs(gg[idx] - fd) < 1e-6, ("qkv"[which], idx, gg[idx], fd)

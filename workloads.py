@@ -40,6 +40,7 @@ class Workload:
     H_kv: int = 0       # key/value heads (0: one per query head)
     window: tuple = (-1, -1)   # local window (left, right); -1: open side
     dropout: tuple = ()        # (p, seed, offset): dropout on P, regenerated in the backward
+    block_density: float = 0.0   # > 0: a block-sparse mask per head (block_mask())
 
     @property
     def kv_heads(self) -> int:
@@ -48,6 +49,10 @@ class Workload:
     @property
     def windowed(self) -> bool:
         return tuple(self.window) != (-1, -1)
+
+    @property
+    def sparse(self) -> bool:
+        return self.block_density > 0
 
     @property
     def scale(self) -> float:
@@ -60,6 +65,10 @@ class Workload:
     def fwd_flops(self) -> float:
         """Forward FLOPs counted as 4*B*H*N^2*d, halved under the causal mask; with a
         local window, 4*B*H*d per visible (query, key) pair."""
+        if self.sparse:
+            bm = block_mask(self)
+            return 4.0 * self.B * self.d * sum(block_pairs(self.N, self.causal, bm[h])
+                                               for h in range(self.H))
         if self.windowed:
             return 4.0 * self.B * self.H * self.d * visible_pairs(self.N, self.causal, self.window)
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
@@ -82,6 +91,40 @@ def visible_pairs(n: int, causal: bool, window) -> int:
     total = 0
     for i in range(n):   # n is at most a few tens of thousands
         total += min(n - 1, i + right) - max(0, i - left) + 1
+    return total
+
+
+BLOCK_Q, BLOCK_K = 256, 128   # block sizes of a block-sparse mask (queries x keys)
+
+
+def block_mask(w) -> torch.Tensor:
+    """uint8 [H, ceil(N / 256), ceil(N / 128)]: each block kept with probability
+    block_density (seeded with seed + 1), the key blocks of a query block's own
+    rows always kept (so that no row is empty)."""
+    nbq, nbk = -(-w.N // BLOCK_Q), -(-w.N // BLOCK_K)
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 1)
+    m = (torch.rand((w.H, nbq, nbk), generator=g) < w.block_density).to(torch.uint8)
+    for qb in range(nbq):
+        m[:, qb, (qb * BLOCK_Q) // BLOCK_K:min(nbk, ((qb + 1) * BLOCK_Q + BLOCK_K - 1) // BLOCK_K)] = 1
+    return m.contiguous()
+
+
+def block_pairs(n: int, causal: bool, bm) -> int:
+    """(query, key) pairs a block mask [nbq, nbk] keeps (under the causal mask,
+    those with key <= query), counted block by block."""
+    total = 0
+    nbq, nbk = bm.shape
+    for qb in range(nbq):
+        q0, q1 = qb * BLOCK_Q, min(n, (qb + 1) * BLOCK_Q)
+        for kb in range(nbk):
+            if not bm[qb, kb]:
+                continue
+            k0, k1 = kb * BLOCK_K, min(n, (kb + 1) * BLOCK_K)
+            if not causal:
+                total += (q1 - q0) * (k1 - k0)
+            else:
+                for i in range(q0, q1):
+                    total += max(0, min(k1, i + 1) - k0)
     return total
 
 
@@ -117,7 +160,13 @@ DROPOUT_BF16 = Workload("b2h32n8192d128-bf16-dropout0.1", 2, 32, 8192, 128, "bf1
                         dropout=(0.1, 0x5EED_0001_2345_6789, 7))
 DROPOUT = (DROPOUT_BF16,)
 
-BY_NAME = {w.name: w for w in ALL + GQA + WINDOWED + DROPOUT}
+# Block-sparse attention at the offset workload's shape: a quarter of the
+# 256 x 128 blocks kept at random per head (the block-diagonal always).
+SPARSE_BF16 = Workload("b2h32n8192d128-bf16-blocksparse25", 2, 32, 8192, 128, "bf16", False, 1012,
+                       block_density=0.25)
+SPARSE = (SPARSE_BF16,)
+
+BY_NAME = {w.name: w for w in ALL + GQA + WINDOWED + DROPOUT + SPARSE}
 
 
 def make_inputs(w: Workload) -> dict:
