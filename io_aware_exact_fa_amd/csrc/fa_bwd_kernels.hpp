@@ -581,7 +581,9 @@ struct Dq16 {
   static constexpr int NLD = 2 * BC / NW / TileLds<D>::ROWS_PER_COPY;   // copies per wave per tile
 };
 
-template <typename T, int D, bool CAUSAL, int NW, bool DROP>
+// BSPARSE as for the dK/dV kernel: the tile queue only in the block-sparse
+// instance, plain consecutive tiles otherwise.
+template <typename T, int D, bool CAUSAL, int NW, bool DROP, bool BSPARSE>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   using C = Dq16<D, NW>;
   static_assert(NW == 8 || (NW == 4 && D == 128), "4-wave dQ workgroups copy 4-row groups");
@@ -632,9 +634,15 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   const TileRange tr = tile_range(q0, min(q0 + C::BR, N) - 1, N, a.wl, wr, C::BC, false);
   // The key tiles to visit: consecutive, or the active ones of the
   // workgroup's row of a block mask.
-  BlockSkip sk = block_row(a, hd, q0 / kBlockQ, C::BC);
+  BlockSkip sk;
   TileQueue tq;
-  tq.start(sk, tr.lo, tr.hi, lane);
+  if constexpr (BSPARSE) {
+    sk = block_row(a, hd, q0 / kBlockQ, C::BC);
+    tq.start(sk, tr.lo, tr.hi, lane);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) tq.t[t] = tr.lo + t;
+  }
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -790,11 +798,18 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   // Tiles [lo, ml) and [mu, hi) need masks in some row (the window's edges,
   // the causal diagonal, N); [ml, mu) none.  Separate loops, each with its own
   // register allocation.
-  // The queue skips the inactive tiles of a block mask; tnext is the tile copied
-  // during this one.
-  for (; tq.t[0] < tr.ml; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[C::NB - 1], std::true_type{});
-  for (; tq.t[0] < tr.mu; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[C::NB - 1], std::false_type{});
-  for (; tq.t[0] < tr.hi; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[C::NB - 1], std::true_type{});
+  if constexpr (BSPARSE) {
+    // The queue skips the inactive tiles of the block mask; tnext is the tile
+    // copied during this one.
+    for (; tq.t[0] < tr.ml; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[C::NB - 1], std::true_type{});
+    for (; tq.t[0] < tr.mu; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[C::NB - 1], std::false_type{});
+    for (; tq.t[0] < tr.hi; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[C::NB - 1], std::true_type{});
+  } else {
+    int kt = tr.lo;
+    for (; kt < tr.ml; ++kt) tile(kt, kt + C::NB - 1, std::true_type{});
+    for (; kt < tr.mu; ++kt) tile(kt, kt + C::NB - 1, std::false_type{});
+    for (; kt < tr.hi; ++kt) tile(kt, kt + C::NB - 1, std::true_type{});
+  }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   if (myq < N) {
@@ -1219,7 +1234,10 @@ static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
     constexpr int NW = CAUSAL && D == 128 ? 4 : 8;
     using C = Dq16<D, NW>;
     dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
-    hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL, NW, DROP>), grid, dim3(C::NT), 0, s, a);
+    if (!DROP && a.bm.mask)
+      hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL, NW, false, true>), grid, dim3(C::NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL, NW, DROP, false>), grid, dim3(C::NT), 0, s, a);
   } else {
     dim3 grid((a.N + DqTile<T, D>::BR - 1) / DqTile<T, D>::BR, a.H, a.B);
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, DROP>), grid, dim3(DqTile<T, D>::NT), 0, s, a);

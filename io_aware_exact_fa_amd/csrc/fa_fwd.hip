@@ -77,7 +77,9 @@ __device__ inline int vt_index(int d, int key) {
   return ((key / KPC) ^ swz) * KPC + (key % KPC);
 }
 
-template <typename T, int D, bool CAUSAL, bool DROP>
+// BSPARSE: a block mask is given and tiles of dropped blocks are skipped one by
+// one; without it the per-tile test is compiled out (it costs this kernel 8-12 %).
+template <typename T, int D, bool CAUSAL, bool DROP, bool BSPARSE>
 __global__ __launch_bounds__((FwdTile<T, D>::NT), (FwdTile<T, D>::WAVES_PER_SIMD))
 void fwd_kernel(FwdArgs a) {
   using C = FwdTile<T, D>;
@@ -262,7 +264,10 @@ void fwd_kernel(FwdArgs a) {
   // Tiles this wave computes: inside its range and in an active block of a block
   // mask (the whole workgroup lies in one block row).
   auto proc = [&](int j) {
-    return j < ntiles && j >= wfirst && j <= wlast && block_on(a, (int)head, q0, j * C::BC);
+    if constexpr (BSPARSE)
+      return j < ntiles && j >= wfirst && j <= wlast && block_on(a, (int)head, q0, j * C::BC);
+    else
+      return j >= wfirst && j <= wlast;
   };
   f32x16 sc[2];
   if (proc(j0)) s_tile(j0 & 1, sc);
@@ -271,9 +276,11 @@ void fwd_kernel(FwdArgs a) {
   for (int j = j0; j < ntiles; ++j) {
     if (j + 2 < ntiles) gload_k(j + 2);
     if (j + 1 < ntiles) gload_v(j + 1);
-    // A wave that skips this tile but computes the next one takes its S now.
+    // A wave that skips this tile but computes the next one takes its S now
+    // (without a block mask: the wave's first tile is the next one).
     const bool pj = proc(j);
-    if (!pj && proc(j + 1)) s_tile((j + 1) & 1, sc);
+    if (BSPARSE ? (!pj && proc(j + 1)) : (j + 1 == wfirst && wfirst <= wlast))
+      s_tile((j + 1) & 1, sc);
     if (pj) {
       const int key0 = j * C::BC;
       const bool masked = (key0 + C::BC - 1 > qw + wr) || (key0 < qw + 31 - wl) || (key0 + C::BC > N);
@@ -729,10 +736,12 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   } else {
     using C = FwdTile<T, D>;
     dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
-    if (drop)
-      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, true>), grid, dim3(C::NT), 0, s, a);
+    if (drop)   // dropout with a block mask is refused before any launch
+      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, true, false>), grid, dim3(C::NT), 0, s, a);
+    else if (a.bm.mask)
+      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, false, true>), grid, dim3(C::NT), 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, false>), grid, dim3(C::NT), 0, s, a);
+      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, false, false>), grid, dim3(C::NT), 0, s, a);
   }
   return hipGetLastError();
 }
