@@ -194,11 +194,7 @@ def main():
         if st != fa.FA_OK:
             raise fa.FaError(st, where)
 
-    if w.dropout:
-        print(f"{w.name}: dropout is switched off in this build of the library "
-              "(fa_fwd_ex returns FA_ERR_UNSUPPORTED for dropout_p > 0)", file=sys.stderr)
-        sys.exit(2)
-    if w.windowed or w.sparse:
+    if w.windowed or w.sparse or w.dropout:
         bench_windowed(args, w, fa, inp, q, k, v, do, o, lse, dq, dk, dv, ws, code, stream)
         return
 

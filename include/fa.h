@@ -298,8 +298,6 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  * numbers: as easy as 1, 2, 3", SC 2011) with counter (i, 2 floor(j / 16) +
  * (j mod 2), b H + h, rng_offset) and key (seed mod 2^32, seed / 2^32).  A
  * caller advances rng_offset (or the seed) between steps.
- * Currently switched off: dropout_p > 0 returns FA_ERR_UNSUPPORTED while a
- * memory fault seen in a run of the dropout kernel instances is investigated.
  * Tensors, workspace (fa_bwd_workspace_size(B, H, N, d)), ownership and errors
  * as for the entry points above (dense or packed); in addition p == NULL, a
  * window value below -1, dropout_p outside [0, 1] or block_mask_heads other

@@ -55,6 +55,12 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     sources = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    # Objects of sources that no longer exist would define the same template
+    # kernels (against older argument layouts) if anything linked them.
+    names = {os.path.basename(s) + ".o" for s in sources}
+    for f in os.listdir(BUILD):
+        if f.endswith(".o") and f not in names:
+            os.remove(os.path.join(BUILD, f))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         objs = list(ex.map(_compile, sources))
     tmp = LIB + ".tmp"

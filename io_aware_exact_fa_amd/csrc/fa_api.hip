@@ -62,9 +62,6 @@ fa_status check_attn(const fa_attn* p) {
   if (!p) return FA_ERR_INVALID_ARGUMENT;
   if (p->window_left < -1 || p->window_right < -1) return FA_ERR_INVALID_ARGUMENT;
   if (!(p->dropout_p >= 0.f && p->dropout_p <= 1.f)) return FA_ERR_INVALID_ARGUMENT;   // NaN too
-  // The dropout instances are switched off: a run of them faulted after the
-  // tile-queue change and the cause is not yet found.
-  if (p->dropout_p > 0.f) return FA_ERR_UNSUPPORTED;
   if (p->block_mask && p->block_mask_heads != 1 && p->block_mask_heads != p->H)
     return FA_ERR_INVALID_ARGUMENT;
   if (p->block_mask && p->dropout_p > 0.f) return FA_ERR_UNSUPPORTED;   // no such instance

@@ -437,11 +437,21 @@ __device__ inline i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // and before the barrier that hands it to the other waves.  The instruction
 // offset is left at zero: it would move the LDS address as well.  Expects every
 // lane of the wave active.
+//
+// The compiler does not look inside inline assembly for hazards, so the wait
+// states before each copy are this code's business: one (s_nop 0) after the
+// SALU write of M0 that the compiler places just before the copy, and five
+// after any VALU write of an SGPR the copy reads (v_readlane of a spilled
+// descriptor, v_readfirstlane).  The second is not paid on every copy: the
+// compiler rarely puts such a write there, and a test of the built library
+// checks every copy for it (a descriptor reloaded right before a copy gave a
+// garbage base address and a memory fault).
 template <bool HALF>
 __device__ inline void copy_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   if constexpr (HALF) {
     uint64_t saved;
     asm volatile(
+        "s_nop 0\n\t"
         "s_mov_b64 %0, exec\n\t"
         "s_mov_b32 exec_hi, 0\n\t"
         "buffer_load_dword %1, %2, %3 offen lds\n\t"
@@ -450,7 +460,7 @@ __device__ inline void copy_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t so
         : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
         : "memory");
   } else {
-    asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
                  "{m0}"(lds)
                  : "memory");
   }
@@ -458,10 +468,11 @@ __device__ inline void copy_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t so
 
 // Copy 16 bytes per lane from a buffer straight into LDS: lane i reads bytes
 // soff + voff_i .. + 15 of the range of rsrc and they land at LDS byte address
-// lds + 16 i, so one copy fills 1 KB of LDS.  Range checking, waits and the
-// instruction offset as for copy_to_lds.  Expects every lane active.
+// lds + 16 i, so one copy fills 1 KB of LDS.  Range checking, waits, the
+// instruction offset and the leading wait state as for copy_to_lds.  Expects
+// every lane active.
 __device__ inline void copy16_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
                "{m0}"(lds)
                : "memory");
 }

@@ -193,9 +193,9 @@ def test_ex_rejects():
         assert fwd(fa.attn(**good, window=window)) == E
         assert bwd(fa.attn(**good, window=window)) == E
     assert fwd(fa.attn(**{**good, "H_kv": 3})) == E
-    # Dropout instances are switched off for now.
-    assert fwd(fa.attn(**good, dropout=(0.25, 1, 0))) == fa.FA_ERR_UNSUPPORTED
-    assert bwd(fa.attn(**good, dropout=(0.25, 1, 0))) == fa.FA_ERR_UNSUPPORTED
+    # Dropout with a block mask has no kernel instance.
+    assert fwd(fa.attn(**good, dropout=(0.25, 1, 0), block_mask=P)) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(fa.attn(**good, dropout=(0.25, 1, 0), block_mask=P)) == fa.FA_ERR_UNSUPPORTED
     for heads in (0, 3, 9):   # a mask needs 1 or H (= 8) heads
         assert fwd(fa.attn(**good, block_mask=P, block_mask_heads=heads)) == E
     for pd in (-0.1, 1.5, float("nan")):

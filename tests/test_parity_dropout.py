@@ -14,12 +14,7 @@ import workloads
 from oracle import philox
 from tests.test_parity import TOL, f64, rel_err, say
 
-pytestmark = [
-    pytest.mark.gpu,
-    pytest.mark.skip(reason="dropout is switched off in the library: a run of the dropout kernel "
-                            "instances (keep-bit test, d = 64, bf16) faulted the GPU after the "
-                            "tile-queue change, and the cause is not found yet"),
-]
+pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
