@@ -259,7 +259,7 @@ def main():
         "data": "synthetic (seeded normal Q/K/V/dO of the workload's shape and distribution)",
         "config": {
             "workload": w.name, "B": B, "H": H, "H_kv": Hkv, "N": N, "d": d, "causal": w.causal,
-            "step": "fa_fwd + fa_bwd (preprocess, dkdv, dq)",
+            "step": "fa_fwd + fa_bwd (preprocess, dkdv, dq)", "step_gpu_ms": step_spread(events),
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "bwd_pre_ms": round(pre_ms, 4), "bwd_dkdv_ms": round(dkdv_ms, 4),
             "bwd_dq_ms": round(dq_ms, 4),
@@ -298,6 +298,7 @@ def two_call_result(args, w, events, wall, peak_dtype, config, data, kernel_name
     bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
     config = dict(config)
     config.update({
+        "step_gpu_ms": step_spread(events),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
         "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
         "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),
@@ -330,6 +331,14 @@ def two_call_result(args, w, events, wall, peak_dtype, config, data, kernel_name
             "traffic": None,
         },
     }
+
+
+def step_spread(events):
+    """Median and 10th / 90th percentiles (ms) of the per-step GPU time, first to
+    last event of each timed step."""
+    t = sorted(e[0].elapsed_time(e[-1]) for e in events)
+    q = lambda f: t[min(len(t) - 1, max(0, round(f * (len(t) - 1))))]
+    return {"median": round(q(0.5), 4), "p10": round(q(0.1), 4), "p90": round(q(0.9), 4)}
 
 
 def time_two_calls(args, step):
@@ -510,7 +519,7 @@ def bench_varlen(args, w):
         "config": {
             "workload": w.name, "B": w.B, "H": H, "H_kv": Hkv, "total": total, "max_s": w.max_s,
             "d": d, "causal": w.causal, "lens": list(w.lens),
-            "step": "fa_fwd_varlen + fa_bwd_varlen",
+            "step": "fa_fwd_varlen + fa_bwd_varlen", "step_gpu_ms": step_spread(events),
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
             "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),
