@@ -47,8 +47,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=sorted(workloads.BY_NAME) + sorted(workloads.VARLEN_BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
