@@ -149,6 +149,8 @@ def code_objects(tmp_path, lib_path=LIB):
                 if ins.startswith(("s_branch", "s_cbranch")) and t:
                     branch.append((t[1], int(t[2], 16)))
                 lines.append(ins)
+        missing = [(f, off) for f, off in branch if f in start and start[f] + off not in addr]
+        assert not missing, f"branch targets that start no parsed instruction: {missing[:3]}"
         targets = frozenset(addr[start[f] + off] for f, off in branch if f in start)
         out.append((names, lines, targets))
     return out
