@@ -52,15 +52,21 @@ def _compile(src: str) -> str:
     return obj
 
 
+def remove_stale_objects(build_dir: str, sources) -> list:
+    """Delete the objects in build_dir whose source is not among `sources`; they
+    would define the same template kernels (against older argument layouts) if
+    anything linked them.  Returns the names removed."""
+    names = {os.path.basename(s) + ".o" for s in sources}
+    stale = sorted(f for f in os.listdir(build_dir) if f.endswith(".o") and f not in names)
+    for f in stale:
+        os.remove(os.path.join(build_dir, f))
+    return stale
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     sources = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
-    # Objects of sources that no longer exist would define the same template
-    # kernels (against older argument layouts) if anything linked them.
-    names = {os.path.basename(s) + ".o" for s in sources}
-    for f in os.listdir(BUILD):
-        if f.endswith(".o") and f not in names:
-            os.remove(os.path.join(BUILD, f))
+    remove_stale_objects(BUILD, sources)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         objs = list(ex.map(_compile, sources))
     tmp = LIB + ".tmp"

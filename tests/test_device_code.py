@@ -208,3 +208,14 @@ def test_each_kernel_in_one_code_object(tmp_path):
     assert n > 50, f"only {n} kernels found: the disassembly was not parsed"
     dup = kernels_in_several_objects(objs)
     assert not dup, f"{len(dup)} kernels defined in more than one code object, e.g. {dup[:3]}"
+
+
+def test_build_removes_objects_of_removed_sources(tmp_path):
+    """Objects whose source is gone are deleted before linking (a relink that
+    picked such objects up once ran an old preprocess kernel)."""
+    from io_aware_exact_fa_amd import _build
+    for f in ("fa_api.hip.o", "fa_bwd_bf16.hip.o", "fa_fwd.hip.o", "notes.txt"):
+        (tmp_path / f).write_text("x")
+    srcs = ["/x/csrc/fa_api.hip", "/x/csrc/fa_fwd.hip"]
+    assert _build.remove_stale_objects(str(tmp_path), srcs) == ["fa_bwd_bf16.hip.o"]
+    assert sorted(p.name for p in tmp_path.iterdir()) == ["fa_api.hip.o", "fa_fwd.hip.o", "notes.txt"]
