@@ -37,7 +37,8 @@
  *    not alias outputs.
  *  - Errors: a status code, never an exception.  Every argument check runs
  *    before any HIP call; on an argument error nothing is launched and no
- *    output is touched.  Checks: null pointers, B/H/N <= 0, element counts
+ *    output is touched.  Checks: null or misaligned pointers (tensors 16
+ *    bytes, lse and cu_seqlens 4 bytes), B/H/N <= 0, element counts
  *    that overflow 64 bits, non-finite scale (FA_ERR_INVALID_ARGUMENT);
  *    unknown dtype, d outside {64, 128}, B or H above 65535, B*H above 2^24,
  *    N above 2^23 or B*H*N above 2^34 (FA_ERR_UNSUPPORTED); workspace

@@ -237,6 +237,13 @@ def _check(name, t, shape, dtype):
         raise ValueError(f"{name}: expected contiguous {dtype} cuda tensor of shape {tuple(shape)}, "
                          f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} "
                          f"device={t.device}")
+    # fa.h: [.., d] tensors 16-byte aligned (16-byte loads and LDS-direct copies),
+    # float32 row statistics 4-byte aligned.
+    align = 4 if name == "lse" else 16
+    if t.data_ptr() % align != 0:
+        raise ValueError(f"{name}: data pointer {t.data_ptr():#x} is not {align}-byte aligned "
+                         "(a view at an offset into another tensor?)")
+
 
 
 def _stream(stream):

@@ -4,7 +4,12 @@ Usage: ``python io_aware_exact_fa_amd/_build.py`` (or ``__graft_entry__.build()`
 run it by path, not as ``-m io_aware_exact_fa_amd._build``, which would import
 the package and load the library that is about to be replaced.
 Every call compiles from scratch: each ``csrc/*.hip`` file to an object in
-``_build/`` (in parallel), then links ``libfa.so`` next to this file.
+``_build/`` (in parallel), then links ``libfa.so.tmp``, checks its device code
+(``_devcheck.check_library``: the wait states before every inline-asm
+LDS-direct copy, one definition per kernel) and only then installs it as
+``libfa.so`` next to this file.  A library that fails the check is deleted and
+the build raises, so a register allocation that puts a VALU write of a copy's
+SGPR operand too close to the copy never reaches a GPU.
 """
 from __future__ import annotations
 
@@ -63,6 +68,28 @@ def remove_stale_objects(build_dir: str, sources) -> list:
     return stale
 
 
+def _load_devcheck():
+    """_devcheck.py, loaded by path (importing the package would load the
+    library that is about to be replaced)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_fa_devcheck", os.path.join(PKG, "_devcheck.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def install_checked(tmp: str, lib: str, check) -> dict:
+    """Runs `check` on the linked library `tmp`; installs it as `lib` only if
+    the check passes, else deletes it and re-raises."""
+    try:
+        info = check(tmp)
+    except Exception:
+        os.remove(tmp)
+        raise
+    os.replace(tmp, lib)
+    return info
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     sources = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
@@ -74,9 +101,10 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    info = install_checked(tmp, LIB, _load_devcheck().check_library)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} (device code checked: {info['lds_dma_loads']} LDS-direct loads, "
+              f"{info['kernels']} kernels)")
     return LIB
 
 

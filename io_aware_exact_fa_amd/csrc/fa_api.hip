@@ -20,6 +20,15 @@ constexpr uint64_t kMaxRows = (uint64_t)1 << 34;  // keeps 1-D row grids below 2
 constexpr uint64_t kMaxHeads = (uint64_t)1 << 24;  // B*H: with kMaxRows keeps tile grids below 2^31
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Tensor pointers: non-null and 16-byte aligned (the kernels read and write
+// them in 16-byte pieces, and the LDS-direct copies move 16 bytes per lane).
+template <class... P>
+bool tensors_ok(P... p) {
+  return ((p != nullptr && ((uintptr_t)p & 15) == 0) && ...);
+}
+// Float32 row statistics (lse) and int32 offsets: non-null, 4-byte aligned.
+bool words_ok(const void* p) { return p != nullptr && ((uintptr_t)p & 3) == 0; }
 // Rows per head of the workspace arrays: N rounded up to whole 64-row tiles.
 int padded_rows(int N) { return (N + 63) / 64 * 64; }
 
@@ -62,6 +71,7 @@ fa_status check_attn(const fa_attn* p) {
   if (!p) return FA_ERR_INVALID_ARGUMENT;
   if (p->window_left < -1 || p->window_right < -1) return FA_ERR_INVALID_ARGUMENT;
   if (!(p->dropout_p >= 0.f && p->dropout_p <= 1.f)) return FA_ERR_INVALID_ARGUMENT;   // NaN too
+  if (p->cu_seqlens && !words_ok(p->cu_seqlens)) return FA_ERR_INVALID_ARGUMENT;
   if (p->block_mask && p->block_mask_heads != 1 && p->block_mask_heads != p->H)
     return FA_ERR_INVALID_ARGUMENT;
   if (p->block_mask && p->dropout_p > 0.f) return FA_ERR_UNSUPPORTED;   // no such instance
@@ -152,7 +162,7 @@ const char* fa_status_string(fa_status status) {
 fa_status fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int H, int H_kv, int N, int d, int causal, float scale, fa_dtype dtype,
                      void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
+  if (!tensors_ok(q, k, v, o) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
   fa_status st = check_shape(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
   if (H_kv <= 0 || H % H_kv != 0) return FA_ERR_INVALID_ARGUMENT;
@@ -171,7 +181,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens, int B, int max_s, int total, int H, int H_kv,
                         int d, int causal, float scale, fa_dtype dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
+  if (!tensors_ok(q, k, v, o) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens && !words_ok(cu_seqlens)) return FA_ERR_INVALID_ARGUMENT;
   fa_status st = check_varlen(cu_seqlens, B, max_s, total, H, H_kv, d, scale, dtype);
   if (st != FA_OK) return st;
   st = check_device();
@@ -193,7 +204,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
 fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H,
                             int N, int d, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  if (!o || !dout || !lse) return FA_ERR_INVALID_ARGUMENT;
+  if (!tensors_ok(o, dout) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
   fa::BwdArgs a{};
   fa_status st = bwd_setup(B, H, H, N, d, 1.0f, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
@@ -207,7 +218,7 @@ fa_status fa_bwd_dkdv_gqa(const void* q, const void* k, const void* v, const voi
                           const float* lse, void* dk, void* dv, int B, int H, int H_kv, int N,
                           int d, int causal, float scale, fa_dtype dtype, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !dout || !lse || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
+  if (!tensors_ok(q, k, v, dout, dk, dv) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
   fa::BwdArgs a{};
   fa_status st = bwd_setup(B, H, H_kv, N, d, scale, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
@@ -233,7 +244,7 @@ fa_status fa_bwd_dq_gqa(const void* q, const void* k, const void* v, const void*
                         const float* lse, void* dq, int B, int H, int H_kv, int N, int d,
                         int causal, float scale, fa_dtype dtype, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !dout || !lse || !dq) return FA_ERR_INVALID_ARGUMENT;
+  if (!tensors_ok(q, k, v, dout, dq) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
   fa::BwdArgs a{};
   fa_status st = bwd_setup(B, H, H_kv, N, d, scale, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
@@ -256,7 +267,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
 
 fa_status fa_fwd_ex(const fa_attn* p, const void* q, const void* k, const void* v, void* o,
                     float* lse, void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARGUMENT;
+  if (!tensors_ok(q, k, v, o) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
   fa_status st = check_attn(p);
   if (st != FA_OK) return st;
   st = check_device();
@@ -269,7 +280,7 @@ fa_status fa_fwd_ex(const fa_attn* p, const void* q, const void* k, const void* 
 fa_status fa_bwd_ex(const fa_attn* p, const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
+  if (!tensors_ok(q, k, v, o, dout, dq, dk, dv) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
   fa_status st = check_attn(p);
   if (st != FA_OK) return st;
   fa::BwdArgs a{};
@@ -284,7 +295,7 @@ fa_status fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv,
                      int N, int d, int causal, float scale, fa_dtype dtype, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
+  if (!tensors_ok(q, k, v, o, dout, dq, dk, dv) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
   fa::BwdArgs a{};
   fa_status st = bwd_setup(B, H, H_kv, N, d, scale, dtype, workspace, workspace_bytes, &a);
   if (st != FA_OK) return st;
@@ -296,7 +307,8 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         const int* cu_seqlens, int B, int max_s, int total, int H, int H_kv,
                         int d, int causal, float scale, fa_dtype dtype, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARGUMENT;
+  if (!tensors_ok(q, k, v, o, dout, dq, dk, dv) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens && !words_ok(cu_seqlens)) return FA_ERR_INVALID_ARGUMENT;
   fa_status st = check_varlen(cu_seqlens, B, max_s, total, H, H_kv, d, scale, dtype);
   if (st != FA_OK) return st;
   fa::BwdArgs a{};

@@ -260,3 +260,55 @@ def test_binding_refuses_missing_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError):
         spec.loader.exec_module(mod)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o"])
+def test_fwd_rejects_misaligned_tensor(name):
+    """fa.h: tensors are 16-byte aligned (16-byte loads, LDS-direct copies)."""
+    for off in (2, 8):
+        assert _fwd(**{name: P + off}) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_fwd_ex(fa.attn(1, 1, 1, 128, 64, 0, 0.125, fa.FA_BF16),
+                        *[P + 8 if n == name else P for n in ("q", "k", "v", "o", "lse")],
+                        None) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "dout", "dq", "dk", "dv"])
+def test_bwd_rejects_misaligned_tensor(name):
+    assert _bwd(**{name: P + 4}) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _bwd_varlen(**{name: P + 8}) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+def test_misaligned_statistics_and_offsets_rejected():
+    """lse (float32) and cu_seqlens (int32) need 4-byte alignment; the split
+    backward entry points check their tensors too."""
+    assert _fwd(lse=P + 2) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _bwd(lse=P + 1) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _fwd_varlen(cu_seqlens=P + 2) == fa.FA_ERR_INVALID_ARGUMENT
+    assert _bwd_varlen(cu_seqlens=P + 1) == fa.FA_ERR_INVALID_ARGUMENT
+    ws, nb = 0x10000, fa.fa_bwd_workspace_size(1, 1, 128, 64)
+    assert fa.fa_bwd_preprocess(P + 8, P, P, 1, 1, 128, 64, fa.FA_F16, ws, nb, None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_bwd_dkdv(P, P, P, P, P, P + 8, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws, nb,
+                          None) == fa.FA_ERR_INVALID_ARGUMENT
+    assert fa.fa_bwd_dq(P, P + 8, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, ws, nb,
+                        None) == fa.FA_ERR_INVALID_ARGUMENT
+    p = fa.attn(3, 8, 2, 128, 64, 0, 0.1, fa.FA_F16, cu_seqlens=P + 2, total=300)
+    assert fa.fa_fwd_ex(p, P, P, P, P, P, None) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+def test_binding_rejects_misaligned_view():
+    """A contiguous view at an odd element offset passes the shape checks but not
+    the alignment check, before any launch (CPU tensors are refused earlier)."""
+    import torch
+
+    class FakeCuda:
+        shape, dtype, is_cuda = (1, 1, 8, 64), torch.bfloat16, True
+
+        def is_contiguous(self):
+            return True
+
+        def data_ptr(self):
+            return 0x10002
+
+    with pytest.raises(ValueError, match="not 16-byte aligned"):
+        fa._check("q", FakeCuda(), (1, 1, 8, 64), torch.bfloat16)
+

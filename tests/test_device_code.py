@@ -1,168 +1,35 @@
 """Checks of the device code in the built library (no GPU).
 
-1. Wait states before the LDS-direct buffer loads.  The 16-bit kernels copy
-   tiles with `buffer_load_dword{,x4} ... offen lds`, issued as inline assembly.
-   The compiler's hazard recognizer does not look inside inline assembly, so
-   the wait states the hardware needs before such a load are the copy helper's
-   own business:
-
-     * a VALU write of an SGPR (v_readlane of a spilled descriptor,
-       v_readfirstlane, the SGPR result of a compare or carry) needs 5 wait
-       states before a VMEM instruction reads that SGPR (the descriptor, the
-       soffset, M0);
-     * a SALU write of M0 needs 1 wait state before a load that writes LDS.
-
-   A load that reads its descriptor too early takes stale SGPRs as the base
-   address: a build whose dK/dV dropout instance reloaded the descriptor with
-   v_readlane right before the copy faulted with an illegal address.  Every
-   gfx950 code object of libfa.so is disassembled and the instructions before
-   each such load are checked (a straight-line scan back from the load).
-
-2. One definition per kernel.  Kernels are templates, so their host-side
-   handles are weak symbols: an object file of an older source linked into
-   the library would silently supply some of them, compiled against an older
-   argument layout.  No kernel may appear in two code objects."""
-import glob
+The checks themselves live in ``io_aware_exact_fa_amd/_devcheck.py``, which
+``build()`` runs on every freshly linked library before installing it (see
+that module for the two rules: wait states before the inline-asm LDS-direct
+copies, one definition per kernel).  Here: the scanner flags the hazards it
+is meant to flag, the installed library passes both checks, and ``build()``
+refuses a library that fails them."""
+import importlib.util
 import os
-import re
-import shutil
-import subprocess
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LIB = os.path.join(ROOT, "io_aware_exact_fa_amd", "libfa.so")
-OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
-
-VALU_SGPR_TO_VMEM = 5
-SALU_M0_TO_LDS_DMA = 1
-
-_NAMED = {"vcc": {106, 107}, "vcc_lo": {106}, "vcc_hi": {107}, "m0": {"m0"}}
+PKG = os.path.join(ROOT, "io_aware_exact_fa_amd")
+LIB = os.path.join(PKG, "libfa.so")
 
 
-def sgprs(tok: str) -> set:
-    tok = tok.strip()
-    if tok in _NAMED:
-        return set(_NAMED[tok])
-    m = re.fullmatch(r"s\[(\d+):(\d+)\]", tok)
-    if m:
-        return set(range(int(m[1]), int(m[2]) + 1))
-    m = re.fullmatch(r"s(\d+)", tok)
-    return {int(m[1])} if m else set()
+def _by_path(name):
+    """A module of the package loaded by path: importing the package would load
+    libfa.so, which these CPU checks do not need."""
+    spec = importlib.util.spec_from_file_location(f"_fa_{name}", os.path.join(PKG, f"{name}.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
 
 
-# VALU opcodes whose e64 form has an SGPR destination after the VGPR one (carry
-# or flags), and whose e32 form writes VCC.
-_CARRY = ("v_add_co_", "v_sub_co_", "v_subrev_co_", "v_addc_co_", "v_subb_co_", "v_subbrev_co_",
-          "v_mad_u64_u32", "v_mad_i64_i32", "v_div_scale_")
-
-
-def writes(ins: str):
-    """('valu' | 'salu' | 'other', set of SGPRs (and 'm0') the instruction writes)."""
-    op, _, rest = ins.partition(" ")
-    ops = [o.strip() for o in rest.split(",")] if rest else []
-    if op.startswith("v_"):
-        # A VALU destination that is an SGPR comes first (v_readlane,
-        # v_readfirstlane, compares in VOP3 or SDWA form); compares in VOPC form
-        # write VCC; carry-outs come second.
-        out = sgprs(ops[0]) if ops else set()
-        if op.startswith("v_cmp") and not out:
-            out = set(_NAMED["vcc"])
-        elif op.startswith(_CARRY):
-            out |= sgprs(ops[1]) if op.endswith("_e64") or "_e" not in op[-4:] else _NAMED["vcc"]
-        return "valu", out
-    if op.startswith("s_") and ops and not op.startswith(("s_cmp", "s_bitcmp", "s_waitcnt", "s_nop",
-                                                         "s_barrier", "s_branch", "s_cbranch")):
-        return "salu", sgprs(ops[0])
-    return "other", set()
-
-
-def wait_states(ins: str) -> int:
-    m = re.match(r"s_nop\s+(0x[0-9a-fA-F]+|\d+)", ins)
-    return int(m[1], 0) + 1 if m else 1
-
-
-_DMA = re.compile(r"buffer_load_\w+\s+v\d+,\s*(s\[\d+:\d+\]),\s*(\w+)\s.*\blds\b")
-
-
-def violations(lines, targets=frozenset()):
-    """(line index, load, offending instruction, wait states between) for every
-    LDS-direct buffer load with too few wait states after a write of one of its
-    SGPR operands or of M0.  `lines` are bare instructions, None at a function
-    start; `targets` the indices of branch targets: control may reach them from
-    elsewhere, so a window that reaches back past one is a violation unless the
-    wait states counted up to it suffice."""
-    out = []
-    for i, ins in enumerate(lines):
-        m = _DMA.match(ins) if ins else None
-        if not m:
-            continue
-        reads = sgprs(m[1]) | sgprs(m[2]) | {"m0"}
-        ws = 0
-        for j in range(i - 1, -1, -1):
-            prev = lines[j]
-            if prev is None:       # start of a function
-                break
-            if j + 1 in targets:
-                out.append((i, ins, "a branch target", ws))
-                break
-            kind, w = writes(prev)
-            if kind == "valu" and w & reads and ws < VALU_SGPR_TO_VMEM:
-                out.append((i, ins, prev, ws))
-                break
-            if kind == "salu" and "m0" in w and ws < SALU_M0_TO_LDS_DMA:
-                out.append((i, ins, prev, ws))
-                break
-            ws += wait_states(prev)
-            if ws >= VALU_SGPR_TO_VMEM:
-                break
-    return out
-
-
-def code_objects(tmp_path, lib_path=LIB):
-    """Disassembly of every gfx950 code object in the library: a list of
-    (function names, bare instructions with None at each function start)."""
-    lib = tmp_path / "libfa.so"
-    shutil.copy(lib_path, lib)
-    subprocess.run([OBJDUMP, "--offloading", str(lib)], cwd=tmp_path, check=True,
-                   capture_output=True)
-    objs = sorted(glob.glob(str(tmp_path / "libfa.so.*gfx950")))
-    assert objs, "no gfx950 code object in libfa.so"
-    out = []
-    for obj in objs:
-        dis = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", obj], check=True,
-                             capture_output=True, text=True).stdout
-        names, lines, start, addr, branch = [], [], {}, {}, []
-        for raw in dis.splitlines():
-            m = re.match(r"^([0-9a-fA-F]+) <(.*)>:$", raw)
-            if m:
-                names.append(m[2])
-                start[m[2]] = int(m[1], 16)
-                lines.append(None)
-                continue
-            ins = raw.split("//")[0].strip()
-            if ins and not ins.endswith(":") and raw[:1] in ("\t", " "):
-                a = re.search(r"//\s*([0-9a-fA-F]+):", raw)
-                if a:
-                    addr[int(a[1], 16)] = len(lines)
-                t = re.search(r"<(\S+)\+0x([0-9a-fA-F]+)>\s*$", raw)
-                if ins.startswith(("s_branch", "s_cbranch")) and t:
-                    branch.append((t[1], int(t[2], 16)))
-                lines.append(ins)
-        missing = [(f, off) for f, off in branch if f in start and start[f] + off not in addr]
-        assert not missing, f"branch targets that start no parsed instruction: {missing[:3]}"
-        targets = frozenset(addr[start[f] + off] for f, off in branch if f in start)
-        out.append((names, lines, targets))
-    return out
-
-
-def kernels_in_several_objects(objs):
-    seen = {}
-    for i, (names, _, _) in enumerate(objs):
-        for n in names:
-            if n.startswith("_ZN2fa"):
-                seen.setdefault(n, set()).add(i)
-    return sorted(n for n, s in seen.items() if len(s) > 1)
+_build = _by_path("_build")
+_devcheck = _by_path("_devcheck")
+_DMA, OBJDUMP = _devcheck.DMA, _devcheck.OBJDUMP
+code_objects, kernels_in_several_objects = _devcheck.code_objects, _devcheck.kernels_in_several_objects
+violations = _devcheck.violations
 
 
 def test_scanner_flags_the_hazards():
@@ -191,7 +58,7 @@ def test_scanner_flags_the_hazards():
 @pytest.mark.skipif(not os.path.exists(LIB), reason="libfa.so not built")
 @pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="llvm-objdump not installed")
 def test_every_lds_dma_load_has_its_wait_states(tmp_path):
-    objs = code_objects(tmp_path)
+    objs = code_objects(LIB, str(tmp_path))
     n = sum(1 for _, lines, _ in objs for ins in lines if ins and _DMA.match(ins))
     assert n > 1000, f"only {n} LDS-direct loads found: the disassembly was not parsed"
     assert sum(len(t) for _, _, t in objs) > 100, "no branch targets found"
@@ -203,7 +70,7 @@ def test_every_lds_dma_load_has_its_wait_states(tmp_path):
 @pytest.mark.skipif(not os.path.exists(LIB), reason="libfa.so not built")
 @pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="llvm-objdump not installed")
 def test_each_kernel_in_one_code_object(tmp_path):
-    objs = code_objects(tmp_path)
+    objs = code_objects(LIB, str(tmp_path))
     n = sum(1 for names, _, _ in objs for x in names if x.startswith("_ZN2fa"))
     assert n > 50, f"only {n} kernels found: the disassembly was not parsed"
     dup = kernels_in_several_objects(objs)
@@ -213,9 +80,36 @@ def test_each_kernel_in_one_code_object(tmp_path):
 def test_build_removes_objects_of_removed_sources(tmp_path):
     """Objects whose source is gone are deleted before linking (a relink that
     picked such objects up once ran an old preprocess kernel)."""
-    from io_aware_exact_fa_amd import _build
     for f in ("fa_api.hip.o", "fa_bwd_bf16.hip.o", "fa_fwd.hip.o", "notes.txt"):
         (tmp_path / f).write_text("x")
     srcs = ["/x/csrc/fa_api.hip", "/x/csrc/fa_fwd.hip"]
     assert _build.remove_stale_objects(str(tmp_path), srcs) == ["fa_bwd_bf16.hip.o"]
     assert sorted(p.name for p in tmp_path.iterdir()) == ["fa_api.hip.o", "fa_fwd.hip.o", "notes.txt"]
+
+
+def test_build_installs_only_a_checked_library(tmp_path):
+    """build() links to a temporary file and installs it only after the device
+    code check passed; a failing check deletes it and leaves the installed
+    library alone."""
+    lib, tmp = tmp_path / "libfa.so", tmp_path / "libfa.so.tmp"
+    lib.write_text("old")
+    tmp.write_text("new")
+
+    def bad(path):
+        raise RuntimeError("device-code check: 1 of 4440 LDS-direct loads too soon")
+
+    with pytest.raises(RuntimeError, match="too soon"):
+        _build.install_checked(str(tmp), str(lib), bad)
+    assert not tmp.exists() and lib.read_text() == "old"
+    tmp.write_text("new")
+    assert _build.install_checked(str(tmp), str(lib), lambda p: {"ok": p}) == {"ok": str(tmp)}
+    assert not tmp.exists() and lib.read_text() == "new"
+
+
+def test_build_runs_the_device_code_check():
+    """build() passes the linked library through _devcheck.check_library (the
+    guard against the copy hazard that once faulted), not only the tests."""
+    import inspect
+    src = inspect.getsource(_build.build)
+    assert "install_checked(" in src and "check_library" in src
+    assert "os.replace" not in src   # the only install path is install_checked

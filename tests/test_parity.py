@@ -1,9 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
 
-Tolerances: O max-abs 2e-3 (fp16) / 1e-2 (bf16); dQ, dK, dV max-abs error
-relative to the reference's max-abs 5e-3 (fp16) / 2e-2 (bf16).  fp32 has no
-stated tolerance; 1e-5 on O and 1e-4 on gradients is derived from fp32
-accumulation over at most a few thousand terms.  LSE: 1e-3 (16-bit), 1e-4 (fp32).
+Tolerances (tests/tolerances.py): O max-abs 2e-3 (fp16) / 1e-2 (bf16); dQ,
+dK, dV max-abs error relative to the reference's max-abs 5e-3 (fp16) / 2e-2
+(bf16).  LSE max-abs 1e-3 (fp16) / 4e-3 (bf16): the forward's row sum adds P~
+as rounded to the input type, so ln l carries up to that type's unit roundoff.
+fp32 has no stated tolerance; 1e-5 on O and 1e-4 on LSE and gradients is
+derived from fp32 accumulation over at most a few thousand terms.
 """
 import math
 import sys
@@ -15,18 +17,10 @@ import torch
 import oracle
 import workloads
 from tests import pins
+from tests.tolerances import TOL
 
 pytestmark = pytest.mark.gpu
 
-# O and gradient bounds for fp16 / bf16 are the plan's.  LSE: the 16-bit
-# forward sums P~ as rounded to the input type (the values the P~V product
-# uses), so ln l carries up to that type's unit roundoff u: 2^-11 (fp16),
-# 2^-8 (bf16).  fp32: MFMA accumulation over a few thousand terms.
-TOL = {
-    "f32": dict(o=1e-5, lse=1e-4, grad=1e-4),
-    "f16": dict(o=2e-3, lse=1e-3, grad=5e-3),
-    "bf16": dict(o=1e-2, lse=4e-3, grad=2e-2),
-}
 TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
@@ -249,14 +243,37 @@ def test_small_workloads_full(fa, w):
 LARGE = [workloads.CAUSAL_BF16, workloads.LONG_CAUSAL_F16, workloads.PEAKED_BF16]
 
 
+def xcd_sample_heads(B, H, limit=9):
+    """(b, h) pairs of the flat heads 0, n/8, 2n/8, ..., 7n/8 and n - 1 (n = B H):
+    the first head of each of the 8 contiguous head ranges that the kernels hand
+    to the 8 XCDs, and the last head.  With more than ``limit`` of them (oracle
+    memory at long N), the first and the last only."""
+    n = B * H
+    flat = sorted({(x * n) // 8 for x in range(8)} | {n - 1})
+    if len(flat) > limit:
+        flat = [0, n - 1]
+    return [(f // H, f % H) for f in flat]
+
+
+def test_xcd_sample_heads():
+    assert xcd_sample_heads(2, 32) == [(0, 0), (0, 8), (0, 16), (0, 24), (1, 0), (1, 8), (1, 16),
+                                       (1, 24), (1, 31)]
+    assert xcd_sample_heads(1, 16, limit=2) == [(0, 0), (0, 15)]
+    assert len(xcd_sample_heads(4, 32)) == 9 and xcd_sample_heads(4, 32)[-1] == (3, 31)
+
+
 @pytest.mark.parametrize("w", LARGE, ids=lambda w: w.name)
 def test_large_workloads_sampled_heads(fa, w):
-    """Full-size launch (the configuration the benchmark times); the oracle checks the
-    last head exactly, and properties that hold for every head are checked on all."""
+    """Full-size launch (the configuration the benchmark times).  The oracle checks
+    every element of one head in each XCD's range of heads and of the last head
+    (the XCD-aware and heavy-first work orders decide which workgroup gets which
+    head; the N = 16384 workload: the first and the last head, for oracle
+    memory), and properties that hold for every head are checked on all."""
     inp = workloads.make_inputs(w)
     say(f"case {w.name} full size")
     out = gpu_run(fa, inp, w.causal, w.scale)
-    heads = [(w.B - 1, w.H - 1)]
+    heads = xcd_sample_heads(w.B, w.H, limit=9 if w.N <= 8192 else 2)
+    say(f"  oracle heads {heads}")
     compare(out, inp, w.causal, w.scale, w.dtype, heads=heads, tag=w.name)
     # Every head: sum_j dV_j = sum_i dO_i (rows of P sum to 1) and sum_j dK_j = 0
     # (rows of dS sum to 0), both in fp64 over the GPU's outputs.
@@ -345,3 +362,45 @@ def test_large_gqa_sampled_groups(fa, w):
     out = gpu_run(fa, inp, w.causal, w.scale)
     groups = [(0, 0), (w.B - 1, w.kv_heads - 1)]
     compare_gqa(out, inp, w.causal, w.scale, w.dtype, tag=w.name, groups=groups)
+
+
+# ------------------------------------------------------------------ the plain entry points
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_plain_entry_points_by_name(fa, dtype):
+    """fa_fwd, fa_bwd, and fa_bwd_preprocess + fa_bwd_dkdv + fa_bwd_dq called by
+    those names through ctypes (not through their grouped forms), causal, ragged
+    N = 333 over 3 heads of 2 batch entries: every element against the oracle, and
+    the split backward bit for bit equal to fa_bwd."""
+    w = workloads.Workload(f"plain-{dtype}", 2, 3, 333, 128, dtype, True, seed=83)
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    code = fa.dtype_code(q.dtype)
+    sh = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=dev)
+    say(f"case {w.name}: fa_fwd")
+    assert fa.fa_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, N, d, 1, w.scale, code, sh) == fa.FA_OK
+    ws = fa.workspace(B, H, N, d, dev)
+    g1 = [torch.full_like(q, float("nan")) for _ in range(3)]
+    say(f"case {w.name}: fa_bwd")
+    assert fa.fa_bwd(P(q), P(k), P(v), P(o), P(do), P(lse), *(P(t) for t in g1), B, H, N, d, 1,
+                     w.scale, code, P(ws), ws.numel(), sh) == fa.FA_OK
+    g2 = [torch.full_like(q, float("nan")) for _ in range(3)]
+    ws2 = fa.workspace(B, H, N, d, dev)
+    say(f"case {w.name}: fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq")
+    assert fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, code, P(ws2), ws2.numel(),
+                                sh) == fa.FA_OK
+    assert fa.fa_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(g2[1]), P(g2[2]), B, H, N, d, 1,
+                          w.scale, code, P(ws2), ws2.numel(), sh) == fa.FA_OK
+    assert fa.fa_bwd_dq(P(q), P(k), P(v), P(do), P(lse), P(g2[0]), B, H, N, d, 1, w.scale, code,
+                        P(ws2), ws2.numel(), sh) == fa.FA_OK
+    torch.cuda.synchronize()
+    out = dict(o=o, lse=lse, dq=g1[0], dk=g1[1], dv=g1[2])
+    compare(out, inp, True, w.scale, dtype, tag=w.name)
+    for name, a, b in zip(("dq", "dk", "dv"), g1, g2):
+        assert torch.equal(a, b), f"split backward {name} differs from fa_bwd"
