@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 /* Block sizes (queries x keys) of the block-sparse mask of fa_attn. */
 #define FA_BLOCK_Q 256
@@ -121,6 +121,33 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  int B, int H, int N, int d, int causal, float scale,
                  fa_dtype dtype, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/*
+ * Backward pass for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fa_bwd without the workspace arguments.  D and L2 (the layout at
+ * fa_bwd_workspace_size) go to one static device array of
+ * FA_NOALLOC_SCRATCH_BYTES per GPU, part of the library's code object; each
+ * GPU the library runs on holds its array until the process ends.  The entry
+ * point allocates nothing and calls no allocating routine; on its first call
+ * on a device it looks up that device's array address once (the current HIP
+ * device must be the one `stream` belongs to).
+ *
+ * Arguments, results and errors as for fa_bwd, plus: a shape whose
+ * fa_bwd_workspace_size exceeds FA_NOALLOC_SCRATCH_BYTES (B * H * Np above
+ * 4 Mi rows, Np = N rounded up to 64) is FA_ERR_WORKSPACE, before any launch.
+ * Every call on one GPU uses the same array: calls that overlap in time on
+ * one GPU (on different streams, or from several threads without ordering)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * Each call rewrites the array completely, so nothing needs clearing.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv,
+                         int B, int H, int N, int d, int causal, float scale,
+                         fa_dtype dtype, void* stream);
 
 /*
  * Backward step 1: D_i = rowsum(dout_i * o_i) and L2_i = LSE_i * log2(e) in

@@ -37,7 +37,9 @@ FA_BF16 = 2
 EXPORTED = ("fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
             "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
             "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_ex",
-            "fa_bwd_ex")
+            "fa_bwd_ex", "fa_bwd_noalloc")
+
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class FaAttn(ctypes.Structure):
@@ -83,6 +85,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_dkdv.restype = i
@@ -147,6 +151,12 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype,
            workspace, workspace_bytes, stream) -> int:
     return _lib.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
                        int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype,
+                   stream) -> int:
+    return _lib.fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal),
+                               float(scale), int(dtype), stream)
 
 
 def fa_bwd_preprocess(o, dout, lse, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:

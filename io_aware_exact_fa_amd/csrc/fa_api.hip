@@ -125,6 +125,28 @@ fa_status check_device() {
   return ok ? FA_OK : FA_ERR_DEVICE;
 }
 
+// Backward workspace of fa_bwd_noalloc: one array per GPU, part of the
+// library's code object, so that calls made where nothing may be allocated
+// (graph capture, serving loops) still have D and L2.  The name is the host
+// stand-in only; kernels get the device address that hipGetSymbolAddress
+// returns for the current device, cached per device on the first call.
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of this device's `scratch`, or null if it cannot be had.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  if (dev < kMaxDevices) {
+    void* known = g_scratch[dev].load(std::memory_order_acquire);
+    if (known) return known;
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  if (dev < kMaxDevices) g_scratch[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
 fa::Dt to_dt(fa_dtype d) {
   return d == FA_F32 ? fa::Dt::f32 : (d == FA_F16 ? fa::Dt::f16 : fa::Dt::bf16);
 }
@@ -326,6 +348,25 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* stream) {
   return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, causal, scale, dtype,
                     workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int H, int N, int d, int causal, float scale, fa_dtype dtype,
+                         void* stream) {
+  if (!tensors_ok(q, k, v, o, dout, dq, dk, dv) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
+  fa_status st = check_shape(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d);
+  if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  st = check_device();
+  if (st != FA_OK) return st;
+  void* ws = scratch_address();
+  if (!ws) return FA_ERR_DEVICE;
+  fa::BwdArgs a{};
+  st = bwd_setup(B, H, H, N, d, scale, dtype, ws, FA_NOALLOC_SCRATCH_BYTES, &a);
+  if (st != FA_OK) return st;
+  return bwd_all(a, q, k, v, o, dout, lse, dq, dk, dv, d, causal, dtype, stream);
 }
 
 }  // extern "C"

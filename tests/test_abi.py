@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 7
+    assert fa.fa_abi_version() == 8
     for st in range(6):
         assert fa.fa_status_string(st) and fa.fa_status_string(st) != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -312,3 +312,35 @@ def test_binding_rejects_misaligned_view():
     with pytest.raises(ValueError, match="not 16-byte aligned"):
         fa._check("q", FakeCuda(), (1, 1, 8, 64), torch.bfloat16)
 
+
+def _bwd_noalloc(**kw):
+    args = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, H=1, N=128, d=64,
+                causal=0, scale=0.125, dtype=fa.FA_BF16, stream=None)
+    args.update(kw)
+    return fa.fa_bwd_noalloc(**args)
+
+
+def test_noalloc_rejects():
+    """The allocation-free backward checks what fa_bwd checks, and refuses shapes
+    whose D and L2 do not fit its static array (B*H*Np > 4 Mi rows)."""
+    E = fa.FA_ERR_INVALID_ARGUMENT
+    for name in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"):
+        assert _bwd_noalloc(**{name: None}) == E
+    assert _bwd_noalloc(dq=P + 8) == E and _bwd_noalloc(lse=P + 2) == E
+    assert _bwd_noalloc(N=0) == E and _bwd_noalloc(scale=math.nan) == E
+    assert _bwd_noalloc(d=96) == fa.FA_ERR_UNSUPPORTED
+    rows = fa.FA_NOALLOC_SCRATCH_BYTES // 8            # D and L2, 4 bytes each per row
+    assert fa.fa_bwd_workspace_size(1, 64, rows // 64, 128) <= fa.FA_NOALLOC_SCRATCH_BYTES
+    assert _bwd_noalloc(B=1, H=64, N=rows // 64 + 64, d=128) == fa.FA_ERR_WORKSPACE
+    assert _bwd_noalloc(B=2, H=32, N=131072, d=128) == fa.FA_ERR_WORKSPACE
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m[1]) << int(m[2]) == fa.FA_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.skipif(_has_gpu(), reason="would launch kernels on the bogus pointers")
+def test_noalloc_valid_arguments_without_gpu_report_device_error():
+    assert _bwd_noalloc() == fa.FA_ERR_DEVICE
