@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=sorted(workloads.BY_NAME) + sorted(workloads.VARLEN_BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", default="two-pass", choices=["two-pass", "one-pass"],
+                    help="fa_bwd's two-pass backward (dQ by its own pass), or the one-pass "
+                         "steps (dQ by atomic adds inside the dK/dV kernel; 16-bit types)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="time only --workload (not also the causal bf16 workload)")
     ap.add_argument("--mode", default="step", choices=["step", "copy"])
@@ -171,10 +174,12 @@ def cpu_baseline(w, inp, gpu_out, budget_s: float = 10.0):
 
 
 class ClockSampler:
-    """Samples the GPU's shader (GFX) clock in a background thread through
-    amdsmi while the timed steps run; median and range in MHz, or None where
-    the clock cannot be read (no amdsmi, no permission).  The published dense
-    peak assumes 2.4 GHz; under sustained MFMA load the clock runs lower, so the
+    """Samples the GPU's shader (GFX) clock in a background thread while the
+    timed steps run: amdsmi's GPU metrics table (the mean of the per-XCC
+    current_gfxclks; readings at the idle clock, below 500 MHz, are dropped:
+    the table lags the start of the load).  Median and range in MHz, or None
+    where the table cannot be read.  The published dense peak
+    assumes 2.4 GHz; under sustained MFMA load the clock runs lower, so the
     peak at the sampled clock is reported beside it."""
 
     def __init__(self, period_s: float = 0.005):
@@ -189,8 +194,16 @@ class ClockSampler:
             import amdsmi
             amdsmi.amdsmi_init()
             h = amdsmi.amdsmi_get_processor_handles()[0]
-            read = lambda: amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)["clk"]
-            read()
+
+            def read():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                clks = [c for c in m.get("current_gfxclks") or []
+                        if isinstance(c, (int, float)) and 0 < c < 10000]
+                busy = m.get("average_gfx_activity")
+                return (sum(clks) / len(clks) if clks else None,
+                        busy if isinstance(busy, (int, float)) else None)
+            if read()[0] is None:
+                raise RuntimeError("no per-XCC gfx clocks in the GPU metrics table")
             return read
         except Exception as e:   # no amdsmi or no access: report no clock
             self.error = f"{type(e).__name__}: {e}"[:200]
@@ -199,7 +212,9 @@ class ClockSampler:
     def _run(self):
         while not self._stop.is_set():
             try:
-                self.samples.append(float(self._read()))
+                clk, _ = self._read()
+                if clk is not None and clk >= 500:
+                    self.samples.append(float(clk))
             except Exception as e:
                 self.error = f"{type(e).__name__}: {e}"[:200]
                 return
@@ -219,8 +234,9 @@ class ClockSampler:
         if not self.samples:
             return {"sclk_mhz": None, "error": self.error}
         t = sorted(self.samples)
-        return {"sclk_mhz": t[len(t) // 2], "sclk_mhz_min": t[0], "sclk_mhz_max": t[-1],
-                "samples": len(t)}
+        return {"sclk_mhz": round(t[len(t) // 2], 1), "sclk_mhz_min": round(t[0], 1),
+                "sclk_mhz_max": round(t[-1], 1), "samples": len(t),
+                "source": "amdsmi gpu metrics, mean of current_gfxclks over the XCCs"}
 
 
 def run_conditions(dev_index: int = 0) -> dict:
@@ -247,19 +263,24 @@ def run_conditions(dev_index: int = 0) -> dict:
     return cond
 
 
-# MFMA work each backward kernel executes per unit of its algorithmic share, by
-# design (masked diagonal tiles aside): the dQ pass recomputes S and dP to form
-# dS, three products where its share of the backward count is one.
-EXECUTED_RATIO = {"fwd": 1.0, "dkdv": 1.0, "dq": 3.0}
+# MFMA work each kernel executes per unit of its algorithmic share, by design
+# (masked diagonal tiles aside): the two-pass backward's dQ pass recomputes S
+# and dP to form dS, three products where its share of the backward count is
+# one; the one-pass kernel computes each of the five products once.
+EXECUTED_RATIO = {"fwd": 1.0, "dkdv": 1.0, "dq": 3.0, "dkdvq": 1.0}
 KERNEL_NAMES = {"fwd": "fwd16_kernel", "pre": "bwd_pre_kernel", "dkdv": "bwd_dkdv16_kernel",
-                "dq": "bwd_dq16_kernel"}
+                "dq": "bwd_dq16_kernel", "dkdvq": "bwd_dkdv16_kernel (one pass, dQ by atomics)",
+                "dqfin": "bwd_dqfin_kernel"}
 
 
 def time_dense(args, w, fa, steps=None):
     """Seeded inputs of a dense workload on the GPU, `args.warmup` untimed steps,
-    then `steps` timed ones; one step = fa_fwd_gqa, fa_bwd_preprocess,
-    fa_bwd_dkdv_gqa, fa_bwd_dq_gqa on one stream, HIP events around each launch.
-    Returns the timings and, for the oracle check, the inputs and outputs."""
+    then `steps` timed ones; one step = fa_fwd_gqa and the backward's launches
+    called one by one on one stream, HIP events around each: fa_bwd's two-pass
+    backward (fa_bwd_preprocess, fa_bwd_dkdv_gqa, fa_bwd_dq_gqa), or with
+    --backward one-pass (16-bit types) fa_bwd_preprocess, fa_bwd_dkdv_dq,
+    fa_bwd_dq_finalize.  Returns the timings and, for the oracle check, the
+    inputs and outputs."""
     import torch
     steps = steps or args.steps
     dev = torch.device("cuda:0")
@@ -270,7 +291,8 @@ def time_dense(args, w, fa, steps=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
-    ws = fa.workspace(B, H, N, d, dev)
+    one_pass = args.backward == "one-pass" and w.dtype != "f32"
+    ws = fa.workspace(B, H, N, d, dev, one_pass=one_pass)
     code = fa.dtype_code(q.dtype)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -290,12 +312,20 @@ def time_dense(args, w, fa, steps=None):
         check(fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, code, P(ws), ws.numel(), sh), "pre")
         if ev is not None:
             ev[2].record(stream)
-        check(fa.fa_bwd_dkdv_gqa(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, Hkv, N, d,
-                                 w.causal, w.scale, code, P(ws), ws.numel(), sh), "dkdv")
+        if one_pass:
+            check(fa.fa_bwd_dkdv_dq(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, Hkv, N, d,
+                                    w.causal, w.scale, code, P(ws), ws.numel(), sh), "dkdv_dq")
+        else:
+            check(fa.fa_bwd_dkdv_gqa(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, Hkv, N,
+                                     d, w.causal, w.scale, code, P(ws), ws.numel(), sh), "dkdv")
         if ev is not None:
             ev[3].record(stream)
-        check(fa.fa_bwd_dq_gqa(P(q), P(k), P(v), P(do), P(lse), P(dq), B, H, Hkv, N, d, w.causal,
-                               w.scale, code, P(ws), ws.numel(), sh), "dq")
+        if one_pass:
+            check(fa.fa_bwd_dq_finalize(P(dq), B, H, N, d, w.scale, code, P(ws), ws.numel(), sh),
+                  "dq_finalize")
+        else:
+            check(fa.fa_bwd_dq_gqa(P(q), P(k), P(v), P(do), P(lse), P(dq), B, H, Hkv, N, d,
+                                   w.causal, w.scale, code, P(ws), ws.numel(), sh), "dq")
         if ev is not None:
             ev[4].record(stream)
 
@@ -311,7 +341,10 @@ def time_dense(args, w, fa, steps=None):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     ms = lambda a, b_: sum(e[a].elapsed_time(e[b_]) for e in events) / steps
-    kms = {"fwd": ms(0, 1), "pre": ms(1, 2), "dkdv": ms(2, 3), "dq": ms(3, 4)}
+    if one_pass:
+        kms = {"fwd": ms(0, 1), "pre": ms(1, 2), "dkdvq": ms(2, 3), "dqfin": ms(3, 4)}
+    else:
+        kms = {"fwd": ms(0, 1), "pre": ms(1, 2), "dkdv": ms(2, 3), "dq": ms(3, 4)}
     return {"w": w, "shape": (B, H, Hkv, N, d), "steps": steps, "wall": wall, "events": events,
             "kernel_ms": kms, "clock": clock.summary(), "inp": inp,
             "out": {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}}
@@ -319,14 +352,17 @@ def time_dense(args, w, fa, steps=None):
 
 def kernel_entries(w, kms, peak):
     """Per launch of each kernel: algorithmic FLOPs (the method's count split
-    over the kernels: forward 4 B H N^2 d, dK/dV 4/5 of the backward's 2.5x,
-    dQ 1/5), MFMA FLOPs executed by design, time and rate against the peak;
-    the preprocess against HBM (its algorithmic bytes)."""
+    over the kernels: forward 4 B H N^2 d; two-pass backward: dK/dV 4/5 of the
+    backward's 2.5x, dQ 1/5; one-pass: all of it), MFMA FLOPs executed by
+    design, time and rate against the peak; the preprocess and the dQ finalize
+    against HBM, at the bytes they move."""
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
-    alg = {"fwd": fwd_f, "dkdv": 0.8 * bwd_f, "dq": 0.2 * bwd_f}
-    e16 = 4 if w.dtype == "f32" else 2
+    alg = {"fwd": fwd_f, "dkdv": 0.8 * bwd_f, "dq": 0.2 * bwd_f, "dkdvq": bwd_f}
+    e = 4 if w.dtype == "f32" else 2
     out = []
-    for key in ("fwd", "dkdv", "dq"):
+    for key in ("fwd", "dkdv", "dq", "dkdvq"):
+        if key not in kms:
+            continue
         t = kms[key] * 1e-3
         out.append({"kernel": KERNEL_NAMES[key], "ms": round(kms[key], 4), "bound": "mfma",
                     "algorithmic_tflop": round(alg[key] / 1e12, 4),
@@ -335,11 +371,20 @@ def kernel_entries(w, kms, peak):
                     "frac": round(alg[key] / t / 1e12 / peak, 4),
                     "executed_frac": round(alg[key] * EXECUTED_RATIO[key] / t / 1e12 / peak, 4)})
     rows = w.B * w.H * w.N
-    pre_bytes = 2 * rows * w.d * e16 + 4 * rows + 8 * w.B * w.H * ((w.N + 63) // 64 * 64)
-    out.append({"kernel": KERNEL_NAMES["pre"], "ms": round(kms["pre"], 4), "bound": "hbm",
-                "algorithmic_gb": round(pre_bytes / 1e9, 4),
-                "achieved": round(pre_bytes / (kms["pre"] * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(pre_bytes / (kms["pre"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    prow = w.B * w.H * ((w.N + 63) // 64 * 64)
+    hbm = {
+        # O and dO read, LSE read, D and L2 written (+ the accumulator zeroed, one pass)
+        "pre": 2 * rows * w.d * e + 4 * rows + 8 * prow + (4 * prow * w.d if "dkdvq" in kms else 0),
+        # accumulator read, dq written
+        "dqfin": 4 * rows * w.d + rows * w.d * e,
+    }
+    for key in ("pre", "dqfin"):
+        if key not in kms:
+            continue
+        rate = hbm[key] / (kms[key] * 1e-3) / 1e9
+        out.append({"kernel": KERNEL_NAMES[key], "ms": round(kms[key], 4), "bound": "hbm",
+                    "bytes": hbm[key], "achieved": round(rate, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(rate / HBM_PEAK_GBS, 4)})
     return out
 
 
@@ -347,7 +392,7 @@ def summary(res, peak):
     """fwd / bwd / step rates of one timed dense workload."""
     w, kms, steps = res["w"], res["kernel_ms"], res["steps"]
     fwd_ms = kms["fwd"]
-    bwd_ms = kms["pre"] + kms["dkdv"] + kms["dq"]
+    bwd_ms = sum(v for k_, v in kms.items() if k_ != "fwd")
     ms_per_step = res["wall"] * 1e3 / steps
     fwd_f, bwd_f = w.fwd_flops(), w.bwd_flops()
     value = (fwd_f + bwd_f) / (ms_per_step * 1e-3) / 1e12
@@ -356,11 +401,12 @@ def summary(res, peak):
     clk = res["clock"]["sclk_mhz"]
     d = {
         "workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d,
-        "causal": w.causal, "step": "fa_fwd + fa_bwd (preprocess, dkdv, dq)",
+        "causal": w.causal,
+        "step": ("fa_fwd + fa_bwd one pass (preprocess, dkdv_dq, dq_finalize)" if "dkdvq" in kms
+                 else "fa_fwd + fa_bwd two pass (preprocess, dkdv, dq)"),
         "step_gpu_ms": step_spread(res["events"]),
         "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
-        "bwd_pre_ms": round(kms["pre"], 4), "bwd_dkdv_ms": round(kms["dkdv"], 4),
-        "bwd_dq_ms": round(kms["dq"], 4),
+        **{f"bwd_{k_}_ms": round(v, 4) for k_, v in kms.items() if k_ != "fwd"},
         "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
         "step_tflops": round(value, 2),
         "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 8
+#define FA_ABI_VERSION 9
 
 /* Block sizes (queries x keys) of the block-sparse mask of fa_attn. */
 #define FA_BLOCK_Q 256
@@ -102,7 +102,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *                                             (rows i >= N: +inf)
  * so that a tile of 64 rows can be copied whole, and P = exp2(S log2(e) - L2)
  * is exactly 0 on padding rows.  Size 2 * 4 * B * H * Np rounded up to 256 B.
- * fa_bwd (and fa_bwd_preprocess) rewrite it completely on every call.
+ * fa_bwd (and fa_bwd_preprocess) rewrite it completely on every call.  The
+ * one-pass steps (fa_bwd_dkdv_dq) need more: this size plus the dQ
+ * accumulator, 4 * B * H * Np * d bytes, right after it.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -111,8 +113,9 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  *
  * o and lse must be what fa_fwd wrote for the same q, k, v, causal and scale.
  * Equivalent to fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq enqueued in that
- * order on `stream` with the same arguments.  Writes every element of dq, dk,
- * dv (dtype, rounded to nearest even from fp32 accumulators) and of the
+ * order on `stream` with the same arguments (the two-pass backward: dQ by a
+ * separate reduction over the key tiles).  Writes every element of dq, dk, dv
+ * (dtype, rounded to nearest even from fp32 accumulators) and of the
  * workspace.  No atomics: results are bitwise repeatable.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -151,7 +154,10 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void
 
 /*
  * Backward step 1: D_i = rowsum(dout_i * o_i) and L2_i = LSE_i * log2(e) in
- * float32 into the workspace (layout at fa_bwd_workspace_size).  D is the row
+ * float32 into the workspace (layout at fa_bwd_workspace_size); when
+ * workspace_bytes also covers the one-pass dQ accumulator
+ * (fa_bwd_workspace_size(B, H, N, d) + 4 * B * H * Np * d), it zeroes that
+ * too, for fa_bwd_dkdv_dq.  D is the row
  * term of the softmax gradient, precomputed from O instead of from P and dP
  * ("FlashAttention-2: Faster Attention with Better Parallelism and Work
  * Partitioning", sections "Standard Attention Implementation / Backward Pass"
@@ -182,13 +188,45 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* d
  * key tile and write dq = scale * dS k.  This is the separate pass that sums
  * dQ over all key tiles (same FlashAttention-2 page, section "Parallelism:
  * 시퀀스 길이 차원 병렬화", which allows dQ by atomic adds or by a separate
- * reduction).  Needs the workspace as left by fa_bwd_preprocess.
+ * reduction).  Needs the workspace as left by fa_bwd_preprocess.  Bitwise
+ * repeatable.
  */
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                     const float* lse, void* dq,
                     int B, int H, int N, int d, int causal, float scale,
                     fa_dtype dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * One-pass backward, the other reading of the same FlashAttention-2 page
+ * (section "Parallelism: 시퀀스 길이 차원 병렬화": dQ by atomic adds instead of a
+ * separate reduction).  Step 2 of 3 (after fa_bwd_preprocess with the larger
+ * workspace, which zeroes the accumulator): fa_bwd_dkdv (dk and dv written
+ * bit for bit the same) that also adds, for every key tile, its share dS k of
+ * dQ into the float32 accumulator [B,H,Np,d] that follows D and L2 in the
+ * workspace, by atomic adds.  On MI355X it is slower than fa_bwd_dkdv +
+ * fa_bwd_dq: the dQ products themselves cost little inside this kernel, but
+ * its fp32 atomic adds (B H N d (N / 128) of them) are bound by the L2's
+ * atomic rate.  dq then differs in its last bits from call to call (the
+ * order of the adds).  k, v, dk, dv have H_kv heads as for the _gqa entry
+ * points (H_kv = H: plain heads).  16-bit types only (fp32:
+ * FA_ERR_UNSUPPORTED).  workspace_bytes must be at least
+ * fa_bwd_workspace_size(B, H, N, d) + 4 * B * H * Np * d.
+ */
+fa_status fa_bwd_dkdv_dq(const void* q, const void* k, const void* v, const void* dout,
+                         const float* lse, void* dk, void* dv,
+                         int B, int H, int H_kv, int N, int d, int causal, float scale,
+                         fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * One-pass backward, step 3: dq = scale * the accumulator, rounded to dtype
+ * (nearest even); rows past N are not read.  16-bit types only; the same
+ * workspace size as step 2.
+ */
+fa_status fa_bwd_dq_finalize(void* dq, int B, int H, int N, int d, float scale,
+                             fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * Grouped key/value heads.  The page "Transformer 효율화 기법" (ailab.paldyn.com),

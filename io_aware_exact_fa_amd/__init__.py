@@ -37,7 +37,7 @@ FA_BF16 = 2
 EXPORTED = ("fa_abi_version", "fa_status_string", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd",
             "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa",
             "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_ex",
-            "fa_bwd_ex", "fa_bwd_noalloc")
+            "fa_bwd_ex", "fa_bwd_noalloc", "fa_bwd_dkdv_dq", "fa_bwd_dq_finalize")
 
 FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -87,6 +87,10 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_noalloc.restype = i
     lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_dkdv_dq.restype = i
+    lib.fa_bwd_dkdv_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dq_finalize.restype = i
+    lib.fa_bwd_dq_finalize.argtypes = [vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_dkdv.restype = i
@@ -157,6 +161,17 @@ def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale,
                    stream) -> int:
     return _lib.fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal),
                                float(scale), int(dtype), stream)
+
+
+def fa_bwd_dkdv_dq(q, k, v, dout, lse, dk, dv, B, H, H_kv, N, d, causal, scale, dtype,
+                   workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_dkdv_dq(q, k, v, dout, lse, dk, dv, B, H, H_kv, N, d, int(causal),
+                               float(scale), int(dtype), workspace, workspace_bytes, stream)
+
+
+def fa_bwd_dq_finalize(dq, B, H, N, d, scale, dtype, workspace, workspace_bytes, stream) -> int:
+    return _lib.fa_bwd_dq_finalize(dq, B, H, N, d, float(scale), int(dtype), workspace,
+                                   workspace_bytes, stream)
 
 
 def fa_bwd_preprocess(o, dout, lse, B, H, N, d, dtype, workspace, workspace_bytes, stream) -> int:
@@ -295,12 +310,16 @@ def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, 
     return o, lse
 
 
-def workspace(B, H, N, d, device):
-    """A torch uint8 buffer big enough (and aligned) for fa_bwd at this shape."""
+def workspace(B, H, N, d, device, one_pass=False):
+    """A torch uint8 buffer big enough (and aligned) for fa_bwd at this shape; with
+    one_pass, also for the one-pass steps (fa_bwd_dkdv_dq, fa_bwd_dq_finalize):
+    fa_bwd_workspace_size plus the float32 dQ accumulator [B, H, Np, d]."""
     import torch
     n = fa_bwd_workspace_size(B, H, N, d)
     if n == 0:
         raise FaError(FA_ERR_INVALID_ARGUMENT, "fa_bwd_workspace_size")
+    if one_pass:
+        n += 4 * B * H * ((N + 63) // 64 * 64) * d
     return torch.empty(n, dtype=torch.uint8, device=device)   # caching allocator: 512 B aligned
 
 

@@ -155,9 +155,22 @@ fa_status launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNC
 
 static_assert(FA_BLOCK_Q == fa::kBlockQ && FA_BLOCK_K == fa::kBlockK, "block sizes of fa.h");
 
-// Shared checks of the backward entry points, then the workspace split.
+// Bytes of the D and L2 part of the backward workspace, and of the whole
+// workspace (that part, then the float32 dQ accumulator of the one-pass
+// backward), for a valid shape.
+size_t ws_stats_bytes(int B, int H, int N) {
+  return align_up(2 * (uint64_t)B * H * padded_rows(N) * sizeof(float));
+}
+size_t ws_full_bytes(int B, int H, int N, int d) {
+  return ws_stats_bytes(B, H, N) + align_up((uint64_t)B * H * padded_rows(N) * d * sizeof(float));
+}
+
+// Shared checks of the backward entry points, then the workspace split: the
+// workspace must hold D and L2, and the whole workspace when `need_acc`; the
+// accumulator is set (a->dqacc) whenever the workspace holds it.
 fa_status bwd_setup(int B, int H, int H_kv, int N, int d, float scale, fa_dtype dtype,
-                    void* workspace, size_t workspace_bytes, fa::BwdArgs* a);
+                    void* workspace, size_t workspace_bytes, fa::BwdArgs* a,
+                    bool need_acc = false);
 // Sets the tensor pointers and enqueues preprocess, dK/dV and dQ.
 fa_status bwd_all(fa::BwdArgs& a, const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse, void* dq, void* dk, void* dv, int d,
@@ -219,8 +232,8 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
   if (elements(B, H, N, d) == 0) return 0;
-  const uint64_t rows = (uint64_t)B * H * padded_rows(N);
-  return align_up(2 * rows * sizeof(float));
+  if (elements(B, H, padded_rows(N), d) == 0) return 0;
+  return ws_stats_bytes(B, H, N);
 }
 
 fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H,
@@ -285,6 +298,36 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
                     void* stream) {
   return fa_bwd_dq_gqa(q, k, v, dout, lse, dq, B, H, H, N, d, causal, scale, dtype, workspace,
                        workspace_bytes, stream);
+}
+
+fa_status fa_bwd_dkdv_dq(const void* q, const void* k, const void* v, const void* dout,
+                         const float* lse, void* dk, void* dv, int B, int H, int H_kv, int N,
+                         int d, int causal, float scale, fa_dtype dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!tensors_ok(q, k, v, dout, dk, dv) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;   // no one-pass instance
+  fa::BwdArgs a{};
+  fa_status st = bwd_setup(B, H, H_kv, N, d, scale, dtype, workspace, workspace_bytes, &a, true);
+  if (st != FA_OK) return st;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dk = dk;
+  a.dv = dv;
+  return launched(fa::launch_bwd_dkdvq(to_dt(dtype), d, causal != 0, a, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_dq_finalize(void* dq, int B, int H, int N, int d, float scale, fa_dtype dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!tensors_ok(dq)) return FA_ERR_INVALID_ARGUMENT;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  fa::BwdArgs a{};
+  fa_status st = bwd_setup(B, H, H, N, d, scale, dtype, workspace, workspace_bytes, &a, true);
+  if (st != FA_OK) return st;
+  a.dq = dq;
+  return launched(fa::launch_bwd_dqfin(to_dt(dtype), d, a, (hipStream_t)stream));
 }
 
 fa_status fa_fwd_ex(const fa_attn* p, const void* q, const void* k, const void* v, void* o,
@@ -357,14 +400,14 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void
   if (!tensors_ok(q, k, v, o, dout, dq, dk, dv) || !words_ok(lse)) return FA_ERR_INVALID_ARGUMENT;
   fa_status st = check_shape(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
-  const size_t need = fa_bwd_workspace_size(B, H, N, d);
-  if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  if (ws_stats_bytes(B, H, N) > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
   st = check_device();
   if (st != FA_OK) return st;
   void* ws = scratch_address();
   if (!ws) return FA_ERR_DEVICE;
   fa::BwdArgs a{};
-  st = bwd_setup(B, H, H, N, d, scale, dtype, ws, FA_NOALLOC_SCRATCH_BYTES, &a);
+  // D and L2 only: the two-pass backward (dQ by its own pass, no accumulator).
+  st = bwd_setup(B, H, H, N, d, scale, dtype, ws, ws_stats_bytes(B, H, N), &a);
   if (st != FA_OK) return st;
   return bwd_all(a, q, k, v, o, dout, lse, dq, dk, dv, d, causal, dtype, stream);
 }
@@ -374,18 +417,22 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void
 namespace {
 
 fa_status bwd_setup(int B, int H, int H_kv, int N, int d, float scale, fa_dtype dtype,
-                    void* workspace, size_t workspace_bytes, fa::BwdArgs* a) {
+                    void* workspace, size_t workspace_bytes, fa::BwdArgs* a, bool need_acc) {
   fa_status st = check_shape(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
   if (H_kv <= 0 || H % H_kv != 0) return FA_ERR_INVALID_ARGUMENT;
-  const size_t need = fa_bwd_workspace_size(B, H, N, d);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0)
+  const size_t stats = ws_stats_bytes(B, H, N), full = ws_full_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < (need_acc ? full : stats) ||
+      ((uintptr_t)workspace % kAlign) != 0)
     return FA_ERR_WORKSPACE;
   st = check_device();
   if (st != FA_OK) return st;
   a->Np = padded_rows(N);
   a->delta = static_cast<float*>(workspace);
   a->l2 = a->delta + (size_t)B * H * a->Np;
+  a->dqacc = workspace_bytes >= full
+                 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + stats)
+                 : nullptr;
   a->B = B;
   a->H = H;
   a->N = N;
@@ -409,6 +456,9 @@ fa_status bwd_all(fa::BwdArgs& a, const void* q, const void* k, const void* v, c
   a.dv = dv;
   const fa::Dt dt = to_dt(dtype);
   hipStream_t s = (hipStream_t)stream;
+  // The two-pass backward (dQ by its own pass; no accumulator to zero, even
+  // when the caller's workspace could hold one).
+  a.dqacc = nullptr;
   st = launched(fa::launch_bwd_pre(dt, d, a, s));
   if (st != FA_OK) return st;
   st = launched(fa::launch_bwd_dkdv(dt, d, causal != 0, a, s));

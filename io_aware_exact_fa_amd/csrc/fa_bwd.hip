@@ -32,4 +32,12 @@ hipError_t launch_bwd_dq(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_
   return launch_step(BwdStep::dq, dt, d, causal, a, s);
 }
 
+hipError_t launch_bwd_dkdvq(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s) {
+  return launch_step(BwdStep::dkdvq, dt, d, causal, a, s);
+}
+
+hipError_t launch_bwd_dqfin(Dt dt, int d, const BwdArgs& a, hipStream_t s) {
+  return launch_step(BwdStep::dqfin, dt, d, false, a, s);
+}
+
 }  // namespace fa

@@ -66,6 +66,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long rows) {
   }
 #pragma unroll
   for (int m = LPR / 2; m > 0; m >>= 1) part += __shfl_xor(part, m, LPR);
+  if (a.dqacc && row < rows) {
+    // One-pass backward: this lane's E16 floats of the row's dQ accumulator start at 0.
+    f32x4* z = reinterpret_cast<f32x4*>(a.dqacc + (size_t)row * D + sub * E16);
+#pragma unroll
+    for (int e = 0; e < E16 / 4; ++e) z[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   if (row < rows && sub == 0) {
     float l2 = INFINITY;   // P = exp2(-inf) = 0 on padding rows and rows that see no key
     if (live) {
@@ -77,6 +83,28 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long rows) {
   }
 }
 
+
+// dq = -scale * (accumulated -dS K) of the one-pass backward, rounded to T;
+// one thread per 8 consecutive elements of a row (rows of every head; rows
+// past a sequence's length are not written).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_dqfin_kernel(BwdArgs a, long rows) {
+  constexpr int TPR = D / 8;   // threads per row
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = t / TPR;
+  if (row >= rows) return;
+  const int sub = (int)(t - row * TPR);
+  const long head = row / a.Np;
+  const int q = (int)(row - head * a.Np);
+  const Span sp = span_of(a, (int)head);
+  if (q >= sp.n) return;
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.dqacc + (size_t)row * D + sub * 8);
+  const f32x4 x0 = src[0], x1 = src[1];
+  const float f = -a.scale;   // the accumulator holds -dS K (see the one-pass kernel)
+  T* dst = static_cast<T*>(a.dq) + (sp.q + q) * D + sub * 8;
+  store4<T>(dst, x0[0] * f, x0[1] * f, x0[2] * f, x0[3] * f);
+  store4<T>(dst + 4, x1[0] * f, x1[1] * f, x1[2] * f, x1[3] * f);
+}
 
 // ------------------------------------------------------------------ dQ
 
@@ -865,15 +893,34 @@ struct Dkv16 {
 // BSPARSE: a block mask is given (the tile queue skips its dropped blocks);
 // without it the tiles are consecutive and the loops step plainly, which
 // keeps this kernel's code as small as before the queue (1-2 % faster).
-template <typename T, int D, bool CAUSAL, bool DROP, bool BSPARSE>
+//
+// DQ (the one-pass backward): the workgroup also adds its key tile's share of
+// dQ, dS K over its 128 keys, into the float32 accumulator a.dqacc by atomic
+// adds ("FlashAttention-2: Faster Attention with Better Parallelism and Work
+// Partitioning", section "Parallelism: 시퀀스 길이 차원 병렬화": dQ by atomic adds
+// across the key-tile workgroups).  Each wave stores its rounded dS (as dS^T,
+// keys x queries) into LDS; after the tile's barrier, during the next tile,
+// wave w reads the whole 128-key dS^T of the tile and multiplies it with K
+// (held in registers for the whole kernel) for its part of the 64 x D dQ
+// tile: D = 128: head-dim block w of both 32-query blocks; D = 64: query block
+// w / 2, head-dim block w % 2.  Rows past N land in the accumulator's padding
+// rows (their dS is 0).  Not with dropout (its LDS area does not fit beside
+// the two dS^T buffers).
+template <typename T, int D, bool CAUSAL, bool DROP, bool BSPARSE, bool DQ = false>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   using C = Dkv16<D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
+  static_assert(!(DQ && DROP), "the one-pass backward has no dropout instance");
   // Dropout: per wave and 32-query block, the 16-bit uniforms of its 32 x 32
   // (query, key) elements, 2 KB, after the tile buffers.
   constexpr int DSCR = 2048;
-  __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF + (DROP ? 8 * DSCR : 0)];
+  // DQ: two dS^T buffers (128 keys x 64 queries, the 64-column tile layout).
+  using LayS = TileLds<64>;
+  constexpr int DST = C::BKC * LayS::PB;
+  constexpr int DSB = C::NB * C::BUF;   // first dS^T buffer
+  __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF + (DROP ? 8 * DSCR : 0) +
+                                                    (DQ ? 2 * DST : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, h = lane >> 5;
@@ -919,6 +966,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     dv[db] = f32x16{};
     dk[db] = f32x16{};
   }
+  // DQ: this wave's dQ blocks (query block qbq + j, j < NQB; head-dim block dbq).
+  constexpr int NQB = D / 64;
+  const int dbq = D == 128 ? w : (w & 1), qbq = D == 128 ? 0 : (w >> 1);
+  const LayS lays(lane);
+  frag kq[DQ ? C::BKC / 16 : 1];
   // Window: queries [myk - wr, myk + wl] see this lane's key.  Query tiles of
   // the workgroup: [lo, hi), of which [ml, mu) need no mask.
   const int wl = a.wl, wr = CAUSAL ? min(a.wr, 0) : a.wr;
@@ -1012,11 +1064,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // Slot of copy k of the next-but-one tile.
   constexpr auto copy_slot = [](int k) { return 1 + (k * (NM - 6)) / C::NLD; };
   int bcur = 0;
+  // DQ: the dS^T buffer the current tile writes, the tile whose dS^T the other
+  // buffer holds (-1: none), and this lane's row and swizzle in a dS^T buffer.
+  int dpar = 0, dprev = -1;
+  const int dsrow = (32 * w + col) * LayS::PB, dsswz = (col >> 3) & 1;
+  // dQ of query tile qtp of the current query head from dS^T buffer par: this
+  // wave's blocks, 8 MFMAs each over the 128 keys, added into the accumulator.
+  // Element i of lane (col, h) is accumulator row 32 qb + 16 (i / 8) + 8 h +
+  // 2 (i % 4) + (i / 4) % 2 of the tile (the query of logical slot
+  // 8 (i / 4) + 4 h + i % 4 of block qb), column 32 dbq + col.
+  auto dq_flush = [&](int par, int qtp) {
+    if constexpr (DQ) {
+      float* base = a.dqacc + ((size_t)qhead * a.Np + (size_t)qtp * C::BQ + 8 * h) * D + dbq * 32 + col;
+      const char* dsb = smem + DSB + par * DST;
+#pragma unroll
+      for (int j = 0; j < NQB; ++j) {
+        const int qb = qbq + j;
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < C::BKC / 16; ++ks) {
+          s16x4 v[2];
+#pragma unroll
+          for (int rp = 0; rp < 2; ++rp)
+            v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(dsb + lays.T(rp, qb) + (16 * ks + 8 * rp) * LayS::PB));
+          acc = M::mma(__builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
+                                                      v[1][0], v[1][1], v[1][2], v[1][3]}),
+                       kq[ks], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          unsafeAtomicAdd(base + (32 * qb + 16 * (i >> 3) + 2 * (i & 3) + ((i >> 2) & 1)) * D, acc[i]);
+      }
+    }
+  };
   // One query tile (tnext: the tile copied meanwhile).  MASK: some query of the
   // tile lies outside the window of some key of the workgroup.
   auto tile = [&](int qt, int tnext, auto maskc) {
     constexpr bool MASK = decltype(maskc)::value;
     const int qi0 = qt * C::BQ;
+    // DQ: the previous tile's dQ (its dS^T was written before the last barrier).
+    if constexpr (DQ)
+      if (dprev >= 0) dq_flush(dpar ^ 1, dprev);
     // Masked tiles: query offsets (q - qi0 - h) rlo .. rlo + rspan see this
     // lane's key (sides of kNoLimit keep the sums below 2^31).
     const int rlo = myk - wr - qi0 - h;
@@ -1166,6 +1255,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
             if ((i + 1) % 8 == 0) {
               pa[b][i / 8] = pack_frag<T>(p[b], i / 8);
               sa[b][i / 8] = pack_frag<T>(ds[b], i / 8);
+              if constexpr (DQ) {
+                // dS^T row 32 w + col (this lane's key); logical query slots
+                // 32 b + 16 u + 8 h + t hold queries 32 b + 16 u + 8 (t / 4) +
+                // 2 (t % 4) + h, the elements of this fragment in order.
+                *reinterpret_cast<s16x8*>(smem + DSB + dpar * DST + dsrow +
+                                          16 * ((4 * b + 2 * (i / 8) + h) ^ dsswz)) =
+                    __builtin_bit_cast(s16x8, sa[b][i / 8]);
+              }
             }
           }
       __builtin_amdgcn_sched_barrier(0);
@@ -1175,11 +1272,59 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
     __syncthreads();
     bcur = b1;
+    if constexpr (DQ) {
+      dprev = qt;
+      dpar ^= 1;
+    }
   };
   // Tiles [lo, ml) and [mu, hi) need masks in some key column (the causal
   // diagonal and the window's near edge, its far edge); [ml, mu) none, rows past
   // N included (their L2 is +inf).  Separate loops, each with its own register
   // allocation.
+  if constexpr (DQ) {
+    // K rows k0 .. k0 + 127 into buffer 2 (rows past N land as zero), read back
+    // as the B operands of dQ: lane (col, h) of k step ks holds K[k0 + 16 ks +
+    // 8 rp + 2 s + h][32 dbq + col] (rp < 2, s < 4), the keys that the dS^T
+    // reads of the same step give it.  Held in AGPRs for the whole kernel.
+    const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
+    const uint32_t kbuf = lds_address(smem) + 2 * C::BUF;
+    if constexpr (D == 128) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = 8 * w + j;   // 4-row group
+        copy16_to_lds(rsk, lay.c[(q >> 1) & 1], (uint32_t)(k0 + 4 * q) * (2 * D),
+                      kbuf + q * 4 * C::PB);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int r = 32 * w + j;
+        copy_to_lds<C::HALF>(rsk, lay.c[(r >> 3) & 1], (uint32_t)(k0 + r) * (2 * D),
+                             kbuf + r * C::PB);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    // Lane offsets of head-dim block dbq, selected rather than indexed (a
+    // runtime index into the layout's offset array would move it to memory).
+    int tq[2];
+#pragma unroll
+    for (int rp = 0; rp < 2; ++rp)
+      tq[rp] = ((dbq & 1) ? lay.T(rp, 1) : lay.T(rp, 0)) + (dbq >> 1) * (lay.T(rp, 2) - lay.T(rp, 0));
+#pragma unroll
+    for (int ks = 0; ks < C::BKC / 16; ++ks) {
+      s16x4 v[2];
+#pragma unroll
+      for (int rp = 0; rp < 2; ++rp)
+        v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(smem + 2 * C::BUF + tq[rp] + (16 * ks + 8 * rp) * C::PB));
+      kq[ks] = __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
+                                              v[1][0], v[1][1], v[1][2], v[1][3]});
+      asm volatile("" : "+a"(kq[ks]));
+    }
+    // (Buffer 2 is next written by the first tile's copies, after use_head's
+    // barrier, which every wave reaches only with these reads done.)
+  }
   for (int g = 0; g < a.G; ++g) {
     use_head(g);
     bcur = 0;
@@ -1199,6 +1344,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     // workgroup ends, and every wave is done with the buffers.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    // DQ: the head's last tile (its dS^T is complete after that barrier).
+    if constexpr (DQ) {
+      if (dprev >= 0) dq_flush(dpar ^ 1, dprev);
+      dprev = -1;
+    }
   }
 
   // Epilogue: lane (col = d, h) holds keys kw + 8(i/4) + 4h + i%4.
@@ -1238,6 +1388,24 @@ static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
       dim3 grid((a.N + DkvTile<T, D>::BKC - 1) / DkvTile<T, D>::BKC, a.H / a.G, a.B);
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, DROP>), grid, dim3(256), 0, s, a);
     }
+  } else if (step == BwdStep::dkdvq) {
+    // The one-pass backward: 16-bit types without dropout only (the host
+    // never asks for anything else).
+    if constexpr (sizeof(T) == 2 && !DROP) {
+      dim3 grid((a.N + Dkv16<D>::BKC - 1) / Dkv16<D>::BKC, a.H / a.G, a.B);
+      if (a.bm.mask)
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL, false, true, true>), grid, dim3(256), 0,
+                           s, a);
+      else
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL, false, false, true>), grid, dim3(256), 0,
+                           s, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (step == BwdStep::dqfin) {
+    const long threads = rows * (D / 8);
+    hipLaunchKernelGGL((bwd_dqfin_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                       0, s, a, rows);
   } else if constexpr (sizeof(T) == 2) {
     // Causal d = 128: 128-row workgroups, two per CU, balance the triangle.
     constexpr int NW = CAUSAL && D == 128 ? 4 : 8;

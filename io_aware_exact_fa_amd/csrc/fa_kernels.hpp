@@ -65,6 +65,10 @@ struct BwdArgs {
   void* dv;
   float* delta;   // workspace [B,H,Np]: D_i = rowsum(dO_i * O_i), 0 past N
   float* l2;      // workspace [B,H,Np]: LSE_i * log2(e), +inf past N
+  // Workspace [B,H,Np,d] float32 of the one-pass backward: dS K summed over the
+  // key tiles by atomic adds (null: the two-pass backward, dQ by its own pass).
+  // The preprocess zeroes it when set.
+  float* dqacc = nullptr;
   int B, H, N;
   int Np;         // N rounded up to a multiple of 64
   float scale;
@@ -223,10 +227,14 @@ hipError_t launch_fwd(Dt dt, int d, bool causal, const FwdArgs& a, hipStream_t s
 hipError_t launch_bwd_pre(Dt dt, int d, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s);
+// The one-pass backward (16-bit types without dropout): dK, dV and the atomic
+// dQ accumulation in one launch, then dq = scale * accumulator.
+hipError_t launch_bwd_dkdvq(Dt dt, int d, bool causal, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dqfin(Dt dt, int d, const BwdArgs& a, hipStream_t s);
 
 // Backward instances per dtype (T = float, _Float16, __bf16) and head dimension
 // (D = 64, 128), defined in one translation unit each (fa_bwd_<dtype>_d<D>.hip).
-enum class BwdStep { pre, dkdv, dq };
+enum class BwdStep { pre, dkdv, dq, dkdvq, dqfin };
 template <typename T, int D>
 hipError_t launch_bwd_inst(BwdStep st, bool causal, const BwdArgs& a, hipStream_t s);
 #define FA_BWD_EXTERN(T, D) \

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fa.fa_abi_version() == 8
+    assert fa.fa_abi_version() == 9
     for st in range(6):
         assert fa.fa_status_string(st) and fa.fa_status_string(st) != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
@@ -214,12 +214,24 @@ def test_too_many_heads_rejected():
     assert _fwd(B=4097, H=4096, N=1) == fa.FA_ERR_UNSUPPORTED
 
 
+def _up(x):
+    return (x + 255) // 256 * 256
+
+
+def _stats_bytes(B, H, N):
+    """The D and L2 part of the workspace: two float32 arrays [B, H, Np]."""
+    return _up(2 * 4 * B * H * ((N + 63) // 64 * 64))
+
+
+def _one_pass_bytes(B, H, N, d):
+    """Workspace of the one-pass steps: D and L2, then the float32 dQ accumulator."""
+    return _stats_bytes(B, H, N) + 4 * B * H * ((N + 63) // 64 * 64) * d
+
+
 def test_workspace_size():
     # Two float32 arrays [B, H, Np], Np = N rounded up to a multiple of 64.
-    up = lambda x: (x + 255) // 256 * 256
     for B, H, N, d in ((2, 3, 100, 64), (1, 1, 64, 128), (1, 1, 65, 128), (4, 32, 4096, 128)):
-        Np = (N + 63) // 64 * 64
-        assert fa.fa_bwd_workspace_size(B, H, N, d) == up(2 * 4 * B * H * Np)
+        assert fa.fa_bwd_workspace_size(B, H, N, d) == _stats_bytes(B, H, N)
     assert fa.fa_bwd_workspace_size(0, 1, 1, 64) == 0
     assert fa.fa_bwd_workspace_size(1, 1, -3, 64) == 0
 
@@ -330,7 +342,8 @@ def test_noalloc_rejects():
     assert _bwd_noalloc(N=0) == E and _bwd_noalloc(scale=math.nan) == E
     assert _bwd_noalloc(d=96) == fa.FA_ERR_UNSUPPORTED
     rows = fa.FA_NOALLOC_SCRATCH_BYTES // 8            # D and L2, 4 bytes each per row
-    assert fa.fa_bwd_workspace_size(1, 64, rows // 64, 128) <= fa.FA_NOALLOC_SCRATCH_BYTES
+    assert _stats_bytes(1, 64, rows // 64) <= fa.FA_NOALLOC_SCRATCH_BYTES
+    assert _stats_bytes(1, 64, rows // 64 + 64) > fa.FA_NOALLOC_SCRATCH_BYTES
     assert _bwd_noalloc(B=1, H=64, N=rows // 64 + 64, d=128) == fa.FA_ERR_WORKSPACE
     assert _bwd_noalloc(B=2, H=32, N=131072, d=128) == fa.FA_ERR_WORKSPACE
 
@@ -344,3 +357,44 @@ def test_noalloc_scratch_size_matches_header():
 @pytest.mark.skipif(_has_gpu(), reason="would launch kernels on the bogus pointers")
 def test_noalloc_valid_arguments_without_gpu_report_device_error():
     assert _bwd_noalloc() == fa.FA_ERR_DEVICE
+
+
+def _dkdv_dq(**kw):
+    args = dict(q=P, k=P, v=P, dout=P, lse=P, dk=P, dv=P, B=1, H=8, H_kv=2, N=128, d=64, causal=1,
+                scale=0.125, dtype=fa.FA_BF16, workspace=0x10000,
+                workspace_bytes=_one_pass_bytes(1, 8, 128, 64), stream=None)
+    args.update(kw)
+    return fa.fa_bwd_dkdv_dq(**args)
+
+
+def _dq_fin(**kw):
+    args = dict(dq=P, B=1, H=8, N=128, d=64, scale=0.125, dtype=fa.FA_BF16, workspace=0x10000,
+                workspace_bytes=_one_pass_bytes(1, 8, 128, 64), stream=None)
+    args.update(kw)
+    return fa.fa_bwd_dq_finalize(**args)
+
+
+def test_one_pass_steps_reject():
+    """fa_bwd_dkdv_dq and fa_bwd_dq_finalize: the usual checks, 16-bit types only,
+    and a workspace that also holds the accumulator."""
+    E = fa.FA_ERR_INVALID_ARGUMENT
+    for name in ("q", "k", "v", "dout", "lse", "dk", "dv"):
+        assert _dkdv_dq(**{name: None}) == E
+    assert _dkdv_dq(dk=P + 8) == E and _dq_fin(dq=None) == E and _dq_fin(dq=P + 4) == E
+    assert _dkdv_dq(H_kv=3) == E and _dkdv_dq(N=0) == E and _dq_fin(scale=math.inf) == E
+    assert _dkdv_dq(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert _dq_fin(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert _dkdv_dq(d=96) == fa.FA_ERR_UNSUPPORTED and _dq_fin(d=96) == fa.FA_ERR_UNSUPPORTED
+    full = _one_pass_bytes(1, 8, 128, 64)
+    assert _dkdv_dq(workspace_bytes=full - 1) == fa.FA_ERR_WORKSPACE
+    assert _dq_fin(workspace_bytes=fa.fa_bwd_workspace_size(1, 8, 128, 64)) == fa.FA_ERR_WORKSPACE
+    assert _dkdv_dq(workspace=0x10008) == fa.FA_ERR_WORKSPACE
+
+
+@pytest.mark.skipif(_has_gpu(), reason="would launch kernels on the bogus pointers")
+def test_one_pass_steps_without_gpu_report_device_error():
+    assert _dkdv_dq() == fa.FA_ERR_DEVICE and _dq_fin() == fa.FA_ERR_DEVICE
+    nb = fa.fa_bwd_workspace_size(1, 1, 128, 64)
+    assert fa.fa_bwd_preprocess(P, P, P, 1, 1, 128, 64, fa.FA_F16, 0x10000, nb, None) == fa.FA_ERR_DEVICE
+    assert fa.fa_bwd_dkdv(P, P, P, P, P, P, P, 1, 1, 128, 64, 0, 0.1, fa.FA_F16, 0x10000, nb,
+                          None) == fa.FA_ERR_DEVICE

@@ -59,6 +59,16 @@ def rel_err(got, ref):
     return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
 
 
+def same_but_summation_order(a, b, dtype):
+    """dQ of the one-pass backward, which sums the key tiles' shares by atomic
+    adds in an order that may change, against another summation: equal up to
+    one unit in the last place of the storage type (relative to the largest
+    element)."""
+    ulp = {"f32": 2.0 ** -23, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}[dtype]
+    da, db_ = a.double(), b.double()
+    return (da - db_).abs().max().item() <= ulp * max(da.abs().max().item(), 1e-30)
+
+
 def compare(out, inp, causal, scale, dtype, heads=None, backward=True, tag=""):
     """Compare GPU outputs with the oracle on the given (b, h) heads (all if None)."""
     tol = TOL[dtype]
@@ -369,10 +379,12 @@ def test_large_gqa_sampled_groups(fa, w):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_plain_entry_points_by_name(fa, dtype):
-    """fa_fwd, fa_bwd, and fa_bwd_preprocess + fa_bwd_dkdv + fa_bwd_dq called by
-    those names through ctypes (not through their grouped forms), causal, ragged
-    N = 333 over 3 heads of 2 batch entries: every element against the oracle, and
-    the split backward bit for bit equal to fa_bwd."""
+    """fa_fwd, fa_bwd, the two-pass steps (fa_bwd_preprocess + fa_bwd_dkdv +
+    fa_bwd_dq) and the one-pass steps (fa_bwd_preprocess + fa_bwd_dkdv_dq +
+    fa_bwd_dq_finalize) called by those names through ctypes (not through their
+    grouped forms), causal, ragged N = 333 over 3 heads of 2 batch entries:
+    every element against the oracle; the two-pass steps bit for bit equal to
+    fa_bwd; the one-pass dK and dV too, its dQ up to the order of its sums."""
     w = workloads.Workload(f"plain-{dtype}", 2, 3, 333, 128, dtype, True, seed=83)
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
@@ -399,8 +411,25 @@ def test_plain_entry_points_by_name(fa, dtype):
                           w.scale, code, P(ws2), ws2.numel(), sh) == fa.FA_OK
     assert fa.fa_bwd_dq(P(q), P(k), P(v), P(do), P(lse), P(g2[0]), B, H, N, d, 1, w.scale, code,
                         P(ws2), ws2.numel(), sh) == fa.FA_OK
+    g3 = [torch.full_like(q, float("nan")) for _ in range(3)]
+    ws3 = fa.workspace(B, H, N, d, dev, one_pass=True)
+    ws3.fill_(255)   # NaN in every float32 of the workspace: the accumulator must be zeroed
+    say(f"case {w.name}: fa_bwd_preprocess, fa_bwd_dkdv_dq, fa_bwd_dq_finalize")
+    assert fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, code, P(ws3), ws3.numel(),
+                                sh) == fa.FA_OK
+    assert fa.fa_bwd_dkdv_dq(P(q), P(k), P(v), P(do), P(lse), P(g3[1]), P(g3[2]), B, H, H, N, d,
+                             1, w.scale, code, P(ws3), ws3.numel(), sh) == fa.FA_OK
+    assert fa.fa_bwd_dq_finalize(P(g3[0]), B, H, N, d, w.scale, code, P(ws3), ws3.numel(),
+                                 sh) == fa.FA_OK
     torch.cuda.synchronize()
     out = dict(o=o, lse=lse, dq=g1[0], dk=g1[1], dv=g1[2])
     compare(out, inp, True, w.scale, dtype, tag=w.name)
-    for name, a, b in zip(("dq", "dk", "dv"), g1, g2):
-        assert torch.equal(a, b), f"split backward {name} differs from fa_bwd"
+    compare(dict(o=o, lse=lse, dq=g3[0], dk=g3[1], dv=g3[2]), inp, True, w.scale, dtype,
+            tag=w.name + " one-pass")
+    # fa_bwd is the two-pass backward, bit for bit; the one-pass kernel does the
+    # same dK/dV arithmetic, and sums dQ by atomic adds instead.
+    for name, a, b, c in zip(("dq", "dk", "dv"), g1, g2, g3):
+        assert torch.equal(a, b), f"{name}: fa_bwd differs from its steps"
+        if name != "dq":
+            assert torch.equal(a, c), f"{name}: the one-pass kernel differs"
+    assert same_but_summation_order(g3[0], g1[0], dtype)
