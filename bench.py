@@ -252,13 +252,15 @@ def run_conditions(dev_index: int = 0) -> dict:
             cond["rocm"] = f.read().strip()
     except OSError:
         cond["rocm"] = None
+    # The compiler that built libfa.so, from the ident string it left in the
+    # library (no child process: this process has initialised the GPU).
     try:
-        import subprocess
-        hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-        r = subprocess.run([hipcc, "--version"], capture_output=True, text=True, timeout=30)
-        cond["compiler"] = next((l.strip() for l in r.stdout.splitlines() if "clang version" in l),
-                                None)
-    except Exception:
+        import re
+        import io_aware_exact_fa_amd as fa
+        with open(fa.LIB_PATH, "rb") as f:
+            m = re.search(rb"AMD clang version [^\x00)]*\)?", f.read())
+        cond["compiler"] = m.group(0).decode() if m else None
+    except OSError:
         cond["compiler"] = None
     return cond
 

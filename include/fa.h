@@ -348,8 +348,9 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
  * its block is kept and the causal mask and the window allow it; a row that
  * sees no key gets O = 0 and LSE = -inf, and no gradient.  The mask is read by
  * the kernels, which skip the tiles of blocks it drops (the register-staged
- * fp32 kernels and the d = 64 forward test them one by one).  Dropout together
- * with a block mask is FA_ERR_UNSUPPORTED. *
+ * fp32 kernels and the d = 64 forward test them one by one).  With dropout as
+ * well, the dropout applies to P of the kept blocks.
+ *
  * Dropout.  The forward computes O = dropout(P) V: element (i, j) of P is kept
  * with probability keep = K / 65536, K = round((1 - dropout_p) 65536), and kept
  * elements are multiplied by 1 / keep; LSE is that of the undropped softmax.

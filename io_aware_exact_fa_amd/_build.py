@@ -42,6 +42,7 @@ COMMON = [
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA = {f"fa_bwd_{t}_d{d}.hip": VGPR_FORM for t in ("bf16", "f16") for d in (64, 128)}
 EXTRA["fa_fwd.hip"] = VGPR_FORM
+EXTRA["fa_fwd64.hip"] = VGPR_FORM
 
 
 def _compile(src: str) -> str:

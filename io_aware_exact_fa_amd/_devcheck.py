@@ -164,6 +164,13 @@ def code_objects(lib_path: str, workdir: str):
     return out
 
 
+def function_at(names, lines, i):
+    """Name of the function whose code holds line i (lines hold None at each
+    function start, in the order of `names`)."""
+    k = sum(1 for x in lines[:i + 1] if x is None)
+    return names[k - 1] if k else "?"
+
+
 def kernels_in_several_objects(objs):
     seen = {}
     for i, (names, _, _) in enumerate(objs):
@@ -188,12 +195,14 @@ def check_library(lib_path: str) -> dict:
     if n < 1000 or kernels < 50 or sum(len(t) for _, _, t in objs) < 100:
         raise RuntimeError(f"device-code check: disassembly not parsed ({n} LDS-direct loads, "
                            f"{kernels} kernels)")
-    bad = [v for _, lines, targets in objs for v in violations(lines, targets)]
+    bad = [(function_at(names, lines, v[0]),) + v for names, lines, targets in objs
+           for v in violations(lines, targets)]
     if bad:
+        where = sorted({f for f, *_ in bad})
         raise RuntimeError(
             f"device-code check: {len(bad)} of {n} LDS-direct loads too soon after an SGPR/M0 "
-            "write, e.g. " + "; ".join(f"{p!r} {w} wait states before {ins!r}"
-                                       for _, ins, p, w in bad[:4]))
+            f"write, in {where}; e.g. " + "; ".join(f"{p!r} {w} wait states before {ins!r}"
+                                                     for _, _, ins, p, w in bad[:4]))
     dup = kernels_in_several_objects(objs)
     if dup:
         raise RuntimeError(f"device-code check: {len(dup)} kernels defined in more than one code "

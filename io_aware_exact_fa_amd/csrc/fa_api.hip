@@ -74,7 +74,6 @@ fa_status check_attn(const fa_attn* p) {
   if (p->cu_seqlens && !words_ok(p->cu_seqlens)) return FA_ERR_INVALID_ARGUMENT;
   if (p->block_mask && p->block_mask_heads != 1 && p->block_mask_heads != p->H)
     return FA_ERR_INVALID_ARGUMENT;
-  if (p->block_mask && p->dropout_p > 0.f) return FA_ERR_UNSUPPORTED;   // no such instance
   if (p->cu_seqlens)
     return check_varlen(p->cu_seqlens, p->B, p->N, p->total, p->H, p->H_kv, p->d, p->scale,
                         p->dtype);

@@ -1001,21 +1001,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     asm volatile("" : "+s"(x.row_lds), "+s"(x.row_glb), "+s"(x.buf_lds), "+s"(x.ld_glb));
     return x;
   };
+  // The dropout instances (the most registers of all) pay the full wait states
+  // before every copy rather than rely on where the compiler reloads spilled
+  // descriptors.
+  constexpr bool SAFE = DROP;
   auto copy_op = [&](const Bases& x, int j) {
     if (j < NROW) {
       const int mat = j / (NROW / 2), jj = j % (NROW / 2);
       if constexpr (D == 128) {
         // Group 4 w + jj: rows 16 w + 4 jj .. + 3.
-        copy16_to_lds(mat ? rsg : rsq, lay.c[(jj >> 1) & 1], x.row_glb + 4 * jj * (2 * D),
-                      x.row_lds + mat * C::TILE + 4 * jj * C::PB);
+        copy16_to_lds<SAFE>(mat ? rsg : rsq, lay.c[(jj >> 1) & 1], x.row_glb + 4 * jj * (2 * D),
+                            x.row_lds + mat * C::TILE + 4 * jj * C::PB);
       } else {
         // Row 16 w + jj.
-        copy_to_lds<C::HALF>(mat ? rsg : rsq, lay.c[(jj >> 3) & 1], x.row_glb + jj * (2 * D),
-                             x.row_lds + mat * C::TILE + jj * C::PB);
+        copy_to_lds<C::HALF, SAFE>(mat ? rsg : rsq, lay.c[(jj >> 3) & 1], x.row_glb + jj * (2 * D),
+                                   x.row_lds + mat * C::TILE + jj * C::PB);
       }
     } else {
-      copy_to_lds<false>(j == NROW ? rsl : rsd, 4 * row_pi(lane), x.ld_glb,
-                         x.buf_lds + 2 * C::TILE + (j - NROW) * C::BQ * 4);
+      copy_to_lds<false, SAFE>(j == NROW ? rsl : rsd, 4 * row_pi(lane), x.ld_glb,
+                               x.buf_lds + 2 * C::TILE + (j - NROW) * C::BQ * 4);
     }
   };
 
@@ -1379,9 +1383,8 @@ static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
   } else if (step == BwdStep::dkdv) {
     if constexpr (sizeof(T) == 2) {
       dim3 grid((a.N + Dkv16<D>::BKC - 1) / Dkv16<D>::BKC, a.H / a.G, a.B);
-      // Dropout with a block mask is refused before any launch.
-      if (!DROP && a.bm.mask)
-        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL, false, true>), grid, dim3(256), 0, s, a);
+      if (a.bm.mask)
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL, DROP, true>), grid, dim3(256), 0, s, a);
       else
         hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL, DROP, false>), grid, dim3(256), 0, s, a);
     } else {
@@ -1411,8 +1414,8 @@ static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
     constexpr int NW = CAUSAL && D == 128 ? 4 : 8;
     using C = Dq16<D, NW>;
     dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
-    if (!DROP && a.bm.mask)
-      hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL, NW, false, true>), grid, dim3(C::NT), 0, s, a);
+    if (a.bm.mask)
+      hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL, NW, DROP, true>), grid, dim3(C::NT), 0, s, a);
     else
       hipLaunchKernelGGL((bwd_dq16_kernel<T, D, CAUSAL, NW, DROP, false>), grid, dim3(C::NT), 0, s, a);
   } else {

@@ -325,13 +325,21 @@ __device__ inline int xcd_work_index() {
 // Tile rank (position in its head's range) and head of this workgroup, for a
 // grid of nt tiles per head.  Without HEAVY_FIRST: xcd_work_index order.  With
 // it (causal launches, whose tiles differ in cost by rank): each XCD still
-// takes a contiguous range of heads, but walks their tiles rank-major, rank 0
-// (the heaviest) of every head first, so that the last workgroups it starts
-// are the shortest.  Inside an XCD, workgroups go to its shader engines in
-// turn (measured: the i-th one of an XCD lands on engine i mod 4 whatever the
-// engines' load), so within a rank the heads are rotated by the rank: each
-// engine then gets every head's tiles in turn instead of a fixed quarter of
-// the heads, which matters when heads differ in length (packed batches).
+// takes a contiguous range of heads, and walks them in groups of up to
+// kHeavyGroup heads, each group rank-major, rank 0 (the heaviest) of every
+// head of the group first, so that the shortest workgroups come last in each
+// group and fill the gaps of the next.  A group rather than all of the XCD's
+// heads: the workgroups that run together then stream the K/V (or Q/dO) tiles
+// of only a few heads, which stay in the XCD's L2 (walking all 16 heads of an
+// XCD at once made the causal kernels fetch 5-6x their algorithmic bytes;
+// groups of 4 measured 4-6 % faster than 16 or 8 on B4 H32 N4096, and than 1
+// or 2).  Inside an XCD, workgroups go to its shader engines in turn
+// (measured: the i-th one of an XCD lands on engine i mod 4 whatever the
+// engines' load), so within a rank the heads of a group are rotated by the
+// rank: each engine then gets every head's tiles in turn instead of a fixed
+// share of the heads, which matters when heads differ in length (packed
+// batches).
+constexpr int kHeavyGroup = 4;
 template <bool HEAVY_FIRST>
 __device__ inline void work_item(int nt, int& rank, int& head) {
   const int nwork = gridDim.x * gridDim.y * gridDim.z;
@@ -339,8 +347,13 @@ __device__ inline void work_item(int nt, int& rank, int& head) {
   if (HEAVY_FIRST && (nheads & 7) == 0) {
     const int id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const int hpx = nheads >> 3, li = id >> 3;
-    rank = li / hpx;
-    head = (id & 7) * hpx + (li + rank) % hpx;
+    const int gs = hpx < kHeavyGroup ? hpx : kHeavyGroup;
+    const int grp = li / (gs * nt), within = li - grp * (gs * nt);
+    // The last group of an XCD holds fewer heads when gs does not divide hpx;
+    // within a group of gn heads, `within` runs over gn nt (rank, head) pairs.
+    const int gn = min(gs, hpx - grp * gs);
+    rank = within / gn;
+    head = (id & 7) * hpx + grp * gs + (within + rank) % gn;
   } else {
     const int lin = xcd_work_index();
     head = lin / nt;
@@ -443,12 +456,25 @@ __device__ inline i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // SALU write of M0 that the compiler places just before the copy, and five
 // after any VALU write of an SGPR the copy reads (v_readlane of a spilled
 // descriptor, v_readfirstlane).  The second is not paid on every copy: the
-// compiler rarely puts such a write there, and a test of the built library
-// checks every copy for it (a descriptor reloaded right before a copy gave a
-// garbage base address and a memory fault).
-template <bool HALF>
+// compiler rarely puts such a write there, and the build checks every copy of
+// the linked library for it (a descriptor reloaded right before a copy gave a
+// garbage base address and a memory fault).  SAFE pays it (s_nop 4, five wait
+// states), for instances whose register pressure makes the compiler spill
+// copy descriptors to VGPR lanes.
+template <bool HALF, bool SAFE = false>
 __device__ inline void copy_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  if constexpr (HALF) {
+  if constexpr (HALF && SAFE) {
+    uint64_t saved;
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b64 %0, exec\n\t"
+        "s_mov_b32 exec_hi, 0\n\t"
+        "buffer_load_dword %1, %2, %3 offen lds\n\t"
+        "s_mov_b64 exec, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
+        : "memory");
+  } else if constexpr (HALF) {
     uint64_t saved;
     asm volatile(
         "s_nop 0\n\t"
@@ -459,6 +485,10 @@ __device__ inline void copy_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t so
         : "=&s"(saved)
         : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
         : "memory");
+  } else if constexpr (SAFE) {
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+                 "{m0}"(lds)
+                 : "memory");
   } else {
     asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
                  "{m0}"(lds)
@@ -469,12 +499,18 @@ __device__ inline void copy_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t so
 // Copy 16 bytes per lane from a buffer straight into LDS: lane i reads bytes
 // soff + voff_i .. + 15 of the range of rsrc and they land at LDS byte address
 // lds + 16 i, so one copy fills 1 KB of LDS.  Range checking, waits, the
-// instruction offset and the leading wait state as for copy_to_lds.  Expects
-// every lane active.
+// instruction offset and the leading wait states (SAFE) as for copy_to_lds.
+// Expects every lane active.
+template <bool SAFE = false>
 __device__ inline void copy16_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
-               "{m0}"(lds)
-               : "memory");
+  if constexpr (SAFE)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+                 "s"(soff), "{m0}"(lds)
+                 : "memory");
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc),
+                 "s"(soff), "{m0}"(lds)
+                 : "memory");
 }
 
 // ------------------------------------------------- tile layouts of the 16-bit kernels

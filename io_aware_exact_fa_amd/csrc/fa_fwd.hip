@@ -731,6 +731,13 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   // the triangle better; without it one 256-row workgroup per CU copies half
   // as much.
   const bool drop = a.drop.keep_t < 65536;
+  if constexpr (sizeof(T) == 2 && D == 128 && !CAUSAL) {
+    // Without the causal mask and dropout, and with enough key tiles per
+    // workgroup (measured: 2 % faster at N = 8192, 2 % slower at N = 1024):
+    // 64 query rows per wave.
+    if (!drop && a.N >= 2048)
+      return launch_fwd64(std::is_same<T, __bf16>::value ? Dt::bf16 : Dt::f16, a, s);
+  }
   if constexpr (sizeof(T) == 2 && D == 128) {
     constexpr int NW = CAUSAL ? 4 : 8;
     using C = Fwd16<D, NW>;
@@ -742,7 +749,9 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   } else {
     using C = FwdTile<T, D>;
     dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
-    if (drop)   // dropout with a block mask is refused before any launch
+    if (drop && a.bm.mask)
+      hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, true, true>), grid, dim3(C::NT), 0, s, a);
+    else if (drop)
       hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, true, false>), grid, dim3(C::NT), 0, s, a);
     else if (a.bm.mask)
       hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, false, true>), grid, dim3(C::NT), 0, s, a);

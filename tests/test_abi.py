@@ -193,9 +193,6 @@ def test_ex_rejects():
         assert fwd(fa.attn(**good, window=window)) == E
         assert bwd(fa.attn(**good, window=window)) == E
     assert fwd(fa.attn(**{**good, "H_kv": 3})) == E
-    # Dropout with a block mask has no kernel instance.
-    assert fwd(fa.attn(**good, dropout=(0.25, 1, 0), block_mask=P)) == fa.FA_ERR_UNSUPPORTED
-    assert bwd(fa.attn(**good, dropout=(0.25, 1, 0), block_mask=P)) == fa.FA_ERR_UNSUPPORTED
     for heads in (0, 3, 9):   # a mask needs 1 or H (= 8) heads
         assert fwd(fa.attn(**good, block_mask=P, block_mask_heads=heads)) == E
     for pd in (-0.1, 1.5, float("nan")):
@@ -253,6 +250,11 @@ def test_valid_arguments_without_gpu_report_device_error():
     assert _bwd_varlen() == fa.FA_ERR_DEVICE
     p = fa.attn(1, 8, 2, 128, 64, 1, 0.1, fa.FA_F16, window=(16, 0))
     assert fa.fa_fwd_ex(p, P, P, P, P, P, None) == fa.FA_ERR_DEVICE
+    # Dropout together with a block mask is a valid description.
+    pdm = fa.attn(1, 8, 2, 128, 64, 1, 0.1, fa.FA_F16, dropout=(0.25, 1, 0), block_mask=P)
+    assert fa.fa_fwd_ex(pdm, P, P, P, P, P, None) == fa.FA_ERR_DEVICE
+    assert fa.fa_bwd_ex(pdm, P, P, P, P, P, P, P, P, P, 0x10000,
+                        fa.fa_bwd_workspace_size(1, 8, 128, 64), None) == fa.FA_ERR_DEVICE
     assert fa.fa_bwd_ex(p, P, P, P, P, P, P, P, P, P, 0x10000,
                         fa.fa_bwd_workspace_size(1, 8, 128, 64), None) == fa.FA_ERR_DEVICE
     nb = fa.fa_bwd_workspace_size(1, 1, 128, 64)

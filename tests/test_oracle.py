@@ -725,3 +725,67 @@ def test_block_mask_finite_differences():
             ap[which], am[which] = xp, xm
             fd = (loss(*ap) - loss(*am)) / (2 * hstep)
             assert abs(gg[idx] - fd) < 1e-6, ("qkv"[which], idx, gg[idx], fd)
+
+
+# ----------------------------------------------------------- dropout with a block mask
+
+
+def test_dropout_with_block_mask_reduces_to_each_alone():
+    """With both, the block mask hides keys before the softmax and dropout acts on
+    the resulting P: a full block mask gives dropout alone, no dropped element
+    (p = 0) gives the block mask alone, and the kept P of a block-masked row is
+    exactly the block-masked P with the dropped elements zeroed and the rest
+    scaled by 1 / keep."""
+    from oracle import philox
+    q, k, v, do = _win_inputs(n=300)
+    blocks = np.array([[1, 0, 1], [0, 1, 1]])
+    mask = philox.keep_mask(5, 300, 300, 0.3, 77, 2)
+    sc = 65536.0 / philox.keep_threshold(0.3)
+    drop = (mask, sc)
+    o_d, lse_d = oracle.forward_head(q, k, v, 0.6, False, drop=drop)
+    o_fd, lse_fd = oracle.forward_head(q, k, v, 0.6, False, drop=drop, blocks=np.ones((2, 3)))
+    np.testing.assert_array_equal(o_d, o_fd)
+    np.testing.assert_array_equal(lse_d, lse_fd)
+    o_b, lse_b = oracle.forward_head(q, k, v, 0.6, False, blocks=blocks)
+    keep_all = (np.ones((300, 300), dtype=bool), 1.0)
+    o_b0, _ = oracle.forward_head(q, k, v, 0.6, False, drop=keep_all, blocks=blocks)
+    np.testing.assert_allclose(o_b0, o_b, rtol=0, atol=1e-14)
+    # O of the combination = (block-masked P, then dropped and scaled) V, by hand.
+    s = 0.6 * q @ k.T
+    vis = oracle.block_visible(300, 300, blocks)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    p /= p.sum(axis=1, keepdims=True)
+    o_both, lse_both = oracle.forward_head(q, k, v, 0.6, False, drop=drop, blocks=blocks)
+    np.testing.assert_allclose(o_both, (np.where(mask, p * sc, 0.0)) @ v, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(lse_both, lse_b)
+
+
+def test_dropout_with_block_mask_finite_differences():
+    """Gradients with both a block mask and a (fixed) dropout mask match central
+    differences, at block edges, and D = rowsum(dO * O) holds."""
+    from oracle import philox
+    r = np.random.default_rng(6)
+    n = 260
+    q, k, v, do = (r.standard_normal((n, 2)) for _ in range(4))
+    blocks = np.array([[1, 0, 1], [0, 1, 1]])
+    drop = (philox.keep_mask(2, n, n, 0.25, 31, 4), 65536.0 / philox.keep_threshold(0.25))
+    scale, hstep = 0.9, 1e-6
+    g = oracle.backward_head(q, k, v, do, scale, True, drop=drop, blocks=blocks)
+    o, _ = oracle.forward_head(q, k, v, scale, True, drop=drop, blocks=blocks)
+    np.testing.assert_allclose(g["D"], (do * o).sum(axis=1), atol=1e-12)
+
+    def loss(qq, kk, vv):
+        return float((oracle.forward_head(qq, kk, vv, scale, True, drop=drop, blocks=blocks)[0]
+                      * do).sum())
+
+    for which, (x, gg) in enumerate(zip((q, k, v), (g["dq"], g["dk"], g["dv"]))):
+        for idx in [(i, c) for i in (0, 5, 127, 128, 200, 255, 256, 259) for c in range(2)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += hstep
+            xm[idx] -= hstep
+            ap, am = [q, k, v], [q, k, v]
+            ap[which], am[which] = xp, xm
+            fd = (loss(*ap) - loss(*am)) / (2 * hstep)
+            assert abs(gg[idx] - fd) < 1e-6, ("qkv"[which], idx, gg[idx], fd)

@@ -17,7 +17,7 @@ import torch
 import oracle
 import workloads
 from tests import pins
-from tests.tolerances import TOL
+from tests.tolerances import TOL, o_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -433,3 +433,46 @@ def test_plain_entry_points_by_name(fa, dtype):
         if name != "dq":
             assert torch.equal(a, c), f"{name}: the one-pass kernel differs"
     assert same_but_summation_order(g3[0], g1[0], dtype)
+
+
+# ------------------------------------------------------------------ the 64-row forward
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", ["plain", "window", "gqa-blocks", "negative-scale", "peaked"])
+def test_long_rows_forward_kernel(fa, dtype, case):
+    """Without the causal mask and dropout, at N >= 2048, the forward runs 64 query
+    rows per wave (its own kernel).  N = 2085: eight full 256-row workgroups and a
+    ragged ninth, a ragged last key tile; every element of every head against the
+    oracle, with a window (both edges masked), grouped K/V heads with a block
+    mask, a negative scale, and peaked scores (row maxima that keep growing,
+    so the accumulators are rescaled)."""
+    n = 2085
+    qk_std = 3.0 if case == "peaked" else 1.0
+    H, Hkv = (4, 2) if case == "gqa-blocks" else (2, 2)
+    w = workloads.Workload(f"rows64-{case}-{dtype}", 1, H, n, 128, dtype, False, 191 + len(case),
+                           qk_std=qk_std, H_kv=Hkv)
+    inp = workloads.make_inputs(w)
+    say(f"case {w.name}")
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    scale = -w.scale if case == "negative-scale" else w.scale
+    window = (300, 100) if case == "window" else None
+    bm = None
+    if case == "gqa-blocks":
+        g = torch.Generator(device="cpu").manual_seed(7)
+        bm = (torch.rand((H, -(-n // 256), -(-n // 128)), generator=g) < 0.6).to(torch.uint8)
+        bm[0, -1, :] = 0   # head 0: the last query block sees nothing
+    o, lse = fa.forward(q, k, v, False, scale, window=window,
+                        block_mask=bm.to(dev) if bm is not None else None)
+    torch.cuda.synchronize()
+    qh, kh, vh = (f64(inp[x]) for x in ("q", "k", "v"))
+    o_ref, lse_ref = oracle.forward_gqa(qh, kh, vh, scale, False, window=window,
+                                        block_mask=bm.numpy() if bm is not None else None)
+    fin = np.isfinite(lse_ref)
+    lg = f64(lse)
+    assert np.array_equal(np.isneginf(lg), ~fin)
+    err_o = float(np.max(np.abs(f64(o) - o_ref)))
+    err_l = float(np.max(np.abs(lg[fin] - lse_ref[fin])))
+    say(f"  O max-abs {err_o:.3e} (bound {o_bound(dtype, o_ref):.1e}) LSE {err_l:.3e}")
+    assert err_o <= o_bound(dtype, o_ref) and err_l <= TOL[dtype]["lse"]

@@ -1,8 +1,8 @@
 """Parity of block-sparse attention (fa_fwd_ex / fa_bwd_ex with a block mask) with
 the fp64 oracle on the GPU, through the C ABI: random masks per head with empty
 query blocks, all dtypes and head sizes, causal and not, packed batches, the
-equivalence of a block-diagonal mask with a packed batch, and the full-size
-workload."""
+equivalence of a block-diagonal mask with a packed batch, block masks together
+with dropout, and the full-size workload."""
 import numpy as np
 import pytest
 import torch
@@ -166,3 +166,37 @@ def test_large_block_sparse_sampled(fa, w):
         errs = [rel_err(f64(out[n][b, h]), g[n]) for n in ("dq", "dk", "dv")]
         say(f"  b{b} h{h}: O {err_o:.3e} LSE {err_l:.3e} " + " ".join(f"{e:.3e}" for e in errs))
         assert err_o <= tol["o"] and err_l <= tol["lse"] and max(errs) <= tol["grad"]
+
+
+@pytest.mark.parametrize("dtype,d,causal", list(cases()))
+def test_block_sparse_with_dropout(fa, dtype, d, causal):
+    """A block mask per head (one head with an empty query block) together with
+    dropout p = 0.25: the mask hides keys before the softmax, dropout acts on the
+    kept P; every element against the oracle.  N = 300, 4 query heads over 2 K/V
+    heads, two batch entries."""
+    from tests.test_parity_dropout import o_tol, p32
+    w = workloads.Workload(f"bsdrop-{dtype}-d{d}", 2, 4, 300, d, dtype, causal, 171 + d, H_kv=2)
+    inp = workloads.make_inputs(w)
+    bm = random_mask(4, 300, 0.6, 181 + d)
+    drop = (p32(0.25), 0x5EED_0000_4242 + d, 5)
+    say(f"case {w.name} causal={causal}")
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+    bmd = bm.to(DEV)
+    o, lse = fa.forward(q, k, v, causal, w.scale, dropout=drop, block_mask=bmd)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal, w.scale, dropout=drop, block_mask=bmd)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    qh, kh, vh, doh = (f64(inp[n]) for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = oracle.forward_gqa(qh, kh, vh, w.scale, causal, dropout=drop,
+                                        block_mask=bm.numpy())
+    g_ref = oracle.backward_gqa(qh, kh, vh, doh, w.scale, causal, dropout=drop,
+                                block_mask=bm.numpy())
+    fin = np.isfinite(lse_ref)
+    lg = f64(lse)
+    assert np.array_equal(np.isneginf(lg), ~fin), "empty rows must have LSE = -inf"
+    err_o = float(np.max(np.abs(f64(o) - o_ref)))
+    err_l = float(np.max(np.abs(lg[fin] - lse_ref[fin])))
+    errs = [rel_err(f64(x), r) for x, r in zip((dq, dk, dv), g_ref)]
+    say(f"  O {err_o:.3e} (tol {o_tol(dtype, o_ref):.1e}) LSE {err_l:.3e} grads "
+        + " ".join(f"{e:.3e}" for e in errs))
+    assert err_o <= o_tol(dtype, o_ref) and err_l <= tol["lse"] and max(errs) <= tol["grad"]

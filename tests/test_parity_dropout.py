@@ -3,8 +3,6 @@ on the GPU, through the C ABI.  The oracle builds the keep mask from its own
 Philox4x32-10; besides the tolerance checks, two tests read every keep bit off
 the outputs (the forward's and the dK/dV kernel's, which generate the mask in
 different lane layouts) and require them to equal the oracle's bit for bit."""
-import math
-
 import numpy as np
 import pytest
 import torch
@@ -13,6 +11,7 @@ import oracle
 import workloads
 from oracle import philox
 from tests.test_parity import TOL, f64, rel_err, say
+from tests.tolerances import o_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -33,13 +32,9 @@ def p32(p):
 
 
 def o_tol(dtype, o_ref):
-    """The O bound scaled to the binade of the largest output.  The plain bounds hold
-    for |O| < 4 (a convex combination of N(0,1) rows); dropout scales the kept
-    weights by 1 / keep, so |O| can reach the next binades, where the final
-    rounding of O to the storage type alone is proportionally larger (a half ulp
-    of bf16 at |O| in [4, 8) is 2^-6 = 0.0156)."""
-    m = float(np.nanmax(np.abs(o_ref)))
-    return TOL[dtype]["o"] * max(1.0, 2.0 ** math.ceil(math.log2(max(m, 1e-30))) / 4.0)
+    """The O bound scaled to the binade of the largest output (dropout's 1 / keep
+    scaling lets |O| reach past 4; tests/tolerances.py)."""
+    return o_bound(dtype, o_ref)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
