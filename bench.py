@@ -14,8 +14,9 @@ Prints ONE JSON line.  Besides the step throughput it reports:
     the workload's dtype, with HBM traffic from committed rocprofv3 counter
     runs when they were taken on the current kernel source, and "per_kernel"
     entries for every kernel of the step (algorithmic and executed FLOPs);
-  * the shader clock sampled during the timed steps and the peak at that
-    clock, and the run's conditions (device, ROCm, compiler, torch versions);
+  * the shader clock under the same load (sampled while the step runs again
+    after the timed region) and the peak at that clock, and the run's
+    conditions (device, ROCm, compiler, torch versions);
   * "secondary": with the default workload, the causal bf16 workload
     (B=4 H=32 N=4096 d=128), the other one the throughput target is stated
     on, timed the same way in the same process;
@@ -239,6 +240,27 @@ class ClockSampler:
                 "source": "amdsmi gpu metrics, mean of current_gfxclks over the XCCs"}
 
 
+def sustained_clock(step, seconds: float = 1.5) -> dict:
+    """The shader clock under the step's load: after the timed steps (outside the
+    timed region), the same step runs again for `seconds` while ClockSampler
+    reads the metrics table, whose readings lag the load by a few hundred ms;
+    the second half of the samples is reported."""
+    import torch
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(5):
+                step()
+            torch.cuda.synchronize()
+    s = clock.summary()
+    if clock.samples:
+        t = sorted(clock.samples[len(clock.samples) // 2:])
+        s.update(sclk_mhz=round(t[len(t) // 2], 1), sclk_mhz_min=round(t[0], 1),
+                 sclk_mhz_max=round(t[-1], 1), samples=len(t),
+                 window_s=seconds / 2)
+    return s
+
+
 def run_conditions(dev_index: int = 0) -> dict:
     """Versions and device of the run (the conditions a throughput figure needs)."""
     import platform
@@ -336,19 +358,19 @@ def time_dense(args, w, fa, steps=None):
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for i in range(steps):
-            step(events[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    clock = sustained_clock(step)
     ms = lambda a, b_: sum(e[a].elapsed_time(e[b_]) for e in events) / steps
     if one_pass:
         kms = {"fwd": ms(0, 1), "pre": ms(1, 2), "dkdvq": ms(2, 3), "dqfin": ms(3, 4)}
     else:
         kms = {"fwd": ms(0, 1), "pre": ms(1, 2), "dkdv": ms(2, 3), "dq": ms(3, 4)}
     return {"w": w, "shape": (B, H, Hkv, N, d), "steps": steps, "wall": wall, "events": events,
-            "kernel_ms": kms, "clock": clock.summary(), "inp": inp,
+            "kernel_ms": kms, "clock": clock, "inp": inp,
             "out": {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}}
 
 
@@ -416,7 +438,7 @@ def summary(res, peak):
         "step_pct_of_peak": round(100 * value / peak, 2),
         "peak_tflops": peak,
         "sclk": res["clock"],
-        # The same peak at the shader clock sampled during the timed steps.
+        # The same peak at the shader clock measured under the same load.
         "peak_tflops_at_sclk": round(peak * clk / 2400.0, 1) if clk else None,
         "fwd_pct_of_peak_at_sclk": round(100 * fwd_tf / (peak * clk / 2400.0), 2) if clk else None,
         "bwd_pct_of_peak_at_sclk": round(100 * bwd_tf / (peak * clk / 2400.0), 2) if clk else None,
