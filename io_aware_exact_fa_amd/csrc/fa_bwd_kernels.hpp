@@ -597,16 +597,16 @@ struct Dq16 {
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;             // queries per workgroup
   static constexpr int BC = 64;                  // keys per tile
-  static constexpr int PB = TileLds<D>::PB;      // bytes per row (4-row multiples)
+  static constexpr int PB = TileLds<D>::PB;      // bytes per row (multiples of RPC rows)
   static constexpr int TILE = BC * PB;
   static constexpr int BUF = 2 * TILE;           // K, V
   static constexpr int NB = NW == 8 ? 3 : 2;
-  static constexpr bool HALF = D == 64;
+  static constexpr int RPC = TileLds<D>::ROWS_PER_COPY;
   static constexpr int NKS = D / 16;
   static constexpr int NS = 2 * NKS;             // S/dP MFMAs per 32-key block
   static constexpr int NQ = 2 * (D / 32);        // dQ MFMAs per 32-key block
   static constexpr int NM = 2 * NS + 2 * NQ;     // MFMAs per tile
-  static constexpr int NLD = 2 * BC / NW / TileLds<D>::ROWS_PER_COPY;   // copies per wave per tile
+  static constexpr int NLD = 2 * BC / NW / RPC;  // copies per wave per tile
 };
 
 // BSPARSE as for the dK/dV kernel: the tile queue only in the block-sparse
@@ -614,7 +614,7 @@ struct Dq16 {
 template <typename T, int D, bool CAUSAL, int NW, bool DROP, bool BSPARSE>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   using C = Dq16<D, NW>;
-  static_assert(NW == 8 || (NW == 4 && D == 128), "4-wave dQ workgroups copy 4-row groups");
+  static_assert(NW == 8 || (NW == 4 && D == 128), "4-wave dQ workgroups are built for d = 128");
   using M = Mfma<T>;
   using frag = typename M::frag;
   __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF];
@@ -678,26 +678,19 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const TileLds<D> lay(lane);
-  // Copy op j of key tile kt into buffer b.  NW = 8: waves 0-3 copy K, 4-7
-  // copy V, wave w rows 16 (w & 3) + 4 j .. + 3 (d = 128: one 4-row group per
-  // copy) or row 16 (w & 3) + j (d = 64).  NW = 4: wave w copies groups
-  // 4 w + j of K (j < 4) and 4 w + j - 4 of V.  Rows past N read as zero (and
-  // are masked through khi).
+  // Copy op j of key tile kt into buffer b, one group of RPC rows (4 at
+  // d = 128, 8 at d = 64) starting at row r0.  NW = 8: waves 0-3 copy K, 4-7
+  // copy V, wave w rows 16 (w & 3) + RPC j ..  NW = 4: wave w copies rows
+  // 16 w + 4 j .. of K (j < 4) and 16 w + 4 (j - 4) .. of V.  Rows past N read
+  // as zero (and are masked through khi).
   const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
   const i32x4 rsv = buffer_rsrc(V, (uint32_t)N * (2 * D));
   auto copy_op = [&](int b, int kt, int j) {
     const int mat = NW == 8 ? w >> 2 : j >> 2;
     const i32x4& rsrc = mat ? rsv : rsk;
     const uint32_t base = lds_address(smem) + b * C::BUF + mat * C::TILE;
-    if constexpr (D == 128) {
-      const int q = NW == 8 ? 4 * (w & 3) + j : 4 * w + (j & 3);
-      copy16_to_lds(rsrc, lay.c[(q >> 1) & 1], (uint32_t)(kt * C::BC + 4 * q) * (2 * D),
-                    base + q * 4 * C::PB);
-    } else {
-      const int rr = 16 * (w & 3) + j;
-      copy_to_lds<C::HALF>(rsrc, lay.c[(j >> 3) & 1], (uint32_t)(kt * C::BC + rr) * (2 * D),
-                           base + rr * C::PB);
-    }
+    const int r0 = NW == 8 ? 16 * (w & 3) + C::RPC * j : 16 * w + C::RPC * (j & 3);
+    copy16_to_lds(rsrc, lay.c[(r0 >> 3) & 1], (uint32_t)(kt * C::BC + r0) * (2 * D), base + r0 * C::PB);
   };
 
   // Prologue: queue tiles t0 and t1 (NW = 8) or t0 (NW = 4).  The copies go
@@ -877,17 +870,17 @@ template <int D>
 struct Dkv16 {
   static constexpr int BKC = 128;                // keys per workgroup (32 per wave)
   static constexpr int BQ = 64;                  // queries per tile
-  static constexpr int PB = TileLds<D>::PB;      // bytes per row (4-row multiples)
+  static constexpr int PB = TileLds<D>::PB;      // bytes per row (multiples of RPC rows)
   static constexpr int TILE = BQ * PB;           // bytes of one Q or dO tile
   static constexpr int BUF = 2 * TILE + 2 * BQ * 4;   // Q, dO, L2, D
   static constexpr int NB = 3;
-  static constexpr bool HALF = D == 64;          // a row (128 bytes) is copied by lanes 0..31
+  static constexpr int RPC = TileLds<D>::ROWS_PER_COPY;   // rows per copy
   static constexpr int NKS = D / 16;             // k steps of S and dP
   static constexpr int NS = 2 * NKS;             // S/dP MFMAs per 32-query block
   static constexpr int NVB = 2 * (D / 32);       // dV/dK MFMAs per 16 queries
   static constexpr int NV = 2 * NVB;             // dV/dK MFMAs per block
   static constexpr int NM = 2 * NS + 2 * NV;     // MFMAs per tile
-  static constexpr int NLD = 2 * BQ / 4 / TileLds<D>::ROWS_PER_COPY + 2;   // copies per wave per tile: Q, dO; L2, D
+  static constexpr int NLD = 2 * BQ / 4 / RPC + 2;   // copies per wave per tile: Q, dO; L2, D
 };
 
 // BSPARSE: a block mask is given (the tile queue skips its dropped blocks);
@@ -916,7 +909,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // (query, key) elements, 2 KB, after the tile buffers.
   constexpr int DSCR = 2048;
   // DQ: two dS^T buffers (128 keys x 64 queries, the 64-column tile layout).
-  using LayS = TileLds<64>;
+  using LayS = RowLds64;
   constexpr int DST = C::BKC * LayS::PB;
   constexpr int DSB = C::NB * C::BUF;   // first dS^T buffer
   __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF + (DROP ? 8 * DSCR : 0) +
@@ -979,8 +972,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const TileLds<D> lay(lane);
   // Copy op j of tile qt into buffer b: j < NROW: rows of Q (first half of
-  // the ops) or dO, wave w taking rows 16 w .. 16 w + 15 (d = 128: 4-row groups
-  // 4 w + jj; d = 64: row 16 w + jj); j = NROW, NROW + 1: the tile's L2 and
+  // the ops) or dO, wave w taking rows 16 w .. 16 w + 15 in groups of RPC rows
+  // (16 w + RPC jj ..); j = NROW, NROW + 1: the tile's L2 and
   // D, lane p holding query row_pi(p) of the tile (the order of a lane half's
   // P elements).  Every wave copies the same L2 and D.  Rows past N read as
   // zero (the padding rows of L2 are +inf, so their P is 0; past Np all of Q,
@@ -1007,19 +1000,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   constexpr bool SAFE = DROP;
   auto copy_op = [&](const Bases& x, int j) {
     if (j < NROW) {
-      const int mat = j / (NROW / 2), jj = j % (NROW / 2);
-      if constexpr (D == 128) {
-        // Group 4 w + jj: rows 16 w + 4 jj .. + 3.
-        copy16_to_lds<SAFE>(mat ? rsg : rsq, lay.c[(jj >> 1) & 1], x.row_glb + 4 * jj * (2 * D),
-                            x.row_lds + mat * C::TILE + 4 * jj * C::PB);
-      } else {
-        // Row 16 w + jj.
-        copy_to_lds<C::HALF, SAFE>(mat ? rsg : rsq, lay.c[(jj >> 3) & 1], x.row_glb + jj * (2 * D),
-                                   x.row_lds + mat * C::TILE + jj * C::PB);
-      }
+      const int mat = j / (NROW / 2), r = C::RPC * (j % (NROW / 2));
+      copy16_to_lds<SAFE>(mat ? rsg : rsq, lay.c[(r >> 3) & 1], x.row_glb + r * (2 * D),
+                          x.row_lds + mat * C::TILE + r * C::PB);
     } else {
-      copy_to_lds<false, SAFE>(j == NROW ? rsl : rsd, 4 * row_pi(lane), x.ld_glb,
-                               x.buf_lds + 2 * C::TILE + (j - NROW) * C::BQ * 4);
+      copy_to_lds<SAFE>(j == NROW ? rsl : rsd, 4 * row_pi(lane), x.ld_glb,
+                        x.buf_lds + 2 * C::TILE + (j - NROW) * C::BQ * 4);
     }
   };
 
@@ -1292,20 +1278,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     // reads of the same step give it.  Held in AGPRs for the whole kernel.
     const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
     const uint32_t kbuf = lds_address(smem) + 2 * C::BUF;
-    if constexpr (D == 128) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = 8 * w + j;   // 4-row group
-        copy16_to_lds(rsk, lay.c[(q >> 1) & 1], (uint32_t)(k0 + 4 * q) * (2 * D),
-                      kbuf + q * 4 * C::PB);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const int r = 32 * w + j;
-        copy_to_lds<C::HALF>(rsk, lay.c[(r >> 3) & 1], (uint32_t)(k0 + r) * (2 * D),
-                             kbuf + r * C::PB);
-      }
+    for (int j = 0; j < 32 / C::RPC; ++j) {
+      const int r = 32 * w + C::RPC * j;   // first row of the group
+      copy16_to_lds(rsk, lay.c[(r >> 3) & 1], (uint32_t)(k0 + r) * (2 * D), kbuf + r * C::PB);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();

@@ -444,8 +444,7 @@ __device__ inline i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // at byte soff + voff_i of the range of rsrc (soff wave-uniform, voff_i per
 // lane) and it lands at LDS byte address lds + 4 i (lds wave-uniform).  A dword
 // at or past the end of the range is not read and lands as zero, so rows past
-// the end of a matrix need no clamping.  With HALF, only lanes 0..31 copy (128
-// bytes).  Issued as inline assembly so that the compiler adds no waits of its
+// the end of a matrix need no clamping.  Issued as inline assembly so that the compiler adds no waits of its
 // own for it: the caller waits with s_waitcnt vmcnt before the data is read,
 // and before the barrier that hands it to the other waves.  The instruction
 // offset is left at zero: it would move the LDS address as well.  Expects every
@@ -461,31 +460,9 @@ __device__ inline i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // garbage base address and a memory fault).  SAFE pays it (s_nop 4, five wait
 // states), for instances whose register pressure makes the compiler spill
 // copy descriptors to VGPR lanes.
-template <bool HALF, bool SAFE = false>
+template <bool SAFE = false>
 __device__ inline void copy_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  if constexpr (HALF && SAFE) {
-    uint64_t saved;
-    asm volatile(
-        "s_nop 4\n\t"
-        "s_mov_b64 %0, exec\n\t"
-        "s_mov_b32 exec_hi, 0\n\t"
-        "buffer_load_dword %1, %2, %3 offen lds\n\t"
-        "s_mov_b64 exec, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
-        : "memory");
-  } else if constexpr (HALF) {
-    uint64_t saved;
-    asm volatile(
-        "s_nop 0\n\t"
-        "s_mov_b64 %0, exec\n\t"
-        "s_mov_b32 exec_hi, 0\n\t"
-        "buffer_load_dword %1, %2, %3 offen lds\n\t"
-        "s_mov_b64 exec, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds)
-        : "memory");
-  } else if constexpr (SAFE) {
+  if constexpr (SAFE) {
     asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
                  "{m0}"(lds)
                  : "memory");
@@ -521,34 +498,70 @@ __device__ inline void copy16_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t 
 // 16-byte chunk) and transposing reads (8 bytes per lane; a lane half reads
 // rows 2s + h, s = 0..3, of an 8-row step, 64 bytes each).  Both layouts below
 // keep every 16-lane quarter of an A read and every lane half of a
-// transposing read on distinct banks.  Offsets between rows that are a
-// multiple of 4 apart are (rows) * PB in both.
+// transposing read on distinct banks, and are filled one group of rows (1 KB,
+// 64 lanes x 16 bytes) per copy.  Offsets between rows that are a multiple of
+// ROWS_PER_COPY apart are (rows) * PB in both.
 //
-// d = 64: rows 160 bytes apart (128 + 32 of padding); 16-byte chunk c of row r
-// at chunk c ^ ((r >> 3) & 1).  Copied one row (32 lanes x 4 bytes) per copy.
+// d = 64: 8-row groups of 1 KB, dense (rows 128 bytes apart).  Row r = 8 g + x
+// sits at row slot slot(x, g & 1) = 2 x0 + (x1 ^ g0) + 4 x2 of its group, its
+// 16-byte chunk c at chunk c ^ x (x0..x2, g0: bits of x and g).  The rows of a
+// quarter-wave A read then cover bank groups 8 (x1 ^ g0) + (c ^ x) once each,
+// and so do the 4 rows x 4 chunks of a half-wave transposing read.
 // d = 128: 4-row groups of 1 KB (rows 256 bytes apart), groups 1152 bytes
 // apart; chunk c of row r at chunk c ^ swz(r), swz(r) = r0 | r3 << 1 | r1 << 2
-// (bits of r).  Copied one group (64 lanes x 16 bytes) per copy.
+// (bits of r).
 template <int D> struct TileLds;
 
 template <> struct TileLds<64> {
-  static constexpr int PB = 160;
-  static constexpr int ROWS_PER_COPY = 1;
-  // Lane offsets: A reads of k step ks at a + 32 ks; transposing reads of the
-  // 8-row step with bit 3 of its rows = rp, head-dim block db, at t[rp] + 64 db;
-  // row copies of rows with (r >> 3) & 1 = x from global byte offset c[x].
-  int a, t[2], c[2];
+  static constexpr int PB = 128;             // per row, for multiples of 8 rows
+  static constexpr int ROWS_PER_COPY = 8;
+  __device__ static constexpr int slot(int x, int g0) {
+    return 2 * (x & 1) + (((x >> 1) & 1) ^ g0) + 4 * (x >> 2);
+  }
+  // Byte address of chunk c of row r (from the start of the tile).
+  __device__ static constexpr int at(int r, int c) {
+    return (r >> 3) * 1024 + 128 * slot(r & 7, (r >> 3) & 1) + 16 * ((c ^ r) & 7);
+  }
+  // Lane offsets: A reads of k step ks at a[ks]; transposing reads of the
+  // 8-row step with bit 3 of its rows = rp at t[rp][db] (the caller adds the
+  // step's rows * PB); group copies of groups g with g & 1 = x from global byte
+  // offset c[x] (relative to the group's first row).
+  int a[4], t[2][2], c[2];
   __device__ TileLds(int lane) {
     const int col = lane & 31, h = lane >> 5;
     const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
-    a = row_pi(col) * PB + 16 * (h ^ ((col >> 3) & 1));
+    const int ra = row_pi(col);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = at(ra, 2 * k + h);
+#pragma unroll
+    for (int rp = 0; rp < 2; ++rp)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        t[rp][db] = at(2 * ts + h + 8 * rp, 4 * db + 2 * tg + (ta >> 1)) - 1024 * rp + 8 * (ta & 1);
+    // Lane i fills row slot i >> 3, chunk slot i & 7 of the group.
+    const int s = lane >> 3;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      t[x] = (2 * ts + h) * PB + 16 * ((2 * tg + (ta >> 1)) ^ x) + 8 * (ta & 1);
-      c[x] = 16 * ((lane >> 2) ^ x) + 4 * (lane & 3);
+      const int r = ((s >> 1) & 1) | (((s & 1) ^ x) << 1) | ((s >> 2) << 2);
+      c[x] = 128 * r + 16 * ((lane & 7) ^ r);
     }
   }
-  __device__ int A(int ks) const { return a + 32 * ks; }
+  __device__ int A(int ks) const { return a[ks]; }
+  __device__ int T(int rp, int db) const { return t[rp][db & 1]; }
+};
+
+// A 64-column tile written from registers rather than copied (the dS^T buffers
+// of the one-pass backward): rows 160 bytes apart (128 + 32 of padding), the
+// 16-byte chunk c of row r at chunk c ^ ((r >> 3) & 1); reads as in TileLds.
+struct RowLds64 {
+  static constexpr int PB = 160;
+  int t[2];
+  __device__ RowLds64(int lane) {
+    const int h = lane >> 5;
+    const int ts = (lane >> 2) & 3, ta = lane & 3, tg = (lane >> 4) & 1;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) t[x] = (2 * ts + h) * PB + 16 * ((2 * tg + (ta >> 1)) ^ x) + 8 * (ta & 1);
+  }
   __device__ int T(int rp, int db) const { return t[rp] + 64 * db; }
 };
 

@@ -397,7 +397,6 @@ struct Fwd16 {
   static constexpr int TILE = BC * PB;
   static constexpr int BUF = 2 * TILE;           // K, V
   static constexpr int NB = NW == 8 ? 4 : 2;     // K/V buffers
-  static constexpr bool HALF = D == 64;
   static constexpr int NKS = D / 16;
   static constexpr int NS = 2 * NKS;             // S MFMAs per tile (two 32-key blocks)
   static constexpr int NV = 4 * (D / 32);        // P~V MFMAs per tile
@@ -724,19 +723,20 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-  // d = 64 keeps the register-staged kernel: with two head-dim blocks the
-  // stream of fwd16_kernel has too few independent accumulators to hide the
-  // MFMA latency.
-  // Under the causal mask, 128 query rows per workgroup (two per CU) balance
-  // the triangle better; without it one 256-row workgroup per CU copies half
-  // as much.
+  // Under the causal mask at d = 128, 128 query rows per workgroup (two per
+  // CU) balance the triangle better; without it one 256-row workgroup per CU
+  // copies half as much.
   const bool drop = a.drop.keep_t < 65536;
+  [[maybe_unused]] constexpr Dt dt = std::is_same<T, __bf16>::value ? Dt::bf16 : Dt::f16;
+  if constexpr (sizeof(T) == 2 && D == 64) {
+    // d = 64 without dropout: 64 query rows per wave.
+    if (!drop) return launch_fwd64(dt, 64, CAUSAL, a, s);
+  }
   if constexpr (sizeof(T) == 2 && D == 128 && !CAUSAL) {
     // Without the causal mask and dropout, and with enough key tiles per
     // workgroup (measured: 2 % faster at N = 8192, 2 % slower at N = 1024):
     // 64 query rows per wave.
-    if (!drop && a.N >= 2048)
-      return launch_fwd64(std::is_same<T, __bf16>::value ? Dt::bf16 : Dt::f16, a, s);
+    if (!drop && a.N >= 2048) return launch_fwd64(dt, 128, false, a, s);
   }
   if constexpr (sizeof(T) == 2 && D == 128) {
     constexpr int NW = CAUSAL ? 4 : 8;

@@ -1,5 +1,5 @@
-// Forward attention for 16-bit types at d = 128 without the causal mask:
-// 64 query rows per wave, one wave per SIMD.
+// Forward attention for 16-bit types: 64 query rows per wave, one wave per
+// SIMD (d = 64 and 128).
 //
 // One workgroup of 4 waves computes 256 query rows of one (batch, head); wave
 // w owns rows q0 + 64 w .. + 63 as two 32-row blocks A and B.  Per key tile of
@@ -7,7 +7,7 @@
 // fragment the S^T = K Q^T products of A and B, a V^T fragment (transposing
 // read) their O^T += V^T P~^T products.  That halves the LDS reads per MFMA of
 // a 32-row wave, and with one wave per SIMD the instruction stream is this
-// wave's alone.  The O^T accumulators of both blocks (128 registers) live in
+// wave's alone.  The O^T accumulators of both blocks (4 D registers) live in
 // AGPRs, the rest (S^T, read by the softmax) in VGPRs: the P~V MFMAs are
 // issued as inline assembly with AGPR accumulators (mma_agpr below), the S^T
 // MFMAs by the compiler in their VGPR form.
@@ -28,8 +28,9 @@
 
 namespace fa {
 
+template <int D_>
 struct Fwd64 {
-  static constexpr int D = 128;
+  static constexpr int D = D_;
   static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 64 * NW;             // query rows per workgroup
@@ -39,10 +40,12 @@ struct Fwd64 {
   static constexpr int BUF = 2 * TILE;           // K, V
   static constexpr int NB = 4;
   static constexpr int NKS = D / 16;             // k steps of one 32 x 32 block of S^T
+  static constexpr int NDB = D / 32;             // head-dim blocks of O^T
   static constexpr int NS = 2 * 2 * NKS;         // S^T MFMAs per tile: 2 key blocks x 2 query blocks
-  static constexpr int NV = 2 * 2 * 4 * 2;       // P~V MFMAs: key block x step x head-dim block x query block
+  static constexpr int NV = 2 * 2 * NDB * 2;     // P~V MFMAs: key block x step x head-dim block x query block
   static constexpr int NM = NS + NV;
-  static constexpr int NLD = 2 * BC / NW / TileLds<D>::ROWS_PER_COPY;   // copies per wave per tile
+  static constexpr int RPC = TileLds<D>::ROWS_PER_COPY;
+  static constexpr int NLD = 2 * BC / NW / RPC;  // copies per wave per tile
   static constexpr int NA = NS / 2;              // slots of the row max
 };
 
@@ -70,11 +73,14 @@ __device__ inline void agpr_settle(f32x16 (&acc)[2][4]) {
                : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
                  "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
 }
+__device__ inline void agpr_settle(f32x16 (&acc)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[1][0]), "+a"(acc[1][1]));
+}
 
-template <typename T>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
-  using C = Fwd64;
-  constexpr int D = C::D;
+  using C = Fwd64<D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
   __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF];
@@ -84,14 +90,15 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntq = gridDim.x;
   int rank, hd;
-  work_item<false>(ntq, rank, hd);
+  work_item<CAUSAL>(ntq, rank, hd);
   hd = packed_head(a, hd, a.H);
   const size_t head = (size_t)hd;
   const Span sp = span_of(a, hd);
   const int N = sp.n;
   const int ntq_own = (N + C::BR - 1) / C::BR;
-  const int qt = rank;
-  if (qt >= ntq_own) return;   // a tile past the end of a shorter sequence
+  // Under the causal mask the last query tiles see the most keys and come first.
+  const int qt = CAUSAL ? ntq_own - 1 - rank : rank;
+  if (qt < 0 || qt >= ntq_own) return;   // a tile past the end of a shorter sequence
   const int q0 = qt * C::BR;
   const T* Q = static_cast<const T*>(a.q) + sp.q * D;
   const T* K = static_cast<const T*>(a.k) + sp.kv * D;
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) asm volatile("" : "+a"(qf[qb][ks]));
-  const int wr = a.wr;
+  const int wr = CAUSAL ? min(a.wr, 0) : a.wr;
   int khi[2], klo[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -135,23 +142,24 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
   const TileLds<D> lay(lane);
   const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
   const i32x4 rsv = buffer_rsrc(V, (uint32_t)N * (2 * D));
-  // Copy k (< NLD) of key tile t into buffer b: K groups 4 w .. + 3 (k < 4),
-  // then V groups 4 w .. + 3.
+  // Copy k (< NLD) of key tile t into buffer b: the row groups of K that
+  // start at 16 w + RPC j (k = j < NLD / 2), then those of V.
   auto copy_op = [&](int b, int t, int k) {
-    const int mat = k >> 2, q = 4 * w + (k & 3);
+    const int mat = k / (C::NLD / 2), r = 16 * w + C::RPC * (k % (C::NLD / 2));
     const uint32_t base = lds_address(smem) + b * C::BUF + mat * C::TILE;
-    copy16_to_lds(mat ? rsv : rsk, lay.c[(q >> 1) & 1], (uint32_t)(t * C::BC + 4 * q) * (2 * D),
-                  base + q * 4 * C::PB);
+    copy16_to_lds(mat ? rsv : rsk, lay.c[(r >> 3) & 1], (uint32_t)(t * C::BC + r) * (2 * D),
+                  base + r * C::PB);
   };
   // Operand of MFMA pair p (two MFMAs, query blocks A and B): p < NS / 2: K
   // fragment of k step p / 2, key block p % 2; else V^T fragment of pair
-  // pr = p - NS / 2: key block pr / 8, 16-key step (pr / 4) % 2, head-dim block pr % 4.
+  // pr = p - NS / 2: key block pr / (2 NDB), 16-key step (pr / NDB) % 2,
+  // head-dim block pr % NDB.
   auto opS = [&](int kboff, int p) -> frag {
     const int off = kboff + (p & 1) * 32 * C::PB;
     return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + lay.A(p >> 1) + off));
   };
   auto opV = [&](int vboff, int pr) -> frag {
-    const int kb = pr >> 3, u = (pr >> 2) & 1, db = pr & 3;
+    const int kb = pr / (2 * C::NDB), u = (pr / C::NDB) & 1, db = pr % C::NDB;
     s16x4 v[2];
 #pragma unroll
     for (int rp = 0; rp < 2; ++rp) {
@@ -199,13 +207,14 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
   // the exponentials of the four P~ fragments of each query block in the
   // order the P~V MFMAs use them, each group of 16 (one fragment of both
   // query blocks) spread evenly up to the slot before its first use:
-  // fragment (kb, u) first feeds slot NS + 16 kb + 8 u.
+  // fragment f = (kb, u) = 2 kb + u first feeds slot NS + 2 NDB f.
+  constexpr int NF = 2 * C::NDB;                  // P~V slots per fragment
   constexpr auto max_slot = [](int e) { return (e * NA) / 64; };
   constexpr auto exp_slot = [](int qb, int kb, int i) {
     const int f = 2 * kb + i / 8;                 // fragment (kb, u), in order of use
     const int j = 8 * qb + (i % 8);               // 0..15 within the group
-    const int first = NA + 1 + (f * (NM - 8 - NA - 1)) / 4;   // groups overlap evenly
-    const int last = NS + 8 * f - 1;              // the slot before the first use
+    const int first = NA + 1 + (f * (NM - NF - NA - 1)) / 4;   // groups overlap evenly
+    const int last = NS + NF * f - 1;             // the slot before the first use
     return first + (j * (last - first)) / 16;
   };
   constexpr auto copy_slot = [](int k) { return NS + (k * (NM - NS)) / C::NLD; };
@@ -242,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
       if constexpr (m < NS) {
         sn[qb][p & 1] = M::mma(x, qf[qb][p >> 1], sn[qb][p & 1]);
       } else {
-        constexpr int pr = p - NS / 2, kb = pr >> 3, u = (pr >> 2) & 1, db = pr & 3;
+        constexpr int pr = p - NS / 2, kb = pr / NF, u = (pr / C::NDB) & 1, db = pr % C::NDB;
         mma_agpr<T>(acc[qb][db], x, pf[qb][kb][u]);
       }
 #pragma unroll
@@ -371,16 +380,27 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
   }
 }
 
-template <typename T>
-static hipError_t launch_fwd64_t(const FwdArgs& a, hipStream_t s) {
-  dim3 grid((a.N + Fwd64::BR - 1) / Fwd64::BR, a.H, a.B);
-  hipLaunchKernelGGL((fwd64_kernel<T>), grid, dim3(Fwd64::NT), 0, s, a);
+template <typename T, int D>
+static hipError_t launch_fwd64_t(bool causal, const FwdArgs& a, hipStream_t s) {
+  using C = Fwd64<D>;
+  dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);
+  if (causal)
+    hipLaunchKernelGGL((fwd64_kernel<T, D, true>), grid, dim3(C::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd64_kernel<T, D, false>), grid, dim3(C::NT), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd64(Dt dt, const FwdArgs& a, hipStream_t s) {
-  if (dt == Dt::bf16) return launch_fwd64_t<__bf16>(a, s);
-  if (dt == Dt::f16) return launch_fwd64_t<_Float16>(a, s);
+template <typename T>
+static hipError_t launch_fwd64_d(int d, bool causal, const FwdArgs& a, hipStream_t s) {
+  if (d == 64) return launch_fwd64_t<T, 64>(causal, a, s);
+  if (d == 128) return launch_fwd64_t<T, 128>(causal, a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd64(Dt dt, int d, bool causal, const FwdArgs& a, hipStream_t s) {
+  if (dt == Dt::bf16) return launch_fwd64_d<__bf16>(d, causal, a, s);
+  if (dt == Dt::f16) return launch_fwd64_d<_Float16>(d, causal, a, s);
   return hipErrorInvalidValue;
 }
 
