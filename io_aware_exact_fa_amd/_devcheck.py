@@ -28,6 +28,13 @@ on the installed one and tests the scanner itself.
    handles are weak symbols: an object file of an older source linked into
    the library would silently supply some of them, compiled against an older
    argument layout.  No kernel may appear in two code objects.
+
+3. Wait states before the MFMAs.  Some kernels issue MFMAs with AGPR
+   accumulators as inline assembly, which the hazard recognizer does not see
+   either: an MFMA must not read a VGPR (as A, B or C) sooner than two wait
+   states after a VALU instruction other than a dot product wrote it, or it
+   may read the old value.  Every MFMA of the library is checked (those the
+   compiler issued pass by construction).
 """
 from __future__ import annotations
 
@@ -125,10 +132,89 @@ def violations(lines, targets=frozenset()):
     return out
 
 
+VALU_VGPR_TO_MFMA = 2
+
+
+def vgprs(tok: str) -> set:
+    tok = tok.strip()
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m[1]), int(m[2]) + 1))
+    m = re.fullmatch(r"v(\d+)", tok)
+    return {int(m[1])} if m else set()
+
+
+def valu_vgpr_writes(ins: str) -> set:
+    """VGPRs a VALU instruction other than an MFMA or a dot product writes (its
+    first operand; compares and lane reads write SGPRs)."""
+    op, _, rest = ins.partition(" ")
+    if not op.startswith("v_") or op.startswith(("v_mfma", "v_dot", "v_cmp", "v_readlane",
+                                                 "v_readfirstlane")):
+        return set()
+    ops = [o.strip() for o in rest.split(",")] if rest else []
+    return vgprs(ops[0]) if ops else set()
+
+
+MFMA = re.compile(r"v_mfma\w*\s+(\S+),\s*(\S+),\s*(\S+),\s*(\S+)")
+
+
+def mfma_violations(lines, targets=frozenset()):
+    """(line index, MFMA, offending instruction, wait states between) for every
+    MFMA that reads a VGPR fewer than VALU_VGPR_TO_MFMA wait states after a
+    VALU write of it.  `targets` maps each branch target to the lines of the
+    branches that reach it; the scan back from an MFMA follows those branches
+    as well as the fall-through.  A target whose branches are not known (a
+    set) counts as a violation."""
+    out = []
+
+    def scan(i, ins, reads, j, ws, depth):
+        # Instructions j, j - 1, ... precede the MFMA, ws wait states already
+        # between.  Returns the offending instruction, or None.
+        while j >= 0 and ws < VALU_VGPR_TO_MFMA:
+            prev = lines[j]
+            if prev is None:
+                return None
+            if valu_vgpr_writes(prev) & reads:
+                return prev
+            ws += wait_states(prev)
+            if j in targets and ws < VALU_VGPR_TO_MFMA:
+                srcs = targets[j] if isinstance(targets, dict) else None
+                if srcs is None or depth > 8:
+                    return "a branch target"
+                for b in srcs:
+                    hit = scan(i, ins, reads, b, ws, depth + 1)
+                    if hit:
+                        return hit
+                if j > 0 and lines[j - 1] and lines[j - 1].startswith("s_branch"):
+                    return None   # no fall-through into the target
+            j -= 1
+        return None
+
+    for i, ins in enumerate(lines):
+        m = MFMA.match(ins) if ins else None
+        if not m:
+            continue
+        reads = vgprs(m[2]) | vgprs(m[3]) | vgprs(m[4])
+        if i in targets:
+            # The MFMA itself is a branch target: check its other entries too.
+            srcs = targets[i] if isinstance(targets, dict) else None
+            hit = "a branch target" if srcs is None else next(
+                (h for b in srcs for h in [scan(i, ins, reads, b, 0, 1)] if h), None)
+            if hit:
+                out.append((i, ins, hit, 0))
+                continue
+            if i > 0 and lines[i - 1] and lines[i - 1].startswith("s_branch"):
+                continue
+        hit = scan(i, ins, reads, i - 1, 0, 0)
+        if hit:
+            out.append((i, ins, hit, None))
+    return out
+
+
 def code_objects(lib_path: str, workdir: str):
     """Disassembly of every gfx950 code object in the library: a list of
     (function names, bare instructions with None at each function start,
-    indices of branch targets).  `workdir` receives the unbundled objects."""
+    {index of a branch target: indices of the branches to it}).  `workdir` receives the unbundled objects."""
     lib = os.path.join(workdir, "libfa.so")
     shutil.copy(lib_path, lib)
     subprocess.run([OBJDUMP, "--offloading", lib], cwd=workdir, check=True, capture_output=True)
@@ -139,7 +225,7 @@ def code_objects(lib_path: str, workdir: str):
     for obj in objs:
         dis = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", obj], check=True,
                              capture_output=True, text=True).stdout
-        names, lines, start, addr, branch = [], [], {}, {}, []
+        names, lines, start, addr, branch, branch_line = [], [], {}, {}, [], []
         for raw in dis.splitlines():
             m = re.match(r"^([0-9a-fA-F]+) <(.*)>:$", raw)
             if m:
@@ -155,11 +241,15 @@ def code_objects(lib_path: str, workdir: str):
                 t = re.search(r"<(\S+)\+0x([0-9a-fA-F]+)>\s*$", raw)
                 if ins.startswith(("s_branch", "s_cbranch")) and t:
                     branch.append((t[1], int(t[2], 16)))
+                    branch_line.append(len(lines))
                 lines.append(ins)
         missing = [(f, off) for f, off in branch if f in start and start[f] + off not in addr]
         if missing:
             raise RuntimeError(f"branch targets that start no parsed instruction: {missing[:3]}")
-        targets = frozenset(addr[start[f] + off] for f, off in branch if f in start)
+        targets = {}
+        for (f, off), src in zip(branch, branch_line):
+            if f in start:
+                targets.setdefault(addr[start[f] + off], []).append(src)
         out.append((names, lines, targets))
     return out
 
@@ -203,6 +293,14 @@ def check_library(lib_path: str) -> dict:
             f"device-code check: {len(bad)} of {n} LDS-direct loads too soon after an SGPR/M0 "
             f"write, in {where}; e.g. " + "; ".join(f"{p!r} {w} wait states before {ins!r}"
                                                      for _, _, ins, p, w in bad[:4]))
+    bad = [(function_at(names, lines, v[0]),) + v for names, lines, targets in objs
+           for v in mfma_violations(lines, targets)]
+    if bad:
+        where = sorted({f for f, *_ in bad})
+        raise RuntimeError(
+            f"device-code check: {len(bad)} MFMAs read a VGPR too soon after a VALU write, in "
+            f"{where}; e.g. " + "; ".join(f"{p!r} {w} wait states before {ins!r}"
+                                          for _, _, ins, p, w in bad[:4]))
     dup = kernels_in_several_objects(objs)
     if dup:
         raise RuntimeError(f"device-code check: {len(dup)} kernels defined in more than one code "

@@ -1347,6 +1347,472 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
     }
 }
 
+// dK/dV for 16-bit types with the tile stream pipelined across query tiles.
+//
+// The work split and data flow are those of bwd_dkdv16_kernel (4 waves x 32
+// keys; K and V of the lane's key in registers; the Q, dO, L2 and D tiles of
+// 64 queries copied straight into LDS; P recomputed from L2, dS = P (dP - D);
+// "FlashAttention-2: Faster Attention with Better Parallelism and Work
+// Partitioning", section "Backward Pass").  Three things differ:
+//   * The stream of query tile t runs four phases of MFMAs: A, S and dP of its
+//     query block 0; D', dV and dK of block 1 of tile t - 1; B, S and dP of its
+//     block 1; C, dV and dK of its block 0.  The P / dS arithmetic of block 1
+//     of tile t - 1 runs beside A and that of block 0 beside D' and B, so the
+//     vector work spreads over the whole tile instead of crowding its second
+//     half.
+//   * dK and dV accumulate in AGPRs (mma_agpr), which leaves the VGPRs to the
+//     S / dP of both blocks and to the state carried into the next tile.
+//   * Four buffers (tile t - 1 is still read during tile t), copies two tiles
+//     ahead, and the barrier before phase C.  Past it the first operands and
+//     D of tile t + 1 are read while tile t still runs, so a tile starts
+//     without waiting for LDS.
+// A run of tiles with one mask flag starts with a tile without phase D' and
+// ends with phase D' alone (drain).  The launcher takes it at d = 64, where a
+// tile has half the MFMAs per element of P of d = 128 and the spread-out
+// arithmetic pays; at d = 128 it measured slower than bwd_dkdv16_kernel.
+template <typename T, int D, bool CAUSAL, bool DROP, bool BSPARSE>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv16p_kernel(BwdArgs a) {
+  using C = Dkv16<D>;
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr int NB = 4;
+  // Dropout: per wave and 32-query block, the 16-bit uniforms of its 32 x 32
+  // (query, key) elements, 2 KB, after the tile buffers.
+  constexpr int DSCR = 2048;
+  __shared__ __attribute__((aligned(16))) char smem[NB * C::BUF + (DROP ? 8 * DSCR : 0)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, col = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntk = gridDim.x;
+  int kt, hd;
+  // Under the causal mask the key tiles near the start see the most queries and
+  // come first.
+  work_item<CAUSAL>(ntk, kt, hd);
+  hd = packed_head(a, hd, a.H / a.G);
+  const int k0 = kt * C::BKC;
+  // hd is a K/V head; its query heads hd G .. hd G + G - 1 run one after another.
+  const size_t kvhead = (size_t)hd;
+  const Span sp = span_of(a, hd * a.G);
+  const int N = sp.n;
+  if (k0 >= N) return;   // a tile past the end of a shorter sequence
+  const T* K = static_cast<const T*>(a.k) + sp.kv * D;
+  const T* V = static_cast<const T*>(a.v) + sp.kv * D;
+  const float c = a.scale * kLog2e;
+
+  const int kw = k0 + 32 * w;    // first key of this wave
+  const int myk = kw + col;      // this lane's key (column of S)
+  const int kg = min(myk, N - 1);
+  // K and V operands (B of S = Q K^T and of dP = dO V^T) of this lane's key,
+  // pinned in AGPRs.  V is negated (exact): the dP accumulators start at D
+  // and end at D - dP, so dS = -P (D - dP) needs one multiply, and the sign
+  // goes into dK's scale.
+  frag kf[C::NKS], vf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    kf[ks] = load_frag<T>(K + (size_t)kg * D + ks * 16 + 8 * h);
+    vf[ks] = neg_frag<T>(load_frag<T>(V + (size_t)kg * D + ks * 16 + 8 * h));
+  }
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    asm volatile("" : "+a"(kf[ks]));
+    asm volatile("" : "+a"(vf[ks]));
+  }
+  // dV (acc[0]) and dK (acc[1]) of the lane's key, in AGPRs.
+  f32x16 acc[2][D / 32];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[j][db] = f32x16{};
+  agpr_settle(acc);
+  // Window: queries [myk - wr, myk + wl] see this lane's key.  Query tiles of
+  // the workgroup: [lo, hi), of which [ml, mu) need no mask.
+  const int wl = a.wl, wr = CAUSAL ? min(a.wr, 0) : a.wr;
+  const TileRange tr = tile_range(k0, k0 + C::BKC - 1, N, wr, wl, C::BQ, true);
+  const uint32_t rspan = (uint32_t)wl + (uint32_t)wr;
+
+  const TileLds<D> lay(lane);
+  // Copies as in bwd_dkdv16_kernel: op j < NROW a group of RPC rows of Q (first
+  // half of the ops) or dO, wave w taking rows 16 w ..; ops NROW, NROW + 1 the
+  // tile's L2 and D, lane p holding query row_pi(p).
+  i32x4 rsq, rsg, rsl, rsd;
+  int qhead = 0;
+  constexpr int NROW = C::NLD - 2;
+  struct Bases { uint32_t row_lds, row_glb, buf_lds, ld_glb; };
+  auto bases = [&](int b, int qt) {
+    Bases x{lds_address(smem) + b * C::BUF + 16 * w * C::PB, (uint32_t)(qt * C::BQ + 16 * w) * (2 * D),
+            lds_address(smem) + b * C::BUF, (uint32_t)(qt * C::BQ) * 4};
+    asm volatile("" : "+s"(x.row_lds), "+s"(x.row_glb), "+s"(x.buf_lds), "+s"(x.ld_glb));
+    return x;
+  };
+  constexpr bool SAFE = DROP;
+  auto copy_op = [&](const Bases& x, int j) {
+    if (j < NROW) {
+      const int mat = j / (NROW / 2), r = C::RPC * (j % (NROW / 2));
+      copy16_to_lds<SAFE>(mat ? rsg : rsq, lay.c[(r >> 3) & 1], x.row_glb + r * (2 * D),
+                          x.row_lds + mat * C::TILE + r * C::PB);
+    } else {
+      copy_to_lds<SAFE>(j == NROW ? rsl : rsd, 4 * row_pi(lane), x.ld_glb,
+                        x.buf_lds + 2 * C::TILE + (j - NROW) * C::BQ * 4);
+    }
+  };
+
+  BlockSkip sk;
+  TileQueue tq;
+  // Start query head g of the group: resources and tile queue, then copy tiles
+  // t0 and t1 into buffers 0 and 1.
+  auto use_head = [&](int g) {
+    const size_t head = kvhead * a.G + g;
+    qhead = (int)head;
+    if constexpr (BSPARSE) {
+      sk = block_col(a, qhead, k0 / kBlockK, C::BQ);
+      tq.start(sk, tr.lo, tr.hi, lane);
+    } else {
+      tq.t[0] = tr.lo;
+      tq.t[1] = tr.lo + 1;
+    }
+    rsq = buffer_rsrc(static_cast<const T*>(a.q) + (sp.q + g * sp.hs) * D, (uint32_t)N * (2 * D));
+    rsg = buffer_rsrc(static_cast<const T*>(a.dout) + (sp.q + g * sp.hs) * D, (uint32_t)N * (2 * D));
+    rsl = buffer_rsrc(a.l2 + head * a.Np, (uint32_t)a.Np * 4);
+    rsd = buffer_rsrc(a.delta + head * a.Np, (uint32_t)a.Np * 4);
+    const Bases x0 = bases(0, tq.t[0]), x1 = bases(1, tq.t[1]);
+#pragma unroll
+    for (int j = 0; j < C::NLD; ++j) copy_op(x0, j);
+#pragma unroll
+    for (int j = 0; j < C::NLD; ++j) copy_op(x1, j);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  };
+
+  constexpr int NS = C::NS, NV = C::NV, NVB = C::NVB, NM = C::NM;
+  constexpr int PD = 4;                           // operands read ahead (slots)
+  // Phase starts (MFMA slots of one tile).
+  constexpr int P_D = NS, P_B = NS + NV, P_C = 2 * NS + NV;
+  constexpr int XB = P_C - 2;                     // the tile's barrier
+  // Element i of block 1 of the previous tile (its P and dS) at e1_slot(i):
+  // elements 0..7 before phase D' starts, 8..15 before its second half.
+  constexpr auto e1_slot = [](int i) { return (i * (NS + NVB - 2)) / 16; };
+  // D (the dP accumulator's start) of block 1 of this tile, after the previous
+  // tile's block 1 is done with the registers.
+  constexpr int DRL1 = NS + NVB - 1;
+  // Element i of block 0 of this tile: 0..7 before phase C, 8..15 before its
+  // second half.
+  constexpr int E0S = NS + NVB;
+  constexpr auto e0_slot = [](int i) { return E0S + (i * (P_C + NVB - 2 - E0S)) / 16; };
+  // D of block 0 of the next tile (past the barrier and past this tile's
+  // block 0 arithmetic), and L2 (with D under dropout) of block 1 of this tile
+  // for the next tile's arithmetic.
+  constexpr int DRL0 = e0_slot(15) + 2 > XB + 1 ? e0_slot(15) + 2 : XB + 1;
+  constexpr int L1S = P_C;
+  // Copy k of the tile two ahead, all before the barrier.
+  constexpr auto copy_slot = [](int k) { return 1 + (k * (XB - 3)) / C::NLD; };
+
+  // Carried from tile to tile: S and D - dP of both blocks (block 1's are the
+  // previous tile's until DRL1), the packed P and dS, L2 / D / keep bits of
+  // the previous tile's block 1, the operands read ahead.
+  f32x16 s[2], dp[2];
+  frag pa[2][2], sa[2][2];
+  f32x4 l4p[4];
+  float d4p[4][4];
+  uint32_t kb[2] = {0u, 0u};
+  frag opq[PD];
+  int step = 0, qprev = 0;
+
+  auto l2_at = [&](int boff) { return reinterpret_cast<const float*>(smem + boff + 2 * C::TILE); };
+  // D of the 16 queries of this lane's elements of block b, in element order.
+  auto load_d = [&](int boff, int b) -> f32x16 {
+    const float* dl = l2_at(boff) + C::BQ + b * 32 + 4 * h;
+    f32x16 r;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(dl + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[4 * g + e] = q[e];
+    }
+    return r;
+  };
+  // A operand of S (mat 0: Q rows) or dP (mat 1: dO rows), k step ks, query
+  // block qb, from the buffer at boff.
+  auto opA = [&](int boff, int qb, int ks, int mat) -> frag {
+    const int off = boff + mat * C::TILE + qb * 32 * C::PB;
+    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(smem + lay.A(ks) + off));
+  };
+  // B operand of dV (mat 1: dO^T) or dK (mat 0: Q^T): 16-query step u, head-dim
+  // block db, query block qb; two transposing reads.
+  auto opT = [&](int boff, int qb, int u, int db, int mat) -> frag {
+    s16x4 v[2];
+#pragma unroll
+    for (int rp = 0; rp < 2; ++rp) {
+      const int off = boff + mat * C::TILE + (qb * 32 + 16 * u + 8 * rp) * C::PB;
+      v[rp] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + lay.T(rp, db) + off));
+    }
+    return __builtin_bit_cast(frag, s16x8{v[0][0], v[0][1], v[0][2], v[0][3],
+                                          v[1][0], v[1][1], v[1][2], v[1][3]});
+  };
+  // P and dS of element i of one block: e = 2^(c S - L2) (zero outside the
+  // window when MASK), P = e (dropped and scaled under dropout), and -dS = P
+  // (D - dP) from the accumulator that holds D - dP.  Element i of lane half h
+  // is query 8 (i / 4) + 2 (i % 4) + h of its block.
+  auto elem = [&](auto maskc, int b, int i, float sv, float dpv, float l2v, float ddv, uint32_t kbits,
+                  int rl, f32x16& pv, f32x16& dsv) {
+    constexpr bool MASK = decltype(maskc)::value;
+    float e = exp2_fast(fmaf(sv, c, -l2v));
+    if (MASK) {
+      const int qe = b * 32 + 8 * (i / 4) + 2 * (i % 4);   // q - qi0 - h
+      if ((uint32_t)(qe - rl) > rspan) e = 0.f;
+    }
+    if constexpr (DROP) {
+      const bool keep = (kbits >> i) & 1u;
+      pv[i] = keep ? e * a.drop.scale : 0.f;
+      dsv[i] = e * (keep ? fmaf(a.drop.scale, dpv - ddv, ddv) : ddv);
+    } else {
+      pv[i] = e;
+      dsv[i] = e * dpv;
+    }
+  };
+  // Dropout keep bits of both blocks of query tile qi0 for this lane's key, bit
+  // i of block b for query 8 (i / 4) + 2 (i % 4) + h of the block (as in
+  // bwd_dkdv16_kernel: each lane makes the generator calls of one query and
+  // key half into the wave's LDS area and reads its own key column back).
+  auto keep_bits = [&](int qi0) {
+    if constexpr (DROP) {
+      const int kgrp = (kw >> 4) + h;
+      char* scr = smem + NB * C::BUF + w * 2 * DSCR;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+          uint32_t wv[4];
+          drop_call(a.drop, qhead, qi0 + 32 * b + col, kgrp, par, wv);
+          *reinterpret_cast<uint4*>(scr + b * DSCR + ((col * 2 + h) * 2 + par) * 16) =
+              uint4{wv[0], wv[1], wv[2], wv[3]};
+        }
+      __builtin_amdgcn_wave_barrier();
+      const int kp = col >> 4, kpar = col & 1, kt2 = (col & 15) >> 1;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ql = 8 * (i / 4) + 2 * (i % 4) + h;
+          const uint16_t u = *reinterpret_cast<const uint16_t*>(
+              scr + b * DSCR + ((ql * 2 + kp) * 2 + kpar) * 16 + 2 * kt2);
+          bits |= ((uint32_t)u < a.drop.keep_t ? 1u : 0u) << i;
+        }
+        kb[b] = bits;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+  // L2 (and D under dropout) of block 1 of the tile in buffer boff.
+  auto load_l4p = [&](int boff) {
+    const float* l2 = l2_at(boff);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l4p[g] = *reinterpret_cast<const f32x4*>(&l2[32 + 8 * g + 4 * h]);
+      if constexpr (DROP) {
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(&l2[C::BQ + 32 + 8 * g + 4 * h]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d4p[g][e] = dd[e];
+      }
+    }
+  };
+
+  // One query tile: qt at queue step `step` (buffer step & 3), tnext the tile
+  // two steps ahead (copied meanwhile).  PREV: phase D' and the arithmetic of
+  // block 1 of the previous tile (qprev) run in it.
+  auto tile = [&](int qt, int tnext, auto maskc, auto prevc) {
+    constexpr bool PREV = decltype(prevc)::value;
+    const int qi0 = qt * C::BQ;
+    const int bc = step & 3;
+    const int boff = bc * C::BUF, bpoff = ((step + 3) & 3) * C::BUF, bnoff = ((step + 1) & 3) * C::BUF;
+    const int rlo = myk - wr - qi0 - h, rlop = myk - wr - qprev * C::BQ - h;
+    const Bases xc = bases((step + 2) & 3, tnext);
+    const uint32_t kbp = kb[1];
+    keep_bits(qi0);
+    f32x4 l4[4];
+    float d40[4][4];
+    f32x16 p1, ds1, p0, ds0;
+    // Operand of slot m (m >= NM: slot m - NM of the next tile).
+    auto operand = [&](auto mc2) -> frag {
+      constexpr int mm = decltype(mc2)::value;
+      if constexpr (mm >= NM) {
+        return opA(bnoff, 0, (mm - NM) / 2, (mm - NM) & 1);
+      } else if constexpr (mm < P_D) {
+        return opA(boff, 0, mm / 2, mm & 1);
+      } else if constexpr (mm < P_B) {
+        if constexpr (PREV) {
+          constexpr int r = mm - P_D;
+          return opT(bpoff, 1, r / NVB, (r % NVB) / 2, (r & 1) ? 0 : 1);
+        } else {
+          return frag{};
+        }
+      } else if constexpr (mm < P_C) {
+        return opA(boff, 1, (mm - P_B) / 2, (mm - P_B) & 1);
+      } else {
+        constexpr int r = mm - P_C;
+        return opT(boff, 0, r / NVB, (r % NVB) / 2, (r & 1) ? 0 : 1);
+      }
+    };
+    static_for<0, NM>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+#pragma unroll
+      for (int k = 0; k < C::NLD; ++k)
+        if (m == copy_slot(k)) copy_op(xc, k);
+      if constexpr (m == XB) {
+        // Tile t + 1 (copied during the previous tile) must have landed; the
+        // copies of t + 2 may still be in flight.  Past the barrier every wave
+        // is done with tile t - 1 and may read tile t + 1.
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));
+        __syncthreads();
+      }
+      // L2 of one element group of block 0, PD slots before first use.
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (m == e0_slot(4 * g) - PD) {
+          const float* l2 = l2_at(boff);
+          l4[g] = *reinterpret_cast<const f32x4*>(&l2[8 * g + 4 * h]);
+          if constexpr (DROP) {
+            const f32x4 dd = *reinterpret_cast<const f32x4*>(&l2[C::BQ + 8 * g + 4 * h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d40[g][e] = dd[e];
+          }
+        }
+      if constexpr (m == DRL1) dp[1] = load_d(boff, 1);
+      if constexpr (m == L1S) load_l4p(boff);
+      if constexpr (m == DRL0) dp[0] = load_d(bnoff, 0);
+      const frag x = opq[m % PD];
+      if constexpr ((m & 1) && m + PD - 1 < NM + PD) {
+        opq[(m + PD) % PD] = operand(std::integral_constant<int, m + PD>{});
+        asm volatile("" ::: "memory");
+        opq[(m + PD - 1) % PD] = operand(std::integral_constant<int, m + PD - 1>{});
+      }
+      if constexpr (m < P_D) {
+        constexpr int ks = m / 2;
+        if constexpr (m & 1) dp[0] = M::mma(x, vf[ks], dp[0]);
+        else s[0] = M::mma(x, kf[ks], ks == 0 ? f32x16{} : s[0]);
+      } else if constexpr (m < P_B) {
+        if constexpr (PREV) {
+          constexpr int r = m - P_D, u = r / NVB, db = (r % NVB) / 2;
+          if constexpr (r & 1) mma_agpr<T>(acc[1][db], sa[1][u], x);
+          else mma_agpr<T>(acc[0][db], pa[1][u], x);
+        }
+      } else if constexpr (m < P_C) {
+        constexpr int ks = (m - P_B) / 2;
+        if constexpr ((m - P_B) & 1) dp[1] = M::mma(x, vf[ks], dp[1]);
+        else s[1] = M::mma(x, kf[ks], ks == 0 ? f32x16{} : s[1]);
+      } else {
+        constexpr int r = m - P_C, u = r / NVB, db = (r % NVB) / 2;
+        if constexpr (r & 1) mma_agpr<T>(acc[1][db], sa[0][u], x);
+        else mma_agpr<T>(acc[0][db], pa[0][u], x);
+      }
+      if constexpr (PREV) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (m == e1_slot(i)) {
+            elem(maskc, 1, i, s[1][i], dp[1][i], l4p[i / 4][i % 4], DROP ? d4p[i / 4][i % 4] : 0.f, kbp,
+                 rlop, p1, ds1);
+            if ((i + 1) % 8 == 0) {
+              pa[1][i / 8] = pack_frag<T>(p1, i / 8);
+              sa[1][i / 8] = pack_frag<T>(ds1, i / 8);
+            }
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (m == e0_slot(i)) {
+          elem(maskc, 0, i, s[0][i], dp[0][i], l4[i / 4][i % 4], DROP ? d40[i / 4][i % 4] : 0.f, kb[0], rlo,
+               p0, ds0);
+          if ((i + 1) % 8 == 0) {
+            pa[0][i / 8] = pack_frag<T>(p0, i / 8);
+            sa[0][i / 8] = pack_frag<T>(ds0, i / 8);
+          }
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    qprev = qt;
+    ++step;
+  };
+  // Phase D' of the last tile of a run, with its block 1 arithmetic first.
+  auto drain = [&](auto maskc) {
+    const int bpoff = ((step + 3) & 3) * C::BUF;
+    const int rlop = myk - wr - qprev * C::BQ - h;
+    f32x16 p1, ds1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      elem(maskc, 1, i, s[1][i], dp[1][i], l4p[i / 4][i % 4], DROP ? d4p[i / 4][i % 4] : 0.f, kb[1], rlop,
+           p1, ds1);
+      if ((i + 1) % 8 == 0) {
+        pa[1][i / 8] = pack_frag<T>(p1, i / 8);
+        sa[1][i / 8] = pack_frag<T>(ds1, i / 8);
+      }
+    }
+    // The packs stay above this point, and an MFMA reads a VGPR no sooner
+    // than two wait states after a VALU instruction wrote it.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 1");
+    static_for<0, NV>([&](auto mc) {
+      constexpr int r = decltype(mc)::value, u = r / NVB, db = (r % NVB) / 2;
+      const frag x = opT(bpoff, 1, u, db, (r & 1) ? 0 : 1);
+      if constexpr (r & 1) mma_agpr<T>(acc[1][db], sa[1][u], x);
+      else mma_agpr<T>(acc[0][db], pa[1][u], x);
+    });
+  };
+  // A run of tiles [.., end) with one mask flag, the queue at its first tile.
+  auto run = [&](int end, auto maskc) {
+    if constexpr (BSPARSE) {
+      if (tq.t[0] >= end) return;
+      tile(tq.t[0], tq.t[2], maskc, std::false_type{});
+      tq.advance(sk, tr.hi, lane);
+      for (; tq.t[0] < end; tq.advance(sk, tr.hi, lane)) tile(tq.t[0], tq.t[2], maskc, std::true_type{});
+    } else {
+      int qt = tq.t[0];
+      if (qt >= end) return;
+      tile(qt, qt + 2, maskc, std::false_type{});
+      for (++qt; qt < end; ++qt) tile(qt, qt + 2, maskc, std::true_type{});
+      tq.t[0] = qt;
+    }
+    drain(maskc);
+  };
+
+  for (int g = 0; g < a.G; ++g) {
+    use_head(g);
+    step = 0;
+    // The first tile's first operands and D.
+    static_for<0, PD>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      opq[m] = opA(0, 0, m / 2, m & 1);
+    });
+    dp[0] = load_d(0, 0);
+    // Tiles [lo, ml) and [mu, hi) need masks in some key column (the causal
+    // diagonal and the window's near edge, its far edge); [ml, mu) none, rows
+    // past N included (their L2 is +inf).
+    run(tr.ml, std::true_type{});
+    run(tr.mu, std::false_type{});
+    run(tr.hi, std::true_type{});
+    // No copy may still be writing LDS when the next head starts or the
+    // workgroup ends, and every wave is done with the buffers.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+
+  // Epilogue: lane (col = d, h) holds keys kw + 8(i/4) + 4h + i%4.
+  agpr_settle(acc);
+  T* dK = static_cast<T*>(a.dk) + sp.kv * D;
+  T* dV = static_cast<T*>(a.dv) + sp.kv * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kw + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (key < N) {
+        const size_t off = (size_t)key * D + db * 32 + col;
+        dK[off] = (T)(acc[1][db][i] * -a.scale);   // holds -dS^T Q
+        dV[off] = (T)acc[0][db][i];
+      }
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 
 template <typename T, int D, bool CAUSAL, bool DROP>
@@ -1359,10 +1825,22 @@ static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
   } else if (step == BwdStep::dkdv) {
     if constexpr (sizeof(T) == 2) {
       dim3 grid((a.N + Dkv16<D>::BKC - 1) / Dkv16<D>::BKC, a.H / a.G, a.B);
-      if (a.bm.mask)
-        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL, DROP, true>), grid, dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL, DROP, false>), grid, dim3(256), 0, s, a);
+      // d = 64: the pipelined kernel (same-process A/B on one MI355X: 11 %
+      // faster on b8h16n1024d64 and b1h16n16384d64 causal).  d = 128 keeps
+      // the single-tile stream, which measured 2 % faster than the pipelined
+      // one on b2h32n8192d128 and b4h32n4096d128 causal (and whose dropout
+      // instance fits beside three buffers only).
+      if constexpr (D == 64) {
+        if (a.bm.mask)
+          hipLaunchKernelGGL((bwd_dkdv16p_kernel<T, D, CAUSAL, DROP, true>), grid, dim3(256), 0, s, a);
+        else
+          hipLaunchKernelGGL((bwd_dkdv16p_kernel<T, D, CAUSAL, DROP, false>), grid, dim3(256), 0, s, a);
+      } else {
+        if (a.bm.mask)
+          hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL, DROP, true>), grid, dim3(256), 0, s, a);
+        else
+          hipLaunchKernelGGL((bwd_dkdv16_kernel<T, D, CAUSAL, DROP, false>), grid, dim3(256), 0, s, a);
+      }
     } else {
       dim3 grid((a.N + DkvTile<T, D>::BKC - 1) / DkvTile<T, D>::BKC, a.H / a.G, a.B);
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, DROP>), grid, dim3(256), 0, s, a);

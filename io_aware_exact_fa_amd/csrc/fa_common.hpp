@@ -197,6 +197,36 @@ __device__ inline float half_sum(float x) {
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- AGPR accumulators
+
+// acc += A B on a 32 x 32 x 16 MFMA whose accumulator lives in AGPRs.  Issued
+// as inline assembly, so the compiler's hazard recognizer does not see it; the
+// kernels that use it keep the hazards on their side: nothing but these MFMAs
+// touches the accumulators between agpr_settle() calls, and A and B are VGPRs
+// the compiler waits for (LDS reads) or that were written many instructions
+// earlier (packed P~, P, dS).  Successive MFMAs on one accumulator (full
+// overlap of the source C with the previous result) need no wait states.
+template <typename T> __device__ inline void mma_agpr(f32x16& acc, const typename Mfma<T>::frag& a,
+                                                      const typename Mfma<T>::frag& b);
+template <> __device__ inline void mma_agpr<__bf16>(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+template <> __device__ inline void mma_agpr<_Float16>(f32x16& acc, const f16x8& a, const f16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last mma_agpr and a VALU access (read or write) of
+// its accumulators, and between a VALU write of them and the next mma_agpr:
+// 20 (a 32 x 32 MFMA's result is readable 18 wait states after it issues).
+__device__ inline void agpr_settle(f32x16 (&acc)[2][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                 "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]));
+}
+__device__ inline void agpr_settle(f32x16 (&acc)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[1][0]), "+a"(acc[1][1]));
+}
+
 // ---------------------------------------------------------------- register transposes
 
 // Four rows of 16 bytes (rows = consecutive keys or queries, 16 bytes = 16/sizeof(T)

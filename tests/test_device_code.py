@@ -2,10 +2,11 @@
 
 The checks themselves live in ``io_aware_exact_fa_amd/_devcheck.py``, which
 ``build()`` runs on every freshly linked library before installing it (see
-that module for the two rules: wait states before the inline-asm LDS-direct
-copies, one definition per kernel).  Here: the scanner flags the hazards it
-is meant to flag, the installed library passes both checks, and ``build()``
-refuses a library that fails them."""
+that module for the rules: wait states before the inline-asm LDS-direct
+copies, one definition per kernel, wait states between a VALU write and an
+MFMA reading it).  Here: the scanners flag the hazards they are meant to
+flag, the installed library passes the checks, and ``build()`` refuses a
+library that fails them."""
 import importlib.util
 import os
 
@@ -30,6 +31,7 @@ _devcheck = _by_path("_devcheck")
 _DMA, OBJDUMP = _devcheck.DMA, _devcheck.OBJDUMP
 code_objects, kernels_in_several_objects = _devcheck.code_objects, _devcheck.kernels_in_several_objects
 violations = _devcheck.violations
+mfma_violations = _devcheck.mfma_violations
 
 
 def test_scanner_flags_the_hazards():
@@ -53,6 +55,36 @@ def test_scanner_flags_the_hazards():
     assert violations(["v_cmp_eq_u32_sdwa s[0:1], v1, v2 src0_sel:WORD_0", "s_nop 1", load])
     assert not violations(["v_add_u32_e32 v1, s3, v2", load])          # an SGPR source only
     assert not violations(["s_mov_b32 s3, 0", load])                  # SALU -> VMEM: no wait
+
+
+def test_mfma_scanner_flags_the_hazards():
+    """A packed P written by the VALU one wait state before the MFMA that reads
+    it as A is flagged, as are B and C operands and the last register of a
+    range; two wait states (or a dot product, or an LDS load) are not."""
+    mfma = "v_mfma_f32_32x32x16_bf16 a[32:47], v[4:7], v[0:3], a[32:47]"
+    assert mfma_violations(["v_cvt_pk_bf16_f32 v4, v13, v15", "s_waitcnt lgkmcnt(0)", mfma])
+    assert mfma_violations(["v_cvt_pk_bf16_f32 v7, v13, v15", mfma])
+    assert mfma_violations(["v_mov_b32_e32 v2, 0", mfma])
+    assert mfma_violations(["v_add_f32_e32 v20, v1, v2",
+                            "v_mfma_f32_32x32x16_bf16 v[20:35], v[4:7], v[0:3], v[20:35]"])
+    assert not mfma_violations(["v_cvt_pk_bf16_f32 v4, v13, v15", "s_nop 1", mfma])
+    assert not mfma_violations(["v_cvt_pk_bf16_f32 v4, v13, v15", "v_add_f32_e32 v9, v1, v2",
+                                "v_mul_f32_e32 v10, v1, v2", mfma])
+    assert not mfma_violations(["v_dot2c_f32_bf16_e32 v4, v1, v2", mfma])
+    assert not mfma_violations(["ds_read_b64_tr_b16 v[0:1], v29 offset:4096", mfma])
+    assert not mfma_violations(["v_cvt_pk_bf16_f32 v8, v13, v15", mfma])       # another VGPR
+    assert mfma_violations(["s_nop 1", "s_nop 0", mfma], targets={1})        # reached by a branch
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libfa.so not built")
+@pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="llvm-objdump not installed")
+def test_every_mfma_has_its_wait_states(tmp_path):
+    objs = code_objects(LIB, str(tmp_path))
+    n = sum(1 for _, lines, _ in objs for ins in lines if ins and _devcheck.MFMA.match(ins))
+    assert n > 1000, f"only {n} MFMAs found: the disassembly was not parsed"
+    bad = [v for _, lines, targets in objs for v in mfma_violations(lines, targets)]
+    assert not bad, f"{len(bad)} of {n} MFMAs too soon after a VALU write, e.g. " + \
+        "; ".join(f"{p!r} {w} wait states before {ins!r}" for _, ins, p, w in bad[:4])
 
 
 @pytest.mark.skipif(not os.path.exists(LIB), reason="libfa.so not built")
