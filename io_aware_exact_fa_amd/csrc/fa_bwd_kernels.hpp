@@ -655,6 +655,16 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   }
   const float l2 = a.l2[head * a.Np + qrow];       // LSE log2(e), +inf if no visible key
   const float dl = a.delta[head * a.Np + qrow];
+  // The dP^T accumulators start at -D (every element of a lane is this lane's
+  // query), so that they end at dP - D and dS = P (dP - D) is one multiply.
+  // Not in the d = 128 dropout instances, whose registers would spill.
+  constexpr bool DINIT = !DROP || D == 64;
+  f32x16 dinit;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dinit[i] = DINIT ? -dl : 0.f;
+  // Under dropout the kept dP is scaled: dS = P (scale (acc + D) - D) =
+  // P (scale acc + D (scale - 1)) for kept elements, -P D for dropped ones.
+  const float dls = DROP ? dl * (a.drop.scale - 1.f) : 0.f;
   // Visible keys of this lane's row: klo .. khi (window, causal and N).
   const int wr = CAUSAL ? min(a.wr, 0) : a.wr;
   const int khi = min(myq + wr, N - 1), klo = myq - a.wl;
@@ -747,11 +757,6 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
     frag sa[2][2];
     frag opq[PD];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = f32x16{};
-      dp[b] = f32x16{};
-    }
-#pragma unroll
     for (int m = 0; m < PD; m += 2) {
       opq[m + 1] = operand(m + 1);
       asm volatile("" ::: "memory");   // keeps the two operands' reads apart
@@ -772,8 +777,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
       }
       if constexpr (m < 2 * NS) {
         constexpr int kb = m / NS, ks = (m % NS) / 2;
-        if constexpr (m & 1) dp[kb] = M::mma(x, gf[ks], dp[kb]);
-        else s[kb] = M::mma(x, qf[ks], s[kb]);
+        if constexpr (m & 1) dp[kb] = M::mma(x, gf[ks], ks == 0 ? (DINIT ? dinit : f32x16{}) : dp[kb]);
+        else s[kb] = M::mma(x, qf[ks], ks == 0 ? f32x16{} : s[kb]);
       } else {
         constexpr int r = m - 2 * NS, kb = r / NQ, u = (r % NQ) / (D / 32), db = r % (D / 32);
         acc[db] = M::mma(x, sa[kb][u], acc[db]);
@@ -791,7 +796,6 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
               const int ke = b * 32 + 8 * (i / 4) + 2 * (i % 4);   // key - key0 - h
               if ((uint32_t)(ke - rlo) > rspan) e = 0.f;
             }
-            float dpi = dp[b][i];
             if constexpr (DROP) {
               // Elements 8 u .. 8 u + 7 are keys key0 + 32 b + 16 u + h + 2 t: one
               // generator call, made at the first of them.
@@ -804,9 +808,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
                   bits |= (((t & 1) ? (wv[t >> 1] >> 16) : (wv[t >> 1] & 0xFFFFu)) < a.drop.keep_t ? 1u : 0u) << t;
                 kbits[b] = (kbits[b] & ~(0xFFu << i)) | (bits << i);
               }
-              dpi = ((kbits[b] >> i) & 1u) ? dpi * a.drop.scale : 0.f;
+              if constexpr (DINIT)
+                ds[b][i] = e * (((kbits[b] >> i) & 1u) ? fmaf(a.drop.scale, dp[b][i], dls) : -dl);
+              else
+                ds[b][i] = e * ((((kbits[b] >> i) & 1u) ? dp[b][i] * a.drop.scale : 0.f) - dl);
+            } else {
+              ds[b][i] = e * dp[b][i];
             }
-            ds[b][i] = e * (dpi - dl);
             if ((i + 1) % 8 == 0) sa[b][i / 8] = pack_frag<T>(ds[b], i / 8);
           }
       __builtin_amdgcn_sched_barrier(0);
