@@ -718,8 +718,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
   // beside the S/dP MFMAs of block 1, that of block 1 beside dQ of block 0.
   constexpr int NS = C::NS, NQ = C::NQ, NM = C::NM;
   constexpr int PD = 4;
+  // Element i of block b: its exponential at elem_slot(b, i), the rest of its
+  // arithmetic one slot later, so that no instruction waits on the
+  // exponential's result in the slot that computes it.
   constexpr auto elem_slot = [](int b, int i) {
-    return b == 0 ? NS + 2 + (i * (NS - 2)) / 16 : 2 * NS + 1 + (i * (NQ - 2)) / 16;
+    return b == 0 ? NS + 2 + (i * (NS - 3)) / 16 : 2 * NS + 1 + (i * (NQ - 3)) / 16;
   };
   // NW = 8: copies of queue tile t2 spread over the stream; NW = 4: copies of
   // t1 early in the stream, since they must land before its end.
@@ -789,8 +792,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq16_kernel(BwdArgs a) {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (m == elem_slot(b, i)) {
-            float e = exp2_fast(fmaf(s[b][i], c, -l2));
+          if (m == elem_slot(b, i)) ds[b][i] = exp2_fast(fmaf(s[b][i], c, -l2));
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (m == elem_slot(b, i) + 1) {
+            float e = ds[b][i];
             if (MASK) {
               // Visible iff klo <= key <= khi, as one unsigned compare.
               const int ke = b * 32 + 8 * (i / 4) + 2 * (i % 4);   // key - key0 - h
@@ -1056,8 +1064,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
   // Element i of block b: the first 8 (P and dS for the first half of the
   // block's dV/dK MFMAs) done before those start, the last 8 overlapping
   // them, before the second half starts.
+  // The exponential of each element at elem_slot(b, i), the rest of its
+  // arithmetic one slot later (nothing waits on the exponential in its slot).
   constexpr auto elem_slot = [](int b, int i) {
-    return (b == 0 ? NS : 2 * NS) + 2 + (i * (NS + NVB - 2)) / 16;
+    return (b == 0 ? NS : 2 * NS) + 2 + (i * (NS + NVB - 3)) / 16;
   };
   // Slot of copy k of the next-but-one tile.
   constexpr auto copy_slot = [](int k) { return 1 + (k * (NM - 6)) / C::NLD; };
@@ -1232,8 +1242,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16_kernel(BwdArgs a) {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (m == elem_slot(b, i)) {
-            float e = exp2_fast(fmaf(s[b][i], c, -l4[b][i / 4][i % 4]));
+          if (m == elem_slot(b, i)) p[b][i] = exp2_fast(fmaf(s[b][i], c, -l4[b][i / 4][i % 4]));
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (m == elem_slot(b, i) + 1) {
+            float e = p[b][i];
             if (MASK) {
               // Visible iff myk - wr <= q <= myk + wl, as one unsigned compare.
               const int qe = b * 32 + 8 * (i / 4) + 2 * (i % 4);   // q - qi0 - h
