@@ -520,6 +520,40 @@ __device__ inline void copy16_to_lds(const i32x4& rsrc, uint32_t voff, uint32_t 
                  : "memory");
 }
 
+// Copy NG row groups of one matrix (1 KB each, 64 lanes x 16 bytes) that lie
+// 1 KB apart in global memory and STEP bytes apart in LDS, in one block: the
+// compiler sets M0 (the first group's LDS address) once, the scalar offset is
+// shared, and the instruction offset g STEP moves both addresses of group g.
+// Lane voff[g] makes up the difference of the two strides: with the
+// resource's base moved back by copy16_shift(NG, STEP) bytes, voff[g] = the
+// lane's offset in a group + copy16_shift - g (STEP - 1024), never negative.
+// Wait states and range checking as for copy16_to_lds.
+__host__ __device__ constexpr int copy16_shift(int NG, int STEP) { return (NG - 1) * (STEP - 1024); }
+
+template <int NG, int STEP, bool SAFE = false>
+__device__ inline void copy16_groups(const i32x4& rsrc, const uint32_t (&voff)[NG], uint32_t soff,
+                                     uint32_t lds) {
+  static_assert((NG == 2 || NG == 4) && STEP >= 1024 && (NG - 1) * STEP < 4096,
+                "two or four groups within the 12-bit instruction offset");
+  if constexpr (NG == 2) {
+    asm volatile("s_nop %4\n\t"
+                 "buffer_load_dwordx4 %0, %2, %3 offen lds\n\t"
+                 "buffer_load_dwordx4 %1, %2, %3 offen offset:%5 lds"
+                 ::"v"(voff[0]), "v"(voff[1]), "s"(rsrc), "s"(soff), "n"(SAFE ? 4 : 0), "n"(STEP),
+                 "{m0}"(lds)
+                 : "memory");
+  } else {
+    asm volatile("s_nop %6\n\t"
+                 "buffer_load_dwordx4 %0, %4, %5 offen lds\n\t"
+                 "buffer_load_dwordx4 %1, %4, %5 offen offset:%7 lds\n\t"
+                 "buffer_load_dwordx4 %2, %4, %5 offen offset:%8 lds\n\t"
+                 "buffer_load_dwordx4 %3, %4, %5 offen offset:%9 lds"
+                 ::"v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rsrc), "s"(soff),
+                 "n"(SAFE ? 4 : 0), "n"(STEP), "n"(2 * STEP), "n"(3 * STEP), "{m0}"(lds)
+                 : "memory");
+  }
+}
+
 // ------------------------------------------------- tile layouts of the 16-bit kernels
 //
 // A tile holds rows of 2D bytes (D 16-bit elements) in LDS.  Two reads use it:

@@ -21,8 +21,10 @@
 // rule: "FlashAttention 원 논문 해부", section "두 tile을 한 row로 합치는 식";
 // rows split across waves: the FlashAttention-2 page, "Work Partitioning Between
 // Warps", split-Q).  Tiles are copied global -> LDS four buffers deep (the
-// copies of tile t + 3 spread over tile t's stream), visited through the tile
-// queue (window edges and N need masks; a block mask skips tiles).
+// copies of tile t + 3 in two blocks, K and V, during tile t's P~V MFMAs;
+// each block one M0 and scalar offset for all the wave's row groups), visited
+// through the tile queue (window edges and N need masks; a block mask skips
+// tiles).
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -46,6 +48,9 @@ struct Fwd64 {
   static constexpr int NM = NS + NV;
   static constexpr int RPC = TileLds<D>::ROWS_PER_COPY;
   static constexpr int NLD = 2 * BC / NW / RPC;  // copies per wave per tile
+  static constexpr int NG = NLD / 2;             // row groups per wave per matrix
+  static constexpr int STEP = RPC * PB;          // LDS bytes between row groups
+  static constexpr int SHIFT = copy16_shift(NG, STEP);
   static constexpr int NA = NS / 2;              // slots of the row max
 };
 
@@ -114,15 +119,18 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
   tq.start(sk, tr.lo, tr.hi, lane);
 
   const TileLds<D> lay(lane);
-  const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
-  const i32x4 rsv = buffer_rsrc(V, (uint32_t)N * (2 * D));
-  // Copy k (< NLD) of key tile t into buffer b: the row groups of K that
-  // start at 16 w + RPC j (k = j < NLD / 2), then those of V.
-  auto copy_op = [&](int b, int t, int k) {
-    const int mat = k / (C::NLD / 2), r = 16 * w + C::RPC * (k % (C::NLD / 2));
-    const uint32_t base = lds_address(smem) + b * C::BUF + mat * C::TILE;
-    copy16_to_lds(mat ? rsv : rsk, lay.c[(r >> 3) & 1], (uint32_t)(t * C::BC + r) * (2 * D),
-                  base + r * C::PB);
+  // The resources start SHIFT bytes before K and V (see copy16_groups).
+  const i32x4 rsk = buffer_rsrc(reinterpret_cast<const char*>(K) - C::SHIFT, (uint32_t)N * (2 * D) + C::SHIFT);
+  const i32x4 rsv = buffer_rsrc(reinterpret_cast<const char*>(V) - C::SHIFT, (uint32_t)N * (2 * D) + C::SHIFT);
+  // Lane offsets of the wave's row groups g (rows 16 w + RPC g ..).
+  uint32_t voff[C::NG];
+#pragma unroll
+  for (int g = 0; g < C::NG; ++g) voff[g] = lay.c[((C::RPC * g) >> 3) & 1] + C::SHIFT - g * (C::STEP - 1024);
+  // Copy of matrix mat (0: K, 1: V) of key tile t into buffer b: the wave's
+  // NG row groups, rows 16 w .. 16 w + 15.
+  auto copy_op = [&](int b, int t, int mat) {
+    copy16_groups<C::NG, C::STEP>(mat ? rsv : rsk, voff, (uint32_t)(t * C::BC + 16 * w) * (2 * D),
+                                  lds_address(smem) + b * C::BUF + mat * C::TILE + 16 * w * C::PB);
   };
   // Operand of MFMA pair p (two MFMAs, query blocks A and B): p < NS / 2: K
   // fragment of k step p / 2, key block p % 2; else V^T fragment of pair
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
 #pragma unroll
   for (int t = 0; t < 3; ++t)
 #pragma unroll
-    for (int k = 0; k < C::NLD; ++k) copy_op(t, tq.t[t], k);
+    for (int mat = 0; mat < 2; ++mat) copy_op(t, tq.t[t], mat);
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // t2 may still be in flight
   __syncthreads();
   // S^T of the current tile and of the next one, [query block][key block];
@@ -191,7 +199,8 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
     const int last = NS + NF * f - 1;             // the slot before the first use
     return first + (j * (last - first)) / 16;
   };
-  constexpr auto copy_slot = [](int k) { return NS + (k * (NM - NS)) / C::NLD; };
+  // Copies of K and of V of the tile three ahead.
+  constexpr auto copy_slot = [](int mat) { return NS + (mat * (NM - NS)) / 2; };
 
   int b0 = 0;   // buffer of tile t0
   auto iteration = [&](const TileQueue& q, auto maskc, f32x16 (&sc)[2][2], f32x16 (&sn)[2][2]) {
@@ -229,8 +238,8 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
         mma_agpr<T>(acc[qb][db], x, pf[qb][kb][u]);
       }
 #pragma unroll
-      for (int k = 0; k < C::NLD; ++k)
-        if (m == copy_slot(k)) copy_op(bc, q.t[3], k);
+      for (int mat = 0; mat < 2; ++mat)
+        if (m == copy_slot(mat)) copy_op(bc, q.t[3], mat);
 #pragma unroll
       for (int e = 0; e < 64; ++e)
         if (m == max_slot(e)) {
