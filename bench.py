@@ -297,6 +297,25 @@ KERNEL_NAMES = {"fwd": "fwd16_kernel", "pre": "bwd_pre_kernel", "dkdv": "bwd_dkd
                 "dqfin": "bwd_dqfin_kernel"}
 
 
+def kernel_name(key: str, w) -> str:
+    """The kernel the library launches for step `key` of workload w (its
+    launchers choose by dtype, head dimension, mask, dropout and length)."""
+    wide = w.dtype != "f32"
+    drop = bool(getattr(w, "dropout", ())) and w.dropout[0] > 0.0
+    if key == "fwd":
+        if not wide:
+            return "fwd_kernel"
+        if w.d == 64:
+            return "fwd_kernel" if drop else "fwd64_kernel"
+        n = w.max_s if hasattr(w, "max_s") else w.N   # a packed batch launches with its longest length
+        return "fwd64_kernel" if not (w.causal or drop) and n >= 2048 else "fwd16_kernel"
+    if key == "dkdv":
+        return ("bwd_dkdv16p_kernel" if w.d == 64 else "bwd_dkdv16_kernel") if wide else "bwd_dkdv_kernel"
+    if key == "dq":
+        return "bwd_dq16_kernel" if wide else "bwd_dq_kernel"
+    return KERNEL_NAMES[key]
+
+
 def time_dense(args, w, fa, steps=None):
     """Seeded inputs of a dense workload on the GPU, `args.warmup` untimed steps,
     then `steps` timed ones; one step = fa_fwd_gqa and the backward's launches
@@ -388,7 +407,7 @@ def kernel_entries(w, kms, peak):
         if key not in kms:
             continue
         t = kms[key] * 1e-3
-        out.append({"kernel": KERNEL_NAMES[key], "ms": round(kms[key], 4), "bound": "mfma",
+        out.append({"kernel": kernel_name(key, w), "ms": round(kms[key], 4), "bound": "mfma",
                     "algorithmic_tflop": round(alg[key] / 1e12, 4),
                     "executed_tflop": round(alg[key] * EXECUTED_RATIO[key] / 1e12, 4),
                     "achieved": round(alg[key] / t / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
@@ -406,7 +425,7 @@ def kernel_entries(w, kms, peak):
         if key not in kms:
             continue
         rate = hbm[key] / (kms[key] * 1e-3) / 1e9
-        out.append({"kernel": KERNEL_NAMES[key], "ms": round(kms[key], 4), "bound": "hbm",
+        out.append({"kernel": kernel_name(key, w), "ms": round(kms[key], 4), "bound": "hbm",
                     "bytes": hbm[key], "achieved": round(rate, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(rate / HBM_PEAK_GBS, 4)})
     return out
