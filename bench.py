@@ -306,7 +306,7 @@ def kernel_name(key: str, w) -> str:
         if not wide:
             return "fwd_kernel"
         if w.d == 64:
-            return "fwd_kernel" if drop else "fwd64_kernel"
+            return "fwd16_kernel"
         n = w.max_s if hasattr(w, "max_s") else w.N   # a packed batch launches with its longest length
         return "fwd64_kernel" if not (w.causal or drop) and n >= 2048 else "fwd16_kernel"
     if key == "dkdv":

@@ -408,7 +408,9 @@ struct Fwd16 {
 template <typename T, int D, bool CAUSAL, int NW, bool DROP>
 __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   using C = Fwd16<D, NW>;
-  static_assert(D == 128 && (NW == 4 || NW == 8), "fwd16_kernel is built for d = 128");
+  static_assert((D == 64 || D == 128) && (NW == 4 || NW == 8), "fwd16_kernel: d = 64 or 128");
+  // Row groups (one copy each) per wave and matrix: 16 rows of RPC each.
+  constexpr int RPC = TileLds<D>::ROWS_PER_COPY, GPW = 16 / RPC;
   using M = Mfma<T>;
   using frag = typename M::frag;
   __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF];
@@ -460,14 +462,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const TileLds<D> lay(lane);
-  // Copy of the 4-row group q of K (mat 0) or V (mat 1) of key tile t into
-  // buffer b.  Rows past N read as zero (and are masked through khi).
+  // Copy of the row group q (rows RPC q ..) of K (mat 0) or V (mat 1) of key
+  // tile t into buffer b.  Rows past N read as zero (and are masked through khi).
   const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
   const i32x4 rsv = buffer_rsrc(V, (uint32_t)N * (2 * D));
   auto copy_group = [&](int b, int mat, int t, int q) {
     const uint32_t base = lds_address(smem) + b * C::BUF + mat * C::TILE;
-    copy16_to_lds(mat ? rsv : rsk, lay.c[(q >> 1) & 1], (uint32_t)(t * C::BC + 4 * q) * (2 * D),
-                  base + q * 4 * C::PB);
+    copy16_to_lds(mat ? rsv : rsk, lay.c[((RPC * q) >> 3) & 1], (uint32_t)(t * C::BC + RPC * q) * (2 * D),
+                  base + q * RPC * C::PB);
   };
   // S^T MFMA m of a tile (m < NS): key block kb = m & 1, k step ks = m >> 1.
   auto opS = [&](int kboff, int m) -> frag {
@@ -496,22 +498,22 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   float l_run = 0.f;
 
   // Prologue (queue tiles t0, t1, t2): NW = 8: t0, t1, t2 into buffers 0, 1, 2
-  // (wave w copies groups 4 (w & 3) .. + 3 of K (w < 4) or V); NW = 4: K and V
-  // of t0 into buffer 0 and K of t1 into buffer 1 (wave w copies groups
-  // 4 w .. + 3 of each).  Then S of t0.
+  // (wave w copies the groups of rows 16 (w & 3) .. + 15 of K (w < 4) or V);
+  // NW = 4: K and V of t0 into buffer 0 and K of t1 into buffer 1 (wave w
+  // copies the groups of rows 16 w .. + 15 of each).  Then S of t0.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if constexpr (NW == 8) {
 #pragma unroll
     for (int t = 0; t < 3; ++t)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) copy_group(t, w >> 2, tq.t[t], 4 * (w & 3) + kk);
+      for (int kk = 0; kk < GPW; ++kk) copy_group(t, w >> 2, tq.t[t], GPW * (w & 3) + kk);
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // t2 may still be in flight
   } else {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      copy_group(0, 0, tq.t[0], 4 * w + kk);
-      copy_group(0, 1, tq.t[0], 4 * w + kk);
-      copy_group(1, 0, tq.t[1], 4 * w + kk);
+    for (int kk = 0; kk < GPW; ++kk) {
+      copy_group(0, 0, tq.t[0], GPW * w + kk);
+      copy_group(0, 1, tq.t[0], GPW * w + kk);
+      copy_group(1, 0, tq.t[1], GPW * w + kk);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
@@ -588,9 +590,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
 #pragma unroll
       for (int k = 0; k < C::NLD; ++k)
         if (m == copy_slot(k)) {
-          if constexpr (NW == 8) copy_group(bc, w >> 2, q.t[3], 4 * (w & 3) + k);
-          else if (k < 4) copy_group(q.s & 1, 0, q.t[2], 4 * w + k);
-          else copy_group((q.s + 1) & 1, 1, q.t[1], 4 * w + k - 4);
+          if constexpr (NW == 8) copy_group(bc, w >> 2, q.t[3], GPW * (w & 3) + k);
+          else if (k < GPW) copy_group(q.s & 1, 0, q.t[2], GPW * w + k);
+          else copy_group((q.s + 1) & 1, 1, q.t[1], GPW * w + k - GPW);
         }
 #pragma unroll
       for (int e = 0; e < 32; ++e)
@@ -728,17 +730,18 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   // copies half as much.
   const bool drop = a.drop.keep_t < 65536;
   [[maybe_unused]] constexpr Dt dt = std::is_same<T, __bf16>::value ? Dt::bf16 : Dt::f16;
-  if constexpr (sizeof(T) == 2 && D == 64) {
-    // d = 64 without dropout: 64 query rows per wave.
-    if (!drop) return launch_fwd64(dt, 64, CAUSAL, a, s);
-  }
   if constexpr (sizeof(T) == 2 && D == 128 && !CAUSAL) {
     // Without the causal mask and dropout, and with enough key tiles per
     // workgroup (measured: 2 % faster at N = 8192, 2 % slower at N = 1024):
     // 64 query rows per wave.
     if (!drop && a.N >= 2048) return launch_fwd64(dt, 128, false, a, s);
   }
-  if constexpr (sizeof(T) == 2 && D == 128) {
+  // 16-bit types otherwise (d = 128 causal or short, d = 64, dropout): 32 query
+  // rows per wave, two waves per SIMD.  At d = 64 this measured 9-10 % faster
+  // than 64 rows per wave (same-process A/B on b8h16n1024d64-f16 and
+  // b1h16n16384d64-f16 causal), the other wave hiding the softmax, which at
+  // d = 64 is twice the arithmetic per MFMA of d = 128.
+  if constexpr (sizeof(T) == 2) {
     constexpr int NW = CAUSAL ? 4 : 8;
     using C = Fwd16<D, NW>;
     dim3 grid((a.N + C::BR - 1) / C::BR, a.H, a.B);

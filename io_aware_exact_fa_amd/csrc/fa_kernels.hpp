@@ -222,8 +222,8 @@ __device__ inline Span span_of(const Args& a, int hd) {
 enum class Dt { f32 = 0, f16 = 1, bf16 = 2 };
 
 hipError_t launch_fwd(Dt dt, int d, bool causal, const FwdArgs& a, hipStream_t s);
-// The forward with 64 query rows per wave (fa_fwd64.hip): 16-bit types, d = 64
-// or 128, no dropout.
+// The forward with 64 query rows per wave (fa_fwd64.hip): 16-bit types,
+// d = 128, no dropout.
 hipError_t launch_fwd64(Dt dt, int d, bool causal, const FwdArgs& a, hipStream_t s);
 // The backward in three launches: D; dK and dV; dQ.  Only the fields each step
 // reads or writes need to be set.
