@@ -409,8 +409,10 @@ template <typename T, int D, bool CAUSAL, int NW, bool DROP>
 __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   using C = Fwd16<D, NW>;
   static_assert((D == 64 || D == 128) && (NW == 4 || NW == 8), "fwd16_kernel: d = 64 or 128");
-  // Row groups (one copy each) per wave and matrix: 16 rows of RPC each.
-  constexpr int RPC = TileLds<D>::ROWS_PER_COPY, GPW = 16 / RPC;
+  // Row groups (one copy each) per wave and matrix: 16 rows of RPC each, STEP
+  // bytes apart in LDS (see copy16_groups).
+  constexpr int RPC = TileLds<D>::ROWS_PER_COPY, GPW = 16 / RPC, STEP = RPC * C::PB;
+  constexpr int SHIFT = copy16_shift(GPW, STEP);
   using M = Mfma<T>;
   using frag = typename M::frag;
   __shared__ __attribute__((aligned(16))) char smem[C::NB * C::BUF];
@@ -462,14 +464,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
 
   // Lane parts of the LDS addresses (bytes from the start of a buffer).
   const TileLds<D> lay(lane);
-  // Copy of the row group q (rows RPC q ..) of K (mat 0) or V (mat 1) of key
-  // tile t into buffer b.  Rows past N read as zero (and are masked through khi).
-  const i32x4 rsk = buffer_rsrc(K, (uint32_t)N * (2 * D));
-  const i32x4 rsv = buffer_rsrc(V, (uint32_t)N * (2 * D));
-  auto copy_group = [&](int b, int mat, int t, int q) {
-    const uint32_t base = lds_address(smem) + b * C::BUF + mat * C::TILE;
-    copy16_to_lds(mat ? rsv : rsk, lay.c[((RPC * q) >> 3) & 1], (uint32_t)(t * C::BC + RPC * q) * (2 * D),
-                  base + q * RPC * C::PB);
+  // Copy of the GPW row groups of 16 rows starting at row r0 (a multiple of 16)
+  // of K (mat 0) or V (mat 1) of key tile t into buffer b, in one block.  Rows
+  // past N read as zero (and are masked through khi).  The resources start
+  // SHIFT bytes before K and V.
+  const i32x4 rsk = buffer_rsrc(reinterpret_cast<const char*>(K) - SHIFT, (uint32_t)N * (2 * D) + SHIFT);
+  const i32x4 rsv = buffer_rsrc(reinterpret_cast<const char*>(V) - SHIFT, (uint32_t)N * (2 * D) + SHIFT);
+  uint32_t voff[GPW];
+#pragma unroll
+  for (int g = 0; g < GPW; ++g) voff[g] = lay.c[((RPC * g) >> 3) & 1] + SHIFT - g * (STEP - 1024);
+  auto copy_rows = [&](int b, int mat, int t, int r0) {
+    copy16_groups<GPW, STEP>(mat ? rsv : rsk, voff, (uint32_t)(t * C::BC + r0) * (2 * D),
+                             lds_address(smem) + b * C::BUF + mat * C::TILE + r0 * C::PB);
   };
   // S^T MFMA m of a tile (m < NS): key block kb = m & 1, k step ks = m >> 1.
   auto opS = [&](int kboff, int m) -> frag {
@@ -504,17 +510,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if constexpr (NW == 8) {
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
-#pragma unroll
-      for (int kk = 0; kk < GPW; ++kk) copy_group(t, w >> 2, tq.t[t], GPW * (w & 3) + kk);
+    for (int t = 0; t < 3; ++t) copy_rows(t, w >> 2, tq.t[t], 16 * (w & 3));
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(C::NLD));   // t2 may still be in flight
   } else {
-#pragma unroll
-    for (int kk = 0; kk < GPW; ++kk) {
-      copy_group(0, 0, tq.t[0], GPW * w + kk);
-      copy_group(0, 1, tq.t[0], GPW * w + kk);
-      copy_group(1, 0, tq.t[1], GPW * w + kk);
-    }
+    copy_rows(0, 0, tq.t[0], 16 * w);
+    copy_rows(0, 1, tq.t[0], 16 * w);
+    copy_rows(1, 0, tq.t[1], 16 * w);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
   __syncthreads();
@@ -536,12 +537,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   constexpr auto exp_slot = [](int kb, int i) {
     return kb == 0 ? NA + 1 + (i * (NS - NA - 1)) / 16 : NS + (i * (NV / 2)) / 16;
   };
-  // NW = 8: the copies of queue tile t3 spread over the P~V MFMAs; NW = 4: the
-  // copies of the step (K of t2, V of t1) early in the stream, since they must
+  // NW = 8: the wave's block of queue tile t3 as the P~V MFMAs start; NW = 4:
+  // the step's blocks (K of t2, V of t1) early in the stream, since they must
   // land before its end.
-  constexpr auto copy_slot = [](int k) {
-    return NW == 8 ? NS + (k * NV) / C::NLD : 1 + 2 * k;
-  };
+  constexpr auto copy_slot = [](int k) { return NW == 8 ? NS : 1 + 2 * k; };
 
   int b0 = 0;   // buffer of tile t0 (NW = 8)
   // One step: S of queue tile t1 (into sn) with the softmax of t0 (S in sc),
@@ -588,11 +587,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
         acc[db] = M::mma(x, pf[kb][u], acc[db]);
       }
 #pragma unroll
-      for (int k = 0; k < C::NLD; ++k)
+      for (int k = 0; k < (NW == 8 ? 1 : 2); ++k)
         if (m == copy_slot(k)) {
-          if constexpr (NW == 8) copy_group(bc, w >> 2, q.t[3], GPW * (w & 3) + k);
-          else if (k < GPW) copy_group(q.s & 1, 0, q.t[2], GPW * w + k);
-          else copy_group((q.s + 1) & 1, 1, q.t[1], GPW * w + k - GPW);
+          if constexpr (NW == 8) copy_rows(bc, w >> 2, q.t[3], 16 * (w & 3));
+          else if (k == 0) copy_rows(q.s & 1, 0, q.t[2], 16 * w);
+          else copy_rows((q.s + 1) & 1, 1, q.t[1], 16 * w);
         }
 #pragma unroll
       for (int e = 0; e < 32; ++e)
