@@ -377,15 +377,17 @@ def test_large_gqa_sampled_groups(fa, w):
 # ------------------------------------------------------------------ the plain entry points
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_plain_entry_points_by_name(fa, dtype):
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 128), ("bf16", 64), ("f16", 64)])
+def test_plain_entry_points_by_name(fa, dtype, d):
     """fa_fwd, fa_bwd, the two-pass steps (fa_bwd_preprocess + fa_bwd_dkdv +
     fa_bwd_dq) and the one-pass steps (fa_bwd_preprocess + fa_bwd_dkdv_dq +
     fa_bwd_dq_finalize) called by those names through ctypes (not through their
     grouped forms), causal, ragged N = 333 over 3 heads of 2 batch entries:
     every element against the oracle; the two-pass steps bit for bit equal to
-    fa_bwd; the one-pass dK and dV too, its dQ up to the order of its sums."""
-    w = workloads.Workload(f"plain-{dtype}", 2, 3, 333, 128, dtype, True, seed=83)
+    fa_bwd; the one-pass dK and dV too (at d = 64 the two-pass dK/dV kernel is the
+    pipelined one, which accumulates in the same order), its dQ up to the order
+    of its sums."""
+    w = workloads.Workload(f"plain-{dtype}-d{d}", 2, 3, 333, d, dtype, True, seed=83)
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
     q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
