@@ -1399,10 +1399,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16p_kernel(BwdArgs a) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   constexpr int NB = 4;
-  // Dropout: per wave and 32-query block, the 16-bit uniforms of its 32 x 32
-  // (query, key) elements, 2 KB, after the tile buffers.
+  // Dropout: per wave, the 16-bit uniforms of the 32 x 32 (query, key)
+  // elements of one 32-query block, 2 KB, after the tile buffers (the two
+  // blocks of a tile use it in turn).
   constexpr int DSCR = 2048;
-  __shared__ __attribute__((aligned(16))) char smem[NB * C::BUF + (DROP ? 8 * DSCR : 0)];
+  __shared__ __attribute__((aligned(16))) char smem[NB * C::BUF + (DROP ? 4 * DSCR : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, col = lane & 31, h = lane >> 5;
@@ -1600,31 +1601,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv16p_kernel(BwdArgs a) {
   auto keep_bits = [&](int qi0) {
     if constexpr (DROP) {
       const int kgrp = (kw >> 4) + h;
-      char* scr = smem + NB * C::BUF + w * 2 * DSCR;
+      char* scr = smem + NB * C::BUF + w * DSCR;
+      const int kp = col >> 4, kpar = col & 1, kt2 = (col & 15) >> 1;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b) {
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
           uint32_t wv[4];
           drop_call(a.drop, qhead, qi0 + 32 * b + col, kgrp, par, wv);
-          *reinterpret_cast<uint4*>(scr + b * DSCR + ((col * 2 + h) * 2 + par) * 16) =
-              uint4{wv[0], wv[1], wv[2], wv[3]};
+          *reinterpret_cast<uint4*>(scr + ((col * 2 + h) * 2 + par) * 16) = uint4{wv[0], wv[1], wv[2], wv[3]};
         }
-      __builtin_amdgcn_wave_barrier();
-      const int kp = col >> 4, kpar = col & 1, kt2 = (col & 15) >> 1;
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
+        __builtin_amdgcn_wave_barrier();
         uint32_t bits = 0u;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int ql = 8 * (i / 4) + 2 * (i % 4) + h;
-          const uint16_t u = *reinterpret_cast<const uint16_t*>(
-              scr + b * DSCR + ((ql * 2 + kp) * 2 + kpar) * 16 + 2 * kt2);
+          const uint16_t u = *reinterpret_cast<const uint16_t*>(scr + ((ql * 2 + kp) * 2 + kpar) * 16 + 2 * kt2);
           bits |= ((uint32_t)u < a.drop.keep_t ? 1u : 0u) << i;
         }
         kb[b] = bits;
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_wave_barrier();
     }
   };
   // L2 (and D under dropout) of block 1 of the tile in buffer boff.
@@ -1851,9 +1848,8 @@ static hipError_t launch_bwd_t(BwdStep step, const BwdArgs& a, hipStream_t s) {
       // d = 64: the pipelined kernel (same-process A/B on one MI355X: 11 %
       // faster on b8h16n1024d64 and b1h16n16384d64 causal).  d = 128 keeps
       // the single-tile stream, which measured 2 % faster than the pipelined
-      // one on b2h32n8192d128 and b4h32n4096d128 causal (and whose dropout
-      // instance fits beside three buffers only).
-      if constexpr (D == 64) {
+      // one on b2h32n8192d128 and b4h32n4096d128 causal, except with dropout.
+      if constexpr (D == 64 || DROP) {
         if (a.bm.mask)
           hipLaunchKernelGGL((bwd_dkdv16p_kernel<T, D, CAUSAL, DROP, true>), grid, dim3(256), 0, s, a);
         else
