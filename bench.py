@@ -310,7 +310,7 @@ def kernel_name(key: str, w) -> str:
         n = w.max_s if hasattr(w, "max_s") else w.N   # a packed batch launches with its longest length
         return "fwd64_kernel" if not (w.causal or drop) and n >= 2048 else "fwd16_kernel"
     if key == "dkdv":
-        return ("bwd_dkdv16p_kernel" if w.d == 64 else "bwd_dkdv16_kernel") if wide else "bwd_dkdv_kernel"
+        return ("bwd_dkdv16p_kernel" if w.d == 64 or drop else "bwd_dkdv16_kernel") if wide else "bwd_dkdv_kernel"
     if key == "dq":
         return "bwd_dq16_kernel" if wide else "bwd_dq_kernel"
     return KERNEL_NAMES[key]
