@@ -502,6 +502,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
   // This lane's share of the running normalizer: the sum of P~ as rounded to T
   // for the MFMA, so that the weights of O sum to 1 exactly as used.
   float l_run = 0.f;
+  float nm_run = 0.f;            // -m_run, 0 while m_run is -inf
+  float thr_run = -INFINITY;     // m_run + kMaxSlack
 
   // Prologue (queue tiles t0, t1, t2): NW = 8: t0, t1, t2 into buffers 0, 1, 2
   // (wave w copies the groups of rows 16 (w & 3) .. + 15 of K (w < 4) or V);
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
     frag pf[2][2];
     sn[0] = f32x16{};
     sn[1] = f32x16{};
-    float mx = -INFINITY, m_new = m_run, nm = 0.f;
+    float mx = -INFINITY, m_new;   // m_new: set and used only when grow
     bool grow = false;
     // Masked tiles: visible element offsets (key - key0 - h) of this lane's row.
     const int rlo = klo - key0 - h;
@@ -607,13 +609,19 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
       if constexpr (m == NA) {
         // The reference max of the exponentials moves only when the max of
         // some row of the wave grew by more than kMaxSlack (log2 units), so
-        // P~ <= 2^kMaxSlack and most tiles skip the rescale.
-        mx = half_max(mx);
-        const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-        m_new = fmaxf(m_run, mt);
-        grow = __any(m_new > m_run + kMaxSlack);
-        const float ref = grow ? m_new : m_run;
-        nm = (ref == -INFINITY) ? 0.f : -ref;
+        // P~ <= 2^kMaxSlack and most tiles skip the rescale.  The test runs
+        // per lane, on its half of the row (c > 0: the same decision as on the
+        // exchanged row max); the exchange and the new reference only when
+        // some row grew.  Both rare branches are marked unlikely, so the
+        // common path runs straight through (a taken branch costs the wave
+        // its instruction fetch).
+        grow = __builtin_amdgcn_ballot_w64(mx * c > thr_run) != 0;
+        if (__builtin_expect(grow, 0)) {
+          const float mh = half_max(mx);
+          const float mt = (mh == -INFINITY) ? -INFINITY : mh * c;
+          m_new = fmaxf(m_run, mt);
+          nm_run = (m_new == -INFINITY) ? 0.f : -m_new;
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -621,7 +629,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
         for (int i = 0; i < 16; ++i)
           if (m == exp_slot(kb, i)) {
             const float xs = sc[kb][i];
-            float p = exp2_fast(fmaf(xs, c, nm));
+            float p = exp2_fast(fmaf(xs, c, nm_run));
             if constexpr (MASK) p = (xs == -INFINITY) ? 0.f : p;
             sc[kb][i] = p;
             if ((i + 1) % 8 == 0) {
@@ -649,12 +657,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
     auto rescale = [&]() {
-      if (grow) {
+      if (__builtin_expect(grow, 0)) {
         const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
         m_run = m_new;
+        thr_run = m_new + kMaxSlack;
       }
     };
     // With two waves on a SIMD (8-wave workgroups), the wave in the S half of

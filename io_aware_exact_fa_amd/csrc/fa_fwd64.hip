@@ -21,8 +21,9 @@
 // rule: "FlashAttention 원 논문 해부", section "두 tile을 한 row로 합치는 식";
 // rows split across waves: the FlashAttention-2 page, "Work Partitioning Between
 // Warps", split-Q).  Tiles are copied global -> LDS four buffers deep (the
-// copies of tile t + 3 in two blocks, K and V, during tile t's P~V MFMAs;
-// each block one M0 and scalar offset for all the wave's row groups), visited
+// copies of tile t + 3 in two blocks, K and V, among tile t's first MFMAs,
+// as soon as the barrier has freed their buffer; each block one M0 and
+// scalar offset for all the wave's row groups), visited
 // through the tile queue (window edges and N need masks; a block mask skips
 // tiles).
 #include "fa_common.hpp"
@@ -160,6 +161,8 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
   agpr_settle(acc);
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
+  float nm_run[2] = {0.f, 0.f};                  // -m_run, 0 while m_run is -inf
+  float thr_run[2] = {-INFINITY, -INFINITY};     // m_run + slack
 
   // Prologue: queue tiles t0, t1, t2 into buffers 0, 1, 2; then S^T of t0.
 #pragma unroll
@@ -199,8 +202,10 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
     const int last = NS + NF * f - 1;             // the slot before the first use
     return first + (j * (last - first)) / 16;
   };
-  // Copies of K and of V of the tile three ahead.
-  constexpr auto copy_slot = [](int mat) { return NS + (mat * (NM - NS)) / 2; };
+  // Copies of K and of V of the tile three ahead, early in the tile so that
+  // they have the most time to land (the barrier at the end of the previous
+  // tile freed their buffer).
+  constexpr auto copy_slot = [](int mat) { return 2 + 8 * mat; };
 
   int b0 = 0;   // buffer of tile t0
   auto iteration = [&](const TileQueue& q, auto maskc, f32x16 (&sc)[2][2], f32x16 (&sn)[2][2]) {
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) sn[qb][kb] = f32x16{};
-    float mx[2] = {-INFINITY, -INFINITY}, m_new[2] = {m_run[0], m_run[1]}, nm[2] = {0.f, 0.f};
+    float mx[2] = {-INFINITY, -INFINITY}, m_new[2];   // m_new: set and used only when grow
     bool grow = false;
     int rlo[2];
     uint32_t rspan[2];
@@ -250,21 +255,21 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
           }
           mx[eq] = fmaxf(mx[eq], sc[eq][kb][i]);
         }
+      // The growth test per lane (its half of the row against m + slack; c >
+      // 0, so the same decision as on the exchanged row max); the exchange
+      // and the new reference only when some row of the wave grew.  Both
+      // rare branches are marked unlikely, so the common path runs straight
+      // through (a taken branch costs this single wave per SIMD its fetch).
       if constexpr (m == NA) {
-        bool g = false;
-        float ref[2];
+        grow = __builtin_amdgcn_ballot_w64((mx[0] * c > thr_run[0]) || (mx[1] * c > thr_run[1])) != 0;
+        if (__builtin_expect(grow, 0)) {
 #pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          const float mh = half_max(mx[e2]);
-          const float mt = (mh == -INFINITY) ? -INFINITY : mh * c;
-          m_new[e2] = fmaxf(m_run[e2], mt);
-          g = g || (m_new[e2] > m_run[e2] + kMaxSlack64);
-        }
-        grow = __any(g);
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          ref[e2] = grow ? m_new[e2] : m_run[e2];
-          nm[e2] = (ref[e2] == -INFINITY) ? 0.f : -ref[e2];
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const float mh = half_max(mx[e2]);
+            const float mt = (mh == -INFINITY) ? -INFINITY : mh * c;
+            m_new[e2] = fmaxf(m_run[e2], mt);
+            nm_run[e2] = (m_new[e2] == -INFINITY) ? 0.f : -m_new[e2];
+          }
         }
       }
 #pragma unroll
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
           for (int i = 0; i < 16; ++i)
             if (m == exp_slot(eq, kb, i)) {
               const float xs = sc[eq][kb][i];
-              float pv = exp2_fast(fmaf(xs, c, nm[eq]));
+              float pv = exp2_fast(fmaf(xs, c, nm_run[eq]));
               if constexpr (MASK) pv = (xs == -INFINITY) ? 0.f : pv;
               sc[eq][kb][i] = pv;
               if ((i + 1) % 8 == 0) {
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
     auto rescale = [&]() {
-      if (grow) {
+      if (__builtin_expect(grow, 0)) {
         agpr_settle(acc);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -297,6 +302,7 @@ __global__ __launch_bounds__(256, 1) void fwd64_kernel(FwdArgs a) {
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) acc[qb][db] *= alpha;
           m_run[qb] = m_new[qb];
+          thr_run[qb] = m_new[qb] + kMaxSlack64;
         }
         agpr_settle(acc);
       }

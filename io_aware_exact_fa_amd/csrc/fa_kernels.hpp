@@ -91,7 +91,7 @@ struct BlockSkip {
   uint64_t bits = 0;
   // The first active tile >= t, or some tile >= end if there is none below end.
   __device__ int next(int t, int end, int lane) {
-    if (!base) return t;
+    if (__builtin_expect(!base, 1)) return t;   // no block mask: the loops' straight path
     while (t < end) {
       const int blk = t / tpb, c = blk >> 6;
       if (c != chunk) {
