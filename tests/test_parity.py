@@ -205,6 +205,37 @@ def test_peaked_rows_stress_rescaling(fa):
     compare(gpu_run(fa, inp, True, w.scale), inp, True, w.scale, "f16", tag="peaked")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d,causal,n", [(128, False, 2085), (128, True, 700), (64, False, 700),
+                                        (64, True, 700)])
+def test_rising_scores_rescale_every_tile(fa, dtype, d, causal, n):
+    """Keys along one direction with a norm that grows with the key index, so
+    that every 64-key tile raises each row's max by more than the forward's
+    rescale slack (2^8): the growth test, the half-row exchange and the rescale
+    run on every tile (the 64-row forward at d = 128 without the mask, the
+    32-row one otherwise), against the oracle on every element of O and LSE.
+    The forward alone: with every key along one direction, dQ = scale sum_j dS_ij
+    k_j cancels almost completely (the dS_ij of a row sum to zero and the k_j
+    differ little against their norm), so rounding dS to bf16 alone moves dQ by
+    about 14 % of its largest element on this input (fp64 emulation) -- a
+    property of the input, not of the path, which the backward tests cover."""
+    rng = np.random.default_rng(881 + d + n + int(causal))
+    B, H = 1, 2
+    u = np.ones(d)
+    gamma = 2.4 * math.sqrt(d) / 8    # s c grows by 15-30 log2 units per 64-key tile
+    alpha = (0.5 + gamma * np.arange(n) / d)[:, None]
+    qn = u[None, None, None, :] + 0.3 * rng.standard_normal((B, H, n, d))
+    kn = alpha[None, None] * u[None, None, None, :] + 0.3 * rng.standard_normal((B, H, n, d))
+    vn = rng.standard_normal((B, H, n, d))
+    don = rng.standard_normal((B, H, n, d))
+    t = TORCH[dtype]
+    inp = {name: torch.from_numpy(x).to(t) for name, x in (("q", qn), ("k", kn), ("v", vn), ("do", don))}
+    scale = 1.0 / math.sqrt(d)
+    say(f"case rising d={d} causal={causal} n={n} {dtype}")
+    compare(gpu_run(fa, inp, causal, scale, backward=False), inp, causal, scale, dtype,
+            backward=False, tag="rising")
+
+
 # ------------------------------------------------------------------ repeatability, workspace
 
 
