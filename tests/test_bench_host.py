@@ -48,3 +48,26 @@ def test_traffic_is_reported_only_for_the_profiled_source():
     else:
         assert bench.load_traffic(workload) is None
     assert bench.load_traffic("no-such-workload") is None
+
+
+def test_kernel_names_match_the_committed_traces():
+    """bench.py labels each step with the kernel the launchers pick
+    (kernel_name); every profiles/<workload>.md kernel trace, taken from a run of
+    the library, must list exactly those kernels for the forward, dK/dV and dQ
+    steps."""
+    import re
+    import workloads
+    names = dict(workloads.BY_NAME)
+    names.update(workloads.VARLEN_BY_NAME)
+    checked = 0
+    for fn in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        wname = fn[:-3]
+        if not fn.endswith(".md") or wname not in names:
+            continue
+        text = open(os.path.join(ROOT, "profiles", fn)).read()
+        traced = set(re.findall(r"^\| `(\w+_kernel)` \|", text, re.M))
+        w = names[wname]
+        for step in ("fwd", "dkdv", "dq"):
+            assert bench.kernel_name(step, w) in traced, (wname, step, traced)
+        checked += 1
+    assert checked >= 6
